@@ -1,0 +1,178 @@
+"""Pins for the oracle's decoder forward.
+
+The oracle computes a pass over several positions as a loop of single-token forwards.
+Here it is checked against an independent batched implementation built from torch's own
+CPU operators (``rms_norm``, ``scaled_dot_product_attention`` with an explicit causal
+mask, ``silu``): a library special case of the same definition.  Plus closed forms:
+RoPE at position 0 is the identity, q.k after RoPE depends only on the position
+difference, one visible key returns its value, and a trimmed cache reproduces a fresh run
+bit for bit ("Speculative Decoding on Apple Silicon: 119% Faster...", "Why this needed a
+patch to mlx_lm at all": a plain KV cache rolls back by slicing entries off its end).
+"""
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from oracle import numerics
+from oracle.model import KVCache, Spec, attend, forward_tokens, rmsnorm, rope
+from speculative_decoding_token_amd import synth
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.normal(0, 1, 10000), rng.normal(0, 1e-30, 100), rng.normal(0, 1e30, 100),
+                        [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, np.inf, -np.inf,
+                         3.3895313892515355e38]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = numerics.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(numerics.round_bf16(np.array([np.nan], dtype=np.float32))[0])
+
+
+def test_rmsnorm_matches_torch():
+    rng = np.random.default_rng(1)
+    x = rng.normal(0, 3, 257)
+    g = rng.normal(1, 0.1, 257)
+    ref = F.rms_norm(torch.from_numpy(x), (257,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(rmsnorm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_rope_closed_forms():
+    rng = np.random.default_rng(2)
+    x = rng.normal(0, 1, (3, 8))
+    np.testing.assert_allclose(rope(x, 0, 1e6), x, rtol=0, atol=0)
+    # head_dim 4, theta 1e6: pair (0,2) turns by pos*1, pair (1,3) by pos*1e-3
+    v = np.array([[1.0, 2.0, 3.0, 4.0]])
+    pos = 5
+    a0, a1 = 5.0, 5.0 * 1e6 ** (-2 / 4)
+    want = np.array([[1 * np.cos(a0) - 3 * np.sin(a0), 2 * np.cos(a1) - 4 * np.sin(a1),
+                      3 * np.cos(a0) + 1 * np.sin(a0), 4 * np.cos(a1) + 2 * np.sin(a1)]])
+    np.testing.assert_allclose(rope(v, pos, 1e6), want, rtol=1e-13)
+    # relative position: q.k depends only on the position difference
+    q = rng.normal(0, 1, (1, 64))
+    k = rng.normal(0, 1, (1, 64))
+    d1 = float(rope(q, 100, 1e6)[0] @ rope(k, 37, 1e6)[0])
+    d2 = float(rope(q, 1063, 1e6)[0] @ rope(k, 1000, 1e6)[0])
+    assert abs(d1 - d2) < 1e-9 * (1 + abs(d1))
+
+
+def test_attend_single_key_and_gqa_vs_torch():
+    rng = np.random.default_rng(3)
+    q = rng.normal(0, 1, (8, 16))
+    k = rng.normal(0, 1, (2, 1, 16))
+    v = rng.normal(0, 1, (2, 1, 16))
+    out = attend(q, k, v, 2)
+    for h in range(8):
+        np.testing.assert_allclose(out[h], v[h // 4, 0], rtol=0, atol=1e-15)
+    T = 37
+    k = rng.normal(0, 1, (2, T, 16))
+    v = rng.normal(0, 1, (2, T, 16))
+    out = attend(q, k, v, 2)
+    kt = torch.from_numpy(k).repeat_interleave(4, dim=0)     # [8, T, 16]
+    vt = torch.from_numpy(v).repeat_interleave(4, dim=0)
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], kt, vt)[:, 0, :]
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def torch_forward(spec: Spec, W, tokens, k_prefix=None, v_prefix=None, bf16=False):
+    """Batched causal forward over all positions at once, from torch CPU operators."""
+    def w(a):
+        return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+    def rb(t):
+        return t.to(torch.float32).to(torch.bfloat16).to(torch.float64) if bf16 else t
+
+    def rf(t):
+        return t.to(torch.float32).to(torch.float64) if bf16 else t
+
+    P = 0 if k_prefix is None else k_prefix.shape[2]
+    M = len(tokens)
+    T = P + M
+    hd, nq, nkv = spec.head_dim, spec.n_q_heads, spec.n_kv_heads
+    pos = torch.arange(P, T, dtype=torch.float64)
+    inv = spec.rope_theta ** (-2.0 * torch.arange(hd // 2, dtype=torch.float64) / hd)
+    ang = pos[:, None] * inv[None, :]
+    cos, sin = torch.cos(ang), torch.sin(ang)
+
+    def rot(x):  # x [M, heads, hd]
+        a, b = x[..., : hd // 2], x[..., hd // 2:]
+        c, s = cos[:, None, :], sin[:, None, :]
+        return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+    x = w(W["embed"])[torch.as_tensor(tokens, dtype=torch.long)]
+    mask = torch.ones(M, T, dtype=torch.bool).tril(diagonal=P)
+    for l, lw in enumerate(W["layers"]):
+        n1 = rb(F.rms_norm(x, (spec.d_model,), w(lw["attn_norm"]), eps=spec.rms_eps))
+        q = rb(rot((n1 @ w(lw["wq"]).T).view(M, nq, hd)))
+        k = rb(rot((n1 @ w(lw["wk"]).T).view(M, nkv, hd)))
+        v = rb((n1 @ w(lw["wv"]).T).view(M, nkv, hd))
+        kk, vv = k.transpose(0, 1), v.transpose(0, 1)
+        if P:
+            kk = torch.cat([torch.from_numpy(np.asarray(k_prefix[l], np.float64)), kk], dim=1)
+            vv = torch.cat([torch.from_numpy(np.asarray(v_prefix[l], np.float64)), vv], dim=1)
+        kk = kk.repeat_interleave(nq // nkv, dim=0)
+        vv = vv.repeat_interleave(nq // nkv, dim=0)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1), kk, vv, attn_mask=mask)
+        o = rb(o.transpose(0, 1).reshape(M, nq * hd))
+        x = rf(x + o @ w(lw["wo"]).T)
+        n2 = rb(F.rms_norm(x, (spec.d_model,), w(lw["ffn_norm"]), eps=spec.rms_eps))
+        h = rb(F.silu(n2 @ w(lw["wg"]).T) * (n2 @ w(lw["wu"]).T))
+        x = rf(x + h @ w(lw["wd"]).T)
+    xf = rb(F.rms_norm(x, (spec.d_model,), w(W["final_norm"]), eps=spec.rms_eps))
+    return (xf @ w(W["lm_head"]).T).to(torch.float32).numpy()
+
+
+def tiny(seed=0):
+    shape = synth.SHAPES["tiny_target"]
+    W = synth.weights_to_numpy(synth.make_weights(shape, seed))
+    return Spec.from_shape(shape), W
+
+
+def test_forward_matches_batched_torch_fp32_model():
+    spec, W = tiny()
+    toks = synth.make_tokens(21, spec.vocab, 0)
+    kv = KVCache(spec, 64)
+    got = forward_tokens(spec, W, kv, toks)
+    ref = torch_forward(spec, W, toks)
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+    assert kv.length == 21
+
+
+def test_forward_matches_batched_torch_bf16_gqa_with_prefix():
+    shape = synth.ModelShape("t", 2, 64, 4, 2, 16, 96, 50, "bf16")
+    W = synth.weights_to_numpy(synth.make_weights(shape, 3, std=0.2))
+    spec = Spec.from_shape(shape)
+    kp, vp = synth.make_kv_prefix(shape, 9, 3)
+    kp, vp = synth.to_numpy_f32(kp), synth.to_numpy_f32(vp)
+    kv = KVCache(spec, 32)
+    kv.load_prefix(kp, vp)
+    toks = synth.make_tokens(6, 50, 3)
+    got = forward_tokens(spec, W, kv, toks)
+    ref = torch_forward(spec, W, toks, kp, vp, bf16=True)
+    # same rounding points in the same places: identical on these seeded inputs
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err < 1e-6, err
+    # stored keys/values are bf16 values
+    k = kv.k[0][:, 9:15].astype(np.float32)
+    assert np.array_equal(numerics.round_bf16(k), k)
+
+
+def test_causal_invariance_and_trim_rollback():
+    spec, W = tiny(1)
+    prompt = list(synth.make_tokens(10, spec.vocab, 1))
+    kv = KVCache(spec, 64)
+    forward_tokens(spec, W, kv, prompt)
+    L = kv.length
+    rows_a = forward_tokens(spec, W, kv, [5, 6, 7, 8, 9])
+    kv.trim(L + 3)        # accept two drafts: keep t0, d1, d2
+    nxt = forward_tokens(spec, W, kv, [42])
+    # changing drafts after position j leaves rows <= j bit-identical
+    kv2 = KVCache(spec, 64)
+    forward_tokens(spec, W, kv2, prompt)
+    rows_b = forward_tokens(spec, W, kv2, [5, 6, 7, 100, 101])
+    assert np.array_equal(rows_a[:3], rows_b[:3])
+    # a fresh run that only ever saw the accepted tokens matches bit for bit
+    kv3 = KVCache(spec, 64)
+    forward_tokens(spec, W, kv3, prompt + [5, 6, 7])
+    fresh = forward_tokens(spec, W, kv3, [42])
+    assert np.array_equal(nxt, fresh)
