@@ -1,0 +1,222 @@
+"""Benchmark: speculative decoding on one MI355X, 8B-shaped target at K = 4.
+
+Workload: an 8B-shaped bf16 target (36 layers, d 4096, 32 q / 8 kv heads of 128, SwiGLU
+12288, vocab 151936) verifying K = 4 drafts from a 0.6B-shaped bf16 draft (28 layers,
+d 1024, 16 / 8 heads, SwiGLU 3072, tied head), batch 1, a synthetic 2048-token cache,
+random N(0, 0.02) weights.  A step is one cycle of the whole path: draft_step (K draft
+forwards), verify_step (one target forward over K+1 rows + truncation), accept, kv_trim,
+and the one device-to-host read of the emitted tokens.
+
+Prints one JSON line: accepted (emitted) tokens per second over the timed steps, the
+verify pass's HBM bytes per second against the 8 TB/s peak, the roofline of the dominant
+kernel (the gate/up projection + SwiGLU of the target), a teacher-forced upper bound
+(drafts = the target's own greedy continuation, every draft accepted), and the CPU
+oracle timed on a bounded sample of the same cycle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "accepted tokens/sec + verify-pass HBM GB/s (% peak), 8B-shape K=4, 1 GPU"
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--ctx", type=int, default=2048)
+    ap.add_argument("--sampled", action="store_true", help="temperature 1, top_k 20, top_p 0.95")
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-teacher", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="override target layers (debug only)")
+    return ap.parse_args()
+
+
+def verify_bytes(shape, k, L):
+    """Algorithmic HBM bytes of one verify: weights once, cache read and written, logits."""
+    M = k + 1
+    w = shape.streamed_params() * 2
+    kv_read = 2 * shape.n_layers * (L + M) * shape.kv_dim * 2
+    kv_write = 2 * shape.n_layers * M * shape.kv_dim * 2
+    logits = M * shape.vocab * 4
+    emb = M * shape.d_model * 2
+    return w + kv_read + kv_write + logits + emb
+
+
+def gate_up_bytes(shape, M):
+    d, f = shape.d_model, shape.d_ffn
+    return 2 * f * d * 2 + M * d * 2 + M * f * 2
+
+
+def cpu_baseline(tshape, dshape, tw, dw, K):
+    """The oracle (numpy, fp64) timed on one target row and one draft row of the cycle at
+    the full shapes; a cycle at acceptance 0 costs K+1 target rows and K draft rows."""
+    import numpy as np
+    import torch
+    from oracle import model as om
+
+    class Lazy(dict):
+        # host float32 copies of device weights, made when the oracle first reads them
+        def __getitem__(self, key):
+            v = dict.__getitem__(self, key)
+            if isinstance(v, torch.Tensor):
+                v = v.float().cpu().numpy()
+                dict.__setitem__(self, key, v)
+            return v
+
+    def lazy(w):
+        out = Lazy(embed=w["embed"], final_norm=w["final_norm"], lm_head=w["lm_head"])
+        out["layers"] = [Lazy(lw) for lw in w["layers"]]
+        return out
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    res = {}
+    for name, shape, w in (("target", tshape, tw), ("draft", dshape, dw)):
+        spec = om.Spec.from_shape(shape)
+        W = lazy(w)
+        for key in ("embed", "final_norm", "lm_head"):      # host copies, outside the timing
+            W[key]
+        for lw in W["layers"]:
+            for key in list(lw.keys()):
+                lw[key]
+        kv = om.KVCache(spec, 2)
+        # one row at position 0 of an empty cache: every weight is streamed, as in a verify
+        t0 = time.perf_counter()
+        om.forward_one(spec, W, kv, 0, 1)
+        res[name] = time.perf_counter() - t0
+        del W, kv
+    cycle = (K + 1) * res["target"] + K * res["draft"]
+    return {
+        "value": 1.0 / cycle, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+        "sample": (f"one target row ({res['target']:.1f} s) and one draft row ({res['draft']:.1f} s) at the full "
+                   f"shapes, scaled to a K={K} cycle at acceptance 0 (K+1 target rows + K draft rows, 1 token)"),
+        "os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              f"(multi-GPU sharding is design-only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from speculative_decoding_token_amd import runtime, synth
+
+    K = args.k
+    tshape = synth.SHAPES["qwen8b"]
+    if args.layers:
+        tshape = tshape.with_layers(args.layers)
+    dshape = synth.SHAPES["qwen0p6b"]
+    L = args.ctx
+    temp = 1.0 if args.sampled else 0.0
+    t_setup = time.perf_counter()
+    tw = synth.make_weights(tshape, 0, device="cuda")
+    dw = synth.make_weights(dshape, 0, device="cuda")
+    tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
+    dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
+    start = synth.make_tokens(2, tshape.vocab, 0, tag="start")
+    n_cycles = args.warmup + args.steps + args.profile_steps + 2
+    max_ctx = L + n_cycles * (K + 1) + 8
+    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=K)
+
+    def reset():
+        eng.load_prefix(0, 0, tk, tv, L)
+        eng.load_prefix(1, 0, dk, dv, L - 1)
+        eng.set_last(torch.tensor([int(start[1])], dtype=torch.int32, device="cuda"),
+                     torch.tensor([int(start[0])], dtype=torch.int32, device="cuda"))
+
+    reset()
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    ev = {}
+    rnd = 0
+    for _ in range(args.warmup):
+        eng.cycle(1, K, rnd)
+        rnd += 1
+    torch.cuda.synchronize()
+    emitted = accepted = 0
+    verify_ms = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        c = eng.cycle(1, K, rnd, events=ev)
+        emitted += len(c.tokens[0])
+        accepted += c.n[0]
+        verify_ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
+        rnd += 1
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tok_s = emitted / elapsed
+    verify_avg_ms = sum(verify_ms) / len(verify_ms)
+    vbytes = verify_bytes(tshape, K, L + args.warmup + 1)
+    verify_gbs = vbytes / (verify_avg_ms * 1e-3) / 1e9
+
+    # per-kernel durations with events around every launch (separate steps)
+    eng.profile(True)
+    for _ in range(args.profile_steps):
+        eng.cycle(1, K, rnd)
+        rnd += 1
+    prof = eng.profile_read()
+    eng.profile(False)
+    gu = prof.get("target.gate_up", {"ms": float("nan"), "launches": 1})
+    gu_ms = gu["ms"] / gu["launches"]
+    gu_bytes = gate_up_bytes(tshape, K + 1)
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+
+    # teacher-forced upper bound: drafts = the target's own greedy continuation
+    teacher = None
+    if not args.no_teacher and not args.sampled:
+        reset()
+        n_tf = args.steps * (K + 1)
+        plain, _ = eng.generate(n_tf + K + 1, 0)
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, cyc = eng.generate(n_tf, K, rnd0=rnd, teacher=plain[0])
+        torch.cuda.synchronize()
+        tf_elapsed = time.perf_counter() - t0
+        teacher = {"tok_s": n_tf / tf_elapsed, "cycles": len(cyc),
+                   "all_accepted": all(c.n[0] == K for c in cyc[:-1]),
+                   "matches_plain": toks[0] == plain[0][:n_tf]}
+
+    out = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"8B-shape bf16 target verify K={K} + 0.6B-shape draft, batch 1, "
+                               f"KV context {L}, {'sampled T=1 top_k 20 top_p 0.95' if args.sampled else 'greedy'}, "
+                               f"random N(0,0.02) weights" + (f", {tshape.n_layers} layers" if args.layers else ""),
+                   "global_batch": 1, "seq_len": L, "k": K, "parallelism": "none (1 GPU)"},
+        "acceptance": accepted / (K * args.steps),
+        "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
+        "roofline": {"bound": "hbm", "kernel": "target gate/up projection + SwiGLU (gemm_bf16_kernel<EPI_SWIGLU,1>)",
+                     "achieved": gu_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gu_gbs / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+        "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
+                    for k, v in prof.items()},
+        "teacher_forced": teacher,
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(tshape, dshape, tw, dw, K)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,330 @@
+/*
+ * spec.h -- C ABI of the MI355X (gfx950) speculative-decoding verify step.
+ *
+ * The calls follow the statement of the problem on the pages:
+ *   - a drafter proposes K tokens one at a time ("Speculative Decoding on Apple Silicon:
+ *     119% Faster on Qwen3.8, Until It Isn't", section "How speculative decoding works");
+ *   - the target scores all of them in one batched pass, the same way it reads a prompt
+ *     ("What is Speculative Decoding and How Does a Draft Model Work?", section "#2");
+ *   - the longest agreeing prefix is kept plus one token of the target's own: greedy
+ *     match at temperature 0 (same page, "#3"), or acceptance with probability
+ *     min(1, p/q) and a replacement drawn from the clipped, rescaled difference of the
+ *     two distributions ("Qwen3.5 and Qwen3.6 MTP head reaches 1.4x on Apple Silicon after
+ *     three fixes", section "The verify was wrong under sampling"), with the same
+ *     temperature / top_k / top_p truncation on both sides (same page, "Truncation has to
+ *     match on both sides");
+ *   - the key/value cache is rolled back by slicing the rejected entries off its end
+ *     ("Speculative Decoding on Apple Silicon: 119% Faster...", section "Why this needed a
+ *     patch to mlx_lm at all").
+ *
+ * Conventions for every call:
+ *   - "device" pointers are GPU (HBM) addresses, "host" pointers are CPU addresses.
+ *   - Every device buffer is owned by the caller, who keeps it alive until the work that
+ *     uses it has finished on the stream.  The library never allocates device memory: a
+ *     context lives in a caller-provided workspace, and model weights are borrowed, never
+ *     copied ("Qwen3.5 and Qwen3.6 MTP head...", section "Duplicate weights in unified
+ *     memory": drafting must reuse the already-loaded weights).
+ *   - Work is enqueued on the stream given at spec_init (or per call for the stateless
+ *     entry points) and the call returns at once; outputs are valid once that stream has
+ *     been synchronized.  Only the calls documented as synchronizing wait on the stream.
+ *   - Matrices are row-major, weights in the [out_features, in_features] layout.
+ *   - Return value: SPEC_OK (0) or a negative SPEC_E_* code.  Arguments are validated on
+ *     the host before anything is enqueued; on an error nothing is enqueued and the
+ *     context (if any) keeps a message readable with spec_last_error.  No C++ exception
+ *     crosses this interface.  One context per stream; calls on one context are not
+ *     thread-safe.
+ */
+#ifndef SPEC_H_
+#define SPEC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------ */
+#define SPEC_OK 0
+#define SPEC_E_INVAL (-1)       /* bad argument (null pointer, bad shape, bad sampler)   */
+#define SPEC_E_RANGE (-2)       /* would overflow the cache, trim past the end, too big  */
+#define SPEC_E_UNSUPPORTED (-3) /* valid request outside what the kernels implement      */
+#define SPEC_E_STATE (-4)       /* call out of order (e.g. accept before verify)         */
+#define SPEC_E_HIP (-5)         /* a HIP runtime call failed                             */
+
+/* ---- enums ---------------------------------------------------------------------------- */
+#define SPEC_DTYPE_F32 0  /* weights, cache and GEMM inputs in float32                    */
+#define SPEC_DTYPE_BF16 1 /* bf16 weights and cache, bf16 GEMM inputs, fp32 accumulation  */
+
+#define SPEC_DRAFT_NONE 0  /* no drafter: verify_step at k = 0 is plain decoding          */
+#define SPEC_DRAFT_MODEL 1 /* a separate, smaller decoder with the same vocabulary         */
+#define SPEC_DRAFT_MTP 2   /* the target's own multi-token-prediction layer               */
+#define SPEC_DRAFT_NGRAM 3 /* n-gram lookup in the context                                */
+
+#define SPEC_TOPK_MAX 64   /* largest top_k the truncation kernels keep                   */
+#define SPEC_MAX_K 16      /* largest number of drafts per cycle                          */
+
+/* near-tie / status flag bits written per row or per sequence */
+#define SPEC_FLAG_ACCEPT_TIE 1u  /* |u - p/q| < 1e-6 at an accept test                  */
+#define SPEC_FLAG_SAMPLE_TIE 2u  /* |running sum - u*Z| < 1e-6 at the deciding CDF step */
+#define SPEC_FLAG_TOPP_TIE 4u    /* |exclusive running sum - top_p| < 1e-6 at the cut   */
+#define SPEC_FLAG_BAD_ROW 8u     /* row had NaN / +inf, or no finite logit              */
+
+/* ---- model description (all weight pointers are device, borrowed) ------------------- */
+typedef struct spec_layer_weights {
+  const void* attn_norm; /* [d_model]                      */
+  const void* wq;        /* [n_q_heads*head_dim, d_model]  */
+  const void* wk;        /* [n_kv_heads*head_dim, d_model] */
+  const void* wv;        /* [n_kv_heads*head_dim, d_model] */
+  const void* wo;        /* [d_model, n_q_heads*head_dim]  */
+  const void* ffn_norm;  /* [d_model]                      */
+  const void* wg;        /* [d_ffn, d_model]               */
+  const void* wu;        /* [d_ffn, d_model]               */
+  const void* wd;        /* [d_model, d_ffn]               */
+} spec_layer_weights;
+
+typedef struct spec_model_desc {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
+  int32_t dtype;                    /* SPEC_DTYPE_*; every tensor of the model has it     */
+  float rms_eps;                    /* RMSNorm epsilon (1e-6 for the Qwen-shaped models)   */
+  float rope_theta;                 /* rotate-half RoPE base (1e6)                         */
+  const void* embed;                /* [vocab, d_model]                                    */
+  const void* lm_head;              /* [vocab, d_model]; may be the embed pointer (tied)   */
+  const void* final_norm;           /* [d_model]                                           */
+  const spec_layer_weights* layers; /* host array [n_layers]; copied by spec_init          */
+} spec_model_desc;
+
+/* Multi-token-prediction layer: concat(RMSNorm(h_t), RMSNorm(E[x_{t+1}])) -> w_proj ->
+ * one decoder layer -> RMSNorm -> the target's LM head.  Shares the target's embed and
+ * lm_head; d_model and heads are the target's. */
+typedef struct spec_mtp_desc {
+  const void* norm_h;       /* [d_model]                */
+  const void* norm_e;       /* [d_model]                */
+  const void* w_proj;       /* [d_model, 2*d_model]     */
+  const void* final_norm;   /* [d_model]                */
+  spec_layer_weights layer; /* one decoder layer        */
+} spec_mtp_desc;
+
+/* temperature <= 0 selects greedy decoding (argmax, lowest id on ties); otherwise the
+ * row is divided by temperature, cut to the top_k largest (1..SPEC_TOPK_MAX), softmaxed,
+ * cut where the exclusive running sum reaches top_p (0 < top_p <= 1), renormalized. */
+typedef struct spec_sampler {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+} spec_sampler;
+
+typedef struct spec_ngram_cfg {
+  int32_t n_min;     /* shortest match that triggers a draft (3)        */
+  int32_t max_match; /* longest match length considered (16)            */
+} spec_ngram_cfg;
+
+typedef struct spec_config {
+  spec_model_desc target;
+  int32_t draft_kind;     /* SPEC_DRAFT_*                                   */
+  spec_model_desc draft;  /* used when draft_kind == SPEC_DRAFT_MODEL       */
+  spec_mtp_desc mtp;      /* used when draft_kind == SPEC_DRAFT_MTP         */
+  spec_ngram_cfg ngram;   /* used when draft_kind == SPEC_DRAFT_NGRAM       */
+  spec_sampler sampler;
+  uint64_t seed;          /* Philox4x32-10 key for every uniform the method draws */
+  int32_t max_batch;      /* sequences per call (B)                         */
+  int32_t max_ctx;        /* longest context, in tokens, before a verify    */
+  int32_t max_k;          /* largest k passed to draft_step / verify_step   */
+} spec_config;
+
+/* A batch of truncated distributions, one row each: row r holds count[r] (id, prob) pairs,
+ * ids ascending, at ids[r*cap .. r*cap+count[r]).  Device buffers owned by the caller. */
+typedef struct spec_probs {
+  int32_t* ids;   /* device [rows * cap] */
+  float* probs;   /* device [rows * cap] */
+  int32_t* count; /* device [rows]       */
+  int32_t cap;    /* row stride; >= top_k (>= 1 for greedy) */
+} spec_probs;
+
+typedef struct spec_stats {
+  int64_t cycles;           /* accept calls                                   */
+  int64_t drafts_attempted; /* sum of k over accept calls and sequences        */
+  int64_t drafts_accepted;  /* sum of n                                        */
+  int64_t emitted;          /* sum of n + 1                                    */
+} spec_stats;
+
+typedef struct spec_ctx spec_ctx;
+
+/* ---- lifecycle --------------------------------------------------------------------- */
+
+/* Bytes of device workspace spec_init needs for cfg: caches for max_ctx + max_k + 2
+ * positions per sequence, activations for max_batch*(max_k+1) rows, partial results of
+ * the split attention and of the truncation, lengths and counters.  Host only. */
+int spec_workspace_size(const spec_config* cfg /*host*/, size_t* bytes /*host out*/);
+
+/* Validates cfg (head_dim <= 128 and even, d_model and every projection width a multiple
+ * of 16 and of 8 elements, n_q_heads a multiple of n_kv_heads, 1 <= max_k <= SPEC_MAX_K,
+ * vocab >= top_k, draft vocab == target vocab), copies the weight pointer tables, carves
+ * `workspace` (device, >= spec_workspace_size bytes, 256-byte aligned, owned by the
+ * caller) and enqueues its zeroing on `stream` (a hipStream_t, NULL = default stream).
+ * Sequence lengths start at 0.  *out receives a host-allocated context. */
+int spec_init(const spec_config* cfg /*host*/, void* workspace /*device*/, size_t ws_bytes,
+              void* stream, spec_ctx** out /*host out*/);
+
+/* Frees the host context (not the workspace, not the weights).  NULL is accepted. */
+int spec_destroy(spec_ctx* ctx);
+
+/* Last error message of ctx (NULL ctx: the last spec_init error).  Never NULL. */
+const char* spec_last_error(const spec_ctx* ctx);
+
+/* ---- state set-up ------------------------------------------------------------------ */
+
+/* Copies a cache prefix for sequence `seq` of the target (which = 0), the draft model
+ * (1) or the MTP layer (2): k, v are device [n_layers, n_kv_heads, length, head_dim] in
+ * the model dtype (n_layers = 1 for the MTP layer), keys already rotated.  Sets that
+ * cache's length to `length`.  For which = 0 it also sets the sequence's context length;
+ * the draft caches of a sequence must be loaded with the same length as the target. */
+int spec_load_kv(spec_ctx* ctx, int32_t which, int32_t seq, const void* k /*device*/,
+                 const void* v /*device*/, int32_t length);
+
+/* Prefill: runs the target (and a draft model) over tokens[:, 0 .. P-2] appended at the
+ * current length, and makes tokens[:, P-1] each sequence's last accepted token, the first
+ * row of the next verify.  tokens: device int32 [batch, P], P >= 1.  Every sequence must
+ * have the same length before the call.  For the MTP drafter the target's last hidden
+ * state of position P-2 is kept for the head. */
+int spec_prefill(spec_ctx* ctx, const int32_t* tokens /*device*/, int32_t batch, int32_t P);
+
+/* Sets each sequence's last accepted token (device int32 [batch]) without a forward, for
+ * starts from a loaded cache prefix of length L: that token sits at position L.
+ * prev_tok (device int32 [batch]) is the token at position L-1; a draft model's first
+ * forward of every cycle recomputes its cache entry at L-1 from it, so the draft cache
+ * prefix needs only L-1 valid entries.  May be NULL without a draft model.  For the MTP
+ * drafter `hidden` (device float32 [batch, d_model], NULL otherwise) is the target hidden
+ * state at position L-1. */
+int spec_set_last(spec_ctx* ctx, const int32_t* last_tok /*device*/,
+                  const int32_t* prev_tok /*device or NULL*/, const float* hidden,
+                  int32_t batch);
+
+/* ---- the cycle ----------------------------------------------------------------------- */
+
+/* Draft k tokens per sequence (1 <= k <= max_k) from the configured drafter at one row per
+ * forward.  A draft model's first forward of the cycle runs two rows, the tokens at
+ * positions L-1 and L: after a cycle that accepted every draft the entry at L-1 (the last
+ * draft) is missing from its cache, otherwise it is recomputed bit for bit, so no host
+ * round trip is needed to tell the two apart.
+ * Writes draft_tok (device int32 [batch, k]) and the truncated draft distributions q
+ * (rows batch*k, row b*k + j-1 for draft j; one-hot under greedy sampling and for n-gram
+ * drafts).  Draft j of sequence b is sampled with the uniform of counter
+ * (j, round, b, 0).  For SPEC_DRAFT_NGRAM the call synchronizes the stream and writes to
+ * *n_drafted (host, may be NULL) the number of drafts the lookup found (0..k); rows past
+ * it repeat the last found token (or the last accepted token) and are normally not
+ * verified.  Other drafters write k to *n_drafted. */
+int draft_step(spec_ctx* ctx, int32_t batch, int32_t k, uint64_t round,
+               int32_t* draft_tok /*device*/, spec_probs* q /*host struct of device ptrs*/,
+               int32_t* n_drafted /*host, may be NULL*/);
+
+/* One target forward over k+1 rows per sequence: the last accepted token and draft_tok
+ * (device int32 [batch, k], any source; NULL when k = 0) at positions L..L+k, appending
+ * their keys and values to the cache.  Writes the truncated target distributions p (rows
+ * batch*(k+1)) and, when logits_out is not NULL, the float32 logits (device
+ * [batch, k+1, vocab]).  k = 0 is one step of plain decoding.  The host tracks bounds on
+ * the device-side lengths; when L + k + 1 might exceed max_ctx + max_k + 2 the call
+ * synchronizes the stream once to read the exact lengths, and errors with SPEC_E_RANGE if
+ * the rows really do not fit.  draft_step does the same. */
+int verify_step(spec_ctx* ctx, const int32_t* draft_tok /*device*/, int32_t batch, int32_t k,
+                float* logits_out /*device or NULL*/, spec_probs* p /*host struct*/);
+
+/* The accept rule per sequence.  Greedy sampler: d_j is kept iff it equals the argmax of
+ * p_{j-1}; the first mismatch emits that argmax; all kept emits the argmax of p_k.
+ * Otherwise d_j is kept iff u_j < p_{j-1}(d_j) / q_j(d_j) (float32 division, u_j from
+ * counter (j, round, b, 1)); the first rejection emits a draw from max(0, p_{j-1} - q_j)
+ * renormalized (from p_{j-1} if that is all zero), all kept emits a draw from p_k, both
+ * with the uniform of counter (0, round, b, 2) walking ids in ascending order.
+ * Writes n_acc (device int32 [batch], 0..k), out_tok (device int32 [batch, k+1], the first
+ * n+1 entries valid: accepted drafts then the correction or bonus token), near_tie
+ * (device uint8 [batch] of SPEC_FLAG_* bits, may be NULL), updates the device-side last
+ * accepted token and the statistics.  Must follow a verify_step with the same k. */
+int accept(spec_ctx* ctx, const int32_t* draft_tok /*device*/, const spec_probs* q,
+           const spec_probs* p, int32_t batch, int32_t k, uint64_t round,
+           int32_t* n_acc /*device*/, int32_t* out_tok /*device*/, uint8_t* near_tie);
+
+/* Rolls every cache back to the accepted prefix: L <- L + 1 + n_acc[b] (the last accepted
+ * token and its n accepted drafts stay; the emitted last token is the next cycle's first
+ * row).  Must follow accept.  n_acc: device int32 [batch]. */
+int kv_trim(spec_ctx* ctx, const int32_t* n_acc /*device*/, int32_t batch);
+
+/* ---- tracing ------------------------------------------------------------------------- */
+
+/* Profiling slots: slot = kernel class + 16 * model (model 0 = target, 1 = draft); classes
+ * 0 embedding gather, 1 RMSNorm, 2 QKV projection, 3 attention (chunks + combine), 4 output
+ * projection + residual, 5 gate/up projection + SwiGLU, 6 down projection + residual,
+ * 7 LM head, 8 truncation, 9 draft sampling, 10 accept, 11 kv trim. */
+#define SPEC_PROF_SLOTS 32
+
+/* enable != 0: bracket every launch of the context with HIP events on its stream, filed by
+ * slot (launches then go out one by one, not as a replayed graph).  0: stop. */
+int spec_profile(spec_ctx* ctx, int32_t enable);
+
+/* Sums the recorded launches per slot: ms (host double [SPEC_PROF_SLOTS]) = total GPU time
+ * between each launch's events, launches (host int64 [SPEC_PROF_SLOTS]) = launch count;
+ * then forgets them.  Synchronizes the stream. */
+int spec_profile_read(spec_ctx* ctx, double* ms, int64_t* launches);
+
+/* enable != 0 (the default): draft_step and verify_step capture their launches into a HIP
+ * graph on first use for a given (batch, k, buffer addresses) and replay it afterwards;
+ * needs a non-default stream.  0: launch kernel by kernel. */
+int spec_use_graphs(spec_ctx* ctx, int32_t enable);
+
+/* Copies the device counters to *out (synchronizes the stream). */
+int spec_get_stats(spec_ctx* ctx, spec_stats* out /*host*/);
+
+/* Reads the current cache length of each sequence (synchronizes the stream). */
+int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t batch);
+
+/* ---- stateless kernels (the accept workload on its own) ------------------------------ */
+
+/* Scratch bytes spec_truncate needs for `rows` rows of `vocab` logits. */
+int spec_truncate_scratch_size(int32_t rows, int32_t vocab, size_t* bytes /*host out*/);
+
+/* Truncates `rows` rows of logits (device, dtype SPEC_DTYPE_F32 or SPEC_DTYPE_BF16, row r
+ * at logits + r*row_stride elements) with sampler s into out (rows `rows`).  flags (device
+ * uint8 [rows], may be NULL) receives SPEC_FLAG_TOPP_TIE / SPEC_FLAG_BAD_ROW; a bad row
+ * gets count 0.  scratch: device, >= spec_truncate_scratch_size bytes. */
+int spec_truncate(const void* logits /*device*/, int32_t dtype, int32_t rows, int32_t vocab,
+                  int64_t row_stride, const spec_sampler* s /*host*/, spec_probs* out,
+                  uint8_t* flags /*device or NULL*/, void* scratch /*device*/,
+                  size_t scratch_bytes, void* stream);
+
+/* Draws one token per row from lists (rows = batch*per_seq; row r is slot r%per_seq + 1
+ * of sequence r/per_seq) with the uniform of counter (slot, round, seq, stream_id): ids
+ * walked in ascending order, first running sum above u*Z.  tokens: device int32 [rows];
+ * flags: device uint8 [rows] or NULL (SPEC_FLAG_SAMPLE_TIE). */
+int spec_sample(const spec_probs* lists, int32_t batch, int32_t per_seq, uint64_t seed,
+                uint64_t round, int32_t stream_id, int32_t* tokens /*device*/,
+                uint8_t* flags /*device or NULL*/, void* stream);
+
+/* The accept rule of `accept` on explicit lists, without a context: q rows batch*k, p rows
+ * batch*(k+1), greedy != 0 selects the greedy rule. */
+int spec_accept_lists(const int32_t* draft_tok /*device*/, const spec_probs* q,
+                      const spec_probs* p, int32_t batch, int32_t k, int32_t greedy,
+                      uint64_t seed, uint64_t round, int32_t* n_acc /*device*/,
+                      int32_t* out_tok /*device*/, uint8_t* near_tie /*device or NULL*/,
+                      void* stream);
+
+/* n uniforms of Philox4x32-10 under key `seed`: counters ctr (device uint32 [n, 4]) ->
+ * out (device float32 [n]), u = (word0 >> 8) * 2^-24. */
+int spec_philox_uniforms(uint64_t seed, const uint32_t* ctr /*device*/, int32_t n,
+                         float* out /*device*/, void* stream);
+
+/* Longest-then-latest n-gram match for `batch` contexts: ctx (device int32 [batch, ld]),
+ * lengths (device int32 [batch]); for each sequence, among earlier end positions e the
+ * match length is the number of tokens (up to max_match) equal going backwards from e and
+ * from the last token; the largest length >= n_min wins, the latest e among equals.  Writes
+ * drafts (device int32 [batch, k]: the tokens after e, not past the end, then repeats of
+ * the last one written or of the last context token), n_found (device int32 [batch],
+ * 0..k) and match (device int32 [batch, 2]: length, e; 0, -1 when none). */
+int spec_ngram_match(const int32_t* ctx /*device*/, const int32_t* lengths /*device*/,
+                     int32_t batch, int32_t ld, int32_t k, int32_t n_min, int32_t max_match,
+                     int32_t* drafts /*device*/, int32_t* n_found /*device*/,
+                     int32_t* match /*device*/, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_H_ */

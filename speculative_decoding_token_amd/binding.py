@@ -1,0 +1,333 @@
+"""ctypes binding of libspec.so, the HIP library behind ``include/spec.h``.
+
+Argument marshalling only: every function here has the name of a C entry point, turns
+Python ints (device or host addresses), torch tensors and small structs into the C
+arguments, calls the library, and raises ``SpecError`` on a non-zero status.  No step of
+the computation runs here.  Loading fails loudly when the library is missing; there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspec.so")
+
+SPEC_OK = 0
+SPEC_E_INVAL = -1
+SPEC_E_RANGE = -2
+SPEC_E_UNSUPPORTED = -3
+SPEC_E_STATE = -4
+SPEC_E_HIP = -5
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+DRAFT_NONE, DRAFT_MODEL, DRAFT_MTP, DRAFT_NGRAM = 0, 1, 2, 3
+TOPK_MAX = 64
+MAX_K = 16
+FLAG_ACCEPT_TIE, FLAG_SAMPLE_TIE, FLAG_TOPP_TIE, FLAG_BAD_ROW = 1, 2, 4, 8
+
+EXPORTED = [
+    "spec_workspace_size", "spec_init", "spec_destroy", "spec_last_error", "spec_load_kv",
+    "spec_prefill", "spec_set_last", "draft_step", "verify_step", "accept", "kv_trim",
+    "spec_get_stats", "spec_get_lengths", "spec_truncate_scratch_size", "spec_truncate",
+    "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
+    "spec_profile", "spec_profile_read", "spec_use_graphs",
+]
+PROF_SLOTS = 32
+PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
+                "truncate", "sample", "accept", "kv_trim"]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"spec error {code}: {msg}")
+        self.code = code
+
+
+# ---------------------------------------------------------------- structs
+class spec_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")]
+
+
+class spec_model_desc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32),
+                ("vocab", C.c_int32), ("dtype", C.c_int32), ("rms_eps", C.c_float),
+                ("rope_theta", C.c_float), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
+                ("final_norm", C.c_void_p), ("layers", C.POINTER(spec_layer_weights))]
+
+
+class spec_mtp_desc(C.Structure):
+    _fields_ = [("norm_h", C.c_void_p), ("norm_e", C.c_void_p), ("w_proj", C.c_void_p),
+                ("final_norm", C.c_void_p), ("layer", spec_layer_weights)]
+
+
+class spec_sampler(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_k", C.c_int32), ("top_p", C.c_float)]
+
+
+class spec_ngram_cfg(C.Structure):
+    _fields_ = [("n_min", C.c_int32), ("max_match", C.c_int32)]
+
+
+class spec_config(C.Structure):
+    _fields_ = [("target", spec_model_desc), ("draft_kind", C.c_int32), ("draft", spec_model_desc),
+                ("mtp", spec_mtp_desc), ("ngram", spec_ngram_cfg), ("sampler", spec_sampler),
+                ("seed", C.c_uint64), ("max_batch", C.c_int32), ("max_ctx", C.c_int32),
+                ("max_k", C.c_int32)]
+
+
+class spec_probs(C.Structure):
+    _fields_ = [("ids", C.c_void_p), ("probs", C.c_void_p), ("count", C.c_void_p), ("cap", C.c_int32)]
+
+
+class spec_stats(C.Structure):
+    _fields_ = [("cycles", C.c_int64), ("drafts_attempted", C.c_int64),
+                ("drafts_accepted", C.c_int64), ("emitted", C.c_int64)]
+
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libspec.so once; raise if it is missing (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m speculative_decoding_token_amd.build`")
+    L = C.CDLL(path)
+    P, I32, I64, U64, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_size_t
+    sig = {
+        "spec_workspace_size": ([C.POINTER(spec_config), C.POINTER(SZ)], C.c_int),
+        "spec_init": ([C.POINTER(spec_config), P, SZ, P, C.POINTER(P)], C.c_int),
+        "spec_destroy": ([P], C.c_int),
+        "spec_last_error": ([P], C.c_char_p),
+        "spec_load_kv": ([P, I32, I32, P, P, I32], C.c_int),
+        "spec_prefill": ([P, P, I32, I32], C.c_int),
+        "spec_set_last": ([P, P, P, P, I32], C.c_int),
+        "draft_step": ([P, I32, I32, U64, P, C.POINTER(spec_probs), C.POINTER(I32)], C.c_int),
+        "verify_step": ([P, P, I32, I32, P, C.POINTER(spec_probs)], C.c_int),
+        "accept": ([P, P, C.POINTER(spec_probs), C.POINTER(spec_probs), I32, I32, U64, P, P, P], C.c_int),
+        "kv_trim": ([P, P, I32], C.c_int),
+        "spec_get_stats": ([P, C.POINTER(spec_stats)], C.c_int),
+        "spec_get_lengths": ([P, P, I32], C.c_int),
+        "spec_truncate_scratch_size": ([I32, I32, C.POINTER(SZ)], C.c_int),
+        "spec_truncate": ([P, I32, I32, I32, I64, C.POINTER(spec_sampler), C.POINTER(spec_probs), P, P,
+                           SZ, P], C.c_int),
+        "spec_sample": ([C.POINTER(spec_probs), I32, I32, U64, U64, I32, P, P, P], C.c_int),
+        "spec_accept_lists": ([P, C.POINTER(spec_probs), C.POINTER(spec_probs), I32, I32, I32, U64, U64,
+                               P, P, P, P], C.c_int),
+        "spec_philox_uniforms": ([U64, P, I32, P, P], C.c_int),
+        "spec_ngram_match": ([P, P, I32, I32, I32, I32, I32, P, P, P, P], C.c_int),
+        "spec_profile": ([P, I32], C.c_int),
+        "spec_profile_read": ([P, P, P], C.c_int),
+        "spec_use_graphs": ([P, I32], C.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _check(rc: int, ctx=None):
+    if rc != SPEC_OK:
+        msg = lib().spec_last_error(ctx)
+        raise SpecError(rc, msg.decode() if msg else "")
+
+
+def _ptr(x) -> Optional[int]:
+    """Address of a torch tensor (or an int / None) for a pointer argument."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- descriptors from tensors
+def layer_struct(lw: Dict) -> spec_layer_weights:
+    return spec_layer_weights(*[_ptr(lw[n]) for n in
+                                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")])
+
+
+def model_desc(shape, w: Dict, keep: List) -> spec_model_desc:
+    """spec_model_desc from a synth.ModelShape and a weight dict of device tensors.  The
+    ctypes layer array is appended to ``keep`` so it outlives the call that copies it."""
+    arr = (spec_layer_weights * shape.n_layers)(*[layer_struct(lw) for lw in w["layers"]])
+    keep.append(arr)
+    return spec_model_desc(
+        shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+        shape.d_ffn, shape.vocab, DTYPE_BF16 if shape.dtype == "bf16" else DTYPE_F32,
+        shape.rms_eps, shape.rope_theta, _ptr(w["embed"]), _ptr(w["lm_head"]),
+        _ptr(w["final_norm"]), C.cast(arr, C.POINTER(spec_layer_weights)))
+
+
+def sampler(temperature: float = 0.0, top_k: int = 20, top_p: float = 0.95) -> spec_sampler:
+    return spec_sampler(temperature, top_k, top_p)
+
+
+class Probs:
+    """Device buffers of a spec_probs batch (torch tensors) plus the C struct."""
+
+    def __init__(self, rows: int, cap: int, device="cuda"):
+        import torch
+        self.rows, self.cap = rows, cap
+        self.ids = torch.full((rows, cap), -1, dtype=torch.int32, device=device)
+        self.probs = torch.zeros((rows, cap), dtype=torch.float32, device=device)
+        self.count = torch.zeros((rows,), dtype=torch.int32, device=device)
+        self.c = spec_probs(self.ids.data_ptr(), self.probs.data_ptr(), self.count.data_ptr(), cap)
+
+    def to_lists(self):
+        """[(ids, probs)] per row on the host."""
+        ids, pr, cnt = self.ids.cpu().numpy(), self.probs.cpu().numpy(), self.count.cpu().numpy()
+        return [(ids[r, :cnt[r]].astype("int64"), pr[r, :cnt[r]]) for r in range(self.rows)]
+
+
+# ---------------------------------------------------------------- entry points
+def spec_workspace_size(cfg: spec_config) -> int:
+    n = C.c_size_t(0)
+    _check(lib().spec_workspace_size(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
+def spec_init(cfg: spec_config, workspace, ws_bytes: int, stream=None) -> int:
+    out = C.c_void_p(0)
+    _check(lib().spec_init(C.byref(cfg), _ptr(workspace), ws_bytes, _stream(stream), C.byref(out)))
+    return out.value
+
+
+def spec_destroy(ctx: int) -> None:
+    lib().spec_destroy(ctx)
+
+
+def spec_last_error(ctx: Optional[int]) -> str:
+    return lib().spec_last_error(ctx).decode()
+
+
+def spec_load_kv(ctx: int, which: int, seq: int, k, v, length: int) -> None:
+    _check(lib().spec_load_kv(ctx, which, seq, _ptr(k), _ptr(v), length), ctx)
+
+
+def spec_prefill(ctx: int, tokens, batch: int, P: int) -> None:
+    _check(lib().spec_prefill(ctx, _ptr(tokens), batch, P), ctx)
+
+
+def spec_set_last(ctx: int, last_tok, prev_tok, hidden, batch: int) -> None:
+    _check(lib().spec_set_last(ctx, _ptr(last_tok), _ptr(prev_tok), _ptr(hidden), batch), ctx)
+
+
+def draft_step(ctx: int, batch: int, k: int, rnd: int, draft_tok, q: Probs) -> int:
+    n = C.c_int32(0)
+    _check(lib().draft_step(ctx, batch, k, rnd, _ptr(draft_tok), C.byref(q.c), C.byref(n)), ctx)
+    return n.value
+
+
+def verify_step(ctx: int, draft_tok, batch: int, k: int, logits_out, p: Probs) -> None:
+    _check(lib().verify_step(ctx, _ptr(draft_tok), batch, k, _ptr(logits_out), C.byref(p.c)), ctx)
+
+
+def accept(ctx: int, draft_tok, q: Optional[Probs], p: Probs, batch: int, k: int, rnd: int,
+           n_acc, out_tok, near_tie=None) -> None:
+    qc = C.byref(q.c) if q is not None else None
+    _check(lib().accept(ctx, _ptr(draft_tok), qc, C.byref(p.c), batch, k, rnd, _ptr(n_acc),
+                        _ptr(out_tok), _ptr(near_tie)), ctx)
+
+
+def kv_trim(ctx: int, n_acc, batch: int) -> None:
+    _check(lib().kv_trim(ctx, _ptr(n_acc), batch), ctx)
+
+
+def spec_get_stats(ctx: int) -> Dict[str, int]:
+    s = spec_stats()
+    _check(lib().spec_get_stats(ctx, C.byref(s)), ctx)
+    return {"cycles": s.cycles, "drafts_attempted": s.drafts_attempted,
+            "drafts_accepted": s.drafts_accepted, "emitted": s.emitted}
+
+
+def spec_get_lengths(ctx: int, batch: int) -> List[int]:
+    arr = (C.c_int32 * batch)()
+    _check(lib().spec_get_lengths(ctx, C.cast(arr, C.c_void_p), batch), ctx)
+    return list(arr)
+
+
+def spec_truncate_scratch_size(rows: int, vocab: int) -> int:
+    n = C.c_size_t(0)
+    _check(lib().spec_truncate_scratch_size(rows, vocab, C.byref(n)))
+    return n.value
+
+
+def spec_truncate(logits, dtype: int, rows: int, vocab: int, row_stride: int, s: spec_sampler,
+                  out: Probs, flags, scratch, scratch_bytes: int, stream=None) -> None:
+    rc = lib().spec_truncate(_ptr(logits), dtype, rows, vocab, row_stride, C.byref(s), C.byref(out.c),
+                             _ptr(flags), _ptr(scratch), scratch_bytes, _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_truncate")
+
+
+def spec_sample(lists: Probs, batch: int, per_seq: int, seed: int, rnd: int, stream_id: int, tokens,
+                flags=None, stream=None) -> None:
+    rc = lib().spec_sample(C.byref(lists.c), batch, per_seq, seed, rnd, stream_id, _ptr(tokens),
+                           _ptr(flags), _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_sample")
+
+
+def spec_accept_lists(draft_tok, q: Optional[Probs], p: Probs, batch: int, k: int, greedy: bool, seed: int,
+                      rnd: int, n_acc, out_tok, near_tie=None, stream=None) -> None:
+    qc = C.byref(q.c) if q is not None else None
+    rc = lib().spec_accept_lists(_ptr(draft_tok), qc, C.byref(p.c), batch, k, int(greedy), seed, rnd,
+                                 _ptr(n_acc), _ptr(out_tok), _ptr(near_tie), _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_accept_lists")
+
+
+def spec_philox_uniforms(seed: int, ctr, n: int, out, stream=None) -> None:
+    rc = lib().spec_philox_uniforms(seed, _ptr(ctr), n, _ptr(out), _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_philox_uniforms")
+
+
+def spec_ngram_match(ctx_tokens, lengths, batch: int, ld: int, k: int, n_min: int, max_match: int,
+                     drafts, n_found, match, stream=None) -> None:
+    rc = lib().spec_ngram_match(_ptr(ctx_tokens), _ptr(lengths), batch, ld, k, n_min, max_match,
+                                _ptr(drafts), _ptr(n_found), _ptr(match), _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_ngram_match")
+
+
+def spec_profile(ctx: int, enable: bool) -> None:
+    _check(lib().spec_profile(ctx, int(enable)), ctx)
+
+
+def spec_profile_read(ctx: int) -> Dict[str, Dict[str, float]]:
+    """{'target.gate_up': {'ms': total, 'launches': n}, ...} for slots with launches."""
+    ms = (C.c_double * PROF_SLOTS)()
+    n = (C.c_int64 * PROF_SLOTS)()
+    _check(lib().spec_profile_read(ctx, C.cast(ms, C.c_void_p), C.cast(n, C.c_void_p)), ctx)
+    out = {}
+    for slot in range(PROF_SLOTS):
+        if n[slot]:
+            model = "target" if slot < 16 else "draft"
+            out[f"{model}.{PROF_CLASSES[slot % 16]}"] = {"ms": ms[slot], "launches": n[slot]}
+    return out
+
+
+def spec_use_graphs(ctx: int, enable: bool) -> None:
+    _check(lib().spec_use_graphs(ctx, int(enable)), ctx)

@@ -1,0 +1,90 @@
+// Shared device helpers of the HIP library: number formats, the Philox generator, the
+// orderable key of a (value, id) pair, and launch bookkeeping.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/spec.h"
+
+#define SPEC_DEVINL __device__ __forceinline__
+
+namespace spec {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+// ---- number formats ------------------------------------------------------------------
+SPEC_DEVINL float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round-to-nearest-even float32 -> bfloat16 on the bit pattern; NaN stays NaN.
+SPEC_DEVINL bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Activation storage: bf16 models round GEMM inputs and the cache to bfloat16, f32
+// models keep float32.
+template <int DT> struct Act;
+template <> struct Act<SPEC_DTYPE_F32> {
+  typedef float T;
+  static SPEC_DEVINL float load(const float* p, int64_t i) { return p[i]; }
+  static SPEC_DEVINL void store(float* p, int64_t i, float v) { p[i] = v; }
+  static SPEC_DEVINL float round(float v) { return v; }
+};
+template <> struct Act<SPEC_DTYPE_BF16> {
+  typedef bf16_t T;
+  static SPEC_DEVINL float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static SPEC_DEVINL void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+  static SPEC_DEVINL float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) ----------------------------------
+// Ten rounds; each multiplies counter words 0 and 2 by fixed odd constants, swaps in the
+// high halves xor-ed with words 1, 3 and the round key, and advances the key by the two
+// Weyl increments between rounds.
+SPEC_DEVINL uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Uniform in [0, 1 - 2^-24] for counter (slot, round, seq, stream) under key `seed`.
+SPEC_DEVINL float philox_uniform(uint64_t seed, uint32_t slot, uint32_t rnd, uint32_t seq,
+                                 uint32_t stream) {
+  const uint4 o = philox4x32_10(make_uint4(slot, rnd, seq, stream), (uint32_t)seed,
+                                (uint32_t)(seed >> 32));
+  return (float)(o.x >> 8) * (1.0f / 16777216.0f);
+}
+
+enum : uint32_t { STREAM_DRAFT = 0, STREAM_ACCEPT = 1, STREAM_RESIDUAL = 2 };
+
+// ---- ordering of (value, id) ------------------------------------------------------------
+// A 64-bit key that is larger for a larger value and, among equal values, for a lower id.
+// The value is made +0 when it is -0 so that zeros of both signs tie on id.  0 is never a
+// key of a real value (it would be a NaN pattern) and marks an empty slot.
+SPEC_DEVINL uint64_t order_key(float z, uint32_t id) {
+  z = (z == 0.0f) ? 0.0f : z;
+  const uint32_t f = __float_as_uint(z);
+  const uint32_t k32 = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+  return ((uint64_t)k32 << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+SPEC_DEVINL float key_value(uint64_t key) {
+  const uint32_t k32 = (uint32_t)(key >> 32);
+  const uint32_t f = (k32 & 0x80000000u) ? (k32 & 0x7FFFFFFFu) : ~k32;
+  return __uint_as_float(f);
+}
+SPEC_DEVINL uint32_t key_id(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
+
+constexpr float NEAR_TIE = 1e-6f;
+
+}  // namespace spec

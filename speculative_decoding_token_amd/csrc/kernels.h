@@ -1,0 +1,128 @@
+// Kernel argument blocks and host-side launchers of the HIP library.
+#pragma once
+
+#include "common.h"
+
+namespace spec {
+
+// ---- truncation / sampling / accept --------------------------------------------------
+struct TruncArgs {
+  const void* logits;
+  int64_t stride;     // elements between rows
+  int vocab, rows;
+  float temperature;  // <= 0: greedy
+  int ksel;           // entries kept per segment: top_k, or 1 for greedy
+  int nseg, seg_len;  // segments per row and their length (multiple of 8)
+  uint64_t* part;     // [rows][nseg][ksel] keys, descending, 0 = empty
+  uint8_t* bad;       // [rows][nseg]
+};
+
+struct AcceptArgs {
+  const int32_t* drafts;  // [batch, k]
+  spec_probs q, p;        // rows batch*k and batch*(k+1)
+  int batch, k, greedy;
+  uint64_t seed;
+  uint32_t round;
+  int32_t* n_acc;         // [batch]
+  int32_t* out_tok;       // [batch, k+1]
+  uint8_t* near_tie;      // [batch] or null
+  int32_t* last_tok;      // context state or null
+  int32_t* prev_tok;
+  int64_t* stats;         // 4 counters or null
+};
+
+struct NgramArgs {
+  const int32_t* ctx;
+  const int32_t* lengths;
+  int batch, ld, k, n_min, max_match;
+  int32_t* drafts;
+  int32_t* n_found;
+  int32_t* match;
+};
+
+int truncate_scratch_bytes(int rows, int vocab, size_t* bytes);
+// Output row of input row r is r * out_rs.
+hipError_t launch_truncate(const void* logits, int dtype, int rows, int vocab, int64_t stride,
+                           const spec_sampler& s, const spec_probs& out, int out_rs, uint8_t* flags,
+                           void* scratch, hipStream_t st);
+// Row r = (seq r / per_seq, j = r % per_seq) reads list row r * list_rs and draws with slot
+// slot_base + j into tokens[seq * tok_ld + j].  The round is *rnd_ptr when rnd_ptr is not
+// null (device memory, so a captured launch can be replayed for a new round), else rnd.
+hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per_seq, int slot_base,
+                         uint64_t seed, const uint32_t* rnd_ptr, uint32_t rnd, uint32_t stream_id,
+                         int32_t* tokens, int tok_ld, uint8_t* flags, hipStream_t st);
+hipError_t launch_set_u32(uint32_t* p, uint32_t v, hipStream_t st);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
+hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, hipStream_t st);
+hipError_t launch_philox(uint64_t seed, const uint32_t* ctr, int n, float* out, hipStream_t st);
+hipError_t launch_ngram(const NgramArgs& a, hipStream_t st);
+
+// ---- model --------------------------------------------------------------------------
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+
+// Cache layout: [batch][n_layers][n_kv][cap][head_dim] in the model dtype.
+struct CacheView {
+  void* k;
+  void* v;
+  int n_layers, n_kv, cap, hd;
+};
+
+// Rows of a forward: row m belongs to sequence m / mseq at position
+// len[m / mseq] + pos_off + m % mseq.
+struct RowMap {
+  int M, mseq;
+  const int32_t* len;
+  int pos_off;
+};
+
+struct GemmArgs {
+  const void* w[3];   // weight matrices [rows_i, K]; EPI_QKV uses three, EPI_SWIGLU two
+  int rows[3];
+  int K;
+  const void* x;      // [M, K] model dtype
+  RowMap rm;
+  // outputs
+  float* out;         // EPI_STORE / EPI_RESID: [M, ld]
+  int ld;
+  void* h;            // EPI_SWIGLU: [M, rows0] model dtype
+  float* q_stage;     // EPI_QKV: [M, rows0] raw q
+  float* k_stage;     // EPI_QKV: [M, rows1] raw k
+  CacheView cache;    // EPI_QKV: values written at their positions
+  int layer;
+};
+
+struct AttnArgs {
+  const float* q_stage;
+  const float* k_stage;
+  CacheView cache;
+  int layer;
+  RowMap rm;
+  int n_q;
+  const float2* rope;  // [cap][hd/2] cos, sin
+  float scale;
+  float* part;         // [M*n_q][nchunk][hd+2]
+  int nchunk;
+  void* out;           // combine: [M, n_q*hd] model dtype
+};
+
+constexpr int ATTN_CHUNK = 64;
+constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)
+
+hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStream_t st);
+hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
+                        int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
+                        hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, int M, int d,
+                          void* y, hipStream_t st);
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st);
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_copy_rows(const int32_t* src, int src_ld, int32_t* dst, int n, hipStream_t st);
+size_t attention_lds_bytes(int R, int hd);
+hipError_t attention_set_lds_limit();
+hipError_t launch_kv_load(int dtype, const void* k, const void* v, CacheView c, int seq, int length,
+                          hipStream_t st);
+hipError_t launch_set_len(int32_t* len, int seq, int value, hipStream_t st);
+hipError_t launch_add_len(int32_t* len, int batch, int delta, hipStream_t st);
+
+}  // namespace spec

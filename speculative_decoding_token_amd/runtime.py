@@ -1,0 +1,194 @@
+"""Host loop over the C ABI: workspace set-up and the draft / verify / accept / trim cycle.
+
+The loop follows "Speculative Decoding on Apple Silicon: 119% Faster...", section "How
+speculative decoding works" (draft several tokens, verify them in one target pass, keep
+the agreeing prefix plus the target's own token) and reads the emitted tokens back once
+per cycle, which is the only device-to-host transfer of a cycle.  All computation runs in
+libspec.so; this module allocates device buffers with torch and passes their addresses.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+@dataclasses.dataclass
+class Cycle:
+    drafts: List[List[int]]      # [batch][k]
+    n: List[int]
+    tokens: List[List[int]]      # [batch][n+1]
+    near_tie: List[int]
+    logits: Optional[torch.Tensor] = None      # [batch, k+1, V] when kept
+    p: Optional[list] = None                   # host lists when kept
+    q: Optional[list] = None
+
+
+class Engine:
+    """One context: a target, an optional draft model, a sampler and a workspace."""
+
+    def __init__(self, target_shape, target_w: Dict, draft_shape=None, draft_w: Optional[Dict] = None,
+                 temperature: float = 0.0, top_k: int = 20, top_p: float = 0.95, seed: int = 0,
+                 max_batch: int = 1, max_ctx: int = 256, max_k: int = 8, stream=None):
+        self._keep: list = []
+        cfg = B.spec_config()
+        cfg.target = B.model_desc(target_shape, target_w, self._keep)
+        if draft_shape is not None:
+            cfg.draft_kind = B.DRAFT_MODEL
+            cfg.draft = B.model_desc(draft_shape, draft_w, self._keep)
+        else:
+            cfg.draft_kind = B.DRAFT_NONE
+        cfg.ngram = B.spec_ngram_cfg(3, 16)
+        cfg.sampler = B.sampler(temperature, top_k, top_p)
+        cfg.seed = seed
+        cfg.max_batch, cfg.max_ctx, cfg.max_k = max_batch, max_ctx, max_k
+        self.cfg = cfg
+        self.weights = (target_w, draft_w)        # keep the borrowed weights alive
+        self.target_shape, self.draft_shape = target_shape, draft_shape
+        # a stream of its own (default priority) so that draft/verify can be graph-replayed
+        self.stream = stream if stream is not None else torch.cuda.Stream()
+        nbytes = B.spec_workspace_size(cfg)
+        self.workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        base = self.workspace.data_ptr()
+        aligned = (base + 255) // 256 * 256
+        self.stream.wait_stream(torch.cuda.current_stream())
+        self.ctx = B.spec_init(cfg, aligned, nbytes, self.stream)
+        self.greedy = temperature <= 0.0
+        self.cap = 1 if self.greedy else top_k
+        self.vocab = target_shape.vocab
+        self.max_batch, self.max_k = max_batch, max_k
+
+    def close(self):
+        if self.ctx:
+            B.spec_destroy(self.ctx)
+            self.ctx = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- starts
+    def _enter(self):
+        """Order the engine stream after work already queued on the caller's stream."""
+        self.stream.wait_stream(torch.cuda.current_stream())
+        return torch.cuda.stream(self.stream)
+
+    def prefill(self, tokens: torch.Tensor):
+        """tokens: int32 [batch, P] on the device."""
+        with self._enter():
+            b, P = tokens.shape
+            B.spec_prefill(self.ctx, tokens, b, P)
+
+    def load_prefix(self, which: int, seq: int, k: torch.Tensor, v: torch.Tensor, length: int):
+        with self._enter():
+            B.spec_load_kv(self.ctx, which, seq, k, v, length)
+
+    def set_last(self, last_tok: torch.Tensor, prev_tok: Optional[torch.Tensor] = None):
+        with self._enter():
+            B.spec_set_last(self.ctx, last_tok, prev_tok, None, last_tok.shape[0])
+
+    # ---- one cycle
+    def buffers(self, batch: int, k: int):
+        key = (batch, k)
+        if getattr(self, "_buf_key", None) != key:
+            dev = "cuda"
+            self._buf = dict(
+                draft=torch.zeros((batch, max(k, 1)), dtype=torch.int32, device=dev),
+                q=B.Probs(batch * max(k, 1), self.cap),
+                p=B.Probs(batch * (k + 1), self.cap),
+                n=torch.zeros((batch,), dtype=torch.int32, device=dev),
+                out=torch.zeros((batch, k + 1), dtype=torch.int32, device=dev),
+                tie=torch.zeros((batch,), dtype=torch.uint8, device=dev),
+                logits=None,
+            )
+            self._buf_key = key
+        return self._buf
+
+    def cycle(self, batch: int, k: int, rnd: int, drafts: Optional[torch.Tensor] = None,
+              keep: bool = False, sync: bool = True, events: Optional[dict] = None) -> Optional[Cycle]:
+        """draft_step (unless ``drafts`` are given) -> verify_step -> accept -> kv_trim.
+        ``events``: a dict that receives (start, end) CUDA events of each call, recorded on
+        the engine stream."""
+        with self._enter():
+            return self._cycle(batch, k, rnd, drafts, keep, sync, events)
+
+    def _mark(self, events, name, i):
+        if events is not None:
+            if name not in events:
+                events[name] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            events[name][i].record(self.stream)
+
+    def _cycle(self, batch, k, rnd, drafts, keep, sync, events=None):
+        buf = self.buffers(batch, k)
+        if keep and buf["logits"] is None:
+            buf["logits"] = torch.empty((batch, k + 1, self.vocab), dtype=torch.float32, device="cuda")
+        if k > 0:
+            if drafts is None:
+                self._mark(events, "draft", 0)
+                B.draft_step(self.ctx, batch, k, rnd, buf["draft"], buf["q"])
+                self._mark(events, "draft", 1)
+            else:
+                if not self.greedy:
+                    raise ValueError("explicit drafts are supported with the greedy sampler")
+                buf["draft"].copy_(drafts.to(torch.int32))
+        self._mark(events, "verify", 0)
+        B.verify_step(self.ctx, buf["draft"] if k > 0 else None, batch, k,
+                      buf["logits"] if keep else None, buf["p"])
+        self._mark(events, "verify", 1)
+        self._mark(events, "accept", 0)
+        B.accept(self.ctx, buf["draft"] if k > 0 else None, buf["q"] if k > 0 else None, buf["p"],
+                 batch, k, rnd, buf["n"], buf["out"], buf["tie"])
+        B.kv_trim(self.ctx, buf["n"], batch)
+        self._mark(events, "accept", 1)
+        if not sync:
+            return None
+        n = buf["n"].cpu().tolist()
+        out = buf["out"].cpu().tolist()
+        c = Cycle(drafts=buf["draft"].cpu().tolist() if k > 0 else [[] for _ in range(batch)], n=n,
+                  tokens=[out[b][: n[b] + 1] for b in range(batch)], near_tie=buf["tie"].cpu().tolist())
+        if keep:
+            c.logits = buf["logits"].clone()
+            c.p = buf["p"].to_lists()
+            c.q = buf["q"].to_lists() if k > 0 else []
+        return c
+
+    def generate(self, n_new: int, k: int, batch: int = 1, rnd0: int = 0, keep: bool = False,
+                 teacher: Optional[Sequence[int]] = None):
+        """Run cycles until every sequence emitted n_new tokens (batch 1 for ``teacher``).
+        Returns (tokens [batch][n_new], cycles)."""
+        out = [[] for _ in range(batch)]
+        cycles = []
+        rnd = rnd0
+        while min(len(o) for o in out) < n_new:
+            drafts = None
+            if teacher is not None and k > 0:
+                done = len(out[0])
+                t = list(teacher[done: done + k])
+                t += [0] * (k - len(t))
+                drafts = torch.tensor([t], dtype=torch.int32, device="cuda")
+            c = self.cycle(batch, k, rnd, drafts=drafts, keep=keep)
+            for b in range(batch):
+                out[b].extend(c.tokens[b])
+            cycles.append(c)
+            rnd += 1
+        return [o[:n_new] for o in out], cycles
+
+    def profile(self, enable: bool):
+        B.spec_profile(self.ctx, enable)
+
+    def profile_read(self):
+        return B.spec_profile_read(self.ctx)
+
+    def use_graphs(self, enable: bool):
+        B.spec_use_graphs(self.ctx, enable)
+
+    def stats(self):
+        return B.spec_get_stats(self.ctx)
+
+    def lengths(self, batch: int):
+        return B.spec_get_lengths(self.ctx, batch)

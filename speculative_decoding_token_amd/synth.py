@@ -226,3 +226,17 @@ def weights_to_numpy(w: Dict[str, object]) -> Dict[str, object]:
     }
     out["lm_head"] = out["embed"] if w["lm_head"] is w["embed"] else cv(w["lm_head"])
     return out
+
+
+def weights_to(w: Dict[str, object], device: str) -> Dict[str, object]:
+    """Copy a weight dict to ``device``, keeping a tied LM head tied (one tensor)."""
+    def mv(x):
+        return None if x is None else x.to(device)
+    out = {
+        "embed": mv(w["embed"]),
+        "final_norm": mv(w["final_norm"]),
+        "layers": [{k: mv(v) for k, v in lw.items()} for lw in w["layers"]],
+        "mtp": None if w.get("mtp") is None else {k: mv(v) for k, v in w["mtp"].items()},
+    }
+    out["lm_head"] = out["embed"] if w["lm_head"] is w["embed"] else mv(w["lm_head"])
+    return out

@@ -1,0 +1,223 @@
+"""GPU parity of the truncation, sampling, accept, Philox and n-gram kernels against the
+oracle, through the C ABI, on the same seeded inputs and the same Philox counters.
+
+Full-size case: the accept workload of 64 sequences with K in {1, 2, 4, 8} drafts over a
+151936-token vocabulary, target logits N(0, 3) and draft logits = target + N(0, sigma),
+sigma in {0.5, 1, 2}, temperature 1, top_k 20, top_p 0.95.  The GPU runs every row at that
+size; the oracle recomputes a sample of sequences one by one.  Smaller cases span several
+segments and ragged tails and cover the edge cases (ties, -inf, NaN, all-equal rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ngram as ong
+from oracle import philox as oph
+from oracle import sampling as osm
+from speculative_decoding_token_amd import binding as B
+from speculative_decoding_token_amd import synth
+
+pytestmark = pytest.mark.gpu
+F32 = np.float32
+
+
+def run_truncate(logits: torch.Tensor, temperature, top_k, top_p):
+    rows, V = logits.shape
+    dt = B.DTYPE_BF16 if logits.dtype == torch.bfloat16 else B.DTYPE_F32
+    cap = top_k if temperature > 0 else 1
+    out = B.Probs(rows, cap)
+    flags = torch.zeros(rows, dtype=torch.uint8, device="cuda")
+    nbytes = B.spec_truncate_scratch_size(rows, V)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    B.spec_truncate(logits, dt, rows, V, logits.stride(0), B.sampler(temperature, top_k, top_p), out, flags,
+                    scratch, nbytes)
+    torch.cuda.synchronize()
+    return out, flags.cpu().numpy()
+
+
+def check_lists(gpu: B.Probs, flags, host_logits, temperature, top_k, top_p, rows=None):
+    """GPU lists vs oracle lists; returns the number of rows excused as near-ties."""
+    lists = gpu.to_lists()
+    excused = 0
+    for r in (range(len(lists)) if rows is None else rows):
+        ref = osm.truncate(host_logits[r], temperature, top_k, top_p)
+        ids, pr = lists[r]
+        same_ids = len(ids) == len(ref.ids) and np.array_equal(ids, ref.ids)
+        if not same_ids:
+            # only a top_p cut within the near-tie band may differ
+            assert ref.margin < 1e-6 or (flags[r] & B.FLAG_TOPP_TIE), (r, ids, ref.ids)
+            excused += 1
+            continue
+        np.testing.assert_allclose(pr, ref.probs, rtol=1e-5, atol=1e-7)
+        assert (flags[r] & B.FLAG_BAD_ROW) == 0
+    return excused
+
+
+def test_philox_bitwise_over_2_20_counters():
+    n = 1 << 20
+    rng = np.random.default_rng(0)
+    ctr = rng.integers(0, 2 ** 32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    seed = 0x123456789ABCDEF
+    B.spec_philox_uniforms(seed, torch.from_numpy(ctr.view(np.int32)).cuda(), n, out)
+    torch.cuda.synchronize()
+    k0, k1 = oph.seed_key(seed)
+    x0 = oph.philox4x32_10_np(ctr[:, 0], ctr[:, 1], ctr[:, 2], ctr[:, 3], k0, k1)[0]
+    ref = ((x0 >> np.uint64(8)).astype(np.float64) / 16777216.0).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("V,rows,dtype", [(1000, 7, "bf16"), (16391, 5, "f32"), (40000, 9, "bf16"),
+                                          (151936, 6, "bf16"), (151936, 4, "f32")])
+@pytest.mark.parametrize("samp", [(1.0, 20, 0.95), (0.7, 64, 0.5), (1.3, 1, 0.9), (2.0, 40, 1.0), (0.0, 20, 0.95)])
+def test_truncate_parity(V, rows, dtype, samp):
+    g = torch.Generator().manual_seed(V * 7 + rows)
+    x = (torch.randn(rows, V, generator=g) * 3.0)
+    x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    host = x.float().numpy()
+    out, flags = run_truncate(x.cuda(), *samp)
+    check_lists(out, flags, host, *samp)
+
+
+def test_truncate_edge_rows():
+    V = 70000
+    rows = []
+    rows.append(np.zeros(V, np.float32))                          # all equal: ids 0..k-1 (fallback search)
+    r = np.full(V, -np.inf, np.float32); r[[5, 60000]] = [1.0, 1.0]; rows.append(r)   # two finite
+    r = np.random.default_rng(1).normal(0, 1, V).astype(np.float32); r[123] = np.nan; rows.append(r)  # bad
+    rows.append(np.full(V, -np.inf, np.float32))                  # empty support: bad
+    r = np.zeros(V, np.float32); r[::2] = -0.0; r[777] = 5.0; rows.append(r)           # signed zeros
+    r = np.random.default_rng(2).normal(0, 1, V).astype(np.float32); r[40000] = np.inf; rows.append(r)
+    x = torch.from_numpy(np.stack(rows))
+    out, flags = run_truncate(x.cuda(), 1.0, 20, 0.95)
+    lists = out.to_lists()
+    for i in (0, 1, 4):
+        ref = osm.truncate(rows[i], 1.0, 20, 0.95)
+        assert np.array_equal(lists[i][0], ref.ids), i
+        np.testing.assert_allclose(lists[i][1], ref.probs, rtol=1e-6)
+    for i in (2, 3, 5):
+        assert flags[i] & B.FLAG_BAD_ROW and len(lists[i][0]) == 0, i
+        with pytest.raises(ValueError):
+            osm.truncate(rows[i], 1.0, 20, 0.95)
+    # greedy on the same edge rows
+    out, flags = run_truncate(x.cuda(), 0.0, 20, 0.95)
+    lists = out.to_lists()
+    assert list(lists[0][0]) == [0] and list(lists[1][0]) == [5] and list(lists[4][0]) == [777]
+
+
+def test_sample_parity():
+    rows, V, per_seq = 48, 3000, 6
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(rows, V, generator=g) * 2
+    lists_gpu, _ = run_truncate(x.cuda(), 1.0, 20, 0.95)
+    tok = torch.empty(rows, dtype=torch.int32, device="cuda")
+    fl = torch.zeros(rows, dtype=torch.uint8, device="cuda")
+    B.spec_sample(lists_gpu, rows // per_seq, per_seq, 99, 5, 0, tok, fl)
+    torch.cuda.synchronize()
+    tok, fl = tok.cpu().numpy(), fl.cpu().numpy()
+    host = x.numpy()
+    for r in range(rows):
+        ref = osm.truncate(host[r], 1.0, 20, 0.95)
+        u = oph.uniform(99, r % per_seq + 1, 5, r // per_seq, 0)
+        t, margin = osm.sample(ref.ids, ref.probs, u)
+        assert t == tok[r] or margin < 1e-6 or fl[r] & B.FLAG_SAMPLE_TIE, r
+
+
+def accept_case(batch, K, sigma, greedy, seed, check_seqs):
+    """The accept workload end to end on the GPU; the oracle rechecks ``check_seqs``."""
+    V = 151936
+    t, d = synth.make_accept_logits(batch, K, V, sigma, seed=seed)
+    t, d = t[0], d[0]
+    temp = 0.0 if greedy else 1.0
+    tl, tf = run_truncate(t.reshape(batch * (K + 1), V).cuda(), temp, 20, 0.95)
+    dl, df = run_truncate(d.reshape(batch * K, V).cuda(), temp, 20, 0.95)
+    drafts = torch.empty((batch, K), dtype=torch.int32, device="cuda")
+    sfl = torch.zeros(batch * K, dtype=torch.uint8, device="cuda")
+    rnd = 11
+    B.spec_sample(dl, batch, K, seed, rnd, 0, drafts, sfl)
+    n = torch.empty(batch, dtype=torch.int32, device="cuda")
+    out = torch.empty((batch, K + 1), dtype=torch.int32, device="cuda")
+    tie = torch.zeros(batch, dtype=torch.uint8, device="cuda")
+    B.spec_accept_lists(drafts, dl, tl, batch, K, greedy, seed, rnd, n, out, tie)
+    torch.cuda.synchronize()
+    drafts, n, out, tie, sfl = (drafts.cpu().numpy(), n.cpu().numpy(), out.cpu().numpy(),
+                                tie.cpu().numpy(), sfl.cpu().numpy())
+    th = t.float().numpy()
+    dh = d.float().numpy()
+    tlists, dlists = tl.to_lists(), dl.to_lists()
+    excused = 0
+    for b in check_seqs:
+        ps = [osm.truncate(th[b, j], temp, 20, 0.95) for j in range(K + 1)]
+        qs = [osm.truncate(dh[b, j], temp, 20, 0.95) for j in range(K)]
+        # lists are bit-exact in ids
+        near = any(p.margin < 1e-6 for p in ps + qs)
+        for j in range(K + 1):
+            assert near or np.array_equal(tlists[b * (K + 1) + j][0], ps[j].ids)
+        # drafts sampled from q with counters (j, round, b, 0)
+        od = []
+        for j in range(K):
+            if greedy:
+                od.append(qs[j].argmax())
+            else:
+                tok, m = osm.sample(qs[j].ids, qs[j].probs, oph.uniform(seed, j + 1, rnd, b, 0))
+                near = near or m < 1e-6
+                od.append(tok)
+        if near or sfl[b * K:(b + 1) * K].any():
+            excused += 1
+            continue
+        assert list(drafts[b]) == od, b
+        if greedy:
+            r = osm.accept(od, qs, ps, True)
+        else:
+            ua = [oph.uniform(seed, j + 1, rnd, b, 1) for j in range(K)]
+            ur = oph.uniform(seed, 0, rnd, b, 2)
+            r = osm.accept(od, qs, ps, False, ua, ur)
+        if r.margin < 1e-6 or tie[b]:
+            excused += 1
+            continue
+        assert n[b] == r.n and list(out[b, :r.n + 1]) == r.tokens, (b, n[b], r.n)
+    return n, excused
+
+
+@pytest.mark.parametrize("K", [1, 2, 4, 8])
+@pytest.mark.parametrize("sigma", [0.5, 1.0, 2.0])
+def test_accept_workload_full_size(K, sigma):
+    n, excused = accept_case(64, K, sigma, False, seed=int(K * 10 + sigma * 4), check_seqs=range(0, 64, 16))
+    assert excused <= 1
+    assert n.min() >= 0 and n.max() <= K
+
+
+def test_accept_workload_greedy_full_size():
+    n, excused = accept_case(64, 4, 1.0, True, seed=5, check_seqs=range(0, 64, 8))
+    assert excused == 0
+
+
+def test_accept_workload_acceptance_falls_with_sigma():
+    means = [accept_case(64, 4, s, False, seed=3, check_seqs=[])[0].mean() for s in (0.5, 1.0, 2.0)]
+    assert means[0] > means[1] > means[2]
+
+
+def test_ngram_parity():
+    rng = np.random.default_rng(4)
+    batch, ld = 12, 600
+    ctxs = []
+    for b in range(batch):
+        n = int(rng.integers(2, ld))
+        c = list(synth.make_copy_stream(n, 50 if b % 2 else 4000, seed=b, span_lo=8, span_hi=40))
+        ctxs.append(c)
+    buf = np.zeros((batch, ld), np.int32)
+    lens = np.array([len(c) for c in ctxs], np.int32)
+    for b, c in enumerate(ctxs):
+        buf[b, :len(c)] = c
+    k = 8
+    drafts = torch.empty((batch, k), dtype=torch.int32, device="cuda")
+    nf = torch.empty(batch, dtype=torch.int32, device="cuda")
+    match = torch.empty((batch, 2), dtype=torch.int32, device="cuda")
+    B.spec_ngram_match(torch.from_numpy(buf).cuda(), torch.from_numpy(lens).cuda(), batch, ld, k, 3, 16,
+                       drafts, nf, match)
+    torch.cuda.synchronize()
+    drafts, nf, match = drafts.cpu().numpy(), nf.cpu().numpy(), match.cpu().numpy()
+    for b, c in enumerate(ctxs):
+        d, ell, e = ong.ngram_draft(c, k, 3, 16)
+        assert nf[b] == len(d) and list(drafts[b, :len(d)]) == d, b
+        assert (match[b, 0], match[b, 1]) == ((ell, e) if d else (0, -1))
