@@ -79,7 +79,16 @@ struct GemmArgs {
   const void* w[3];   // weight matrices [rows_i, K]; EPI_QKV uses three, EPI_SWIGLU two
   int rows[3];
   int K;
-  const void* x;      // [M, K] model dtype
+  const void* x;      // [M, K] model dtype (GEMM input as stored)
+  // fused RMSNorm input (bf16 path): when xres is set the GEMM input is
+  // bf16(xres * rsqrt(mean(xres^2) + eps) * gain), with the sum of squares of row m given as
+  // np_in partial sums ss_in[m * ss_ld + 0 .. np_in-1] added in order
+  const float* xres;
+  const void* gain;
+  const float* ss_in;
+  int np_in, ss_ld;
+  float eps;
+  float* ss_out;      // EPI_RESID: partial sums of squares of the updated rows, one per block
   RowMap rm;
   // outputs
   float* out;         // EPI_STORE / EPI_RESID: [M, ld]
@@ -106,15 +115,22 @@ struct AttnArgs {
 };
 
 constexpr int ATTN_CHUNK = 64;
+constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions
 constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)
 
 hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStream_t st);
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        hipStream_t st);
+                        float* ss, int ss_ld, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, int M, int d,
                           void* y, hipStream_t st);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st);
+// The fused RMSNorm prologue keeps the M normalized rows in LDS: M * (K + 8) * 2 bytes,
+// used when it fits GEMM_NORM_LDS_MAX; otherwise launch_norm_apply writes them first.
+constexpr size_t GEMM_NORM_LDS_MAX = 64 * 1024;
+size_t gemm_norm_lds_bytes(int M, int K);
+hipError_t launch_norm_apply(const float* x, const void* gain, const float* ss, int np, int ss_ld, float eps,
+                             int M, int K, void* y, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_copy_rows(const int32_t* src, int src_ld, int32_t* dst, int n, hipStream_t st);

@@ -33,19 +33,33 @@ __global__ void rope_table_kernel(float2* table, int cap, int hd, double theta) 
 }
 
 // ---------------------------------------------------------------- embedding gather
-// Row m = (seq b, i): token first[b*first_ld] for i == 0, else rest[b*rest_ld + i-1].
+// Row m = (seq b, i): token first[b*first_ld] for i == 0, else rest[b*rest_ld + i-1].  Also
+// leaves the row's sum of squares in ss[m * ss_ld] (fixed reduction order) for the fused
+// RMSNorm of the first projection.
 template <int DT>
 __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vocab,
                                                     const int32_t* first, int first_ld,
                                                     const int32_t* rest, int rest_ld, int mseq,
-                                                    float* x) {
+                                                    float* x, float* ss, int ss_ld) {
   using A = Act<DT>;
-  const int m = blockIdx.x, b = m / mseq, i = m % mseq;
+  __shared__ float red[256];
+  const int m = blockIdx.x, b = m / mseq, i = m % mseq, t = threadIdx.x;
   const int tok = (i == 0) ? first[(int64_t)b * first_ld] : rest[(int64_t)b * rest_ld + i - 1];
   const bool ok = tok >= 0 && tok < vocab;
   const typename A::T* row = (const typename A::T*)E + (int64_t)(ok ? tok : 0) * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x)
-    x[(int64_t)m * d + c] = ok ? A::load(row, c) : __builtin_nanf("");
+  float sq = 0.0f;
+  for (int c = t; c < d; c += blockDim.x) {
+    const float v = ok ? A::load(row, c) : __builtin_nanf("");
+    x[(int64_t)m * d + c] = v;
+    sq += v * v;
+  }
+  red[t] = sq;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] += red[t + s];
+    __syncthreads();
+  }
+  if (ss && t == 0) ss[(int64_t)m * ss_ld] = red[0];
 }
 
 // ---------------------------------------------------------------- RMSNorm
@@ -108,13 +122,63 @@ SPEC_DEVINL void gemm_epilogue(const GemmArgs& a, int mat, int m, int n, float v
 // A = 16 weight rows x 32 k (lane l loads 16 bytes of row l%16 at k offset 8*(l/16)),
 // B = 32 k x 16 token rows (the same k slice of x, zero for rows >= M).  The MFMA's 16x
 // padding of the token dimension costs nothing here: the pass is bound by streaming W.
+//
+// With NORM the input is the float32 residual stream, normalized on the fly: the block
+// first adds up the row's sum-of-squares partials (left by the previous residual update)
+// and each lane scales its 8 values by rsqrt(mean + eps) and the gain before rounding them
+// to bf16, so RMSNorm costs no launch and no extra pass over the activations.  A residual
+// epilogue leaves, per block, the sum of squares of its 16 updated columns of each row.
 constexpr int GEMM_NW = 8;
 constexpr int GEMM_U = 8;
 
-template <int EPI, int NT>
+SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// RMSNorm pieces shared by the fused prologue and the stand-alone kernel, so both give the
+// same bits.  row_inv: one full wavefront adds the row's sum-of-squares partials (lane j takes
+// partials j, j+64, ... in order, then a fixed xor butterfly) and returns 1/sqrt(mean + eps).
+SPEC_DEVINL float row_inv(const float* ss, int np, int K, float eps, int lane) {
+  float acc = 0.0f;
+  for (int p = lane; p < np; p += 64) acc += ss[p];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  return 1.0f / sqrtf(acc / (float)K + eps);
+}
+// bf16(x * inv * gain) for 8 consecutive elements
+SPEC_DEVINL uint4 norm8(const float* x, const bf16_t* gain, float inv) {
+  const float4 x0 = *(const float4*)(x);
+  const float4 x1 = *(const float4*)(x + 4);
+  const uint4 gg = *(const uint4*)(gain);
+  return make_uint4(
+      pack_bf16x2(x0.x * inv * __uint_as_float(gg.x << 16), x0.y * inv * __uint_as_float(gg.x & 0xFFFF0000u)),
+      pack_bf16x2(x0.z * inv * __uint_as_float(gg.y << 16), x0.w * inv * __uint_as_float(gg.y & 0xFFFF0000u)),
+      pack_bf16x2(x1.x * inv * __uint_as_float(gg.z << 16), x1.y * inv * __uint_as_float(gg.z & 0xFFFF0000u)),
+      pack_bf16x2(x1.z * inv * __uint_as_float(gg.w << 16), x1.w * inv * __uint_as_float(gg.w & 0xFFFF0000u)));
+}
+
+// Stand-alone RMSNorm of bf16 models (rows too many for the fused prologue's LDS).
+__global__ __launch_bounds__(256) void norm_apply_kernel(const float* x, const void* gain, const float* ss,
+                                                         int np, int ss_ld, float eps, int K, bf16_t* y) {
+  __shared__ float s_inv;
+  const int m = blockIdx.x, t = threadIdx.x;
+  if (t < 64) {
+    const float iv = row_inv(ss + (int64_t)m * ss_ld, np, K, eps, t);
+    if (t == 0) s_inv = iv;
+  }
+  __syncthreads();
+  const float iv = s_inv;
+  for (int k8 = t * 8; k8 < K; k8 += 256 * 8)
+    *(uint4*)(y + (int64_t)m * K + k8) = norm8(x + (int64_t)m * K + k8, (const bf16_t*)gain + k8, iv);
+}
+
+template <int EPI, int NT, bool NORM>
 __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int TILES = (EPI == EPI_SWIGLU) ? 2 : 1;
   __shared__ f32x4_t red[GEMM_NW][TILES][NT][64];
+  __shared__ float s_inv[16 * NT];
+  __shared__ float s_sq[16 * NT][17];
+  extern __shared__ __attribute__((aligned(16))) bf16_t xs[];  // NORM: [M][K + 8] normalized rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int mat = 0, r0 = blockIdx.x * 16;
   if (EPI == EPI_QKV) {
@@ -128,18 +192,42 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
   const int K = a.K, nsteps = K >> 5, M = a.rm.M;
+  const int XP = K + 8;
   const int koff = 8 * (lane >> 4);
   const bf16_t* wp[TILES];
   wp[0] = (const bf16_t*)a.w[mat] + (int64_t)(r0 + (lane & 15)) * K + koff;
   if (TILES == 2) wp[TILES - 1] = (const bf16_t*)a.w[1] + (int64_t)(r0 + (lane & 15)) * K + koff;
-  const bf16_t* xp[NT];
   bool xv[NT];
+  int64_t xrow[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int m = nt * 16 + (lane & 15);
     xv[nt] = m < M;
-    xp[nt] = (const bf16_t*)a.x + (int64_t)(xv[nt] ? m : 0) * K + koff;
+    xrow[nt] = NORM ? (int64_t)(xv[nt] ? m : 0) * XP + koff : (int64_t)(xv[nt] ? m : 0) * K + koff;
   }
+  // first group of weights in flight before anything else
+  uint4 wa[TILES][GEMM_U];
+#pragma unroll
+  for (int u = 0; u < GEMM_U; ++u) {
+    const int s = wave + u * GEMM_NW;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+      wa[t][u] = s < nsteps ? *(const uint4*)(wp[t] + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
+  }
+  if (NORM) {
+    for (int m = wave; m < M; m += GEMM_NW) {
+      const float iv = row_inv(a.ss_in + (int64_t)m * a.ss_ld, a.np_in, K, a.eps, lane);
+      if (lane == 0) s_inv[m] = iv;
+    }
+    __syncthreads();
+    const int per_row = K / 8;
+    for (int idx = threadIdx.x; idx < M * per_row; idx += GEMM_NW * 64) {
+      const int m = idx / per_row, k8 = (idx % per_row) * 8;
+      *(uint4*)(xs + m * XP + k8) = norm8(a.xres + (int64_t)m * K + k8, (const bf16_t*)a.gain + k8, s_inv[m]);
+    }
+    __syncthreads();
+  }
+
   f32x4_t acc[TILES][NT];
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
@@ -147,18 +235,28 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int s0 = wave; s0 < nsteps; s0 += GEMM_NW * GEMM_U) {
-    uint4 wa[TILES][GEMM_U];
     uint4 xb[NT][GEMM_U];
 #pragma unroll
     for (int u = 0; u < GEMM_U; ++u) {
       const int s = s0 + u * GEMM_NW;
       const bool ok = s < nsteps;
 #pragma unroll
-      for (int t = 0; t < TILES; ++t)
-        wa[t][u] = ok ? *(const uint4*)(wp[t] + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        if (NORM)
+          xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)(xs + xrow[nt] + s * 32) : make_uint4(0, 0, 0, 0);
+        else
+          xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)((const bf16_t*)a.x + xrow[nt] + (int64_t)s * 32)
+                                     : make_uint4(0, 0, 0, 0);
+      }
+    }
+    // next group of weights while this one is multiplied
+    uint4 wn[TILES][GEMM_U];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)(xp[nt] + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < GEMM_U; ++u) {
+      const int s = s0 + (GEMM_U + u) * GEMM_NW;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+        wn[t][u] = s < nsteps ? *(const uint4*)(wp[t] + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < GEMM_U; ++u)
@@ -169,6 +267,10 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
           acc[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, wa[t][u]), __builtin_bit_cast(bf16x8_t, xb[nt][u]),
               acc[t][nt], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < GEMM_U; ++u)
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) wa[t][u] = wn[t][u];
   }
 #pragma unroll
   for (int t = 0; t < TILES; ++t)
@@ -189,7 +291,25 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
     const int m = nt * 16 + (l & 15);
     const int n = r0 + 4 * (l >> 4) + r;
-    if (m < M) gemm_epilogue<SPEC_DTYPE_BF16, EPI>(a, mat, m, n, v[0], v[TILES - 1]);
+    if (m < M) {
+      if (EPI == EPI_RESID) {
+        const float xn = a.out[(int64_t)m * a.ld + n] + v[0];
+        a.out[(int64_t)m * a.ld + n] = xn;
+        s_sq[m][n - r0] = xn * xn;
+      } else {
+        gemm_epilogue<SPEC_DTYPE_BF16, EPI>(a, mat, m, n, v[0], v[TILES - 1]);
+      }
+    }
+  }
+  if (EPI == EPI_RESID && a.ss_out) {
+    __syncthreads();
+    const int m = threadIdx.x;
+    if (m < M && m < 16 * NT) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss += s_sq[m][j];
+      a.ss_out[(int64_t)m * a.ss_ld + blockIdx.x] = ss;
+    }
   }
 }
 
@@ -402,25 +522,233 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
   }
 }
 
+// bf16 version on MFMA.  Scores S^T = K Q^T come out of v_mfma_f32_16x16x32_bf16 with lane
+// l holding query row l%16 and keys 4*(l/16)+r of each 16-key tile; those are exactly the
+// A-operand slots of the following P V product for two key tiles at once (with the key
+// order inside a 32-key step permuted the same way on the V side), so P never leaves the
+// registers.  V is staged transposed in LDS so that each lane's 8 keys are two 8-byte
+// reads.  P is rounded to bf16 for the product and the row sum uses the same rounded
+// values, so the weights of a row still sum to one.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
+  constexpr int C = ATTN_CHUNK;  // 64 keys
+  constexpr int KP = HD + 8;     // LDS pitch of q and K rows (bf16 elements)
+  constexpr int VP = C + 8;      // LDS pitch of V^T rows
+  constexpr int HALF = HD / 2;
+  extern __shared__ __attribute__((aligned(16))) char smraw[];
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const CacheView& cv = a.cache;
+  const int mseq = a.rm.mseq, G = a.n_q / cv.n_kv;
+  const int L = a.rm.len[b] + a.rm.pos_off;
+  const int total = L + mseq;
+  const int c0 = chunk * C;
+  if (c0 >= total) return;
+  const int R = mseq * G, QT = (R + 15) / 16;
+  const int q_dim = a.n_q * HD, kv_dim = cv.n_kv * HD;
+  bf16_t* qs = (bf16_t*)smraw;   // [QT*16][KP]
+  bf16_t* ks = qs + QT * 16 * KP;  // [C][KP]
+  bf16_t* vt = ks + C * KP;        // [HD][VP]
+
+  const int64_t cbase = ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap) * HD;
+  bf16_t* kc = (bf16_t*)cv.k + cbase;
+  const bf16_t* vc = (const bf16_t*)cv.v + cbase;
+  // cached keys and values, 16 bytes at a time, issued before anything else; zeros past the end
+  constexpr int NV = C * (HD / 8) / 256;
+  uint4 kreg[NV], vreg[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int idx = t + 256 * v;
+    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
+    kreg[v] = p < L ? *(const uint4*)(kc + (int64_t)p * HD + d8) : make_uint4(0, 0, 0, 0);
+    vreg[v] = p < total ? *(const uint4*)(vc + (int64_t)p * HD + d8) : make_uint4(0, 0, 0, 0);
+  }
+  for (int idx = t; idx < QT * 16 * HALF; idx += 256) {
+    const int r = idx / HALF, d = idx % HALF;
+    bf16_t lo = 0, hi = 0;
+    if (r < R) {
+      const int i = r / G, h = kvh * G + r % G;
+      const float* src = a.q_stage + (int64_t)(b * mseq + i) * q_dim + h * HD;
+      const float x0 = src[d], x1 = src[d + HALF];
+      const float2 cs = a.rope[(int64_t)(L + i) * HALF + d];
+      lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
+      hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
+    }
+    qs[r * KP + d] = lo;
+    qs[r * KP + d + HALF] = hi;
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int idx = t + 256 * v;
+    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
+    if (p < L || p >= total) *(uint4*)(ks + j * KP + d8) = kreg[v];
+    const uint32_t w[4] = {vreg[v].x, vreg[v].y, vreg[v].z, vreg[v].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vt[(d8 + 2 * e) * VP + j] = (bf16_t)(w[e] & 0xFFFFu);
+      vt[(d8 + 2 * e + 1) * VP + j] = (bf16_t)(w[e] >> 16);
+    }
+  }
+  // new keys in this chunk: rotate, round, use, and write to the cache
+  {
+    const int p0 = max(c0, L), p1 = min(c0 + C, total);
+    for (int idx = t; idx < (p1 - p0) * HALF; idx += 256) {
+      const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
+      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
+      const float x0 = src[d], x1 = src[d + HALF];
+      const float2 cs = a.rope[(int64_t)p * HALF + d];
+      const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
+      const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
+      ks[j * KP + d] = lo;
+      ks[j * KP + d + HALF] = hi;
+      kc[(int64_t)p * HD + d] = lo;
+      kc[(int64_t)p * HD + d + HALF] = hi;
+    }
+  }
+  __syncthreads();
+
+  const int n = lane & 15, g = lane >> 4;
+  for (int qt = wave; qt < QT; qt += 4) {
+    f32x4_t s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < HD / 32; ++st) {
+        const uint4 av = *(const uint4*)(ks + (kt * 16 + n) * KP + st * 32 + 8 * g);
+        const uint4 bv = *(const uint4*)(qs + (qt * 16 + n) * KP + st * 32 + 8 * g);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                        __builtin_bit_cast(bf16x8_t, bv), s[kt], 0, 0, 0);
+      }
+    }
+    // lane holds query row r = qt*16 + n, keys c0 + kt*16 + 4g + rr
+    const int r = qt * 16 + n;
+    const int pos = (r < R) ? L + r / G : -1;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int p = c0 + kt * 16 + 4 * g + rr;
+        const float v = (p <= pos) ? s[kt][rr] * a.scale : -__builtin_inff();
+        s[kt][rr] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    uint32_t pk[4][2];  // P as packed bf16 pairs, per key tile
+    float l = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float e[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float v = s[kt][rr];
+        const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : expf(v - mx);
+        e[rr] = bf16_to_f32(f32_to_bf16(x));
+        l += e[rr];
+      }
+      pk[kt][0] = (uint32_t)f32_to_bf16(e[0]) | ((uint32_t)f32_to_bf16(e[1]) << 16);
+      pk[kt][1] = (uint32_t)f32_to_bf16(e[2]) | ((uint32_t)f32_to_bf16(e[3]) << 16);
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    // A operand of step st: slots 0-3 = keys 32st + 4g + (0..3), slots 4-7 = 32st + 16 + 4g + (0..3)
+    bf16x8_t pa[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      pa[st] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * st][0], pk[2 * st][1], pk[2 * st + 1][0],
+                                                       pk[2 * st + 1][1]));
+    // this lane's rows of the output tile: 4g + rr
+    int rowoff[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r2 = qt * 16 + 4 * g + rr;
+      rowoff[rr] = -1;
+      if (r2 < R) {
+        const int i2 = r2 / G, h2 = kvh * G + r2 % G;
+        rowoff[rr] = (((b * mseq + i2) * a.n_q + h2) * a.nchunk + chunk) * (HD + 2);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) {
+      f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16_t* vr = vt + (dt * 16 + n) * VP + st * 32 + 4 * g;
+        const uint2 x0 = *(const uint2*)(vr);
+        const uint2 x1 = *(const uint2*)(vr + 16);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[st], __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y)),
+                                                    o, 0, 0, 0);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (rowoff[rr] >= 0) a.part[rowoff[rr] + dt * 16 + n] = o[rr];
+    }
+    if (g == 0 && r < R) {
+      const int i = r / G, h = kvh * G + r % G;
+      float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
+      P[HD] = mx;
+      P[HD + 1] = l;
+    }
+  }
+}
+
+// Merges the chunks of one (row, head): weights exp(m_c - max) from one wavefront (every
+// chunk statistic loaded at once), then the weighted value sums with the chunks split over
+// 256/head_dim thread groups and added back in a fixed order.
 template <int DT>
-__global__ void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   using A = Act<DT>;
-  const int row = blockIdx.x, d = threadIdx.x;
+  __shared__ float s_w[ATTN_MAX_CHUNKS];
+  __shared__ float s_part[256];
+  __shared__ float s_den;
+  const int row = blockIdx.x, t = threadIdx.x;
   const int hd = a.cache.hd;
   const int m = row / a.n_q, h = row % a.n_q;
   const int b = m / a.rm.mseq, i = m % a.rm.mseq;
   const int pos = a.rm.len[b] + a.rm.pos_off + i;
   const int nch = pos / ATTN_CHUNK + 1;
   const float* P = a.part + (int64_t)row * a.nchunk * (hd + 2);
-  float mx = -__builtin_inff();
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, P[c * (hd + 2) + hd]);
-  float den = 0.0f, o = 0.0f;
-  for (int c = 0; c < nch; ++c) {
-    const float w = expf(P[c * (hd + 2) + hd] - mx);
-    den += P[c * (hd + 2) + hd + 1] * w;
-    o += P[c * (hd + 2) + d] * w;
+  if (t < 64) {
+    constexpr int PER = ATTN_MAX_CHUNKS / 64;
+    float mc[PER], lc[PER];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int c = t + 64 * q;
+      mc[q] = c < nch ? P[c * (hd + 2) + hd] : -__builtin_inff();
+      lc[q] = c < nch ? P[c * (hd + 2) + hd + 1] : 0.0f;
+      mx = fmaxf(mx, mc[q]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float den = 0.0f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int c = t + 64 * q;
+      if (c < nch) {
+        const float w = expf(mc[q] - mx);
+        s_w[c] = w;
+        den += lc[q] * w;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    if (t == 0) s_den = den;
   }
-  A::store((typename A::T*)a.out, (int64_t)m * a.n_q * hd + h * hd + d, o / den);
+  __syncthreads();
+  const int groups = 256 / hd, g = t / hd, d = t % hd;
+  float o = 0.0f;
+#pragma unroll 8
+  for (int c = g; c < nch; c += groups) o += P[c * (hd + 2) + d] * s_w[c];
+  s_part[t] = o;
+  __syncthreads();
+  if (t < hd) {
+    float tot = 0.0f;
+    for (int q = 0; q < groups; ++q) tot += s_part[q * hd + t];
+    A::store((typename A::T*)a.out, (int64_t)m * a.n_q * hd + h * hd + t, tot / s_den);
+  }
 }
 
 // ---------------------------------------------------------------- small state kernels
@@ -462,13 +790,13 @@ hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStr
 
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        hipStream_t st) {
+                        float* ss, int ss_ld, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16)
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_BF16>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld);
   else
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_F32>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld);
   return hipGetLastError();
 }
 
@@ -481,15 +809,24 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, i
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, bool NORM>
 static hipError_t gemm_bf16_nt(const GemmArgs& a, int blocks, hipStream_t st) {
   const int M = a.rm.M;
+  const size_t lds = NORM ? gemm_norm_lds_bytes(M, a.K) : 0;
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1>), dim3(blocks), dim3(GEMM_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
   else if (M <= 32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2>), dim3(blocks), dim3(GEMM_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4>), dim3(blocks), dim3(GEMM_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+size_t gemm_norm_lds_bytes(int M, int K) { return (size_t)M * (K + 8) * 2; }
+
+hipError_t launch_norm_apply(const float* x, const void* gain, const float* ss, int np, int ss_ld, float eps,
+                             int M, int K, void* y, hipStream_t st) {
+  hipLaunchKernelGGL(norm_apply_kernel, dim3(M), dim3(256), 0, st, x, gain, ss, np, ss_ld, eps, K, (bf16_t*)y);
   return hipGetLastError();
 }
 
@@ -499,11 +836,16 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st) {
   if (a.rm.M == 0 || rows == 0) return hipSuccess;
   if (dtype == SPEC_DTYPE_BF16) {
     const int blocks = rows / 16;
+    // normalized inputs feed the QKV, gate/up and LM-head projections; the residual ones
+    // (output and down projections) read the attention output / SwiGLU product as stored
     switch (epi) {
-      case EPI_STORE: return gemm_bf16_nt<EPI_STORE>(a, blocks, st);
-      case EPI_RESID: return gemm_bf16_nt<EPI_RESID>(a, blocks, st);
-      case EPI_QKV: return gemm_bf16_nt<EPI_QKV>(a, blocks, st);
-      default: return gemm_bf16_nt<EPI_SWIGLU>(a, blocks, st);
+      case EPI_STORE:
+        return a.xres ? gemm_bf16_nt<EPI_STORE, true>(a, blocks, st) : gemm_bf16_nt<EPI_STORE, false>(a, blocks, st);
+      case EPI_RESID: return gemm_bf16_nt<EPI_RESID, false>(a, blocks, st);
+      case EPI_QKV:
+        return a.xres ? gemm_bf16_nt<EPI_QKV, true>(a, blocks, st) : gemm_bf16_nt<EPI_QKV, false>(a, blocks, st);
+      default:
+        return a.xres ? gemm_bf16_nt<EPI_SWIGLU, true>(a, blocks, st) : gemm_bf16_nt<EPI_SWIGLU, false>(a, blocks, st);
     }
   }
   const int blocks = (rows + 3) / 4;
@@ -524,11 +866,18 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   dim3 g1(a.nchunk, a.cache.n_kv, batch);
   dim3 g2(a.rm.M * a.n_q);
   if (dtype == SPEC_DTYPE_BF16) {
-    hipLaunchKernelGGL(attn_chunk_kernel<SPEC_DTYPE_BF16>, g1, dim3(256), lds, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<SPEC_DTYPE_BF16>, g2, dim3(hd), 0, st, a);
+    const int QT = (R + 15) / 16;
+    const size_t lds2 = 2 * ((size_t)QT * 16 * (hd + 8) + (size_t)ATTN_CHUNK * (hd + 8) + (size_t)hd * (ATTN_CHUNK + 8));
+    if (hd == 128)
+      hipLaunchKernelGGL(attn_chunk_mfma_kernel<128>, g1, dim3(256), lds2, st, a);
+    else if (hd == 64)
+      hipLaunchKernelGGL(attn_chunk_mfma_kernel<64>, g1, dim3(256), lds2, st, a);
+    else
+      hipLaunchKernelGGL(attn_chunk_mfma_kernel<32>, g1, dim3(256), lds2, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<SPEC_DTYPE_BF16>, g2, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_chunk_kernel<SPEC_DTYPE_F32>, g1, dim3(256), lds, st, a);
-    hipLaunchKernelGGL(attn_combine_kernel<SPEC_DTYPE_F32>, g2, dim3(hd), 0, st, a);
+    hipLaunchKernelGGL(attn_combine_kernel<SPEC_DTYPE_F32>, g2, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

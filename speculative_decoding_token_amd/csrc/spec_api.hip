@@ -37,6 +37,7 @@ struct Model {
   void* h = nullptr;
   float* logits = nullptr;
   float* part = nullptr;
+  float* ss = nullptr;  // [Mmax][d/16] partial sums of squares of the residual rows
   float2* rope = nullptr;
 };
 
@@ -238,6 +239,7 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.h = cv.take<void>((size_t)m.Mmax * d.d_ffn * m.act);
   m.logits = cv.take<float>((size_t)m.Mmax * d.vocab * 4);
   m.part = cv.take<float>((size_t)m.Mmax * d.n_q_heads * m.nchunk * (d.head_dim + 2) * 4);
+  m.ss = cv.take<float>((size_t)m.Mmax * (d.d_model / 16 + 1) * 4);
   m.rope = cv.take<float2>((size_t)cap * (d.head_dim / 2) * sizeof(float2));
 }
 
@@ -272,6 +274,8 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
   const spec_config& g = c->cfg;
   if (g.max_batch < 1 || g.max_ctx < 1 || g.max_k < 0 || g.max_k > SPEC_MAX_K)
     return fail(nullptr, SPEC_E_INVAL, "max_batch / max_ctx / max_k out of range");
+  if (g.max_ctx + g.max_k + 2 > ATTN_CHUNK * ATTN_MAX_CHUNKS)
+    return fail(nullptr, SPEC_E_UNSUPPORTED, "max_ctx + max_k + 2 > %d", ATTN_CHUNK * ATTN_MAX_CHUNKS);
   int rc = validate_sampler(g.sampler);
   if (rc) return fail(nullptr, rc, "sampler: temperature / top_k (1..%d) / top_p", SPEC_TOPK_MAX);
   const int maxk = std::max(g.max_k, 1);
@@ -326,11 +330,35 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
   const int M = B * mseq;
   const int dt = d.dtype;
   const int P = 16 * m.mi;
-  LAUNCH(c, P + PROF_EMBED, launch_embed(dt, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld, M, mseq, m.x, st));
+  // bf16 models fuse each RMSNorm into the projection that consumes it (see gemm_bf16_kernel);
+  // f32 models run it as its own kernel
+  const bool fused = dt == SPEC_DTYPE_BF16;
+  const int ss_ld = d.d_model / 16 + 1;
+  LAUNCH(c, P + PROF_EMBED, launch_embed(dt, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld, M, mseq,
+                                         m.x, fused ? m.ss : nullptr, ss_ld, st));
+  int np = 1;  // partial sums of squares per row available in m.ss
   RowMap rm{M, mseq, c->len, pos_off};
+  // the normalized rows live in the consuming projection's LDS when they fit; else a
+  // stand-alone kernel with the same arithmetic writes them to m.xn first
+  const bool in_lds = gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
+  auto norm_input = [&](GemmArgs& g, const void* gain) -> int {
+    if (fused && in_lds) {
+      g.xres = m.x;
+      g.gain = gain;
+      g.ss_in = m.ss;
+      g.np_in = np;
+      g.ss_ld = ss_ld;
+      g.eps = d.rms_eps;
+    } else {
+      if (fused)
+        LAUNCH(c, P + PROF_NORM, launch_norm_apply(m.x, gain, m.ss, np, ss_ld, d.rms_eps, M, d.d_model, m.xn, st));
+      g.x = m.xn;
+    }
+    return SPEC_OK;
+  };
   for (int l = 0; l < d.n_layers; ++l) {
     const spec_layer_weights& w = m.layers[l];
-    LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.attn_norm, d.rms_eps, M, d.d_model, m.xn, st));
+    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.attn_norm, d.rms_eps, M, d.d_model, m.xn, st));
     GemmArgs g{};
     g.w[0] = w.wq;
     g.w[1] = w.wk;
@@ -339,7 +367,7 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     g.rows[1] = m.kv_dim;
     g.rows[2] = m.kv_dim;
     g.K = d.d_model;
-    g.x = m.xn;
+    if (norm_input(g, w.attn_norm)) return SPEC_E_HIP;
     g.rm = rm;
     g.q_stage = m.qst;
     g.k_stage = m.kst;
@@ -367,14 +395,17 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     o.rm = rm;
     o.out = m.x;
     o.ld = d.d_model;
+    o.ss_out = fused ? m.ss : nullptr;
+    o.ss_ld = ss_ld;
     LAUNCH(c, P + PROF_OPROJ, launch_gemm(dt, EPI_RESID, o, st));
-    LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.ffn_norm, d.rms_eps, M, d.d_model, m.xn, st));
+    np = d.d_model / 16;
+    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.ffn_norm, d.rms_eps, M, d.d_model, m.xn, st));
     GemmArgs gu{};
     gu.w[0] = w.wg;
     gu.w[1] = w.wu;
     gu.rows[0] = d.d_ffn;
     gu.K = d.d_model;
-    gu.x = m.xn;
+    if (norm_input(gu, w.ffn_norm)) return SPEC_E_HIP;
     gu.rm = rm;
     gu.h = m.h;
     LAUNCH(c, P + PROF_GATEUP, launch_gemm(dt, EPI_SWIGLU, gu, st));
@@ -386,15 +417,17 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     dn.rm = rm;
     dn.out = m.x;
     dn.ld = d.d_model;
+    dn.ss_out = fused ? m.ss : nullptr;
+    dn.ss_ld = ss_ld;
     LAUNCH(c, P + PROF_DOWN, launch_gemm(dt, EPI_RESID, dn, st));
   }
   if (logits) {
-    LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, d.final_norm, d.rms_eps, M, d.d_model, m.xn, st));
+    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, d.final_norm, d.rms_eps, M, d.d_model, m.xn, st));
     GemmArgs lm{};
     lm.w[0] = d.lm_head;
     lm.rows[0] = d.vocab;
     lm.K = d.d_model;
-    lm.x = m.xn;
+    if (norm_input(lm, d.final_norm)) return SPEC_E_HIP;
     lm.rm = rm;
     lm.out = logits;
     lm.ld = d.vocab;

@@ -194,3 +194,29 @@ def test_profile_counts_launches():
     # draft: 4 forwards of 1 layer each
     assert prof["draft.gate_up"]["launches"] == 4 and prof["draft.sample"]["launches"] == 4
     assert all(v["ms"] > 0 for v in prof.values())
+
+
+def test_fused_and_standalone_norm_paths_bit_identical():
+    """A wide bf16 model (d 4096): at K = 4 the RMSNorm runs in the projections' LDS
+    prologue, at K = 16 (17 rows do not fit) in its own kernel.  Rows 0..4 of both verifies
+    see the same tokens at the same positions and must agree bit for bit (and with the
+    oracle within the bf16 tolerance)."""
+    shape = synth.ModelShape("wide", 2, 4096, 32, 8, 128, 256, 1024, "bf16")
+    w = synth.weights_to(synth.make_weights(shape, 4, std=0.02), "cuda")
+    L = 70
+    k, v = synth.make_kv_prefix(shape, L, 4)
+    t0 = int(synth.make_tokens(1, shape.vocab, 5)[0])
+    drafts = [int(x) for x in synth.make_tokens(16, shape.vocab, 6)]
+    logits = {}
+    for K in (4, 16):
+        eng = runtime.Engine(shape, w, None, None, temperature=0.0, max_ctx=100, max_k=16)
+        eng.load_prefix(0, 0, k.cuda(), v.cuda(), L)
+        eng.set_last(torch.tensor([t0], dtype=torch.int32).cuda())
+        c = eng.cycle(1, K, 0, drafts=torch.tensor([drafts[:K]], dtype=torch.int32).cuda(), keep=True)
+        logits[K] = c.logits[0]
+    assert torch.equal(logits[4], logits[16][:5])
+    spec = om.Spec.from_shape(shape)
+    kv = om.KVCache(spec, L + 20)
+    kv.load_prefix(synth.to_numpy_f32(k), synth.to_numpy_f32(v))
+    ref = om.forward_tokens(spec, synth.weights_to_numpy(w), kv, [t0] + drafts)
+    assert_rows_close(logits[16].cpu().numpy(), ref, RTOL_BF16)
