@@ -128,9 +128,6 @@ SPEC_DEVINL void gemm_epilogue(const GemmArgs& a, int mat, int m, int n, float v
 // and each lane scales its 8 values by rsqrt(mean + eps) and the gain before rounding them
 // to bf16, so RMSNorm costs no launch and no extra pass over the activations.  A residual
 // epilogue leaves, per block, the sum of squares of its 16 updated columns of each row.
-constexpr int GEMM_NW = 8;
-constexpr int GEMM_U = 8;
-
 SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
@@ -172,8 +169,10 @@ __global__ __launch_bounds__(256) void norm_apply_kernel(const float* x, const v
     *(uint4*)(y + (int64_t)m * K + k8) = norm8(x + (int64_t)m * K + k8, (const bf16_t*)gain + k8, iv);
 }
 
-template <int EPI, int NT, bool NORM>
+template <int EPI, int NT, bool NORM, int GEMM_NW>
 __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+  // k-steps per load group: 8 KB of weights in flight per wave and tile either way
+  constexpr int GEMM_U = (GEMM_NW == 16 || NT == 4) ? 4 : 8;
   constexpr int TILES = (EPI == EPI_SWIGLU) ? 2 : 1;
   __shared__ f32x4_t red[GEMM_NW][TILES][NT][64];
   __shared__ float s_inv[16 * NT];
@@ -529,7 +528,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 // registers.  V is staged transposed in LDS so that each lane's 8 keys are two 8-byte
 // reads.  P is rounded to bf16 for the product and the row sum uses the same rounded
 // values, so the weights of a row still sum to one.
-template <int HD>
+template <int HD, int QTM>
 __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   constexpr int C = ATTN_CHUNK;  // 64 keys
   constexpr int KP = HD + 8;     // LDS pitch of q and K rows (bf16 elements)
@@ -556,37 +555,55 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   // cached keys and values, 16 bytes at a time, issued before anything else; zeros past the end
   constexpr int NV = C * (HD / 8) / 256;
   uint4 kreg[NV], vreg[NV];
+  // branch-free: addresses are clamped into the cache, out-of-range values zeroed after the load
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int idx = t + 256 * v;
     const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-    kreg[v] = p < L ? *(const uint4*)(kc + (int64_t)p * HD + d8) : make_uint4(0, 0, 0, 0);
-    vreg[v] = p < total ? *(const uint4*)(vc + (int64_t)p * HD + d8) : make_uint4(0, 0, 0, 0);
+    const int pc = min(p, cv.cap - 1);
+    kreg[v] = *(const uint4*)(kc + (int64_t)pc * HD + d8);
+    vreg[v] = *(const uint4*)(vc + (int64_t)pc * HD + d8);
   }
-  for (int idx = t; idx < QT * 16 * HALF; idx += 256) {
-    const int r = idx / HALF, d = idx % HALF;
-    bf16_t lo = 0, hi = 0;
-    if (r < R) {
+
+  // query rows: every load of the thread first (ATTN_ROWS_MAX*HALF/256 slots), then the rotation
+  {
+    constexpr int NQ = (QTM * 16 * HALF + 255) / 256;  // QTM: most query tiles this instance serves
+    float qx0[NQ], qx1[NQ];
+    float2 qcs[NQ];
+#pragma unroll
+    for (int v = 0; v < NQ; ++v) {
+      const int idx = t + 256 * v, d = idx % HALF;
+      const int r = min(idx / HALF, R - 1);  // clamped: rows >= R are zeroed below
       const int i = r / G, h = kvh * G + r % G;
       const float* src = a.q_stage + (int64_t)(b * mseq + i) * q_dim + h * HD;
-      const float x0 = src[d], x1 = src[d + HALF];
-      const float2 cs = a.rope[(int64_t)(L + i) * HALF + d];
-      lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
-      hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
+      qx0[v] = src[d];
+      qx1[v] = src[d + HALF];
+      qcs[v] = a.rope[(int64_t)(L + i) * HALF + d];
     }
-    qs[r * KP + d] = lo;
-    qs[r * KP + d + HALF] = hi;
+#pragma unroll
+    for (int v = 0; v < NQ; ++v) {
+      const int idx = t + 256 * v, r = idx / HALF, d = idx % HALF;
+      if (r < QT * 16) {
+        qs[r * KP + d] = r < R ? f32_to_bf16(qx0[v] * qcs[v].x - qx1[v] * qcs[v].y) : (bf16_t)0;
+        qs[r * KP + d + HALF] = r < R ? f32_to_bf16(qx1[v] * qcs[v].x + qx0[v] * qcs[v].y) : (bf16_t)0;
+      }
+    }
   }
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int idx = t + 256 * v;
     const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-    if (p < L || p >= total) *(uint4*)(ks + j * KP + d8) = kreg[v];
-    const uint32_t w[4] = {vreg[v].x, vreg[v].y, vreg[v].z, vreg[v].w};
+    if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
+    else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
+    const uint4 vv = p < total ? vreg[v] : make_uint4(0, 0, 0, 0);
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    // V^T rows d8..d8+7 are all in swizzle group d8/8: the key index is xor-ed with 8*(group&7),
+    // which spreads the 16 lanes that write one key over 8 banks and keeps 8-key runs whole
+    const int js = j ^ (((d8 >> 3) & 7) << 3);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      vt[(d8 + 2 * e) * VP + j] = (bf16_t)(w[e] & 0xFFFFu);
-      vt[(d8 + 2 * e + 1) * VP + j] = (bf16_t)(w[e] >> 16);
+      vt[(d8 + 2 * e) * VP + js] = (bf16_t)(w[e] & 0xFFFFu);
+      vt[(d8 + 2 * e + 1) * VP + js] = (bf16_t)(w[e] >> 16);
     }
   }
   // new keys in this chunk: rotate, round, use, and write to the cache
@@ -608,7 +625,13 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   __syncthreads();
 
   const int n = lane & 15, g = lane >> 4;
-  for (int qt = wave; qt < QT; qt += 4) {
+  // waves per query tile: 4 for one tile, 2 for two, else 1; each recomputes the tile's
+  // scores (16 MFMAs) and takes its share of the HD/16 output dim tiles
+  constexpr int DT = HD / 16;
+  const int wpt = min(QT == 1 ? 4 : (QT == 2 ? 2 : 1), DT);
+  const int part = wave % wpt;
+  const int dts = DT / wpt;
+  for (int qt = wave / wpt; qt < QT; qt += 4 / wpt) {
     f32x4_t s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -644,7 +667,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const float v = s[kt][rr];
-        const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : expf(v - mx);
+        const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : __expf(v - mx);
         e[rr] = bf16_to_f32(f32_to_bf16(x));
         l += e[rr];
       }
@@ -670,22 +693,23 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
         rowoff[rr] = (((b * mseq + i2) * a.n_q + h2) * a.nchunk + chunk) * (HD + 2);
       }
     }
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; ++dt) {
+    for (int dt = part * dts; dt < (part + 1) * dts; ++dt) {
       f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int dim = dt * 16 + n;
+      const int swz = ((dim >> 3) & 7) << 3;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16_t* vr = vt + (dt * 16 + n) * VP + st * 32 + 4 * g;
-        const uint2 x0 = *(const uint2*)(vr);
-        const uint2 x1 = *(const uint2*)(vr + 16);
+        const bf16_t* vr = vt + dim * VP;
+        const uint2 x0 = *(const uint2*)(vr + ((st * 32 + 4 * g) ^ swz));
+        const uint2 x1 = *(const uint2*)(vr + ((st * 32 + 16 + 4 * g) ^ swz));
         o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[st], __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y)),
                                                     o, 0, 0, 0);
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        if (rowoff[rr] >= 0) a.part[rowoff[rr] + dt * 16 + n] = o[rr];
+        if (rowoff[rr] >= 0) a.part[rowoff[rr] + dim] = o[rr];
     }
-    if (g == 0 && r < R) {
+    if (part == 0 && g == 0 && r < R) {
       const int i = r / G, h = kvh * G + r % G;
       float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
       P[HD] = mx;
@@ -809,17 +833,24 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, i
   return hipGetLastError();
 }
 
-template <int EPI, bool NORM>
-static hipError_t gemm_bf16_nt(const GemmArgs& a, int blocks, hipStream_t st) {
+// 16 wavefronts per workgroup when there are few 16-row tiles (each wave then has one group
+// of loads in flight for K = 4096), 8 for the LM head's thousands of tiles.
+template <int EPI, bool NORM, int NW>
+static hipError_t gemm_bf16_nw(const GemmArgs& a, int blocks, hipStream_t st) {
   const int M = a.rm.M;
   const size_t lds = NORM ? gemm_norm_lds_bytes(M, a.K) : 0;
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1, NORM, NW>), dim3(blocks), dim3(NW * 64), lds, st, a);
   else if (M <= 32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2, NORM, NW>), dim3(blocks), dim3(NW * 64), lds, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4, NORM>), dim3(blocks), dim3(GEMM_NW * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4, NORM, 8>), dim3(blocks), dim3(8 * 64), lds, st, a);
   return hipGetLastError();
+}
+
+template <int EPI, bool NORM>
+static hipError_t gemm_bf16_nt(const GemmArgs& a, int blocks, hipStream_t st) {
+  return blocks <= 1024 ? gemm_bf16_nw<EPI, NORM, 16>(a, blocks, st) : gemm_bf16_nw<EPI, NORM, 8>(a, blocks, st);
 }
 
 size_t gemm_norm_lds_bytes(int M, int K) { return (size_t)M * (K + 8) * 2; }
@@ -868,12 +899,15 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16) {
     const int QT = (R + 15) / 16;
     const size_t lds2 = 2 * ((size_t)QT * 16 * (hd + 8) + (size_t)ATTN_CHUNK * (hd + 8) + (size_t)hd * (ATTN_CHUNK + 8));
-    if (hd == 128)
-      hipLaunchKernelGGL(attn_chunk_mfma_kernel<128>, g1, dim3(256), lds2, st, a);
-    else if (hd == 64)
-      hipLaunchKernelGGL(attn_chunk_mfma_kernel<64>, g1, dim3(256), lds2, st, a);
-    else
-      hipLaunchKernelGGL(attn_chunk_mfma_kernel<32>, g1, dim3(256), lds2, st, a);
+    if (QT <= 2) {
+      if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 2>), g1, dim3(256), lds2, st, a);
+      else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 2>), g1, dim3(256), lds2, st, a);
+      else hipLaunchKernelGGL((attn_chunk_mfma_kernel<32, 2>), g1, dim3(256), lds2, st, a);
+    } else {
+      if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 6>), g1, dim3(256), lds2, st, a);
+      else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 6>), g1, dim3(256), lds2, st, a);
+      else hipLaunchKernelGGL((attn_chunk_mfma_kernel<32, 6>), g1, dim3(256), lds2, st, a);
+    }
     hipLaunchKernelGGL(attn_combine_kernel<SPEC_DTYPE_BF16>, g2, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(attn_chunk_kernel<SPEC_DTYPE_F32>, g1, dim3(256), lds, st, a);

@@ -24,10 +24,11 @@
 namespace spec {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_EPT = 64;                      // logits held per thread
+constexpr int TK_EPT = 32;                      // logits held per thread
+constexpr int TK_SEG = TK_THREADS * TK_EPT;     // longest segment
 constexpr int TK_CAND = 1024;                   // LDS candidate slots
-constexpr int FIN_THREADS = 64;
-constexpr int FIN_SLOTS = 1024;                 // nseg * ksel must fit
+constexpr int FIN_THREADS = 256;
+constexpr int FIN_SLOTS = 2048;                 // nseg * ksel must fit
 
 // ---------------------------------------------------------------- block helpers
 template <int N>
@@ -56,124 +57,171 @@ SPEC_DEVINL int next_pow2(int x) {
   return p;
 }
 
+SPEC_DEVINL uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+SPEC_DEVINL uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src, 64), hi = __shfl((uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sorts one key per lane of a wavefront, descending: afterwards lane j holds the j-th largest.
+SPEC_DEVINL uint64_t wave_sort_desc(uint64_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor_u64(v, j);
+      const bool up = (lane & j) == 0;          // lower partner of the pair
+      const bool desc = (lane & k) == 0;        // this run sorts descending
+      const bool keep_max = (up == desc);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------- 1. segment top-k
+// Output: the segment's ksel largest keys, descending, zero-padded.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
   constexpr int VW = (DT == SPEC_DTYPE_BF16) ? 8 : 4;  // elements per 16-byte load
   constexpr int NV = TK_EPT / VW;
   __shared__ uint64_t sk[TK_CAND];
-  __shared__ int s_cnt[TK_THREADS];
+  __shared__ uint64_t s_wt[TK_THREADS / 64];
+  __shared__ int s_wcnt[TK_THREADS / 64];
   __shared__ int s_bad, s_total;
   __shared__ unsigned long long s_count;
 
   const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int s0 = seg * a.seg_len;
   const int s1 = min(s0 + a.seg_len, a.vocab);
   const float T = a.temperature;
   const bool scale = T > 0.0f;
-
-  float z[TK_EPT];
-  bool bad = false;
-  uint64_t tmax = 0;
   if (t == 0) s_bad = 0;
 
+  // all loads first, addresses clamped into the row
   const char* base = (const char*)a.logits;
   const int64_t rowoff = (int64_t)row * a.stride;
+  float x[TK_EPT];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int i0 = s0 + (v * TK_THREADS + t) * VW;
-    float x[VW];
-    if (VEC && i0 + VW <= s1) {
+    if (VEC) {
+      const int ic = min(i0, a.vocab - VW);
       if (DT == SPEC_DTYPE_BF16) {
-        const uint4 w = *(const uint4*)(base + (rowoff + i0) * 2);
+        const uint4 w = *(const uint4*)(base + (rowoff + ic) * 2);
         const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = __uint_as_float(ww[e] << 16);
-          x[2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
+          x[v * VW + 2 * e] = __uint_as_float(ww[e] << 16);
+          x[v * VW + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
         }
       } else {
-        const float4 w = *(const float4*)(base + (rowoff + i0) * 4);
-        x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+        const float4 w = *(const float4*)(base + (rowoff + ic) * 4);
+        x[v * VW + 0] = w.x; x[v * VW + 1] = w.y; x[v * VW + 2] = w.z; x[v * VW + 3] = w.w;
       }
     } else {
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
-        const int i = i0 + e;
-        if (i < s1) {
-          x[e] = (DT == SPEC_DTYPE_BF16) ? bf16_to_f32(((const bf16_t*)base)[rowoff + i])
-                                         : ((const float*)base)[rowoff + i];
-        } else {
-          x[e] = __builtin_nanf("");  // outside the segment: never a candidate
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < VW; ++e) {
-      const int i = i0 + e;
-      float v_ = x[e];
-      if (i < s1) {
-        if (__builtin_isnan(v_) || v_ == __builtin_inff()) bad = true;
-        if (scale) v_ = v_ / T;
-      }
-      z[v * VW + e] = v_;
-      if (i < s1 && !__builtin_isnan(v_)) {
-        const uint64_t k = order_key(v_, (uint32_t)i);
-        tmax = k > tmax ? k : tmax;
+        const int ic = min(i0 + e, a.vocab - 1);
+        x[v * VW + e] = (DT == SPEC_DTYPE_BF16) ? bf16_to_f32(((const bf16_t*)base)[rowoff + ic])
+                                                : ((const float*)base)[rowoff + ic];
       }
     }
   }
+  bool bad = false;
+  uint64_t tmax = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+      const int i = s0 + (v * TK_THREADS + t) * VW + e;
+      float z = x[v * VW + e];
+      if (i < s1) {
+        if (__builtin_isnan(z) || z == __builtin_inff()) bad = true;
+        if (scale) z = z / T;
+      } else {
+        z = __builtin_nanf("");  // outside the segment: never a candidate
+      }
+      x[v * VW + e] = z;
+      if (!__builtin_isnan(z)) {
+        const uint64_t k = order_key(z, (uint32_t)i);
+        tmax = k > tmax ? k : tmax;
+      }
+    }
   __syncthreads();
   if (bad) atomicOr(&s_bad, 1);
 
-  // lower bound: the ksel-th largest per-thread maximum
-  sk[t] = tmax;
+  // lower bound: each wave's ceil(ksel/4)-th largest thread maximum; the smallest of the
+  // four leaves at least ksel elements at or above it
+  const int kw = (a.ksel + 3) / 4;
+  const uint64_t srt = wave_sort_desc(tmax, lane);
+  const uint64_t wt = shfl_u64(srt, kw - 1);
+  if (lane == 0) s_wt[wave] = wt;
   __syncthreads();
-  bitonic_desc<TK_THREADS>(sk, TK_THREADS);
-  const uint64_t tau = sk[a.ksel - 1];
-  __syncthreads();
+  uint64_t tau = s_wt[0];
+#pragma unroll
+  for (int w = 1; w < TK_THREADS / 64; ++w) tau = s_wt[w] < tau ? s_wt[w] : tau;
 
   int cnt = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v)
 #pragma unroll
     for (int e = 0; e < VW; ++e) {
+      const float z = x[v * VW + e];
       const int i = s0 + (v * TK_THREADS + t) * VW + e;
-      if (i < s1 && !__builtin_isnan(z[v * VW + e]) && order_key(z[v * VW + e], (uint32_t)i) >= tau)
-        ++cnt;
+      if (!__builtin_isnan(z) && order_key(z, (uint32_t)i) >= tau) ++cnt;
     }
-  s_cnt[t] = cnt;
-  __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int i = 0; i < TK_THREADS; ++i) {
-      const int c = s_cnt[i];
-      s_cnt[i] = run;
-      run += c;
-    }
-    s_total = run;
+  // block exclusive scan of the counts: wave scan by shuffles, wave totals through LDS
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
+  if (lane == 63) s_wcnt[wave] = incl;
   __syncthreads();
-  const int total = s_total;
+  int woff = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < TK_THREADS / 64; ++w) {
+    if (w < wave) woff += s_wcnt[w];
+    total += s_wcnt[w];
+  }
   uint64_t* out = a.part + ((int64_t)row * a.nseg + seg) * a.ksel;
 
   if (total <= TK_CAND) {
-    int off = s_cnt[t];
+    int off = woff + incl - cnt;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
+        const float z = x[v * VW + e];
         const int i = s0 + (v * TK_THREADS + t) * VW + e;
-        if (i < s1 && !__builtin_isnan(z[v * VW + e])) {
-          const uint64_t k = order_key(z[v * VW + e], (uint32_t)i);
+        if (!__builtin_isnan(z)) {
+          const uint64_t k = order_key(z, (uint32_t)i);
           if (k >= tau) sk[off++] = k;
         }
       }
-    const int p2 = next_pow2(max(total, 2));
-    for (int i = total + t; i < p2; i += TK_THREADS) sk[i] = 0;
     __syncthreads();
-    bitonic_desc<TK_THREADS>(sk, p2);
-    for (int i = t; i < a.ksel; i += TK_THREADS) out[i] = i < total ? sk[i] : 0;
+    if (total <= 256) {
+      // rank selection: a candidate's rank is the number of larger candidates (keys are unique)
+      for (int c = t; c < total; c += TK_THREADS) {
+        const uint64_t k = sk[c];
+        int rank = 0;
+        for (int o = 0; o < total; ++o) rank += sk[o] > k;
+        if (rank < a.ksel) out[rank] = k;
+      }
+    } else {
+      const int p2 = next_pow2(total);
+      for (int i = total + t; i < p2; i += TK_THREADS) sk[i] = 0;
+      __syncthreads();
+      bitonic_desc<TK_THREADS>(sk, p2);
+      for (int i = t; i < a.ksel; i += TK_THREADS) out[i] = sk[i];
+    }
+    for (int i = total + t; i < a.ksel; i += TK_THREADS) out[i] = 0;
   } else {
     // exact ksel-th largest key by binary search over the 64-bit key space
     uint64_t lo = 0, hi = ~0ull;
@@ -186,9 +234,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
       for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int e = 0; e < VW; ++e) {
+          const float z = x[v * VW + e];
           const int i = s0 + (v * TK_THREADS + t) * VW + e;
-          if (i < s1 && !__builtin_isnan(z[v * VW + e]) && order_key(z[v * VW + e], (uint32_t)i) >= mid)
-            ++c;
+          if (!__builtin_isnan(z) && order_key(z, (uint32_t)i) >= mid) ++c;
         }
       if (c) atomicAdd(&s_count, (unsigned long long)c);
       __syncthreads();
@@ -196,7 +244,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
       __syncthreads();
       if (enough) lo = mid; else hi = mid - 1;
     }
-    // gather the (at most ksel) keys >= lo
     if (t == 0) s_total = 0;
     for (int i = t; i < TK_CAND; i += TK_THREADS) sk[i] = 0;
     __syncthreads();
@@ -204,9 +251,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
+        const float z = x[v * VW + e];
         const int i = s0 + (v * TK_THREADS + t) * VW + e;
-        if (i < s1 && !__builtin_isnan(z[v * VW + e])) {
-          const uint64_t k = order_key(z[v * VW + e], (uint32_t)i);
+        if (!__builtin_isnan(z)) {
+          const uint64_t k = order_key(z, (uint32_t)i);
           if (k >= lo) {
             const int slot = atomicAdd(&s_total, 1);
             if (slot < TK_CAND) sk[slot] = k;
@@ -222,32 +270,53 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
 }
 
 // ---------------------------------------------------------------- 2. finish
+// Merges the sorted segment lists by rank (a key's rank = its index in its own list plus
+// the number of larger keys in every other list, found by binary search), then lane 0
+// does the float32 softmax / top_p / renormalization in the stated sequential order.
 __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs a, spec_probs out,
                                                                       int out_rs, float top_p,
                                                                       uint8_t* flags) {
   __shared__ uint64_t sk[FIN_SLOTS];
+  __shared__ uint64_t top[SPEC_TOPK_MAX];
   __shared__ float s_p[SPEC_TOPK_MAX];
   __shared__ int s_id[SPEC_TOPK_MAX];
   __shared__ int s_n, s_bad;
   const int row = blockIdx.x, t = threadIdx.x;
-  const int nk = a.nseg * a.ksel;
-  const int p2 = next_pow2(max(nk, 2));
+  const int K = a.ksel, nk = a.nseg * K;
   const uint64_t* src = a.part + (int64_t)row * nk;
-  for (int i = t; i < p2; i += FIN_THREADS) sk[i] = i < nk ? src[i] : 0;
+  for (int i = t; i < nk; i += FIN_THREADS) sk[i] = src[i];
+  for (int i = t; i < K; i += FIN_THREADS) top[i] = 0;
   if (t == 0) {
     int b = 0;
     for (int s = 0; s < a.nseg; ++s) b |= a.bad[(int64_t)row * a.nseg + s];
     s_bad = b;
   }
   __syncthreads();
-  bitonic_desc<FIN_THREADS>(sk, p2);
+  for (int c = t; c < nk; c += FIN_THREADS) {
+    const uint64_t key = sk[c];
+    if (key == 0) continue;
+    const int own = c / K;
+    int rank = c % K;
+    for (int s = 0; s < a.nseg && rank < K; ++s) {
+      if (s == own) continue;
+      const uint64_t* l = sk + s * K;
+      int lo = 0, hi = K;  // first index whose key is smaller (empty slots are 0)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (l[mid] > key) lo = mid + 1; else hi = mid;
+      }
+      rank += lo;
+    }
+    if (rank < K) top[rank] = key;
+  }
+  __syncthreads();
 
   if (t == 0) {
     uint8_t fl = 0;
     int n = 0;
     if (!s_bad) {
-      for (int i = 0; i < a.ksel; ++i) {
-        const uint64_t key = sk[i];
+      for (int i = 0; i < K; ++i) {
+        const uint64_t key = top[i];
         if (key == 0) break;
         const float zi = key_value(key);
         if (zi == -__builtin_inff()) break;  // sorted: the rest is -inf or empty
@@ -540,7 +609,7 @@ __global__ __launch_bounds__(256) void ngram_kernel(NgramArgs a) {
 
 // ---------------------------------------------------------------- launchers
 int truncate_scratch_bytes(int rows, int vocab, size_t* bytes) {
-  const int nseg = (vocab + TK_THREADS * TK_EPT - 1) / (TK_THREADS * TK_EPT);
+  const int nseg = (vocab + TK_SEG - 1) / TK_SEG;
   if (nseg * SPEC_TOPK_MAX > FIN_SLOTS) return SPEC_E_UNSUPPORTED;
   *bytes = (size_t)rows * nseg * SPEC_TOPK_MAX * sizeof(uint64_t) + (size_t)rows * nseg + 256;
   return SPEC_OK;
@@ -556,14 +625,15 @@ hipError_t launch_truncate(const void* logits, int dtype, int rows, int vocab, i
   a.rows = rows;
   a.temperature = s.temperature;
   a.ksel = s.temperature > 0.0f ? s.top_k : 1;
-  a.nseg = (vocab + TK_THREADS * TK_EPT - 1) / (TK_THREADS * TK_EPT);
+  a.nseg = (vocab + TK_SEG - 1) / TK_SEG;
   int seg = (vocab + a.nseg - 1) / a.nseg;
   a.seg_len = (seg + 7) / 8 * 8;
   a.part = (uint64_t*)scratch;
   a.bad = (uint8_t*)scratch + (size_t)rows * a.nseg * SPEC_TOPK_MAX * sizeof(uint64_t);
   if (rows == 0) return hipSuccess;
   const size_t esz = dtype == SPEC_DTYPE_BF16 ? 2 : 4;
-  const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * esz) % 16 == 0);
+  // 16-byte loads need aligned rows and a vocabulary that is a whole number of vectors
+  const bool vec = ((uintptr_t)logits % 16 == 0) && ((stride * esz) % 16 == 0) && (vocab % (int)(16 / esz) == 0);
   dim3 g1(a.nseg, rows);
   if (dtype == SPEC_DTYPE_BF16) {
     if (vec) hipLaunchKernelGGL((topk_segment_kernel<SPEC_DTYPE_BF16, true>), g1, dim3(TK_THREADS), 0, st, a);

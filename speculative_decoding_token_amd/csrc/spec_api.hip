@@ -338,9 +338,10 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
                                          m.x, fused ? m.ss : nullptr, ss_ld, st));
   int np = 1;  // partial sums of squares per row available in m.ss
   RowMap rm{M, mseq, c->len, pos_off};
-  // the normalized rows live in the consuming projection's LDS when they fit; else a
-  // stand-alone kernel with the same arithmetic writes them to m.xn first
-  const bool in_lds = gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
+  // Few rows (the draft, plain decoding): every projection workgroup normalizes them itself
+  // in its LDS prologue, which saves a launch.  More rows: one stand-alone kernel with the
+  // same arithmetic writes them once (redoing them in every workgroup costs more).
+  const bool in_lds = (int64_t)M * d.d_model <= 4096 && gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
   auto norm_input = [&](GemmArgs& g, const void* gain) -> int {
     if (fused && in_lds) {
       g.xres = m.x;
