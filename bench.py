@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-teacher", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override target layers (debug only)")
+    ap.add_argument("--no-graphs", action="store_true", help="plain launches instead of graph replays")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -54,57 +57,69 @@ def verify_bytes(shape, k, L):
     return w + kv_read + kv_write + logits + emb
 
 
+# HBM bytes per launch of the target gate/up kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# (scaled by a 1 GiB copy's readings), with the sha256 prefix of model.hip they were taken on:
+# the figure is reported only while that source is unchanged.
+GATE_UP_TRAFFIC = {"bytes": 202637312, "model_hip_sha256": "fd0426d14351706a"}
+
+
+def gate_up_traffic():
+    import hashlib
+    path = os.path.join(ROOT, "speculative_decoding_token_amd", "csrc", "model.hip")
+    with open(path, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    return GATE_UP_TRAFFIC["bytes"] if sha == GATE_UP_TRAFFIC["model_hip_sha256"] else None
+
+
 def gate_up_bytes(shape, M):
     d, f = shape.d_model, shape.d_ffn
     return 2 * f * d * 2 + M * d * 2 + M * f * 2
 
 
-def cpu_baseline(tshape, dshape, tw, dw, K):
-    """The oracle (numpy, fp64) timed on one target row and one draft row of the cycle at
-    the full shapes; a cycle at acceptance 0 costs K+1 target rows and K draft rows."""
+def cpu_baseline(tshape, dshape, tw, dw, K, t_layers=3, d_layers=4):
+    """The oracle (numpy, fp64) timed on a bounded sample of one cycle at the full shapes:
+    per model, a one-row forward through no layer (embedding, final norm, vocab head) and
+    a few single-row decoder layers, scaled to the model's layer count; a cycle at
+    acceptance 0 costs K+1 target rows and K draft rows for one emitted token."""
     import numpy as np
     import torch
     from oracle import model as om
-
-    class Lazy(dict):
-        # host float32 copies of device weights, made when the oracle first reads them
-        def __getitem__(self, key):
-            v = dict.__getitem__(self, key)
-            if isinstance(v, torch.Tensor):
-                v = v.float().cpu().numpy()
-                dict.__setitem__(self, key, v)
-            return v
-
-    def lazy(w):
-        out = Lazy(embed=w["embed"], final_norm=w["final_norm"], lm_head=w["lm_head"])
-        out["layers"] = [Lazy(lw) for lw in w["layers"]]
-        return out
 
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas = 1
-    res = {}
-    for name, shape, w in (("target", tshape, tw), ("draft", dshape, dw)):
-        spec = om.Spec.from_shape(shape)
-        W = lazy(w)
-        for key in ("embed", "final_norm", "lm_head"):      # host copies, outside the timing
-            W[key]
-        for lw in W["layers"]:
-            for key in list(lw.keys()):
-                lw[key]
-        kv = om.KVCache(spec, 2)
-        # one row at position 0 of an empty cache: every weight is streamed, as in a verify
+    host = lambda t: t.float().cpu().numpy()
+    res, parts = {}, []
+    for name, shape, w, n_s in (("target", tshape, tw, t_layers), ("draft", dshape, dw, d_layers)):
+        W = {"embed": host(w["embed"]), "final_norm": host(w["final_norm"]),
+             "lm_head": host(w["lm_head"]), "layers": []}
+        spec0 = om.Spec.from_shape(shape.with_layers(0))
         t0 = time.perf_counter()
-        om.forward_one(spec, W, kv, 0, 1)
-        res[name] = time.perf_counter() - t0
-        del W, kv
+        om.forward_one(spec0, W, om.KVCache(spec0, 2, n_layers=1), 0, 1)
+        t_head = time.perf_counter() - t0
+        del W
+        spec = om.Spec.from_shape(shape)
+        kv = om.KVCache(spec, 2, n_layers=n_s)
+        x = np.asarray(host(w["embed"][1]), dtype=np.float64)
+        t_lay = 0.0
+        for l in range(n_s):
+            lw = {k: host(v) for k, v in w["layers"][l].items()}
+            t0 = time.perf_counter()
+            x = om.decoder_layer(spec, lw, x, 0, kv, l)
+            t_lay += time.perf_counter() - t0
+            del lw
+        row = t_head + shape.n_layers * t_lay / n_s
+        res[name] = row
+        parts.append(f"{name}: head {t_head:.2f} s + {n_s} layers {t_lay:.2f} s -> row {row:.1f} s "
+                     f"({shape.n_layers} layers)")
     cycle = (K + 1) * res["target"] + K * res["draft"]
     return {
         "value": 1.0 / cycle, "unit": "tokens/s", "cores": blas, "kind": "oracle",
-        "sample": (f"one target row ({res['target']:.1f} s) and one draft row ({res['draft']:.1f} s) at the full "
-                   f"shapes, scaled to a K={K} cycle at acceptance 0 (K+1 target rows + K draft rows, 1 token)"),
+        "sample": ("one row through embedding/final norm/vocab head and through the first few decoder "
+                   "layers of each model at the full shapes, scaled to all layers and to a K=%d cycle at "
+                   "acceptance 0 (K+1 target rows + K draft rows per emitted token); " % K) + "; ".join(parts),
         "os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
     }
 
@@ -117,6 +132,16 @@ def main():
         sys.exit(2)
     import torch
     from speculative_decoding_token_amd import runtime, synth
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}), flush=True)
+        return
 
     K = args.k
     tshape = synth.SHAPES["qwen8b"]
@@ -141,6 +166,8 @@ def main():
         eng.set_last(torch.tensor([int(start[1])], dtype=torch.int32, device="cuda"),
                      torch.tensor([int(start[0])], dtype=torch.int32, device="cuda"))
 
+    if args.no_graphs:
+        eng.use_graphs(False)
     reset()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -172,7 +199,7 @@ def main():
     for _ in range(args.profile_steps):
         eng.cycle(1, K, rnd)
         rnd += 1
-    prof = eng.profile_read()
+    prof = eng.profile_read() if args.profile_steps else {}
     eng.profile(False)
     gu = prof.get("target.gate_up", {"ms": float("nan"), "launches": 1})
     gu_ms = gu["ms"] / gu["launches"]
@@ -207,7 +234,7 @@ def main():
         "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "hbm", "kernel": "target gate/up projection + SwiGLU (gemm_bf16_kernel<EPI_SWIGLU,1>)",
                      "achieved": gu_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gu_gbs / PEAK_HBM_GBS,
-                     "traffic": None, "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+                     "traffic": gate_up_traffic(), "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
         "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
                     for k, v in prof.items()},
         "teacher_forced": teacher,
