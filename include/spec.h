@@ -189,6 +189,11 @@ int spec_load_kv(spec_ctx* ctx, int32_t which, int32_t seq, const void* k /*devi
  * state of position P-2 is kept for the head. */
 int spec_prefill(spec_ctx* ctx, const int32_t* tokens /*device*/, int32_t batch, int32_t P);
 
+/* Copies the token history of sequence `seq` (device int32 [length], positions
+ * 0..length-1) for the n-gram drafter, for starts from a loaded cache prefix.  prefill,
+ * set_last and accept keep the history up to date themselves. */
+int spec_load_history(spec_ctx* ctx, int32_t seq, const int32_t* tokens /*device*/, int32_t length);
+
 /* Sets each sequence's last accepted token (device int32 [batch]) without a forward, for
  * starts from a loaded cache prefix of length L: that token sits at position L.
  * prev_tok (device int32 [batch]) is the token at position L-1; a draft model's first
@@ -211,9 +216,15 @@ int spec_set_last(spec_ctx* ctx, const int32_t* last_tok /*device*/,
  * (rows batch*k, row b*k + j-1 for draft j; one-hot under greedy sampling and for n-gram
  * drafts).  Draft j of sequence b is sampled with the uniform of counter
  * (j, round, b, 0).  For SPEC_DRAFT_NGRAM the call synchronizes the stream and writes to
- * *n_drafted (host, may be NULL) the number of drafts the lookup found (0..k); rows past
- * it repeat the last found token (or the last accepted token) and are normally not
- * verified.  Other drafters write k to *n_drafted. */
+ * *n_drafted (host, may be NULL) the largest number of drafts the lookup found for a
+ * sequence (0..k); rows past a sequence's own count repeat its last found token (or its
+ * last accepted token), and accept tests only that sequence's found drafts.  A batch of
+ * one may then be verified at k = *n_drafted; larger batches are verified at the drafted
+ * k (the row stride of draft_tok).  Other drafters write k to *n_drafted.
+ * SPEC_DRAFT_MTP: the first forward of the cycle catches the MTP layer up on the positions
+ * the target verified since its last draft (rows built from the target's hidden states of
+ * the previous verify, or of the start), so every cycle of that drafter starts with
+ * draft_step; the draft logits come from the target's LM head. */
 int draft_step(spec_ctx* ctx, int32_t batch, int32_t k, uint64_t round,
                int32_t* draft_tok /*device*/, spec_probs* q /*host struct of device ptrs*/,
                int32_t* n_drafted /*host, may be NULL*/);
@@ -247,6 +258,33 @@ int accept(spec_ctx* ctx, const int32_t* draft_tok /*device*/, const spec_probs*
  * token and its n accepted drafts stay; the emitted last token is the next cycle's first
  * row).  Must follow accept.  n_acc: device int32 [batch]. */
 int kv_trim(spec_ctx* ctx, const int32_t* n_acc /*device*/, int32_t batch);
+
+/* ---- n-gram acceptance gate (host only) -------------------------------------------------
+ * "Speculative decoding on Apple Silicon" (OptiQ docs), section "N-gram lookup: any model":
+ * one verify pass is timed per draft length when the model loads, and each step's length
+ * is chosen from how often recent drafts were accepted; with the gate off the longest
+ * draft is always taken.  Reading (the page gives no formula): alpha is an exponential
+ * moving average (weight 0.5, starting at 1) of accepted / attempted per step; the gate
+ * picks the k in 0..n_max that maximizes (1 + alpha + ... + alpha^k) /
+ * (cost[k] + k * draft_cost), costs relative to the verify at k = 0, the smallest k among
+ * values within 1e-12.  k = 0: verify without drafts this step. */
+typedef struct spec_gate {
+  int32_t n_max;
+  int32_t enabled;
+  double weight;                  /* moving-average weight of the old alpha (0.5)        */
+  double alpha;                   /* current acceptance estimate                          */
+  double draft_cost;              /* one draft's cost relative to the k = 0 verify        */
+  double cost[SPEC_MAX_K + 1];    /* verify cost at k drafts relative to k = 0            */
+} spec_gate;
+
+/* verify_cost: host double [n_max + 1] (any time unit, all > 0); draft_cost >= 0 in the
+ * same unit. */
+int spec_gate_init(spec_gate* g /*host*/, int32_t n_max, const double* verify_cost /*host*/,
+                   double draft_cost, int32_t enabled);
+/* The draft length of the next step (>= 0), or SPEC_E_INVAL for a null gate. */
+int32_t spec_gate_choose(const spec_gate* g /*host*/);
+/* Folds one step's accepted / attempted drafts into alpha (nothing when attempted = 0). */
+int spec_gate_update(spec_gate* g /*host*/, int32_t accepted, int32_t attempted);
 
 /* ---- tracing ------------------------------------------------------------------------- */
 

@@ -34,7 +34,8 @@ EXPORTED = [
     "spec_prefill", "spec_set_last", "draft_step", "verify_step", "accept", "kv_trim",
     "spec_get_stats", "spec_get_lengths", "spec_truncate_scratch_size", "spec_truncate",
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
-    "spec_profile", "spec_profile_read", "spec_use_graphs",
+    "spec_profile", "spec_profile_read", "spec_use_graphs", "spec_load_history",
+    "spec_gate_init", "spec_gate_choose", "spec_gate_update",
 ]
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -85,6 +86,11 @@ class spec_probs(C.Structure):
     _fields_ = [("ids", C.c_void_p), ("probs", C.c_void_p), ("count", C.c_void_p), ("cap", C.c_int32)]
 
 
+class spec_gate(C.Structure):
+    _fields_ = [("n_max", C.c_int32), ("enabled", C.c_int32), ("weight", C.c_double), ("alpha", C.c_double),
+                ("draft_cost", C.c_double), ("cost", C.c_double * (MAX_K + 1))]
+
+
 class spec_stats(C.Structure):
     _fields_ = [("cycles", C.c_int64), ("drafts_attempted", C.c_int64),
                 ("drafts_accepted", C.c_int64), ("emitted", C.c_int64)]
@@ -128,6 +134,10 @@ def lib(path: str = LIB_PATH):
         "spec_profile": ([P, I32], C.c_int),
         "spec_profile_read": ([P, P, P], C.c_int),
         "spec_use_graphs": ([P, I32], C.c_int),
+        "spec_load_history": ([P, I32, P, I32], C.c_int),
+        "spec_gate_init": ([C.POINTER(spec_gate), I32, C.POINTER(C.c_double), C.c_double, I32], C.c_int),
+        "spec_gate_choose": ([C.POINTER(spec_gate)], C.c_int32),
+        "spec_gate_update": ([C.POINTER(spec_gate), I32, I32], C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -179,6 +189,13 @@ def model_desc(shape, w: Dict, keep: List) -> spec_model_desc:
         _ptr(w["final_norm"]), C.cast(arr, C.POINTER(spec_layer_weights)))
 
 
+def mtp_desc(w: Dict) -> spec_mtp_desc:
+    """spec_mtp_desc from the MTP weight dict of device tensors (norm_h, norm_e, w_proj,
+    final_norm and one decoder layer's tensors)."""
+    return spec_mtp_desc(_ptr(w["norm_h"]), _ptr(w["norm_e"]), _ptr(w["w_proj"]), _ptr(w["final_norm"]),
+                         layer_struct(w))
+
+
 def sampler(temperature: float = 0.0, top_k: int = 20, top_p: float = 0.95) -> spec_sampler:
     return spec_sampler(temperature, top_k, top_p)
 
@@ -194,10 +211,11 @@ class Probs:
         self.count = torch.zeros((rows,), dtype=torch.int32, device=device)
         self.c = spec_probs(self.ids.data_ptr(), self.probs.data_ptr(), self.count.data_ptr(), cap)
 
-    def to_lists(self):
-        """[(ids, probs)] per row on the host."""
+    def to_lists(self, rows: Optional[int] = None):
+        """[(ids, probs)] per row on the host (the first ``rows`` rows)."""
         ids, pr, cnt = self.ids.cpu().numpy(), self.probs.cpu().numpy(), self.count.cpu().numpy()
-        return [(ids[r, :cnt[r]].astype("int64"), pr[r, :cnt[r]]) for r in range(self.rows)]
+        n = self.rows if rows is None else rows
+        return [(ids[r, :cnt[r]].astype("int64"), pr[r, :cnt[r]]) for r in range(n)]
 
 
 # ---------------------------------------------------------------- entry points
@@ -227,6 +245,10 @@ def spec_load_kv(ctx: int, which: int, seq: int, k, v, length: int) -> None:
 
 def spec_prefill(ctx: int, tokens, batch: int, P: int) -> None:
     _check(lib().spec_prefill(ctx, _ptr(tokens), batch, P), ctx)
+
+
+def spec_load_history(ctx: int, seq: int, tokens, length: int) -> None:
+    _check(lib().spec_load_history(ctx, seq, _ptr(tokens), length), ctx)
 
 
 def spec_set_last(ctx: int, last_tok, prev_tok, hidden, batch: int) -> None:
@@ -331,3 +353,33 @@ def spec_profile_read(ctx: int) -> Dict[str, Dict[str, float]]:
 
 def spec_use_graphs(ctx: int, enable: bool) -> None:
     _check(lib().spec_use_graphs(ctx, int(enable)), ctx)
+
+
+class Gate:
+    """The n-gram acceptance gate of the library (host code): spec_gate_* on a spec_gate."""
+
+    def __init__(self, n_max: int, verify_cost: Sequence[float], draft_cost: float = 0.0, enabled: bool = True):
+        self.g = spec_gate()
+        arr = (C.c_double * len(verify_cost))(*[float(x) for x in verify_cost])
+        rc = lib().spec_gate_init(C.byref(self.g), n_max, arr, float(draft_cost), int(enabled))
+        if rc:
+            raise SpecError(rc, "spec_gate_init")
+
+    def choose(self) -> int:
+        k = lib().spec_gate_choose(C.byref(self.g))
+        if k < 0:
+            raise SpecError(k, "spec_gate_choose")
+        return k
+
+    def update(self, accepted: int, attempted: int) -> None:
+        rc = lib().spec_gate_update(C.byref(self.g), accepted, attempted)
+        if rc:
+            raise SpecError(rc, "spec_gate_update")
+
+    @property
+    def alpha(self) -> float:
+        return self.g.alpha
+
+    @alpha.setter
+    def alpha(self, v: float) -> None:
+        self.g.alpha = v

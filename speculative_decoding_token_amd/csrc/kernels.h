@@ -29,12 +29,16 @@ struct AcceptArgs {
   int32_t* last_tok;      // context state or null
   int32_t* prev_tok;
   int64_t* stats;         // 4 counters or null
+  const int32_t* kcap;    // [batch] drafts found per sequence (fewer than k) or null
+  int32_t* hist;          // token history [batch][hist_ld] or null: the emitted tokens are
+  int hist_ld;            // appended at positions len[b]+1 .. len[b]+1+n
+  const int32_t* len;
 };
 
 struct NgramArgs {
   const int32_t* ctx;
-  const int32_t* lengths;
-  int batch, ld, k, n_min, max_match;
+  const int32_t* lengths;  // tokens in sequence b: lengths[b] + len_add
+  int batch, ld, k, n_min, max_match, len_add;
   int32_t* drafts;
   int32_t* n_found;
   int32_t* match;
@@ -53,7 +57,17 @@ hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per
                          int32_t* tokens, int tok_ld, uint8_t* flags, hipStream_t st);
 hipError_t launch_set_u32(uint32_t* p, uint32_t v, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
-hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, hipStream_t st);
+// len[b] += 1 + n_acc[b]; a second cache length (the MTP layer's) is first clamped to the
+// old len[b] + 1 when mlen is not null.
+hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen, hipStream_t st);
+// One-hot lists for rows b*k + j holding drafts[b*k + j].
+hipError_t launch_onehot(const int32_t* drafts, int rows, const spec_probs& q, hipStream_t st);
+// Token history [batch][ld]: hist[b][pos0 + i] = src[b * src_ld + i] for i < n.
+hipError_t launch_hist_write(int32_t* hist, int ld, const int32_t* src, int src_ld, int batch, int n, int pos0,
+                             hipStream_t st);
+// hist[b][len[b]] = last[b] and, when prev is not null, hist[b][len[b]-1] = prev[b].
+hipError_t launch_hist_set_last(int32_t* hist, int ld, const int32_t* len, const int32_t* last,
+                                const int32_t* prev, int batch, hipStream_t st);
 hipError_t launch_philox(uint64_t seed, const uint32_t* ctr, int n, float* out, hipStream_t st);
 hipError_t launch_ngram(const NgramArgs& a, hipStream_t st);
 
@@ -140,5 +154,33 @@ hipError_t launch_kv_load(int dtype, const void* k, const void* v, CacheView c, 
                           hipStream_t st);
 hipError_t launch_set_len(int32_t* len, int seq, int value, hipStream_t st);
 hipError_t launch_add_len(int32_t* len, int batch, int delta, hipStream_t st);
+// dst[b] = src[b] + add
+hipError_t launch_len_from(int32_t* dst, const int32_t* src, int batch, int add, hipStream_t st);
+
+// Multi-token-prediction input rows (m = b * R + i, M = batch * R): the concatenation of
+// RMSNorm(h, norm_h) and RMSNorm(E[token], norm_e), rounded to the model dtype.
+// h row = h + b * h_ss + i * h_rs (float32 [d]); token = tok[b * tok_ld + (tok_pos ? tok_pos[b] : 0) + i].
+struct MtpInArgs {
+  const float* h;
+  int64_t h_ss, h_rs;
+  const int32_t* tok;
+  int tok_ld;
+  const int32_t* tok_pos;
+  const void* embed;
+  const void* norm_h;
+  const void* norm_e;
+  float eps;
+  int d, R, M, vocab;
+  void* out;  // [M][2d] model dtype
+};
+hipError_t launch_mtp_input(int dtype, const MtpInArgs& a, hipStream_t st);
+// Per sequence b, copies residual row b * R + r and its sum-of-squares partials (ss_ld floats)
+// to row b of x1 / ss1, where r = len[b] - mlen[b] (clamped to 0..R-1) when mlen is not null,
+// else 0.
+hipError_t launch_gather_last(const float* x, const float* ss, int ss_ld, int d, int R, const int32_t* len,
+                              const int32_t* mlen, int batch, float* x1, float* ss1, hipStream_t st);
+// dst[b * dst_ss + i * d + e] = src[b * src_ss + i * d + e] for i < R, e < d.
+hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, int batch, float* dst,
+                                int64_t dst_ss, hipStream_t st);
 
 }  // namespace spec

@@ -62,6 +62,71 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
   if (ss && t == 0) ss[(int64_t)m * ss_ld] = red[0];
 }
 
+// ---------------------------------------------------------------- MTP input
+// The multi-token-prediction layer reads the target's hidden state h at position t-1 and
+// the embedding of the token at t, each RMS-normalized with its own gain, side by side
+// ("What is Speculative Decoding and How Does a Draft Model Work?", section "MTP and the
+// other drafting methods": extra layers predicting the following tokens; "Speculative
+// decoding on Apple Silicon" (OptiQ docs), section "Serving and the Lab": a projection
+// followed by a final layer).  One workgroup per row; both sums of squares in one pass.
+template <int DT>
+__global__ __launch_bounds__(256) void mtp_input_kernel(MtpInArgs a) {
+  using A = Act<DT>;
+  typedef typename A::T T;
+  __shared__ float red[2][256];
+  const int m = blockIdx.x, b = m / a.R, i = m % a.R, t = threadIdx.x, d = a.d;
+  const float* h = a.h + b * a.h_ss + i * a.h_rs;
+  const int tok = a.tok[(int64_t)b * a.tok_ld + (a.tok_pos ? a.tok_pos[b] : 0) + i];
+  const bool ok = tok >= 0 && tok < a.vocab;
+  const T* e = (const T*)a.embed + (int64_t)(ok ? tok : 0) * d;
+  float sh = 0.0f, se = 0.0f;
+  for (int c = t; c < d; c += 256) {
+    const float x = h[c], y = A::load(e, c);
+    sh += x * x;
+    se += y * y;
+  }
+  red[0][t] = sh;
+  red[1][t] = se;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (t < s2) {
+      red[0][t] += red[0][t + s2];
+      red[1][t] += red[1][t + s2];
+    }
+    __syncthreads();
+  }
+  const float ih = 1.0f / sqrtf(red[0][0] / (float)d + a.eps);
+  const float ie = ok ? 1.0f / sqrtf(red[1][0] / (float)d + a.eps) : __builtin_nanf("");
+  T* o = (T*)a.out + (int64_t)m * 2 * d;
+  const T* gh = (const T*)a.norm_h;
+  const T* ge = (const T*)a.norm_e;
+  for (int c = t; c < d; c += 256) {
+    A::store(o, c, h[c] * ih * A::load(gh, c));
+    A::store(o, d + c, A::load(e, c) * ie * A::load(ge, c));
+  }
+}
+
+__global__ void gather_last_kernel(const float* x, const float* ss, int ss_ld, int d, int R, const int32_t* len,
+                                   const int32_t* mlen, float* x1, float* ss1) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int r = mlen ? min(max(len[b] - mlen[b], 0), R - 1) : 0;
+  const float* src = x + ((int64_t)b * R + r) * d;
+  for (int c = t; c < d; c += blockDim.x) x1[(int64_t)b * d + c] = src[c];
+  if (ss)
+    for (int c = t; c < ss_ld; c += blockDim.x) ss1[(int64_t)b * ss_ld + c] = ss[((int64_t)b * R + r) * ss_ld + c];
+}
+
+__global__ void copy_rows_f32_kernel(const float* src, int64_t src_ss, int R, int d, float* dst, int64_t dst_ss) {
+  const int row = blockIdx.x, b = row / R, i = row % R;
+  for (int c = threadIdx.x; c < d; c += blockDim.x)
+    dst[b * dst_ss + (int64_t)i * d + c] = src[b * src_ss + (int64_t)i * d + c];
+}
+
+__global__ void len_from_kernel(int32_t* dst, const int32_t* src, int batch, int add) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) dst[b] = src[b] + add;
+}
+
 // ---------------------------------------------------------------- RMSNorm
 // y = x / sqrt(mean(x^2) + eps) * g, rounded to the model dtype.  Fixed reduction order.
 template <int DT>
@@ -821,6 +886,34 @@ hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_
   else
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_F32>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
                        first_ld, rest, rest_ld, mseq, x, ss, ss_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_mtp_input(int dtype, const MtpInArgs& a, hipStream_t st) {
+  if (a.M == 0) return hipSuccess;
+  if (dtype == SPEC_DTYPE_BF16)
+    hipLaunchKernelGGL(mtp_input_kernel<SPEC_DTYPE_BF16>, dim3(a.M), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(mtp_input_kernel<SPEC_DTYPE_F32>, dim3(a.M), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_last(const float* x, const float* ss, int ss_ld, int d, int R, const int32_t* len,
+                              const int32_t* mlen, int batch, float* x1, float* ss1, hipStream_t st) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_last_kernel, dim3(batch), dim3(256), 0, st, x, ss, ss_ld, d, R, len, mlen, x1, ss1);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, int batch, float* dst,
+                                int64_t dst_ss, hipStream_t st) {
+  if (batch * R == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_f32_kernel, dim3(batch * R), dim3(256), 0, st, src, src_ss, R, d, dst, dst_ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_len_from(int32_t* dst, const int32_t* src, int batch, int add, hipStream_t st) {
+  hipLaunchKernelGGL(len_from_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, dst, src, batch, add);
   return hipGetLastError();
 }
 

@@ -458,12 +458,15 @@ __global__ void accept_kernel(AcceptArgs a) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.batch) return;
   const int k = a.k;
+  // drafts actually proposed for this sequence (an n-gram lookup may find fewer than k);
+  // the rows past them are not tested and the bonus comes from row kb
+  const int kb = a.kcap ? min(max(a.kcap[b], 0), k) : k;
   const int32_t* d = a.drafts + (int64_t)b * k;
   int32_t* out = a.out_tok + (int64_t)b * (k + 1);
   uint8_t fl = 0;
-  int n = k;
+  int n = kb;
   int emitted = -1;
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < kb; ++j) {
     const int64_t pr = (int64_t)b * (k + 1) + j, qr = (int64_t)b * k + j;
     const int32_t* pid = a.p.ids + pr * a.p.cap;
     const float* pp = a.p.probs + pr * a.p.cap;
@@ -507,8 +510,8 @@ __global__ void accept_kernel(AcceptArgs a) {
     break;
   }
   if (emitted < 0) {
-    // every draft kept: bonus token from the last target row
-    const int64_t pr = (int64_t)b * (k + 1) + k;
+    // every draft kept: bonus token from the target row after the last draft
+    const int64_t pr = (int64_t)b * (k + 1) + kb;
     const int32_t* pid = a.p.ids + pr * a.p.cap;
     const float* pp = a.p.probs + pr * a.p.cap;
     const int pn = list_len(a.p, pr);
@@ -521,28 +524,65 @@ __global__ void accept_kernel(AcceptArgs a) {
       const float ur = philox_uniform(a.seed, 0u, a.round, (uint32_t)b, STREAM_RESIDUAL);
       emitted = sample_list(pid, pp, pn, ur, &fl);
     }
-    n = k;
+    n = kb;
   }
   out[n] = emitted;
   a.n_acc[b] = n;
   if (a.near_tie) a.near_tie[b] = fl;
+  // a bad last row leaves -1 in out_tok as the signal; the context state keeps token 0
+  const int32_t kept = emitted < 0 ? 0 : emitted;
   if (a.last_tok) {
     // the token now at position L+n becomes the previous token, the emitted one the last
     a.prev_tok[b] = (n == 0) ? a.last_tok[b] : d[n - 1];
-    a.last_tok[b] = emitted;
+    a.last_tok[b] = kept;
+  }
+  if (a.hist) {
+    int32_t* h = a.hist + (int64_t)b * a.hist_ld + a.len[b] + 1;
+    for (int i = 0; i < n; ++i) h[i] = d[i];
+    h[n] = kept;
   }
   if (a.stats) {
     if (b == 0) atomicAdd((unsigned long long*)&a.stats[0], 1ull);
-    atomicAdd((unsigned long long*)&a.stats[1], (unsigned long long)k);
+    atomicAdd((unsigned long long*)&a.stats[1], (unsigned long long)kb);
     atomicAdd((unsigned long long*)&a.stats[2], (unsigned long long)n);
     atomicAdd((unsigned long long*)&a.stats[3], (unsigned long long)(n + 1));
   }
 }
 
 // ---------------------------------------------------------------- kv trim
-__global__ void trim_kernel(int32_t* len, const int32_t* n_acc, int batch) {
+__global__ void trim_kernel(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < batch) len[b] += 1 + n_acc[b];
+  if (b >= batch) return;
+  // the MTP layer keeps its entries up to the old last position: later ones were built from
+  // its own hidden states rather than the target's
+  if (mlen) mlen[b] = min(mlen[b], len[b] + 1);
+  len[b] += 1 + n_acc[b];
+}
+
+// ---------------------------------------------------------------- token history
+__global__ void onehot_kernel(const int32_t* drafts, int rows, spec_probs q) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  q.ids[(int64_t)r * q.cap] = drafts[r];
+  q.probs[(int64_t)r * q.cap] = 1.0f;
+  q.count[r] = 1;
+}
+
+__global__ void hist_write_kernel(int32_t* hist, int ld, const int32_t* src, int src_ld, int batch, int n,
+                                  int pos0) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= (int64_t)batch * n) return;
+  const int b = (int)(i / n), j = (int)(i % n);
+  hist[(int64_t)b * ld + pos0 + j] = src[(int64_t)b * src_ld + j];
+}
+
+__global__ void hist_set_last_kernel(int32_t* hist, int ld, const int32_t* len, const int32_t* last,
+                                     const int32_t* prev, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int L = len[b];
+  hist[(int64_t)b * ld + L] = last[b];
+  if (prev && L >= 1) hist[(int64_t)b * ld + L - 1] = prev[b];
 }
 
 __global__ void set_u32_kernel(uint32_t* p, uint32_t v) { *p = v; }
@@ -569,7 +609,7 @@ __global__ __launch_bounds__(256) void ngram_kernel(NgramArgs a) {
   __shared__ unsigned long long s_best;
   const int b = blockIdx.x, t = threadIdx.x;
   const int32_t* c = a.ctx + (int64_t)b * a.ld;
-  const int n = min(max(a.lengths[b], 0), a.ld);
+  const int n = min(max(a.lengths[b] + a.len_add, 0), a.ld);
   if (t == 0) s_best = 0;
   __syncthreads();
   unsigned long long best = 0;
@@ -662,8 +702,30 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, hipStream_t st) {
-  hipLaunchKernelGGL(trim_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, len, n_acc, batch);
+hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen, hipStream_t st) {
+  hipLaunchKernelGGL(trim_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, len, n_acc, batch, mlen);
+  return hipGetLastError();
+}
+
+hipError_t launch_onehot(const int32_t* drafts, int rows, const spec_probs& q, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(onehot_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, drafts, rows, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist_write(int32_t* hist, int ld, const int32_t* src, int src_ld, int batch, int n, int pos0,
+                             hipStream_t st) {
+  const int64_t tot = (int64_t)batch * n;
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(hist_write_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, hist, ld, src,
+                     src_ld, batch, n, pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist_set_last(int32_t* hist, int ld, const int32_t* len, const int32_t* last,
+                                const int32_t* prev, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(hist_set_last_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, hist, ld, len, last, prev,
+                     batch);
   return hipGetLastError();
 }
 

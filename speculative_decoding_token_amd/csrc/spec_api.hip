@@ -67,12 +67,25 @@ struct GraphEntry {
 
 struct spec_ctx {
   spec_config cfg{};
-  Model target, draft;
+  Model target, draft, mtp;
   hipStream_t stream = nullptr;
   int32_t* len = nullptr;       // [max_batch] context length L per sequence
   int32_t* last_tok = nullptr;  // [max_batch] token at position L
   int32_t* prev_tok = nullptr;  // [max_batch] token at position L-1
   int64_t* stats = nullptr;     // 4 counters
+  int32_t* hist = nullptr;      // [max_batch][hist_ld] tokens at positions 0..L
+  int hist_ld = 0;
+  int32_t* ndraft = nullptr;    // [max_batch] drafts the n-gram lookup found
+  int32_t* match = nullptr;     // [max_batch][2] n-gram match length and end
+  bool ngram_cycle = false;     // this cycle's drafts came from the n-gram lookup
+  // MTP drafter: its cache length, the target hidden rows it catches up from, the gathered
+  // last row and its partials, the concatenated input rows
+  int32_t* mtp_len = nullptr;
+  float* mtp_h = nullptr;       // [max_batch][max_k+1][d]
+  float* x1 = nullptr;          // [max_batch][d]
+  float* ss1 = nullptr;         // [max_batch][d/16+1]
+  void* mtp_in = nullptr;       // [rows][2d] model dtype
+  int mtp_rows = 1;             // rows of the next catch-up (previous cycle's k + 1)
   void* trunc = nullptr;
   size_t trunc_bytes = 0;
   int cap = 0;
@@ -254,14 +267,29 @@ size_t layout(spec_ctx* c, void* ws) {
   c->prev_tok = cv.take<int32_t>(B * 4);
   c->stats = cv.take<int64_t>(4 * 8);
   c->round_dev = cv.take<uint32_t>(4);
+  c->hist_ld = c->cap + 1;
+  c->hist = cv.take<int32_t>((size_t)B * c->hist_ld * 4);
+  c->ndraft = cv.take<int32_t>(B * 4);
+  c->match = cv.take<int32_t>(B * 8);
   c->target.mseq_max = max_rows_per_seq(c->target.d, g.max_k, B);
   carve_model(c->target, cv, B, c->cap);
   if (c->draft.present) {
     c->draft.mseq_max = std::max(2, max_rows_per_seq(c->draft.d, 1, B));
     carve_model(c->draft, cv, B, c->cap);
   }
+  if (c->mtp.present) {
+    const int d = c->mtp.d.d_model;
+    c->mtp.mseq_max = c->target.mseq_max;
+    carve_model(c->mtp, cv, B, c->cap);
+    c->mtp_len = cv.take<int32_t>(B * 4);
+    c->mtp_h = cv.take<float>((size_t)B * (g.max_k + 1) * d * 4);
+    c->x1 = cv.take<float>((size_t)B * d * 4);
+    c->ss1 = cv.take<float>((size_t)B * (d / 16 + 1) * 4);
+    c->mtp_in = cv.take<void>((size_t)c->mtp.Mmax * 2 * d * c->mtp.act);
+  }
   size_t tb = 0;
-  const int rows = std::max(c->target.Mmax, c->draft.present ? c->draft.Mmax : 0);
+  const int rows = std::max(std::max(c->target.Mmax, c->draft.present ? c->draft.Mmax : 0),
+                            c->mtp.present ? c->mtp.Mmax : 0);
   truncate_scratch_bytes(rows, g.target.vocab, &tb);
   c->trunc_bytes = tb;
   c->trunc = cv.take<void>(tb);
@@ -292,9 +320,20 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
     c->draft.d = g.draft;
     c->draft.present = true;
     c->draft.mi = 1;
+  } else if (g.draft_kind == SPEC_DRAFT_MTP) {
+    // one extra decoder layer at the target's widths, its own final norm, the target's
+    // embedding and LM head
+    c->mtp.d = g.target;
+    c->mtp.d.n_layers = 1;
+    c->mtp.d.final_norm = g.mtp.final_norm;
+    c->mtp.d.layers = nullptr;
+    c->mtp.present = true;
+    c->mtp.mi = 1;
+  } else if (g.draft_kind == SPEC_DRAFT_NGRAM) {
+    if (g.ngram.n_min < 1 || g.ngram.max_match < g.ngram.n_min)
+      return fail(nullptr, SPEC_E_INVAL, "ngram: need 1 <= n_min <= max_match");
   } else if (g.draft_kind != SPEC_DRAFT_NONE) {
-    return fail(nullptr, SPEC_E_UNSUPPORTED, "draft kind %d is not implemented by this library build",
-                g.draft_kind);
+    return fail(nullptr, SPEC_E_INVAL, "draft kind %d", g.draft_kind);
   }
   if (g.sampler.temperature > 0.0f && g.sampler.top_k > g.target.vocab)
     return fail(nullptr, SPEC_E_INVAL, "top_k > vocab");
@@ -321,45 +360,47 @@ int check_probs(spec_ctx* c, const spec_probs* p, const char* name, int need_cap
 
 int list_cap(const spec_sampler& s) { return s.temperature > 0.0f ? s.top_k : 1; }
 
-// One forward of model m over M = B*mseq rows; rows' tokens come from first/rest (see
-// launch_embed) at positions len + pos_off + i.  Logits go to `logits` when non-null.
-int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int first_ld,
-            const int32_t* rest, int rest_ld, int pos_off, float* logits) {
+// RMSNorm input of a projection: bf16 models fuse it into the GEMM (few rows: each workgroup
+// normalizes them in its LDS prologue, which saves a launch) or run one stand-alone kernel
+// with the same arithmetic (more rows: redoing them in every workgroup costs more); f32
+// models run the plain RMSNorm kernel.  x / ss: residual rows and their np sum-of-squares
+// partials per row.
+int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const float* ss, int np,
+               const void* gain) {
+  const spec_model_desc& d = m.d;
+  const int P = 16 * m.mi;
+  if (d.dtype != SPEC_DTYPE_BF16) {
+    LAUNCH(c, P + PROF_NORM, launch_rmsnorm(d.dtype, x, gain, d.rms_eps, M, d.d_model, m.xn, c->stream));
+    g.x = m.xn;
+    return SPEC_OK;
+  }
+  const int ss_ld = d.d_model / 16 + 1;
+  const bool in_lds = (int64_t)M * d.d_model <= 4096 && gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
+  if (in_lds) {
+    g.xres = x;
+    g.gain = gain;
+    g.ss_in = ss;
+    g.np_in = np;
+    g.ss_ld = ss_ld;
+    g.eps = d.rms_eps;
+  } else {
+    LAUNCH(c, P + PROF_NORM, launch_norm_apply(x, gain, ss, np, ss_ld, d.rms_eps, M, d.d_model, m.xn, c->stream));
+    g.x = m.xn;
+  }
+  return SPEC_OK;
+}
+
+// The decoder layers of m over the M rows already in m.x (np sum-of-squares partials per
+// row in m.ss for bf16 models), rows placed by rm.
+int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
   const spec_model_desc& d = m.d;
   const hipStream_t st = c->stream;
-  const int M = B * mseq;
   const int dt = d.dtype;
   const int P = 16 * m.mi;
-  // bf16 models fuse each RMSNorm into the projection that consumes it (see gemm_bf16_kernel);
-  // f32 models run it as its own kernel
   const bool fused = dt == SPEC_DTYPE_BF16;
   const int ss_ld = d.d_model / 16 + 1;
-  LAUNCH(c, P + PROF_EMBED, launch_embed(dt, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld, M, mseq,
-                                         m.x, fused ? m.ss : nullptr, ss_ld, st));
-  int np = 1;  // partial sums of squares per row available in m.ss
-  RowMap rm{M, mseq, c->len, pos_off};
-  // Few rows (the draft, plain decoding): every projection workgroup normalizes them itself
-  // in its LDS prologue, which saves a launch.  More rows: one stand-alone kernel with the
-  // same arithmetic writes them once (redoing them in every workgroup costs more).
-  const bool in_lds = (int64_t)M * d.d_model <= 4096 && gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
-  auto norm_input = [&](GemmArgs& g, const void* gain) -> int {
-    if (fused && in_lds) {
-      g.xres = m.x;
-      g.gain = gain;
-      g.ss_in = m.ss;
-      g.np_in = np;
-      g.ss_ld = ss_ld;
-      g.eps = d.rms_eps;
-    } else {
-      if (fused)
-        LAUNCH(c, P + PROF_NORM, launch_norm_apply(m.x, gain, m.ss, np, ss_ld, d.rms_eps, M, d.d_model, m.xn, st));
-      g.x = m.xn;
-    }
-    return SPEC_OK;
-  };
   for (int l = 0; l < d.n_layers; ++l) {
     const spec_layer_weights& w = m.layers[l];
-    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.attn_norm, d.rms_eps, M, d.d_model, m.xn, st));
     GemmArgs g{};
     g.w[0] = w.wq;
     g.w[1] = w.wk;
@@ -368,7 +409,7 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     g.rows[1] = m.kv_dim;
     g.rows[2] = m.kv_dim;
     g.K = d.d_model;
-    if (norm_input(g, w.attn_norm)) return SPEC_E_HIP;
+    if (norm_input(c, m, g, M, m.x, m.ss, np, w.attn_norm)) return SPEC_E_HIP;
     g.rm = rm;
     g.q_stage = m.qst;
     g.k_stage = m.kst;
@@ -400,13 +441,12 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     o.ss_ld = ss_ld;
     LAUNCH(c, P + PROF_OPROJ, launch_gemm(dt, EPI_RESID, o, st));
     np = d.d_model / 16;
-    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, w.ffn_norm, d.rms_eps, M, d.d_model, m.xn, st));
     GemmArgs gu{};
     gu.w[0] = w.wg;
     gu.w[1] = w.wu;
     gu.rows[0] = d.d_ffn;
     gu.K = d.d_model;
-    if (norm_input(gu, w.ffn_norm)) return SPEC_E_HIP;
+    if (norm_input(c, m, gu, M, m.x, m.ss, np, w.ffn_norm)) return SPEC_E_HIP;
     gu.rm = rm;
     gu.h = m.h;
     LAUNCH(c, P + PROF_GATEUP, launch_gemm(dt, EPI_SWIGLU, gu, st));
@@ -422,19 +462,86 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
     dn.ss_ld = ss_ld;
     LAUNCH(c, P + PROF_DOWN, launch_gemm(dt, EPI_RESID, dn, st));
   }
-  if (logits) {
-    if (!fused) LAUNCH(c, P + PROF_NORM, launch_rmsnorm(dt, m.x, d.final_norm, d.rms_eps, M, d.d_model, m.xn, st));
-    GemmArgs lm{};
-    lm.w[0] = d.lm_head;
-    lm.rows[0] = d.vocab;
-    lm.K = d.d_model;
-    if (norm_input(lm, d.final_norm)) return SPEC_E_HIP;
-    lm.rm = rm;
-    lm.out = logits;
-    lm.ld = d.vocab;
-    LAUNCH(c, P + PROF_LMHEAD, launch_gemm(dt, EPI_STORE, lm, st));
-  }
   return SPEC_OK;
+}
+
+// Final RMSNorm and vocabulary projection of M residual rows x (ss: their partials, np per
+// row) into logits [M, vocab].
+int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const float* ss, int np, float* logits) {
+  const spec_model_desc& d = m.d;
+  GemmArgs lm{};
+  lm.w[0] = d.lm_head;
+  lm.rows[0] = d.vocab;
+  lm.K = d.d_model;
+  if (norm_input(c, m, lm, M, x, ss, np, d.final_norm)) return SPEC_E_HIP;
+  lm.rm = rm;
+  lm.out = logits;
+  lm.ld = d.vocab;
+  LAUNCH(c, 16 * m.mi + PROF_LMHEAD, launch_gemm(d.dtype, EPI_STORE, lm, c->stream));
+  return SPEC_OK;
+}
+
+// One forward of model m over M = B*mseq rows; rows' tokens come from first/rest (see
+// launch_embed) at positions len + pos_off + i.  Logits go to `logits` when non-null.
+int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int first_ld,
+            const int32_t* rest, int rest_ld, int pos_off, float* logits) {
+  const spec_model_desc& d = m.d;
+  const int M = B * mseq;
+  const bool fused = d.dtype == SPEC_DTYPE_BF16;
+  const int ss_ld = d.d_model / 16 + 1;
+  LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_embed(d.dtype, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld,
+                                                 M, mseq, m.x, fused ? m.ss : nullptr, ss_ld, c->stream));
+  RowMap rm{M, mseq, c->len, pos_off};
+  int rc = run_layers(c, m, M, rm, 1);
+  if (rc) return rc;
+  if (logits) return run_head(c, m, M, rm, m.x, m.ss, d.d_model / 16, logits);
+  return SPEC_OK;
+}
+
+// The MTP layer over R rows per sequence at positions mtp_len[b] + pos_off + i: input rows
+// [RMSNorm(h); RMSNorm(E[token])] projected by w_proj into the residual stream, then the
+// layer.  h row (b, i) = h + b * h_ss + i * d; token (b, i) = tok[b * tok_ld + (tok_pos ?
+// tok_pos[b] : 0) + i].
+int mtp_layer(spec_ctx* c, int B, int R, const float* h, int64_t h_ss, const int32_t* tok, int tok_ld,
+              const int32_t* tok_pos, int pos_off) {
+  Model& m = c->mtp;
+  const spec_model_desc& d = m.d;
+  const spec_mtp_desc& w = c->cfg.mtp;
+  const int M = B * R;
+  MtpInArgs in{};
+  in.h = h;
+  in.h_ss = h_ss;
+  in.h_rs = d.d_model;
+  in.tok = tok;
+  in.tok_ld = tok_ld;
+  in.tok_pos = tok_pos;
+  in.embed = d.embed;
+  in.norm_h = w.norm_h;
+  in.norm_e = w.norm_e;
+  in.eps = d.rms_eps;
+  in.d = d.d_model;
+  in.R = R;
+  in.M = M;
+  in.vocab = d.vocab;
+  in.out = c->mtp_in;
+  LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_mtp_input(d.dtype, in, c->stream));
+  // the projection lands in a zeroed residual stream: 0 + v is v exactly, and the residual
+  // epilogue leaves the sum-of-squares partials the layer's first norm reads
+  HIPCHK(c, launch_fill(m.x, (size_t)M * d.d_model * 4, c->stream));
+  const bool fused = d.dtype == SPEC_DTYPE_BF16;
+  GemmArgs g{};
+  g.w[0] = w.w_proj;
+  g.rows[0] = d.d_model;
+  g.K = 2 * d.d_model;
+  g.x = c->mtp_in;
+  RowMap rm{M, R, c->mtp_len, pos_off};
+  g.rm = rm;
+  g.out = m.x;
+  g.ld = d.d_model;
+  g.ss_out = fused ? m.ss : nullptr;
+  g.ss_ld = d.d_model / 16 + 1;
+  LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_gemm(d.dtype, EPI_RESID, g, c->stream));
+  return run_layers(c, m, M, rm, d.d_model / 16);
 }
 
 int need_ctx(spec_ctx* c) { return c ? SPEC_OK : SPEC_E_INVAL; }
@@ -485,6 +592,56 @@ int enqueue_draft(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_
   return SPEC_OK;
 }
 
+// The kernels of one MTP draft_step.  The first forward catches the head up on the target:
+// R rows at positions mtp_len[b] .. from the target hidden states of the previous verify (or
+// the start) and the tokens of the history; the logits come from the row at position L.
+// Every later draft is one row fed with the head's own last hidden state and the previous
+// draft.
+int enqueue_draft_mtp(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_probs& q) {
+  Model& m = c->mtp;
+  const spec_sampler& s = c->cfg.sampler;
+  const int V = m.d.vocab, d = m.d.d_model;
+  const int P = 16 * m.mi;
+  const int ss_ld = d / 16 + 1;
+  const bool fused = m.d.dtype == SPEC_DTYPE_BF16;
+  const int R = c->mtp_rows;
+  const int64_t h_ss = (int64_t)(c->cfg.max_k + 1) * d;
+  for (int j = 1; j <= k; ++j) {
+    int rc;
+    if (j == 1) {
+      rc = mtp_layer(c, batch, R, c->mtp_h, h_ss, c->hist, c->hist_ld, c->mtp_len, 0);
+      if (rc) return rc;
+      HIPCHK(c, launch_gather_last(m.x, fused ? m.ss : nullptr, ss_ld, d, R, c->len, c->mtp_len, batch, c->x1,
+                                   c->ss1, c->stream));
+      // the head's cache now holds positions up to L
+      HIPCHK(c, launch_len_from(c->mtp_len, c->len, batch, 1, c->stream));
+    } else {
+      rc = mtp_layer(c, batch, 1, c->x1, d, draft_tok + (j - 2), k, nullptr, j - 2);
+      if (rc) return rc;
+      HIPCHK(c, launch_gather_last(m.x, fused ? m.ss : nullptr, ss_ld, d, 1, c->len, nullptr, batch, c->x1, c->ss1,
+                                   c->stream));
+    }
+    RowMap rm{batch, 1, c->mtp_len, 0};
+    rc = run_head(c, m, batch, rm, c->x1, c->ss1, d / 16, m.logits);
+    if (rc) return rc;
+    LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits, SPEC_DTYPE_F32, batch, V, V, s, offset_rows(q, j - 1), k,
+                                              nullptr, c->trunc, c->stream));
+    LAUNCH(c, P + PROF_SAMPLE, launch_sample(offset_rows(q, j - 1), k, batch, 1, j, c->cfg.seed, c->round_dev,
+                                             0u, STREAM_DRAFT, draft_tok + (j - 1), k, nullptr, c->stream));
+  }
+  return SPEC_OK;
+}
+
+// The kernels of one n-gram draft_step: the longest-then-latest match in each sequence's
+// history (positions 0..L) and one-hot draft lists.
+int enqueue_draft_ngram(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_probs& q) {
+  NgramArgs a{c->hist, c->len, batch, c->hist_ld, k, c->cfg.ngram.n_min, c->cfg.ngram.max_match, 1,
+              draft_tok, c->ndraft, c->match};
+  LAUNCH(c, 16 + PROF_SAMPLE, launch_ngram(a, c->stream));
+  LAUNCH(c, 16 + PROF_SAMPLE, launch_onehot(draft_tok, batch * k, q, c->stream));
+  return SPEC_OK;
+}
+
 // The kernels of one verify_step: the target forward over k+1 rows and the truncation.
 int enqueue_verify(spec_ctx* c, const int32_t* draft_tok, int batch, int k, float* logits_out,
                    const spec_probs& p) {
@@ -493,6 +650,10 @@ int enqueue_verify(spec_ctx* c, const int32_t* draft_tok, int batch, int k, floa
   float* lg = logits_out ? logits_out : m.logits;
   int rc = forward(c, m, batch, k + 1, c->last_tok, 1, draft_tok, k, 0, lg);
   if (rc) return rc;
+  // the MTP head catches up next cycle from these hidden states (positions L .. L+k)
+  if (c->mtp.present)
+    HIPCHK(c, launch_copy_rows_f32(m.x, (int64_t)(k + 1) * m.d.d_model, k + 1, m.d.d_model, batch, c->mtp_h,
+                                   (int64_t)(c->cfg.max_k + 1) * m.d.d_model, c->stream));
   LAUNCH(c, PROF_TRUNC, launch_truncate(lg, SPEC_DTYPE_F32, batch * (k + 1), V, V, c->cfg.sampler, p, 1, nullptr,
                                         c->trunc, c->stream));
   return SPEC_OK;
@@ -563,6 +724,13 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
   }
   rc = validate_model(c->cfg.target, "target", std::max(c->cfg.max_k, 1), c->cfg.max_batch, true);
   if (!rc && c->draft.present) rc = validate_model(c->cfg.draft, "draft", 1, c->cfg.max_batch, true);
+  if (!rc && c->mtp.present) {
+    const spec_mtp_desc& w = c->cfg.mtp;
+    const spec_layer_weights& l = w.layer;
+    if (!w.norm_h || !w.norm_e || !w.w_proj || !w.final_norm || !l.attn_norm || !l.wq || !l.wk || !l.wv ||
+        !l.wo || !l.ffn_norm || !l.wg || !l.wu || !l.wd)
+      rc = fail(nullptr, SPEC_E_INVAL, "mtp: null weight pointer");
+  }
   if (rc) {
     delete c;
     return rc;
@@ -573,6 +741,7 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
     c->draft.layers.assign(cfg->draft.layers, cfg->draft.layers + cfg->draft.n_layers);
     c->draft.d.layers = nullptr;
   }
+  if (c->mtp.present) c->mtp.layers.assign(1, cfg->mtp.layer);
   const size_t need = layout(c, nullptr);
   if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255)) {
     delete c;
@@ -586,6 +755,8 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
     e = launch_rope_table(c->target.rope, c->cap, c->target.d.head_dim, c->target.d.rope_theta, c->stream);
   if (e == hipSuccess && c->draft.present)
     e = launch_rope_table(c->draft.rope, c->cap, c->draft.d.head_dim, c->draft.d.rope_theta, c->stream);
+  if (e == hipSuccess && c->mtp.present)
+    e = launch_rope_table(c->mtp.rope, c->cap, c->mtp.d.head_dim, c->mtp.d.rope_theta, c->stream);
   if (e != hipSuccess) {
     delete c;
     return fail(nullptr, SPEC_E_HIP, "init kernels: %s", hipGetErrorString(e));
@@ -608,7 +779,8 @@ int spec_load_kv(spec_ctx* c, int32_t which, int32_t seq, const void* k, const v
   if (!k || !v) return fail(c, SPEC_E_INVAL, "null k / v");
   if (seq < 0 || seq >= c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "seq %d", seq);
   if (length < 0 || length > c->cfg.max_ctx) return fail(c, SPEC_E_RANGE, "length %d > max_ctx", length);
-  Model* m = which == 0 ? &c->target : (which == 1 && c->draft.present ? &c->draft : nullptr);
+  Model* m = which == 0 ? &c->target
+                        : (which == 1 && c->draft.present ? &c->draft : (which == 2 && c->mtp.present ? &c->mtp : nullptr));
   if (!m) return fail(c, SPEC_E_INVAL, "cache %d not present", which);
   if (c->phase != IDLE && c->phase != READY) return fail(c, SPEC_E_STATE, "load_kv inside a cycle");
   HIPCHK(c, launch_kv_load(m->d.dtype, k, v, m->cache, seq, length, c->stream));
@@ -625,10 +797,21 @@ int spec_load_kv(spec_ctx* c, int32_t which, int32_t seq, const void* k, const v
   return SPEC_OK;
 }
 
+int spec_load_history(spec_ctx* c, int32_t seq, const int32_t* tokens, int32_t length) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  if (!tokens && length > 0) return fail(c, SPEC_E_INVAL, "null tokens");
+  if (seq < 0 || seq >= c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "seq %d", seq);
+  if (length < 0 || length > c->cfg.max_ctx) return fail(c, SPEC_E_RANGE, "length %d > max_ctx", length);
+  if (c->phase != IDLE && c->phase != READY) return fail(c, SPEC_E_STATE, "load_history inside a cycle");
+  HIPCHK(c, launch_hist_write(c->hist + (int64_t)seq * c->hist_ld, c->hist_ld, tokens, length, 1, length, 0,
+                              c->stream));
+  return SPEC_OK;
+}
+
 int spec_set_last(spec_ctx* c, const int32_t* last_tok, const int32_t* prev_tok, const float* hidden,
                   int32_t batch) {
-  (void)hidden;
   if (need_ctx(c)) return SPEC_E_INVAL;
+  if (c->mtp.present && !hidden) return fail(c, SPEC_E_INVAL, "the MTP drafter needs the hidden state at L-1");
   if (!last_tok) return fail(c, SPEC_E_INVAL, "null last_tok");
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
   if (c->draft.present && !prev_tok) return fail(c, SPEC_E_INVAL, "a draft model needs prev_tok");
@@ -636,6 +819,15 @@ int spec_set_last(spec_ctx* c, const int32_t* last_tok, const int32_t* prev_tok,
   if (!c->started) return fail(c, SPEC_E_STATE, "set_last needs a loaded cache prefix");
   HIPCHK(c, launch_copy_rows(last_tok, 1, c->last_tok, batch, c->stream));
   if (prev_tok) HIPCHK(c, launch_copy_rows(prev_tok, 1, c->prev_tok, batch, c->stream));
+  HIPCHK(c, launch_hist_set_last(c->hist, c->hist_ld, c->len, last_tok, prev_tok, batch, c->stream));
+  if (c->mtp.present) {
+    // the head's cache prefix covers positions 0..L-1; its first row is position L
+    const int d = c->mtp.d.d_model;
+    HIPCHK(c, launch_copy_rows_f32(hidden, d, 1, d, batch, c->mtp_h, (int64_t)(c->cfg.max_k + 1) * d, c->stream));
+    HIPCHK(c, launch_len_from(c->mtp_len, c->len, batch, 0, c->stream));
+    c->mtp_rows = 1;
+  }
+  c->ngram_cycle = false;
   c->phase = READY;
   return SPEC_OK;
 }
@@ -650,7 +842,13 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int32_t batch, int32_t P) {
   if (c->phase != IDLE && c->phase != READY) return fail(c, SPEC_E_STATE, "prefill inside a cycle");
   const int L0 = c->started ? c->len_hi : 0;
   if (L0 + P - 1 > c->cfg.max_ctx) return fail(c, SPEC_E_RANGE, "prompt longer than max_ctx");
-  int done = 0;
+  if (c->mtp.present && (L0 != 0 || P < 2))
+    return fail(c, SPEC_E_UNSUPPORTED, "MTP prefill runs from an empty context over at least two tokens");
+  HIPCHK(c, launch_hist_write(c->hist, c->hist_ld, tokens, P, batch, P, L0, c->stream));
+  // the head's cache starts at position 1: position 0 has no previous hidden state
+  if (c->mtp.present) HIPCHK(c, launch_len_from(c->mtp_len, c->len, batch, 1, c->stream));
+  const int d = c->target.d.d_model;
+  int done = 0, last_chunk = 0;
   while (done < P - 1) {
     const int chunk = std::min(std::min(c->target.mseq_max, P - 1 - done),
                                c->draft.present ? c->draft.mseq_max : 1 << 30);
@@ -660,11 +858,28 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int32_t batch, int32_t P) {
       rc = forward(c, c->draft, batch, chunk, tokens + done, P, tokens + done + 1, P, 0, nullptr);
       if (rc) return rc;
     }
+    if (c->mtp.present) {
+      // head rows at positions done+1 .. from the target hidden states at done .., except
+      // position P-1 (the last token's), which the first draft_step computes
+      const int cnt = (done + chunk == P - 1) ? chunk - 1 : chunk;
+      if (cnt > 0) {
+        rc = mtp_layer(c, batch, cnt, c->target.x, (int64_t)chunk * d, tokens + done + 1, P, nullptr, 0);
+        if (rc) return rc;
+        HIPCHK(c, launch_add_len(c->mtp_len, batch, cnt, c->stream));
+      }
+    }
     HIPCHK(c, launch_add_len(c->len, batch, chunk, c->stream));
     done += chunk;
+    last_chunk = chunk;
+  }
+  if (c->mtp.present) {
+    HIPCHK(c, launch_copy_rows_f32(c->target.x + (int64_t)(last_chunk - 1) * d, (int64_t)last_chunk * d, 1, d,
+                                   batch, c->mtp_h, (int64_t)(c->cfg.max_k + 1) * d, c->stream));
+    c->mtp_rows = 1;
   }
   HIPCHK(c, launch_copy_rows(tokens + (P - 1), P, c->last_tok, batch, c->stream));
   if (P >= 2) HIPCHK(c, launch_copy_rows(tokens + (P - 2), P, c->prev_tok, batch, c->stream));
+  c->ngram_cycle = false;
   c->len_lo = c->len_hi = L0 + P - 1;
   c->started = true;
   c->phase = READY;
@@ -674,23 +889,41 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int32_t batch, int32_t P) {
 int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* draft_tok, spec_probs* q,
                int32_t* n_drafted) {
   if (need_ctx(c)) return SPEC_E_INVAL;
-  if (c->cfg.draft_kind != SPEC_DRAFT_MODEL) return fail(c, SPEC_E_UNSUPPORTED, "no draft model configured");
+  const int kind = c->cfg.draft_kind;
+  if (kind == SPEC_DRAFT_NONE) return fail(c, SPEC_E_UNSUPPORTED, "no drafter configured");
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
   if (k < 1 || k > c->cfg.max_k) return fail(c, SPEC_E_RANGE, "k %d not in 1..max_k", k);
   if (!draft_tok) return fail(c, SPEC_E_INVAL, "null draft_tok");
   int rc = check_probs(c, q, "q", list_cap(c->cfg.sampler));
   if (rc) return rc;
   if (c->phase != READY) return fail(c, SPEC_E_STATE, "draft_step needs a start (prefill / set_last) or a trimmed cycle");
-  if (c->len_lo < 1) return fail(c, SPEC_E_STATE, "draft model needs a token before the last one");
-  rc = ensure_room(c, batch, k + 1);
+  if (kind == SPEC_DRAFT_MODEL && c->len_lo < 1)
+    return fail(c, SPEC_E_STATE, "draft model needs a token before the last one");
+  // the MTP catch-up writes its cache up to mtp_rows - 1 positions past L
+  rc = ensure_room(c, batch, std::max(k, kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0) + 1);
   if (rc) return rc;
-  HIPCHK(c, launch_set_u32(c->round_dev, (uint32_t)round, c->stream));
   const spec_probs qq = *q;
-  const void* key[8] = {draft_tok, qq.ids, qq.probs, qq.count, (const void*)(intptr_t)qq.cap,
-                        nullptr, nullptr, nullptr};
-  rc = run_graphed(c, 1, batch, k, key, [&]() { return enqueue_draft(c, batch, k, draft_tok, qq); });
-  if (rc) return rc;
-  if (n_drafted) *n_drafted = k;
+  if (kind == SPEC_DRAFT_NGRAM) {
+    rc = enqueue_draft_ngram(c, batch, k, draft_tok, qq);
+    if (rc) return rc;
+    std::vector<int32_t> found(batch);
+    HIPCHK(c, hipMemcpyAsync(found.data(), c->ndraft, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, c->stream));
+    HIPCHK(c, hipStreamSynchronize(c->stream));
+    int mx = 0;
+    for (int b = 0; b < batch; ++b) mx = std::max(mx, found[b]);
+    if (n_drafted) *n_drafted = mx;
+    c->ngram_cycle = true;
+  } else {
+    HIPCHK(c, launch_set_u32(c->round_dev, (uint32_t)round, c->stream));
+    const void* key[8] = {draft_tok, qq.ids, qq.probs, qq.count, (const void*)(intptr_t)qq.cap,
+                          (const void*)(intptr_t)(kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0), nullptr, nullptr};
+    if (kind == SPEC_DRAFT_MTP)
+      rc = run_graphed(c, 2, batch, k, key, [&]() { return enqueue_draft_mtp(c, batch, k, draft_tok, qq); });
+    else
+      rc = run_graphed(c, 1, batch, k, key, [&]() { return enqueue_draft(c, batch, k, draft_tok, qq); });
+    if (rc) return rc;
+    if (n_drafted) *n_drafted = k;
+  }
   c->phase = DRAFTED;
   c->phase_k = k;
   c->phase_batch = batch;
@@ -707,6 +940,13 @@ int verify_step(spec_ctx* c, const int32_t* draft_tok, int32_t batch, int32_t k,
   if (rc) return rc;
   if (c->phase != READY && c->phase != DRAFTED)
     return fail(c, SPEC_E_STATE, "verify_step needs a start (prefill / set_last) or a trimmed cycle");
+  if (c->mtp.present && c->phase != DRAFTED)
+    return fail(c, SPEC_E_STATE, "with the MTP drafter every cycle starts with draft_step (the head catches up "
+                                 "only from the previous verify)");
+  if (c->phase == DRAFTED && c->ngram_cycle && batch > 1 && k != c->phase_k)
+    return fail(c, SPEC_E_INVAL, "n-gram drafts of a batch are verified at the drafted k (row stride)");
+  if (c->phase == DRAFTED && k > c->phase_k) return fail(c, SPEC_E_INVAL, "k > drafted k");
+  if (c->phase == READY) c->ngram_cycle = false;
   rc = ensure_room(c, batch, k + 1);
   if (rc) return rc;
   const spec_probs pp = *p;
@@ -748,6 +988,10 @@ int accept(spec_ctx* c, const int32_t* draft_tok, const spec_probs* q, const spe
   a.last_tok = c->last_tok;
   a.prev_tok = c->prev_tok;
   a.stats = c->stats;
+  a.kcap = c->ngram_cycle ? c->ndraft : nullptr;
+  a.hist = c->hist;
+  a.hist_ld = c->hist_ld;
+  a.len = c->len;
   LAUNCH(c, PROF_ACCEPT, launch_accept(a, c->stream));
   c->phase = ACCEPTED;
   return SPEC_OK;
@@ -758,9 +1002,11 @@ int kv_trim(spec_ctx* c, const int32_t* n_acc, int32_t batch) {
   if (c->phase != ACCEPTED) return fail(c, SPEC_E_STATE, "kv_trim must follow accept");
   if (batch != c->phase_batch) return fail(c, SPEC_E_STATE, "batch differs from the cycle");
   if (!n_acc) return fail(c, SPEC_E_INVAL, "null n_acc");
-  LAUNCH(c, PROF_TRIM, launch_trim(c->len, n_acc, batch, c->stream));
+  LAUNCH(c, PROF_TRIM, launch_trim(c->len, n_acc, batch, c->mtp.present ? c->mtp_len : nullptr, c->stream));
   c->len_lo += 1;
   c->len_hi += 1 + c->phase_k;
+  c->mtp_rows = c->phase_k + 1;
+  c->ngram_cycle = false;
   c->phase = READY;
   return SPEC_OK;
 }
@@ -813,6 +1059,45 @@ int spec_get_lengths(spec_ctx* c, int32_t* lengths, int32_t batch) {
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
   HIPCHK(c, hipMemcpyAsync(lengths, c->len, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
+  return SPEC_OK;
+}
+
+// ---------------------------------------------------------------- n-gram gate (host)
+int spec_gate_init(spec_gate* g, int32_t n_max, const double* verify_cost, double draft_cost, int32_t enabled) {
+  if (!g || !verify_cost || n_max < 0 || n_max > SPEC_MAX_K) return SPEC_E_INVAL;
+  if (!(verify_cost[0] > 0.0) || !(draft_cost >= 0.0)) return SPEC_E_INVAL;
+  for (int k = 0; k <= n_max; ++k)
+    if (!(verify_cost[k] > 0.0)) return SPEC_E_INVAL;
+  g->n_max = n_max;
+  g->enabled = enabled != 0;
+  g->weight = 0.5;
+  g->alpha = 1.0;
+  for (int k = 0; k <= SPEC_MAX_K; ++k) g->cost[k] = k <= n_max ? verify_cost[k] / verify_cost[0] : 0.0;
+  g->draft_cost = draft_cost / verify_cost[0];
+  return SPEC_OK;
+}
+
+int32_t spec_gate_choose(const spec_gate* g) {
+  if (!g) return SPEC_E_INVAL;
+  if (!g->enabled) return g->n_max;
+  int best_k = 0;
+  double best_v = -1.0;
+  for (int k = 0; k <= g->n_max; ++k) {
+    // expected tokens of a step that drafts k (1 + alpha + ... + alpha^k) over its cost
+    double gain = 0.0;
+    for (int i = 0; i <= k; ++i) gain += std::pow(g->alpha, (double)i);
+    const double v = gain / (g->cost[k] + k * g->draft_cost);
+    if (v > best_v + 1e-12) {
+      best_k = k;
+      best_v = v;
+    }
+  }
+  return best_k;
+}
+
+int spec_gate_update(spec_gate* g, int32_t accepted, int32_t attempted) {
+  if (!g || accepted < 0 || attempted < 0 || accepted > attempted) return SPEC_E_INVAL;
+  if (attempted > 0) g->alpha = g->weight * g->alpha + (1.0 - g->weight) * ((double)accepted / (double)attempted);
   return SPEC_OK;
 }
 
@@ -881,7 +1166,7 @@ int spec_ngram_match(const int32_t* ctx, const int32_t* lengths, int32_t batch, 
                      void* stream) {
   if (!ctx || !lengths || !drafts || !n_found || !match) return SPEC_E_INVAL;
   if (batch < 0 || ld < 1 || k < 1 || n_min < 1 || max_match < n_min) return SPEC_E_INVAL;
-  NgramArgs a{ctx, lengths, batch, ld, k, n_min, max_match, drafts, n_found, match};
+  NgramArgs a{ctx, lengths, batch, ld, k, n_min, max_match, 0, drafts, n_found, match};
   return launch_ngram(a, (hipStream_t)stream) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
 }
 

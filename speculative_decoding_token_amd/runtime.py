@@ -28,20 +28,34 @@ class Cycle:
 
 
 class Engine:
-    """One context: a target, an optional draft model, a sampler and a workspace."""
+    """One context: a target, an optional drafter (a draft model, the target's MTP layer or
+    n-gram lookup), a sampler and a workspace."""
 
     def __init__(self, target_shape, target_w: Dict, draft_shape=None, draft_w: Optional[Dict] = None,
                  temperature: float = 0.0, top_k: int = 20, top_p: float = 0.95, seed: int = 0,
-                 max_batch: int = 1, max_ctx: int = 256, max_k: int = 8, stream=None):
+                 max_batch: int = 1, max_ctx: int = 256, max_k: int = 8, stream=None,
+                 drafter: Optional[str] = None, ngram: Sequence[int] = (3, 16)):
+        """drafter: None (a draft model when draft_shape is given, else none), "model",
+        "mtp" (target_w["mtp"] holds the layer) or "ngram" (ngram = (n_min, max_match))."""
         self._keep: list = []
         cfg = B.spec_config()
         cfg.target = B.model_desc(target_shape, target_w, self._keep)
-        if draft_shape is not None:
+        if drafter is None:
+            drafter = "model" if draft_shape is not None else "none"
+        self.drafter = drafter
+        if drafter == "model":
             cfg.draft_kind = B.DRAFT_MODEL
             cfg.draft = B.model_desc(draft_shape, draft_w, self._keep)
-        else:
+        elif drafter == "mtp":
+            cfg.draft_kind = B.DRAFT_MTP
+            cfg.mtp = B.mtp_desc(target_w["mtp"])
+        elif drafter == "ngram":
+            cfg.draft_kind = B.DRAFT_NGRAM
+        elif drafter == "none":
             cfg.draft_kind = B.DRAFT_NONE
-        cfg.ngram = B.spec_ngram_cfg(3, 16)
+        else:
+            raise ValueError(f"drafter {drafter!r}")
+        cfg.ngram = B.spec_ngram_cfg(int(ngram[0]), int(ngram[1]))
         cfg.sampler = B.sampler(temperature, top_k, top_p)
         cfg.seed = seed
         cfg.max_batch, cfg.max_ctx, cfg.max_k = max_batch, max_ctx, max_k
@@ -88,26 +102,36 @@ class Engine:
         with self._enter():
             B.spec_load_kv(self.ctx, which, seq, k, v, length)
 
-    def set_last(self, last_tok: torch.Tensor, prev_tok: Optional[torch.Tensor] = None):
+    def set_last(self, last_tok: torch.Tensor, prev_tok: Optional[torch.Tensor] = None,
+                 hidden: Optional[torch.Tensor] = None):
+        """hidden: float32 [batch, d] target hidden state at L-1 (the MTP drafter)."""
         with self._enter():
-            B.spec_set_last(self.ctx, last_tok, prev_tok, None, last_tok.shape[0])
+            B.spec_set_last(self.ctx, last_tok, prev_tok, hidden, last_tok.shape[0])
+
+    def load_history(self, seq: int, tokens: torch.Tensor):
+        """Token history (int32, device) of sequence seq at positions 0..len-1."""
+        with self._enter():
+            B.spec_load_history(self.ctx, seq, tokens, int(tokens.numel()))
 
     # ---- one cycle
     def buffers(self, batch: int, k: int):
-        key = (batch, k)
-        if getattr(self, "_buf_key", None) != key:
-            dev = "cuda"
-            self._buf = dict(
-                draft=torch.zeros((batch, max(k, 1)), dtype=torch.int32, device=dev),
-                q=B.Probs(batch * max(k, 1), self.cap),
-                p=B.Probs(batch * (k + 1), self.cap),
+        """Views of this batch's cycle buffers, sized once for max_k."""
+        if getattr(self, "_buf_batch", None) != batch:
+            dev, mk = "cuda", max(self.max_k, 1)
+            self._flat = dict(
+                draft=torch.zeros((batch * mk,), dtype=torch.int32, device=dev),
+                q=B.Probs(batch * mk, self.cap),
+                p=B.Probs(batch * (mk + 1), self.cap),
                 n=torch.zeros((batch,), dtype=torch.int32, device=dev),
-                out=torch.zeros((batch, k + 1), dtype=torch.int32, device=dev),
+                out=torch.zeros((batch * (mk + 1),), dtype=torch.int32, device=dev),
                 tie=torch.zeros((batch,), dtype=torch.uint8, device=dev),
-                logits=None,
             )
-            self._buf_key = key
-        return self._buf
+            self._buf_batch = batch
+            self._logits = {}
+        f = self._flat
+        kk = max(k, 1)
+        return dict(draft=f["draft"][: batch * kk].view(batch, kk), q=f["q"], p=f["p"], n=f["n"],
+                    out=f["out"][: batch * (k + 1)].view(batch, k + 1), tie=f["tie"])
 
     def cycle(self, batch: int, k: int, rnd: int, drafts: Optional[torch.Tensor] = None,
               keep: bool = False, sync: bool = True, events: Optional[dict] = None) -> Optional[Cycle]:
@@ -125,20 +149,27 @@ class Engine:
 
     def _cycle(self, batch, k, rnd, drafts, keep, sync, events=None):
         buf = self.buffers(batch, k)
-        if keep and buf["logits"] is None:
-            buf["logits"] = torch.empty((batch, k + 1, self.vocab), dtype=torch.float32, device="cuda")
         if k > 0:
             if drafts is None:
                 self._mark(events, "draft", 0)
-                B.draft_step(self.ctx, batch, k, rnd, buf["draft"], buf["q"])
+                found = B.draft_step(self.ctx, batch, k, rnd, buf["draft"], buf["q"])
                 self._mark(events, "draft", 1)
+                if self.drafter == "ngram" and batch == 1 and found < k:
+                    # verify only what the lookup found (one sequence: the row stride is moot)
+                    k = found
+                    buf = dict(buf, out=buf["out"].view(-1)[: batch * (k + 1)].view(batch, k + 1))
             else:
                 if not self.greedy:
                     raise ValueError("explicit drafts are supported with the greedy sampler")
                 buf["draft"].copy_(drafts.to(torch.int32))
+        logits = None
+        if keep:
+            logits = self._logits.get(k)
+            if logits is None:
+                logits = self._logits[k] = torch.empty((batch, k + 1, self.vocab), dtype=torch.float32,
+                                                       device="cuda")
         self._mark(events, "verify", 0)
-        B.verify_step(self.ctx, buf["draft"] if k > 0 else None, batch, k,
-                      buf["logits"] if keep else None, buf["p"])
+        B.verify_step(self.ctx, buf["draft"] if k > 0 else None, batch, k, logits, buf["p"])
         self._mark(events, "verify", 1)
         self._mark(events, "accept", 0)
         B.accept(self.ctx, buf["draft"] if k > 0 else None, buf["q"] if k > 0 else None, buf["p"],
@@ -149,29 +180,35 @@ class Engine:
             return None
         n = buf["n"].cpu().tolist()
         out = buf["out"].cpu().tolist()
-        c = Cycle(drafts=buf["draft"].cpu().tolist() if k > 0 else [[] for _ in range(batch)], n=n,
+        dr = buf["draft"].cpu().tolist() if k > 0 else [[] for _ in range(batch)]
+        c = Cycle(drafts=[row[:k] for row in dr], n=n,
                   tokens=[out[b][: n[b] + 1] for b in range(batch)], near_tie=buf["tie"].cpu().tolist())
         if keep:
-            c.logits = buf["logits"].clone()
-            c.p = buf["p"].to_lists()
-            c.q = buf["q"].to_lists() if k > 0 else []
+            c.logits = logits.clone()
+            c.p = buf["p"].to_lists(batch * (k + 1))
+            c.q = buf["q"].to_lists(batch * k) if k > 0 else []
         return c
 
     def generate(self, n_new: int, k: int, batch: int = 1, rnd0: int = 0, keep: bool = False,
-                 teacher: Optional[Sequence[int]] = None):
-        """Run cycles until every sequence emitted n_new tokens (batch 1 for ``teacher``).
+                 teacher: Optional[Sequence[int]] = None, gate: Optional["B.Gate"] = None):
+        """Run cycles until every sequence emitted n_new tokens (batch 1 for ``teacher`` and
+        ``gate``).  ``gate`` (the n-gram acceptance gate) picks each cycle's k.
         Returns (tokens [batch][n_new], cycles)."""
         out = [[] for _ in range(batch)]
         cycles = []
         rnd = rnd0
         while min(len(o) for o in out) < n_new:
             drafts = None
+            if gate is not None:
+                k = gate.choose()
             if teacher is not None and k > 0:
                 done = len(out[0])
                 t = list(teacher[done: done + k])
                 t += [0] * (k - len(t))
                 drafts = torch.tensor([t], dtype=torch.int32, device="cuda")
             c = self.cycle(batch, k, rnd, drafts=drafts, keep=keep)
+            if gate is not None:
+                gate.update(c.n[0], len(c.drafts[0]))
             for b in range(batch):
                 out[b].extend(c.tokens[b])
             cycles.append(c)

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "spec.h")
 
 
 def declared_functions():
-    return re.findall(r"^(?:int|const char\*)\s+(\w+)\(", open(HEADER).read(), re.M)
+    return re.findall(r"^(?:int|int32_t|const char\*)\s+(\w+)\(", open(HEADER).read(), re.M)
 
 
 def test_library_exports_every_declared_symbol():
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 STRUCTS = ["spec_layer_weights", "spec_model_desc", "spec_mtp_desc", "spec_sampler", "spec_ngram_cfg",
-           "spec_config", "spec_probs", "spec_stats"]
+           "spec_config", "spec_probs", "spec_stats", "spec_gate"]
 
 
 def test_ctypes_layout_matches_c(tmp_path):
@@ -93,7 +93,7 @@ def test_workspace_size_host_only():
     (lambda c: setattr(c.target, "n_kv_heads", 5), B.SPEC_E_INVAL),
     (lambda c: setattr(c.target, "dtype", 7), B.SPEC_E_INVAL),
     (lambda c: setattr(c.draft, "vocab", 1024), B.SPEC_E_INVAL),
-    (lambda c: setattr(c, "draft_kind", 9), B.SPEC_E_UNSUPPORTED),
+    (lambda c: setattr(c, "draft_kind", 9), B.SPEC_E_INVAL),
     (lambda c: setattr(c, "max_batch", 8), B.SPEC_E_UNSUPPORTED),   # 8 x 9 rows > 64
 ])
 def test_config_validation(mut, code):
@@ -115,3 +115,23 @@ def test_truncate_scratch_size():
     assert n >= 576 * 10 * 64 * 8
     with pytest.raises(B.SpecError):
         B.spec_truncate_scratch_size(1, 64 * 16384 * 2)   # too many segments for one merge
+
+
+def test_mtp_and_ngram_configs():
+    t = synth.SHAPES["qwen9b_mtp"]
+    cfg, keep = host_cfg(t, max_ctx=8192, max_k=4)
+    base = B.spec_workspace_size(cfg)
+    cfg.draft_kind = B.DRAFT_MTP
+    with_mtp = B.spec_workspace_size(cfg)
+    # one more cache layer (8 kv heads x (8192+6) positions x 128 x 2 bytes x 2) and activations
+    assert with_mtp - base > 8 * (8192 + 6) * 128 * 2 * 2
+    cfg.draft_kind = B.DRAFT_NGRAM
+    cfg.ngram = B.spec_ngram_cfg(3, 16)
+    assert B.spec_workspace_size(cfg) == base
+    cfg.ngram = B.spec_ngram_cfg(0, 16)
+    with pytest.raises(B.SpecError) as e:
+        B.spec_workspace_size(cfg)
+    assert e.value.code == B.SPEC_E_INVAL
+    cfg.ngram = B.spec_ngram_cfg(5, 4)
+    with pytest.raises(B.SpecError):
+        B.spec_workspace_size(cfg)
