@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-teacher", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override target layers (debug only)")
     ap.add_argument("--no-graphs", action="store_true", help="plain launches instead of graph replays")
+    ap.add_argument("--schedule", default=None, choices=["step", "stream"],
+                    help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -168,6 +170,8 @@ def main():
 
     if args.no_graphs:
         eng.use_graphs(False)
+    if args.schedule:
+        eng.set_schedule(args.schedule)
     reset()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup

@@ -308,6 +308,20 @@ int spec_profile_read(spec_ctx* ctx, double* ms, int64_t* launches);
  * needs a non-default stream.  0: launch kernel by kernel. */
 int spec_use_graphs(spec_ctx* ctx, int32_t enable);
 
+/* Schedule of the forwards of bf16 models over at most 16 rows.
+ *   SPEC_SCHED_STREAM  projections stream their weights through an LDS ring,
+ *                      one workgroup per compute unit; each residual projection also writes
+ *                      the next RMSNorm's output, so no normalization launch is needed;
+ *   SPEC_SCHED_STEP    (the default) one workgroup per 16-row tile of each projection, RMSNorm fused into
+ *                      the projection or run as its own launch.
+ * Shapes the streamed projections do not cover (reduction lengths that are not whole 1 KB
+ * stages, the MTP head) run as SPEC_SCHED_STEP.  The two agree within the float tolerances,
+ * not bit for bit; each is row-count invariant on its own.  Returns SPEC_E_INVAL for an
+ * unknown schedule. */
+#define SPEC_SCHED_STEP 0
+#define SPEC_SCHED_STREAM 1
+int spec_set_schedule(spec_ctx* ctx, int32_t schedule);
+
 /* Copies the device counters to *out (synchronizes the stream). */
 int spec_get_stats(spec_ctx* ctx, spec_stats* out /*host*/);
 

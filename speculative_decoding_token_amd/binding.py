@@ -35,7 +35,7 @@ EXPORTED = [
     "spec_get_stats", "spec_get_lengths", "spec_truncate_scratch_size", "spec_truncate",
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
     "spec_profile", "spec_profile_read", "spec_use_graphs", "spec_load_history",
-    "spec_gate_init", "spec_gate_choose", "spec_gate_update",
+    "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule",
 ]
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -134,6 +134,7 @@ def lib(path: str = LIB_PATH):
         "spec_profile": ([P, I32], C.c_int),
         "spec_profile_read": ([P, P, P], C.c_int),
         "spec_use_graphs": ([P, I32], C.c_int),
+        "spec_set_schedule": ([P, I32], C.c_int),
         "spec_load_history": ([P, I32, P, I32], C.c_int),
         "spec_gate_init": ([C.POINTER(spec_gate), I32, C.POINTER(C.c_double), C.c_double, I32], C.c_int),
         "spec_gate_choose": ([C.POINTER(spec_gate)], C.c_int32),
@@ -349,6 +350,13 @@ def spec_profile_read(ctx: int) -> Dict[str, Dict[str, float]]:
             model = "target" if slot < 16 else "draft"
             out[f"{model}.{PROF_CLASSES[slot % 16]}"] = {"ms": ms[slot], "launches": n[slot]}
     return out
+
+
+SCHEDULES = {"step": 0, "stream": 1}
+
+
+def spec_set_schedule(ctx: int, schedule: str) -> None:
+    _check(lib().spec_set_schedule(ctx, SCHEDULES[schedule]), ctx)
 
 
 def spec_use_graphs(ctx: int, enable: bool) -> None:

@@ -12,6 +12,8 @@
 namespace spec {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;  // one MFMA operand slice
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;    // one 16x16 MFMA accumulator slice
 
 // ---- number formats ------------------------------------------------------------------
 SPEC_DEVINL float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }

@@ -133,9 +133,11 @@ constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions
 constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)
 
 hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStream_t st);
+// y (bf16 models, may be null): also writes the rows times gain (float32), the input of the
+// streamed projections' RMSNorm.
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        float* ss, int ss_ld, hipStream_t st);
+                        float* ss, int ss_ld, float* y, const void* gain, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, int M, int d,
                           void* y, hipStream_t st);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st);
@@ -182,5 +184,43 @@ hipError_t launch_gather_last(const float* x, const float* ss, int ss_ld, int d,
 // dst[b * dst_ss + i * d + e] = src[b * src_ss + i * d + e] for i < R, e < d.
 hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, int batch, float* dst,
                                 int64_t dst_ss, hipStream_t st);
+
+// ---- weight-streaming projections (bf16 models, M <= 16 rows) -------------------------
+// out[m, n] = sum_k W[n, k] x[m, k] with W streamed through an LDS ring by one workgroup per
+// compute unit (see stream.hip).  Epilogues as GemmArgs.  The input rows are either bf16
+// rows x [M, K], or (xres set) an RMSNorm: xres [M, K] holds the float32 residual rows
+// already multiplied by the norm's gain, row m's sum of squares is the np_in partials
+// ss_in[m * ss_ld + 0 ..] added in order, and the input is bf16(xres * rsqrt(mean + eps)).
+// EPI_RESID adds into out (row stride ld) and leaves, when set, ss_out[m * ss_ld + u] = the
+// sum of squares of the 16 updated columns of unit u, and y_out = the updated rows times
+// y_gain (the next norm's input).
+struct StreamArgs {
+  const void* w[3];   // EPI_QKV: W_q, W_k, W_v; EPI_SWIGLU: W_gate, W_up; else W
+  int rows[3];
+  int K, nunits;      // nunits: row tiles of 16 (EPI_SWIGLU: gate/up tile pairs)
+  const void* x;      // [M, K] bf16 input rows (when xres is null)
+  const float* xres;  // normalized input: gain-multiplied residual rows and their partials
+  const float* ss_in;
+  int np_in, ss_ld;
+  float eps;
+  int M;
+  float* out;         // EPI_STORE / EPI_RESID: [M, ld]
+  int ld;
+  float* ss_out;      // EPI_RESID
+  float* y_out;       // EPI_RESID: [M, ld] updated rows times y_gain (bf16 [ld])
+  const void* y_gain;
+  void* h;            // EPI_SWIGLU: [M, rows0] bf16
+  float* q_stage;     // EPI_QKV
+  float* k_stage;
+  CacheView cache;
+  int layer;
+  RowMap rm;
+};
+// Whether M rows and reduction length K are covered: K in whole stages (1024; 512 for
+// SwiGLU); normalized inputs only for K in {1024, 2048, 4096, 5120}.
+bool stream_supported(int M, int K, int epi, bool norm);
+size_t stream_lds_bytes();
+hipError_t stream_init();  // per device: LDS limit of the kernels
+hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_t st);
 
 }  // namespace spec

@@ -15,9 +15,6 @@
 
 namespace spec {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-
 // ---------------------------------------------------------------- RoPE table
 // cos/sin of pos * theta^(-2i/head_dim), evaluated in double and stored as float.
 __global__ void rope_table_kernel(float2* table, int cap, int hd, double theta) {
@@ -35,12 +32,13 @@ __global__ void rope_table_kernel(float2* table, int cap, int hd, double theta) 
 // ---------------------------------------------------------------- embedding gather
 // Row m = (seq b, i): token first[b*first_ld] for i == 0, else rest[b*rest_ld + i-1].  Also
 // leaves the row's sum of squares in ss[m * ss_ld] (fixed reduction order) for the fused
-// RMSNorm of the first projection.
+// RMSNorm of the first projection and, when y is set (bf16), the row times gain.
 template <int DT>
 __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vocab,
                                                     const int32_t* first, int first_ld,
                                                     const int32_t* rest, int rest_ld, int mseq,
-                                                    float* x, float* ss, int ss_ld) {
+                                                    float* x, float* ss, int ss_ld, float* y,
+                                                    const bf16_t* gain) {
   using A = Act<DT>;
   __shared__ float red[256];
   const int m = blockIdx.x, b = m / mseq, i = m % mseq, t = threadIdx.x;
@@ -51,6 +49,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
   for (int c = t; c < d; c += blockDim.x) {
     const float v = ok ? A::load(row, c) : __builtin_nanf("");
     x[(int64_t)m * d + c] = v;
+    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = v * bf16_to_f32(gain[c]);
     sq += v * v;
   }
   red[t] = sq;
@@ -60,6 +59,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
     __syncthreads();
   }
   if (ss && t == 0) ss[(int64_t)m * ss_ld] = red[0];
+
 }
 
 // ---------------------------------------------------------------- MTP input
@@ -879,13 +879,13 @@ hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStr
 
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        float* ss, int ss_ld, hipStream_t st) {
+                        float* ss, int ss_ld, float* y, const void* gain, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16)
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_BF16>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, y, (const bf16_t*)gain);
   else
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_F32>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, nullptr, nullptr);
   return hipGetLastError();
 }
 

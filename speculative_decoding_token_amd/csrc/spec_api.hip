@@ -38,6 +38,7 @@ struct Model {
   float* logits = nullptr;
   float* part = nullptr;
   float* ss = nullptr;  // [Mmax][d/16] partial sums of squares of the residual rows
+  float* y = nullptr;   // [Mmax][d] residual rows times the next RMSNorm's gain (streamed path)
   float2* rope = nullptr;
 };
 
@@ -86,6 +87,10 @@ struct spec_ctx {
   float* ss1 = nullptr;         // [max_batch][d/16+1]
   void* mtp_in = nullptr;       // [rows][2d] model dtype
   int mtp_rows = 1;             // rows of the next catch-up (previous cycle's k + 1)
+  // schedule of bf16 forwards over few rows (SPEC_SCHED_*) and the grid of the streamed
+  // projections (one workgroup per compute unit)
+  int sched = SPEC_SCHED_STEP;
+  int ncu = 0;
   void* trunc = nullptr;
   size_t trunc_bytes = 0;
   int cap = 0;
@@ -253,6 +258,7 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.logits = cv.take<float>((size_t)m.Mmax * d.vocab * 4);
   m.part = cv.take<float>((size_t)m.Mmax * d.n_q_heads * m.nchunk * (d.head_dim + 2) * 4);
   m.ss = cv.take<float>((size_t)m.Mmax * (d.d_model / 16 + 1) * 4);
+  m.y = cv.take<float>((size_t)m.Mmax * d.d_model * 4);
   m.rope = cv.take<float2>((size_t)cap * (d.head_dim / 2) * sizeof(float2));
 }
 
@@ -390,9 +396,112 @@ int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const 
   return SPEC_OK;
 }
 
+// Whether the forwards of m over M rows run on the weight-streaming projections: bf16,
+// at most 16 rows, reduction lengths in whole stages (normalized inputs: d in {1024, 2048,
+// 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
+// gain-multiplied rows.
+bool use_stream(spec_ctx* c, const Model& m, int M) {
+  const spec_model_desc& d = m.d;
+  if (c->sched != SPEC_SCHED_STREAM || c->ncu < 1 || d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp) return false;
+  return stream_supported(M, d.d_model, EPI_QKV, true) && stream_supported(M, d.d_model, EPI_SWIGLU, true) &&
+         stream_supported(M, m.q_dim, EPI_RESID, false) && stream_supported(M, d.d_ffn, EPI_RESID, false) &&
+         (m.q_dim + 2 * m.kv_dim) % 16 == 0 && d.d_ffn % 16 == 0 && d.vocab % 16 == 0;
+}
+
+// The decoder layers of m on the streamed projections over the M rows in m.x (np
+// sum-of-squares partials per row in m.ss).
+int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
+  const spec_model_desc& d = m.d;
+  const int P = 16 * m.mi;
+  const int grid = c->ncu;
+  const int ss_ld = d.d_model / 16 + 1;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const spec_layer_weights& w = m.layers[l];
+    StreamArgs g{};
+    g.w[0] = w.wq;
+    g.w[1] = w.wk;
+    g.w[2] = w.wv;
+    g.rows[0] = m.q_dim;
+    g.rows[1] = m.kv_dim;
+    g.rows[2] = m.kv_dim;
+    g.K = d.d_model;
+    g.nunits = (m.q_dim + 2 * m.kv_dim) / 16;
+    g.xres = m.y;
+    g.ss_in = m.ss;
+    g.np_in = np;
+    g.ss_ld = ss_ld;
+    g.eps = d.rms_eps;
+    g.M = M;
+    g.q_stage = m.qst;
+    g.k_stage = m.kst;
+    g.cache = m.cache;
+    g.layer = l;
+    g.rm = rm;
+    LAUNCH(c, P + PROF_QKV, launch_stream_gemm(EPI_QKV, g, grid, c->stream));
+    AttnArgs at{};
+    at.q_stage = m.qst;
+    at.k_stage = m.kst;
+    at.cache = m.cache;
+    at.layer = l;
+    at.rm = rm;
+    at.n_q = d.n_q_heads;
+    at.rope = m.rope;
+    at.scale = 1.0f / sqrtf((float)d.head_dim);
+    at.part = m.part;
+    at.nchunk = m.nchunk;
+    at.out = m.attn;
+    LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
+    StreamArgs o{};
+    o.w[0] = w.wo;
+    o.rows[0] = d.d_model;
+    o.K = m.q_dim;
+    o.nunits = d.d_model / 16;
+    o.x = m.attn;
+    o.M = M;
+    o.out = m.x;
+    o.ld = d.d_model;
+    o.ss_out = m.ss;
+    o.ss_ld = ss_ld;
+    o.y_out = m.y;
+    o.y_gain = w.ffn_norm;
+    LAUNCH(c, P + PROF_OPROJ, launch_stream_gemm(EPI_RESID, o, grid, c->stream));
+    np = d.d_model / 16;
+    StreamArgs gu{};
+    gu.w[0] = w.wg;
+    gu.w[1] = w.wu;
+    gu.rows[0] = d.d_ffn;
+    gu.K = d.d_model;
+    gu.nunits = d.d_ffn / 16;
+    gu.xres = m.y;
+    gu.ss_in = m.ss;
+    gu.np_in = np;
+    gu.ss_ld = ss_ld;
+    gu.eps = d.rms_eps;
+    gu.M = M;
+    gu.h = m.h;
+    LAUNCH(c, P + PROF_GATEUP, launch_stream_gemm(EPI_SWIGLU, gu, grid, c->stream));
+    StreamArgs dn{};
+    dn.w[0] = w.wd;
+    dn.rows[0] = d.d_model;
+    dn.K = d.d_ffn;
+    dn.nunits = d.d_model / 16;
+    dn.x = m.h;
+    dn.M = M;
+    dn.out = m.x;
+    dn.ld = d.d_model;
+    dn.ss_out = m.ss;
+    dn.ss_ld = ss_ld;
+    dn.y_out = m.y;
+    dn.y_gain = l + 1 < d.n_layers ? m.layers[l + 1].attn_norm : d.final_norm;
+    LAUNCH(c, P + PROF_DOWN, launch_stream_gemm(EPI_RESID, dn, grid, c->stream));
+  }
+  return SPEC_OK;
+}
+
 // The decoder layers of m over the M rows already in m.x (np sum-of-squares partials per
 // row in m.ss for bf16 models), rows placed by rm.
 int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
+  if (use_stream(c, m, M)) return run_layers_stream(c, m, M, rm, np);
   const spec_model_desc& d = m.d;
   const hipStream_t st = c->stream;
   const int dt = d.dtype;
@@ -469,6 +578,23 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
 // row) into logits [M, vocab].
 int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const float* ss, int np, float* logits) {
   const spec_model_desc& d = m.d;
+  if (use_stream(c, m, M) && x == m.x && ss == m.ss) {
+    StreamArgs lm{};
+    lm.w[0] = d.lm_head;
+    lm.rows[0] = d.vocab;
+    lm.K = d.d_model;
+    lm.nunits = d.vocab / 16;
+    lm.xres = m.y;
+    lm.ss_in = ss;
+    lm.np_in = np;
+    lm.ss_ld = d.d_model / 16 + 1;
+    lm.eps = d.rms_eps;
+    lm.M = M;
+    lm.out = logits;
+    lm.ld = d.vocab;
+    LAUNCH(c, 16 * m.mi + PROF_LMHEAD, launch_stream_gemm(EPI_STORE, lm, c->ncu, c->stream));
+    return SPEC_OK;
+  }
   GemmArgs lm{};
   lm.w[0] = d.lm_head;
   lm.rows[0] = d.vocab;
@@ -489,9 +615,11 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
   const int M = B * mseq;
   const bool fused = d.dtype == SPEC_DTYPE_BF16;
   const int ss_ld = d.d_model / 16 + 1;
-  LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_embed(d.dtype, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld,
-                                                 M, mseq, m.x, fused ? m.ss : nullptr, ss_ld, c->stream));
   RowMap rm{M, mseq, c->len, pos_off};
+  const bool stream = use_stream(c, m, M);
+  LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_embed(d.dtype, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld,
+                                                 M, mseq, m.x, fused ? m.ss : nullptr, ss_ld, stream ? m.y : nullptr,
+                                                 m.layers[0].attn_norm, c->stream));
   int rc = run_layers(c, m, M, rm, 1);
   if (rc) return rc;
   if (logits) return run_head(c, m, M, rm, m.x, m.ss, d.d_model / 16, logits);
@@ -667,7 +795,7 @@ template <typename F>
 int run_graphed(spec_ctx* c, int kind, int batch, int k, const void* const key[8], F enqueue) {
   if (c->prof || !c->graphs || c->stream == nullptr) return enqueue();
   for (auto& g : c->gcache) {
-    if (g.kind == kind && g.batch == batch && g.k == k && !memcmp(g.ptrs, key, sizeof g.ptrs)) {
+    if (g.kind == kind + 16 * c->sched && g.batch == batch && g.k == k && !memcmp(g.ptrs, key, sizeof g.ptrs)) {
       HIPCHK(c, hipGraphLaunch(g.exec, c->stream));
       return SPEC_OK;
     }
@@ -682,7 +810,7 @@ int run_graphed(spec_ctx* c, int kind, int batch, int k, const void* const key[8
   }
   if (e != hipSuccess) return fail(c, SPEC_E_HIP, "graph capture: %s", hipGetErrorString(e));
   GraphEntry g;
-  g.kind = kind;
+  g.kind = kind + 16 * c->sched;
   g.batch = batch;
   g.k = k;
   memcpy(g.ptrs, key, sizeof g.ptrs);
@@ -757,6 +885,12 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
     e = launch_rope_table(c->draft.rope, c->cap, c->draft.d.head_dim, c->draft.d.rope_theta, c->stream);
   if (e == hipSuccess && c->mtp.present)
     e = launch_rope_table(c->mtp.rope, c->cap, c->mtp.d.head_dim, c->mtp.d.rope_theta, c->stream);
+  if (e == hipSuccess) e = stream_init();
+  if (e == hipSuccess) {
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  }
   if (e != hipSuccess) {
     delete c;
     return fail(nullptr, SPEC_E_HIP, "init kernels: %s", hipGetErrorString(e));
@@ -1033,6 +1167,14 @@ int spec_profile_read(spec_ctx* c, double* ms, int64_t* launches) {
     c->ev_free.push_back(r.b);
   }
   c->recs.clear();
+  return SPEC_OK;
+}
+
+int spec_set_schedule(spec_ctx* c, int32_t schedule) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  if (schedule != SPEC_SCHED_STEP && schedule != SPEC_SCHED_STREAM)
+    return fail(c, SPEC_E_INVAL, "schedule %d", schedule);
+  c->sched = schedule;
   return SPEC_OK;
 }
 

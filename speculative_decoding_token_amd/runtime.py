@@ -221,6 +221,10 @@ class Engine:
     def profile_read(self):
         return B.spec_profile_read(self.ctx)
 
+    def set_schedule(self, schedule: str):
+        """'step' (the default) or 'stream' (see spec_set_schedule)."""
+        B.spec_set_schedule(self.ctx, schedule)
+
     def use_graphs(self, enable: bool):
         B.spec_use_graphs(self.ctx, enable)
 

@@ -21,13 +21,16 @@ def host_weights(w):
     return out
 
 
+@pytest.mark.parametrize("schedule", ["step", "stream"])
 @pytest.mark.parametrize("name,L,K,temp", [("qwen8b", 2048, 4, 0.0), ("qwen8b", 2048, 8, 1.0),
-                                           ("qwen0p6b", 2047, 16, 1.0), ("qwen27b", 4096, 4, 0.0)])
-def test_full_shape_two_layer_verify_parity(name, L, K, temp):
+                                           ("qwen0p6b", 2047, 16, 1.0), ("qwen0p6b", 2047, 1, 0.0),
+                                           ("qwen27b", 4096, 4, 0.0)])
+def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
     shape = synth.SHAPES[name].with_layers(2)
     w = synth.make_weights(shape, 0, device="cuda")
     k, v = synth.make_kv_prefix(shape, L, 0, device="cuda")
     eng = runtime.Engine(shape, w, temperature=temp, max_ctx=L + 40, max_k=K)
+    eng.set_schedule(schedule)
     eng.load_prefix(0, 0, k, v, L)
     t0 = int(synth.make_tokens(1, shape.vocab, 7)[0])
     eng.set_last(torch.tensor([t0], dtype=torch.int32, device="cuda"))
@@ -51,7 +54,7 @@ def test_full_shape_two_layer_verify_parity(name, L, K, temp):
     kv.load_prefix(k.float().cpu().numpy(), v.float().cpu().numpy())
     ref = om.forward_tokens(spec, W, kv, [t0] + drafts)
     err = assert_rows_close(logits, ref, RTOL_BF16)
-    print(f"{name} L={L} K={K}: worst row error {err:.2e}")
+    print(f"{name} L={L} K={K} {schedule}: worst row error {err:.2e}")
     abs_err = np.abs(logits.astype(np.float64) - ref).max(axis=1)
     for i in range(K + 1):
         o = osm.truncate(ref[i], temp, 20, 0.95)
