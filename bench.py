@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--no-teacher", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override target layers (debug only)")
     ap.add_argument("--no-graphs", action="store_true", help="plain launches instead of graph replays")
-    ap.add_argument("--schedule", default=None, choices=["step", "stream"],
+    ap.add_argument("--schedule", default=None, choices=["step", "stream", "forward"],
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")

@@ -146,6 +146,8 @@ typedef struct spec_stats {
   int64_t drafts_attempted; /* sum of k over accept calls and sequences        */
   int64_t drafts_accepted;  /* sum of n                                        */
   int64_t emitted;          /* sum of n + 1                                    */
+  int64_t sync_timeouts;    /* non-zero once a grid barrier of the one-launch forward timed
+                             * out (its results, and every later one, are invalid)   */
 } spec_stats;
 
 typedef struct spec_ctx spec_ctx;
@@ -309,18 +311,31 @@ int spec_profile_read(spec_ctx* ctx, double* ms, int64_t* launches);
 int spec_use_graphs(spec_ctx* ctx, int32_t enable);
 
 /* Schedule of the forwards of bf16 models over at most 16 rows.
- *   SPEC_SCHED_STREAM  projections stream their weights through an LDS ring,
- *                      one workgroup per compute unit; each residual projection also writes
- *                      the next RMSNorm's output, so no normalization launch is needed;
- *   SPEC_SCHED_STEP    (the default) one workgroup per 16-row tile of each projection, RMSNorm fused into
- *                      the projection or run as its own launch.
- * Shapes the streamed projections do not cover (reduction lengths that are not whole 1 KB
- * stages, the MTP head) run as SPEC_SCHED_STEP.  The two agree within the float tolerances,
- * not bit for bit; each is row-count invariant on its own.  Returns SPEC_E_INVAL for an
- * unknown schedule. */
+ *   SPEC_SCHED_STEP    (the default) one workgroup per 16-row tile of each projection,
+ *                      RMSNorm fused into the projection or run as its own launch;
+ *   SPEC_SCHED_STREAM  one launch per step, projections streaming their weights through an
+ *                      LDS ring with one workgroup per compute unit; each residual projection
+ *                      leaves the next RMSNorm's input, so no normalization launch is needed;
+ *   SPEC_SCHED_FORWARD the whole forward as one persistent (cooperative) launch of the
+ *                      SPEC_SCHED_STREAM steps meeting at grid barriers, the next
+ *                      projection's weights streaming while a barrier is awaited; draft_step
+ *                      and verify_step are then launched directly, not replayed from graphs.
+ * Shapes a schedule does not cover (reduction lengths that are not whole 1 KB stages, head
+ * sizes other than 128 for SPEC_SCHED_FORWARD, the MTP head) fall back to the next simpler
+ * one.  Schedules agree within the float tolerances, not bit for bit; each is row-count
+ * invariant on its own.  Returns SPEC_E_INVAL for an unknown schedule. */
 #define SPEC_SCHED_STEP 0
 #define SPEC_SCHED_STREAM 1
+#define SPEC_SCHED_FORWARD 2
 int spec_set_schedule(spec_ctx* ctx, int32_t schedule);
+
+/* Timeline of the one-launch forward (SPEC_SCHED_FORWARD): with buf set (device, caller
+ * owned, at least grid * 16 bytes), every later launch writes, per grid barrier e and
+ * workgroup g, the 100 MHz constant clock at arrival and at departure to
+ * buf[(e * grid + g) * 2 + {0, 1}] (unsigned 64-bit), for e < bytes / (grid * 16); e = 0 is
+ * the start of the launch.  buf == NULL turns it off.  *grid (host, may be NULL) receives the
+ * launch's workgroup count (0: the one-launch forward is not available). */
+int spec_trace_forward(spec_ctx* ctx, void* buf /*device*/, int64_t bytes, int32_t* grid /*host*/);
 
 /* Copies the device counters to *out (synchronizes the stream). */
 int spec_get_stats(spec_ctx* ctx, spec_stats* out /*host*/);

@@ -35,11 +35,11 @@ EXPORTED = [
     "spec_get_stats", "spec_get_lengths", "spec_truncate_scratch_size", "spec_truncate",
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
     "spec_profile", "spec_profile_read", "spec_use_graphs", "spec_load_history",
-    "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule",
+    "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
 ]
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
-                "truncate", "sample", "accept", "kv_trim"]
+                "truncate", "sample", "accept", "kv_trim", "forward", "13", "14", "15"]
 
 
 class SpecError(RuntimeError):
@@ -93,7 +93,7 @@ class spec_gate(C.Structure):
 
 class spec_stats(C.Structure):
     _fields_ = [("cycles", C.c_int64), ("drafts_attempted", C.c_int64),
-                ("drafts_accepted", C.c_int64), ("emitted", C.c_int64)]
+                ("drafts_accepted", C.c_int64), ("emitted", C.c_int64), ("sync_timeouts", C.c_int64)]
 
 
 _lib = None
@@ -135,6 +135,7 @@ def lib(path: str = LIB_PATH):
         "spec_profile_read": ([P, P, P], C.c_int),
         "spec_use_graphs": ([P, I32], C.c_int),
         "spec_set_schedule": ([P, I32], C.c_int),
+        "spec_trace_forward": ([P, P, C.c_int64, C.POINTER(C.c_int32)], C.c_int),
         "spec_load_history": ([P, I32, P, I32], C.c_int),
         "spec_gate_init": ([C.POINTER(spec_gate), I32, C.POINTER(C.c_double), C.c_double, I32], C.c_int),
         "spec_gate_choose": ([C.POINTER(spec_gate)], C.c_int32),
@@ -281,7 +282,7 @@ def spec_get_stats(ctx: int) -> Dict[str, int]:
     s = spec_stats()
     _check(lib().spec_get_stats(ctx, C.byref(s)), ctx)
     return {"cycles": s.cycles, "drafts_attempted": s.drafts_attempted,
-            "drafts_accepted": s.drafts_accepted, "emitted": s.emitted}
+            "drafts_accepted": s.drafts_accepted, "emitted": s.emitted, "sync_timeouts": s.sync_timeouts}
 
 
 def spec_get_lengths(ctx: int, batch: int) -> List[int]:
@@ -352,7 +353,14 @@ def spec_profile_read(ctx: int) -> Dict[str, Dict[str, float]]:
     return out
 
 
-SCHEDULES = {"step": 0, "stream": 1}
+SCHEDULES = {"step": 0, "stream": 1, "forward": 2}
+
+
+def spec_trace_forward(ctx: int, buf, nbytes: int) -> int:
+    """Sets (buf: a device tensor) or clears (None) the barrier timeline; returns the grid."""
+    g = C.c_int32(0)
+    _check(lib().spec_trace_forward(ctx, _ptr(buf) if buf is not None else None, int(nbytes), C.byref(g)), ctx)
+    return g.value
 
 
 def spec_set_schedule(ctx: int, schedule: str) -> None:

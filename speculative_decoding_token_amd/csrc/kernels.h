@@ -72,7 +72,9 @@ hipError_t launch_philox(uint64_t seed, const uint32_t* ctr, int n, float* out, 
 hipError_t launch_ngram(const NgramArgs& a, hipStream_t st);
 
 // ---- model --------------------------------------------------------------------------
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+// EPI_QKV_ROWS (streamed projections only): the q, k and v rows of one token side by side,
+// out[m, n] for n < rows0 + 2 rows1 with row stride ld.
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_QKV = 2, EPI_SWIGLU = 3, EPI_QKV_ROWS = 4 };
 
 // Cache layout: [batch][n_layers][n_kv][cap][head_dim] in the model dtype.
 struct CacheView {
@@ -195,8 +197,12 @@ hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, 
 // sum of squares of the 16 updated columns of unit u, and y_out = the updated rows times
 // y_gain (the next norm's input).
 struct StreamArgs {
-  const void* w[3];   // EPI_QKV: W_q, W_k, W_v; EPI_SWIGLU: W_gate, W_up; else W
-  int rows[3];
+  // EPI_QKV / EPI_QKV_ROWS: W_q, W_k, W_v; EPI_SWIGLU: W_gate, W_up; else W.  Separate
+  // members, not an array: an indexed member would move the block to scratch memory.
+  const void* w0;
+  const void* w1;
+  const void* w2;
+  int rows0, rows1, rows2;
   int K, nunits;      // nunits: row tiles of 16 (EPI_SWIGLU: gate/up tile pairs)
   const void* x;      // [M, K] bf16 input rows (when xres is null)
   const float* xres;  // normalized input: gain-multiplied residual rows and their partials
@@ -222,5 +228,48 @@ bool stream_supported(int M, int K, int epi, bool norm);
 size_t stream_lds_bytes();
 hipError_t stream_init();  // per device: LDS limit of the kernels
 hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_t st);
+
+// ---- one persistent launch per forward (bf16 models, M <= 16 rows) ------------------
+// The rows, positions and buffers of forward(); x, y, ss, q/k staging, attention partials and
+// outputs and the SwiGLU product are the model's workspace buffers.  layers is a device copy
+// of the layer table.  sync: forward_sync_bytes() of device memory, zero before the first
+// launch (its last word is a sticky error flag: non-zero once a barrier has timed out).
+struct FwdArgs {
+  const spec_layer_weights* layers;
+  int n_layers, d, n_q, n_kv, ffn, vocab, q_dim, kv_dim;
+  float eps, scale;
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  int M, mseq, pos_off;
+  const int32_t* len;
+  const int32_t* first;
+  int first_ld;
+  const int32_t* rest;
+  int rest_ld;
+  CacheView cache;
+  const float2* rope;
+  float* x;       // [M][d] residual rows
+  float* y;       // [M][d] residual rows times the next norm's gain
+  float* ss;      // [M][ss_ld] sum-of-squares partials
+  int ss_ld;
+  float* qkv;     // [M][q_dim + 2 kv_dim] raw q, k, v rows
+  float* part;    // [M * n_q][nchunk][hd + 2]
+  int nchunk;
+  void* attn;     // [M][q_dim] bf16
+  void* h;        // [M][ffn] bf16
+  float* logits;  // [M][vocab] or null
+  unsigned* sync;
+  // optional timeline: barrier e of workgroup g writes the constant-rate clock when the
+  // workgroup arrives and when it leaves to trace[(e * grid + g) * 2 + {0, 1}] (e < trace_cap)
+  unsigned long long* trace;
+  int trace_cap;
+};
+bool forward_supported(int M, int mseq, int d, int n_q, int n_kv, int hd, int ffn, int vocab);
+size_t forward_sync_bytes();
+// per device: LDS limits; *grid = workgroups of one launch (one per compute unit, a multiple
+// of 8), 0 when the launch cannot be co-resident
+hipError_t forward_init(int* grid);
+hipError_t launch_forward(const FwdArgs& a, int grid, hipStream_t st);
 
 }  // namespace spec

@@ -39,6 +39,8 @@ struct Model {
   float* part = nullptr;
   float* ss = nullptr;  // [Mmax][d/16] partial sums of squares of the residual rows
   float* y = nullptr;   // [Mmax][d] residual rows times the next RMSNorm's gain (streamed path)
+  float* qkv = nullptr; // [Mmax][q_dim + 2 kv_dim] raw q, k, v rows (one-launch forward)
+  spec_layer_weights* dev_layers = nullptr;  // device copy of the layer table (one-launch forward)
   float2* rope = nullptr;
 };
 
@@ -48,7 +50,8 @@ enum Phase { IDLE = 0, READY = 1, DRAFTED = 2, VERIFIED = 3, ACCEPTED = 4 };
 
 enum ProfClass {
   PROF_EMBED = 0, PROF_NORM = 1, PROF_QKV = 2, PROF_ATTN = 3, PROF_OPROJ = 4, PROF_GATEUP = 5,
-  PROF_DOWN = 6, PROF_LMHEAD = 7, PROF_TRUNC = 8, PROF_SAMPLE = 9, PROF_ACCEPT = 10, PROF_TRIM = 11
+  PROF_DOWN = 6, PROF_LMHEAD = 7, PROF_TRUNC = 8, PROF_SAMPLE = 9, PROF_ACCEPT = 10, PROF_TRIM = 11,
+  PROF_FORWARD = 12
 };
 
 struct ProfRec {
@@ -91,6 +94,10 @@ struct spec_ctx {
   // projections (one workgroup per compute unit)
   int sched = SPEC_SCHED_STEP;
   int ncu = 0;
+  int fgrid = 0;            // workgroups of the one-launch forward (0: not available)
+  unsigned* fsync = nullptr;  // its barrier words
+  unsigned long long* ftrace = nullptr;  // optional barrier timeline (spec_trace_forward)
+  int ftrace_cap = 0;
   void* trunc = nullptr;
   size_t trunc_bytes = 0;
   int cap = 0;
@@ -259,6 +266,8 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.part = cv.take<float>((size_t)m.Mmax * d.n_q_heads * m.nchunk * (d.head_dim + 2) * 4);
   m.ss = cv.take<float>((size_t)m.Mmax * (d.d_model / 16 + 1) * 4);
   m.y = cv.take<float>((size_t)m.Mmax * d.d_model * 4);
+  m.qkv = cv.take<float>((size_t)m.Mmax * (m.q_dim + 2 * m.kv_dim) * 4);
+  m.dev_layers = cv.take<spec_layer_weights>((size_t)d.n_layers * sizeof(spec_layer_weights));
   m.rope = cv.take<float2>((size_t)cap * (d.head_dim / 2) * sizeof(float2));
 }
 
@@ -277,6 +286,7 @@ size_t layout(spec_ctx* c, void* ws) {
   c->hist = cv.take<int32_t>((size_t)B * c->hist_ld * 4);
   c->ndraft = cv.take<int32_t>(B * 4);
   c->match = cv.take<int32_t>(B * 8);
+  c->fsync = cv.take<unsigned>(forward_sync_bytes());
   c->target.mseq_max = max_rows_per_seq(c->target.d, g.max_k, B);
   carve_model(c->target, cv, B, c->cap);
   if (c->draft.present) {
@@ -418,12 +428,12 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
   for (int l = 0; l < d.n_layers; ++l) {
     const spec_layer_weights& w = m.layers[l];
     StreamArgs g{};
-    g.w[0] = w.wq;
-    g.w[1] = w.wk;
-    g.w[2] = w.wv;
-    g.rows[0] = m.q_dim;
-    g.rows[1] = m.kv_dim;
-    g.rows[2] = m.kv_dim;
+    g.w0 = w.wq;
+    g.w1 = w.wk;
+    g.w2 = w.wv;
+    g.rows0 = m.q_dim;
+    g.rows1 = m.kv_dim;
+    g.rows2 = m.kv_dim;
     g.K = d.d_model;
     g.nunits = (m.q_dim + 2 * m.kv_dim) / 16;
     g.xres = m.y;
@@ -452,8 +462,8 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     at.out = m.attn;
     LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
     StreamArgs o{};
-    o.w[0] = w.wo;
-    o.rows[0] = d.d_model;
+    o.w0 = w.wo;
+    o.rows0 = d.d_model;
     o.K = m.q_dim;
     o.nunits = d.d_model / 16;
     o.x = m.attn;
@@ -467,9 +477,9 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     LAUNCH(c, P + PROF_OPROJ, launch_stream_gemm(EPI_RESID, o, grid, c->stream));
     np = d.d_model / 16;
     StreamArgs gu{};
-    gu.w[0] = w.wg;
-    gu.w[1] = w.wu;
-    gu.rows[0] = d.d_ffn;
+    gu.w0 = w.wg;
+    gu.w1 = w.wu;
+    gu.rows0 = d.d_ffn;
     gu.K = d.d_model;
     gu.nunits = d.d_ffn / 16;
     gu.xres = m.y;
@@ -481,8 +491,8 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     gu.h = m.h;
     LAUNCH(c, P + PROF_GATEUP, launch_stream_gemm(EPI_SWIGLU, gu, grid, c->stream));
     StreamArgs dn{};
-    dn.w[0] = w.wd;
-    dn.rows[0] = d.d_model;
+    dn.w0 = w.wd;
+    dn.rows0 = d.d_model;
     dn.K = d.d_ffn;
     dn.nunits = d.d_model / 16;
     dn.x = m.h;
@@ -580,8 +590,8 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
   const spec_model_desc& d = m.d;
   if (use_stream(c, m, M) && x == m.x && ss == m.ss) {
     StreamArgs lm{};
-    lm.w[0] = d.lm_head;
-    lm.rows[0] = d.vocab;
+    lm.w0 = d.lm_head;
+    lm.rows0 = d.vocab;
     lm.K = d.d_model;
     lm.nunits = d.vocab / 16;
     lm.xres = m.y;
@@ -607,10 +617,64 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
   return SPEC_OK;
 }
 
+// Whether the forward of m over B x mseq rows runs as one persistent launch.
+bool use_forward(spec_ctx* c, const Model& m, int B, int mseq) {
+  const spec_model_desc& d = m.d;
+  if (c->sched != SPEC_SCHED_FORWARD || c->fgrid < 8 || d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp) return false;
+  if (B * mseq > c->fgrid) return false;
+  return forward_supported(B * mseq, mseq, d.d_model, d.n_q_heads, d.n_kv_heads, d.head_dim, d.d_ffn, d.vocab);
+}
+
+int forward_one_launch(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int first_ld,
+                       const int32_t* rest, int rest_ld, int pos_off, float* logits) {
+  const spec_model_desc& d = m.d;
+  FwdArgs a{};
+  a.layers = m.dev_layers;
+  a.n_layers = d.n_layers;
+  a.d = d.d_model;
+  a.n_q = d.n_q_heads;
+  a.n_kv = d.n_kv_heads;
+  a.ffn = d.d_ffn;
+  a.vocab = d.vocab;
+  a.q_dim = m.q_dim;
+  a.kv_dim = m.kv_dim;
+  a.eps = d.rms_eps;
+  a.scale = 1.0f / sqrtf((float)d.head_dim);
+  a.embed = d.embed;
+  a.lm_head = d.lm_head;
+  a.final_norm = d.final_norm;
+  a.M = B * mseq;
+  a.mseq = mseq;
+  a.pos_off = pos_off;
+  a.len = c->len;
+  a.first = first;
+  a.first_ld = first_ld;
+  a.rest = rest ? rest : first;
+  a.rest_ld = rest_ld;
+  a.cache = m.cache;
+  a.rope = m.rope;
+  a.x = m.x;
+  a.y = m.y;
+  a.ss = m.ss;
+  a.ss_ld = d.d_model / 16 + 1;
+  a.qkv = m.qkv;
+  a.part = m.part;
+  a.nchunk = m.nchunk;
+  a.attn = m.attn;
+  a.h = m.h;
+  a.logits = logits;
+  a.sync = c->fsync;
+  a.trace = c->ftrace;
+  a.trace_cap = c->ftrace_cap;
+  LAUNCH(c, 16 * m.mi + PROF_FORWARD, launch_forward(a, c->fgrid, c->stream));
+  return SPEC_OK;
+}
+
 // One forward of model m over M = B*mseq rows; rows' tokens come from first/rest (see
 // launch_embed) at positions len + pos_off + i.  Logits go to `logits` when non-null.
 int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int first_ld,
             const int32_t* rest, int rest_ld, int pos_off, float* logits) {
+  if (use_forward(c, m, B, mseq)) return forward_one_launch(c, m, B, mseq, first, first_ld, rest, rest_ld, pos_off, logits);
   const spec_model_desc& d = m.d;
   const int M = B * mseq;
   const bool fused = d.dtype == SPEC_DTYPE_BF16;
@@ -793,7 +857,8 @@ int enqueue_verify(spec_ctx* c, const int32_t* draft_tok, int batch, int k, floa
 // replay computes exactly what a direct enqueue would.
 template <typename F>
 int run_graphed(spec_ctx* c, int kind, int batch, int k, const void* const key[8], F enqueue) {
-  if (c->prof || !c->graphs || c->stream == nullptr) return enqueue();
+  // cooperative launches stay out of captured graphs
+  if (c->prof || !c->graphs || c->stream == nullptr || c->sched == SPEC_SCHED_FORWARD) return enqueue();
   for (auto& g : c->gcache) {
     if (g.kind == kind + 16 * c->sched && g.batch == batch && g.k == k && !memcmp(g.ptrs, key, sizeof g.ptrs)) {
       HIPCHK(c, hipGraphLaunch(g.exec, c->stream));
@@ -886,6 +951,13 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
   if (e == hipSuccess && c->mtp.present)
     e = launch_rope_table(c->mtp.rope, c->cap, c->mtp.d.head_dim, c->mtp.d.rope_theta, c->stream);
   if (e == hipSuccess) e = stream_init();
+  if (e == hipSuccess) e = forward_init(&c->fgrid);
+  // device copies of the layer tables (the one-launch forward reads them)
+  for (Model* m : {&c->target, &c->draft}) {
+    if (e != hipSuccess || !m->present) continue;
+    e = hipMemcpyAsync(m->dev_layers, m->layers.data(), m->layers.size() * sizeof(spec_layer_weights),
+                       hipMemcpyHostToDevice, c->stream);
+  }
   if (e == hipSuccess) {
     int dev = 0;
     e = hipGetDevice(&dev);
@@ -1172,9 +1244,24 @@ int spec_profile_read(spec_ctx* c, double* ms, int64_t* launches) {
 
 int spec_set_schedule(spec_ctx* c, int32_t schedule) {
   if (need_ctx(c)) return SPEC_E_INVAL;
-  if (schedule != SPEC_SCHED_STEP && schedule != SPEC_SCHED_STREAM)
+  if (schedule != SPEC_SCHED_STEP && schedule != SPEC_SCHED_STREAM && schedule != SPEC_SCHED_FORWARD)
     return fail(c, SPEC_E_INVAL, "schedule %d", schedule);
   c->sched = schedule;
+  return SPEC_OK;
+}
+
+int spec_trace_forward(spec_ctx* c, void* buf, int64_t bytes, int32_t* grid) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  if (grid) *grid = c->fgrid;
+  if (!buf || c->fgrid < 1) {
+    c->ftrace = nullptr;
+    c->ftrace_cap = 0;
+    return SPEC_OK;
+  }
+  const int64_t per = (int64_t)c->fgrid * 2 * 8;
+  if (bytes < per) return fail(c, SPEC_E_INVAL, "trace buffer: need at least %lld bytes", (long long)per);
+  c->ftrace = (unsigned long long*)buf;
+  c->ftrace_cap = (int)std::min<int64_t>(bytes / per, 1 << 20);
   return SPEC_OK;
 }
 
@@ -1193,6 +1280,11 @@ int spec_get_stats(spec_ctx* c, spec_stats* out) {
   out->drafts_attempted = h[1];
   out->drafts_accepted = h[2];
   out->emitted = h[3];
+  unsigned err = 0;
+  HIPCHK(c, hipMemcpyAsync(&err, (const char*)c->fsync + forward_sync_bytes() - 32 * 4, sizeof err,
+                           hipMemcpyDeviceToHost, c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  out->sync_timeouts = err;
   return SPEC_OK;
 }
 

@@ -1,0 +1,477 @@
+// Weight-streaming projections of bf16 models at M <= 16 token rows: the device code shared by
+// the one-launch-per-projection kernels (stream.hip) and the one-launch-per-forward kernel
+// (forward.hip).
+//
+// A verify pass reads every weight once for K+1 rows ("Speculative Decoding on Apple Silicon:
+// 119% Faster...", section "How speculative decoding works": the pass is dominated by moving
+// weights), so each projection is a stream of its weight matrix from HBM with a little
+// arithmetic on the side.  A projection is built around that stream:
+//
+// * One workgroup of 8 wavefronts per compute unit walks units of 16 weight rows (two 16-row
+//   tiles, gate and up, for SwiGLU) over the whole reduction length K, in stages of 32 row
+//   segments of 1 KB.  Every segment is one wavefront instruction that copies 1 KB of one
+//   row straight from HBM into LDS (buffer_load ... lds): whole cache lines, no registers
+//   held, and three stages of a ring of four are in flight while one is multiplied.  The
+//   stages of consecutive units follow each other without a pause.
+// * The input rows (the B operand of the MFMA) are read once per workgroup into registers
+//   that stay resident: each wavefront keeps the k-slices it multiplies (K / 256 slices of 16
+//   bytes per lane).  RMSNorm is applied on the way in: the inputs of the QKV, gate/up and
+//   vocabulary projections are the float32 residual rows already multiplied by the norm's
+//   gain (written next to the residual by the projection or embedding that produced them),
+//   scaled by 1/sqrt(mean square + eps) from the sum-of-squares partials left with them and
+//   rounded to bf16, so no normalization pass exists.  Long reductions (the down projection,
+//   K = d_ffn) load their slices with each stage instead.
+// * Each wavefront multiplies its k-steps of the stage with v_mfma_f32_16x16x32_bf16 (A = 16
+//   weight rows x 32 k read from LDS in the operand layout, B = the same 32 k of the 16 token
+//   rows, zero past M); the 8 partial tiles meet in LDS at the end of a unit.  The token
+//   dimension is padded to 16 at no cost: the kernel is bound by the weight stream.
+// * Residual projections add into the float32 residual stream and leave, per 16 columns and
+//   row, the sum of squares of the updated values and the values times the next norm's gain.
+//
+// A row's result depends only on that row (every reduction order is fixed by K and d
+// alone), so the rows of a K+1-row verify are bit-identical to one-row forwards.
+#pragma once
+
+#include "kernels.h"
+
+namespace spec {
+namespace sk {
+
+constexpr int SNW = 8;                        // wavefronts per workgroup
+constexpr int SEGP = 1024 + 16;               // LDS pitch of a 1 KB row segment (the padding
+                                              // puts 16 rows 4 banks apart: conflict-free reads)
+constexpr int STAGE = 32 * SEGP;              // one stage: 32 segments
+constexpr int RING = 4;                       // stages in the ring
+constexpr int RED_BYTES = SNW * 2 * 64 * 16;  // partial tiles of the 8 wavefronts (two tiles)
+constexpr int INV_BYTES = 16 * 4;             // 1/rms of the 16 token rows
+constexpr int LDS_BYTES = RING * STAGE + RED_BYTES + INV_BYTES;
+constexpr int CPOL_SC1 = 16;                  // cache policy of coherent loads (device scope)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+SPEC_DEVINL __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+SPEC_DEVINL uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Wait until at most N vector memory operations of this wavefront are outstanding.
+template <int N>
+SPEC_DEVINL void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the release fence of __syncthreads (which would wait for every
+// outstanding load, the whole ring).
+SPEC_DEVINL void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// LDS accesses written as inline asm.  The compiler cannot tell the ring's stages from the
+// other LDS data, so it would make every LDS access wait for all LDS-bound loads in flight;
+// these are ordered by the explicit vmcnt waits and barriers instead.  Reads and the wait for
+// them form one statement, so no use can be scheduled before the wait.
+SPEC_DEVINL void lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint4& r0, uint4& r1, uint4& r2,
+                           uint4& r3) {
+  u32x4_t v0, v1, v2, v3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+  r0 = __builtin_bit_cast(uint4, v0);
+  r1 = __builtin_bit_cast(uint4, v1);
+  r2 = __builtin_bit_cast(uint4, v2);
+  r3 = __builtin_bit_cast(uint4, v3);
+}
+SPEC_DEVINL float lds_read_f32(uint32_t a) {
+  float v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+SPEC_DEVINL void lds_write_f32(uint32_t a, float v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(a), "v"(v) : "memory");
+}
+// The value comes straight from an MFMA accumulator.  The compiler inserts no wait states
+// before inline asm, and an LDS write reading an MFMA result needs up to 18 of them; three
+// s_nop 7 give 24.
+SPEC_DEVINL void lds_write_acc(uint32_t addr, f32x4_t v) {
+  asm volatile(
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "s_nop 7\n\t"
+      "ds_write_b128 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(addr), "v"(__builtin_bit_cast(u32x4_t, v))
+      : "memory");
+}
+
+// Stores and loads of data that another workgroup of the same launch reads or wrote (COH):
+// written through and read past the L2 caches, which are private to each XCD.
+template <bool COH, typename T>
+SPEC_DEVINL void st(T* p, T v) {
+  if (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH, typename T>
+SPEC_DEVINL T ld(const T* p) {
+  if (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+SPEC_DEVINL float silu_s(float g) { return g / (1.0f + expf(-g)); }
+
+// A wave-uniform pointer as a value the compiler cannot trace back to its memory.
+SPEC_DEVINL uint64_t uni64(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  // readfirstlane returns int: each half goes through uint32_t, or a low word with its top bit
+  // set would be sign-extended over the high word
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+SPEC_DEVINL uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// First byte of the 16 weight rows of unit u in matrix t (SwiGLU: 0 gate, 1 up); for the QKV
+// projection the unit's rows may lie in W_q, W_k or W_v.
+template <int EPI>
+SPEC_DEVINL const char* unit_rows(const StreamArgs& a, int u, int t, int* mat, int* r0) {
+  int m = 0, r = u * 16;
+  if (EPI == EPI_QKV || EPI == EPI_QKV_ROWS) {
+    if (r >= a.rows0) {
+      r -= a.rows0;
+      m = 1;
+      if (r >= a.rows1) {
+        r -= a.rows1;
+        m = 2;
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    m = t;
+  }
+  *mat = m;
+  *r0 = r;
+  // the pointers pass through readfirstlane before the select: a select of members would be
+  // folded into an indexed load, which keeps the argument block in scratch memory
+  const uint64_t w = m == 0 ? uni64(a.w0) : (m == 1 ? uni64(a.w1) : uni64(a.w2));
+  return (const char*)w + (int64_t)r * a.K * 2;
+}
+
+// One projection over this workgroup's units (blockIdx.x, blockIdx.x + grid, ...).
+// EPI: epilogue.  NST > 0: K = NST stages, input slices resident in registers (normalized on
+// the way in when a.xres is set); NST == 0: any K of whole stages, bf16 input slices loaded
+// with each stage.  COH: activations cross workgroups inside the launch.
+template <int EPI, int NST, bool COH>
+struct Gemm {
+  static constexpr int TILES = EPI == EPI_SWIGLU ? 2 : 1;
+  static constexpr int S = RING;
+  static constexpr int KS = TILES == 1 ? 1024 : 512;  // k per stage
+  static constexpr int WSTEPS = KS / 32 / SNW;        // k-steps of 32 per wavefront and stage
+  static constexpr bool RES = NST > 0;                // resident input slices
+  static constexpr int C = 4 + (RES ? 0 : WSTEPS);    // vector memory instructions per wavefront and stage
+  static constexpr int XS = RES ? NST * WSTEPS : 1;   // resident slices per lane
+  static constexpr int XP = COH ? CPOL_SC1 : 0;       // cache policy of activation loads
+  static_assert(WSTEPS * TILES == 4, "four operand reads per wavefront and stage");
+
+  static SPEC_DEVINL int stages_per_unit(const StreamArgs& a) { return RES ? NST : a.K / KS; }
+  static SPEC_DEVINL int total_stages(const StreamArgs& a) {
+    const int nunits = a.nunits;
+    const int myunits = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    return myunits * stages_per_unit(a);
+  }
+
+  // Weights of stage j of this workgroup (unit blockIdx.x + (j / nst) * grid, k-range j % nst)
+  // into ring slot j % S: four 1 KB segments per wavefront (segment s = wave + 8 i: row s % 16,
+  // and the half (one tile) or the tile (two tiles) s / 16).  The uniform part of each address
+  // is in the resource base; a stage past the end gets a resource of size 0, so its loads
+  // touch no memory.
+  static SPEC_DEVINL void issue_w(const StreamArgs& a, char* sm, int j, int total) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nst = stages_per_unit(a), K = RES ? NST * KS : a.K;
+    const bool ok = j < total;
+    const int u = (int)blockIdx.x + (j / nst) * (int)gridDim.x, ks = j % nst;
+    char* buf = sm + (j % S) * STAGE;
+    int mat, r0;
+    const char* base0 = unit_rows<EPI>(a, ok ? u : 0, 0, &mat, &r0);
+    const char* base1 = TILES == 2 ? unit_rows<EPI>(a, ok ? u : 0, 1, &mat, &r0) : base0;
+    const int64_t kofs = TILES == 1 ? ks * 2048 : ks * 1024;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = wave + SNW * i;
+      const char* base = (TILES == 2 && (s >> 4)) ? base1 : base0;
+      const int64_t org = (int64_t)(s & 15) * K * 2 + kofs + (TILES == 1 ? (s >> 4) * 1024 : 0);
+      const __amdgpu_buffer_rsrc_t r = rsrc(base + (ok ? org : 0), ok ? 0x7fffffffu : 0u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + s * SEGP), 16, (uint32_t)lane * 16u, 0, 0, 0);
+    }
+  }
+  // The wavefront's bf16 input slices of stage j (streamed inputs).
+  static SPEC_DEVINL void issue_x(const StreamArgs& a, int j, uint4 (&xb)[WSTEPS]) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = a.K, ks = j % stages_per_unit(a), m = lane & 15;
+    const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(a.M * K * 2));  // rows >= M: out of range
+    const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
+#pragma unroll
+    for (int i = 0; i < WSTEPS; ++i) {
+      const int st = wave + SNW * i;
+      xb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + st * 32) * 2, XP));
+    }
+  }
+
+  // The first P <= S - 1 weight stages, issued ahead (before the barrier that precedes the
+  // projection, with resident inputs only: their loads must follow the barrier).
+  static SPEC_DEVINL void prefetch(const StreamArgs& a, char* sm, int P) {
+    const int total = total_stages(a);
+    for (int j = 0; j < P; ++j) issue_w(a, sm, j, total);
+  }
+
+  // The projection; P weight stages were prefetched.
+  static SPEC_DEVINL void run(const StreamArgs& a, char* sm, int P) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = RES ? NST * KS : a.K, M = a.M, nst = stages_per_unit(a);
+    const int total = total_stages(a);
+    const int m = lane & 15;
+    const uint32_t sm0 = lds_addr(sm);
+    const uint32_t red0 = sm0 + S * STAGE;
+    const uint32_t inv0 = red0 + RED_BYTES;
+
+    // Resident input slices: slice (ks, i) holds k = ks * KS + (wave + 8 i) * 32 + 8 (lane /
+    // 16) .. + 7 of token row m (zero for m >= M).  Their loads (and the sum-of-squares
+    // partials of the rows) are issued before the remaining first weight stages; the slices
+    // are finished after.
+    constexpr int SSP = 8;   // partials per lane: np <= 512
+    constexpr int YC = 8;    // slices normalized per batch (bounds the float32 values in flight)
+    uint4 xres[XS];
+    float pss[2][SSP];
+    const bool norm = RES && a.xres != nullptr;
+    const __amdgpu_buffer_rsrc_t yr = rsrc(a.xres, (uint32_t)(M * K * 4));
+    // float32 values of slices q0 .. q0 + YC - 1 (zero past the row count)
+    auto load_y = [&](int q0, float4 (&yv)[YC][2]) {
+#pragma unroll
+      for (int qq = 0; qq < YC; ++qq) {
+        const int q = q0 + qq;
+        if (q >= XS) break;
+        const int ks = q / WSTEPS, i = q % WSTEPS;
+        const int k = ks * KS + (wave + SNW * i) * 32 + 8 * (lane >> 4);
+        const uint32_t off = m < M ? (uint32_t)(m * K + k) * 4u : 0x80000000u;
+        yv[qq][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, XP));
+        yv[qq][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(yr, off + 16u, 0, XP));
+      }
+    };
+    auto pack_y = [&](int q0, const float4 (&yv)[YC][2], float inv) {
+#pragma unroll
+      for (int qq = 0; qq < YC; ++qq) {
+        const int q = q0 + qq;
+        if (q >= XS) break;
+        const float4 y0 = yv[qq][0], y1 = yv[qq][1];
+        xres[q] = make_uint4(pack_bf16(y0.x * inv, y0.y * inv), pack_bf16(y0.z * inv, y0.w * inv),
+                             pack_bf16(y1.x * inv, y1.y * inv), pack_bf16(y1.z * inv, y1.w * inv));
+      }
+    };
+    float4 y0v[YC][2];
+    if (RES) {
+      if (norm) {
+        const __amdgpu_buffer_rsrc_t sr = rsrc(a.ss_in, (uint32_t)(M * a.ss_ld * 4));
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          const int r = wave + SNW * rr;
+#pragma unroll
+          for (int t = 0; t < SSP; ++t) {
+            const int p = lane + 64 * t;
+            const uint32_t off = (r < M && p < a.np_in) ? (uint32_t)(r * a.ss_ld + p) * 4u : 0x80000000u;
+            pss[rr][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, XP));
+          }
+        }
+        load_y(0, y0v);
+      } else {
+        const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
+        const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
+#pragma unroll
+        for (int q = 0; q < XS; ++q) {
+          const int ks = q / WSTEPS, i = q % WSTEPS;
+          xres[q] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + (wave + SNW * i) * 32) * 2, XP));
+        }
+      }
+    }
+
+    uint4 xa[RES ? 1 : S][WSTEPS];
+    for (int j = P; j < S - 1; ++j) {
+      issue_w(a, sm, j, total);
+      if (!RES) issue_x(a, j, xa[RES ? 0 : j]);
+    }
+
+    if (norm) {
+      // 1/rms of each row: wavefront w handles rows w and w + 8; lane j adds partials j,
+      // j + 64, ... in order, then a fixed xor butterfly
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = wave + SNW * rr;
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < SSP; ++t) acc += pss[rr][t];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(acc / (float)K + a.eps));
+      }
+      wg_barrier();
+      const float inv = m < M ? lds_read_f32(inv0 + m * 4) : 0.0f;
+      pack_y(0, y0v, inv);
+#pragma unroll
+      for (int q0 = YC; q0 < XS; q0 += YC) {
+        float4 yv[YC][2];
+        load_y(q0, yv);
+        pack_y(q0, yv, inv);
+      }
+    }
+
+    f32x4_t acc[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // Unit end: the 8 partial tiles meet in LDS.  Thread e < 256 takes token mm = e / 16 and
+    // column c = e % 16 of the unit; in the D layout of the 16x16 MFMA that element is held
+    // by lane (c / 4) * 16 + mm, entry c % 4.  The 16 columns of a token are 16 adjacent
+    // lanes, so the residual epilogue adds their squares with a fixed butterfly.
+    auto finish_unit = [&](int u) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        lds_write_acc(red0 + ((wave * TILES + t) * 64 + lane) * 16, acc[t]);
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      wg_barrier();
+      if (threadIdx.x < 256) {
+        const int e = threadIdx.x, mm = e >> 4, c = e & 15, ll = (c >> 2) * 16 + mm, r = c & 3;
+        float v[TILES];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          uint4 p[SNW];
+          uint32_t ad[SNW];
+#pragma unroll
+          for (int w = 0; w < SNW; ++w) ad[w] = red0 + ((w * TILES + t) * 64 + ll) * 16;
+          lds_read4(ad[0], ad[1], ad[2], ad[3], p[0], p[1], p[2], p[3]);
+          lds_read4(ad[4], ad[5], ad[6], ad[7], p[4], p[5], p[6], p[7]);
+          float sacc = 0.0f;
+#pragma unroll
+          for (int w = 0; w < SNW; ++w)
+            sacc += __uint_as_float(r == 0 ? p[w].x : (r == 1 ? p[w].y : (r == 2 ? p[w].z : p[w].w)));
+          v[t] = sacc;
+        }
+        int mat, r0;
+        (void)unit_rows<EPI>(a, u, 0, &mat, &r0);
+        const int n = r0 + c;
+        const bool live = mm < M;
+        if (EPI == EPI_RESID) {
+          float xn = 0.0f;
+          if (live) {
+            float* xp = a.out + (int64_t)mm * a.ld + n;
+            xn = ld<COH>(xp) + v[0];
+            st<COH>(xp, xn);
+            if (a.y_out) st<COH>(a.y_out + (int64_t)mm * a.ld + n, xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
+          }
+          float sq = xn * xn;
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+          if (live && c == 0 && a.ss_out) st<COH>(a.ss_out + (int64_t)mm * a.ss_ld + u, sq);
+        } else if (live) {
+          if (EPI == EPI_STORE) {
+            a.out[(int64_t)mm * a.ld + n] = v[0];
+          } else if (EPI == EPI_QKV_ROWS) {
+            st<COH>(a.out + (int64_t)mm * a.ld + u * 16 + c, v[0]);
+          } else if (EPI == EPI_SWIGLU) {
+            st<COH>((bf16_t*)a.h + (int64_t)mm * a.rows0 + n, f32_to_bf16(silu_s(v[0]) * v[TILES - 1]));
+          } else {  // EPI_QKV
+            if (mat == 0) {
+              st<COH>(a.q_stage + (int64_t)mm * a.rows0 + n, v[0]);
+            } else if (mat == 1) {
+              st<COH>(a.k_stage + (int64_t)mm * a.rows1 + n, v[0]);
+            } else {
+              const CacheView& cv = a.cache;
+              const int b = mm / a.rm.mseq;
+              const int pos = a.rm.len[b] + a.rm.pos_off + mm % a.rm.mseq;
+              const int kvh = n / cv.hd, dd = n % cv.hd;
+              const int64_t idx =
+                  ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap + pos) * cv.hd + dd;
+              st<COH>((bf16_t*)cv.v + idx, f32_to_bf16(v[0]));
+            }
+          }
+        }
+      }
+      // the partial tiles are written again only after the next stage's barrier
+    };
+
+    auto compute = [&](int j, int ks, const uint4 (&xb)[WSTEPS]) {
+      const uint32_t buf = sm0 + (j % S) * STAGE;
+      uint32_t ad[4];
+#pragma unroll
+      for (int i = 0; i < WSTEPS; ++i) {
+        const int st = wave + SNW * i;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const int seg = TILES == 1 ? (st >> 4) * 16 + m : t * 16 + m;
+          const int so = TILES == 1 ? (st & 15) : st;
+          ad[i * TILES + t] = buf + seg * SEGP + so * 64 + (lane >> 4) * 16;
+        }
+      }
+      uint4 wv[4];
+      lds_read4(ad[0], ad[1], ad[2], ad[3], wv[0], wv[1], wv[2], wv[3]);
+#pragma unroll
+      for (int i = 0; i < WSTEPS; ++i) {
+        const uint4 b = RES ? xres[(RES ? ks : 0) * WSTEPS + i] : xb[i];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[i * TILES + t]),
+                                                           __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+      }
+      if (ks == nst - 1) finish_unit((int)blockIdx.x + (j / nst) * (int)gridDim.x);
+    };
+
+    // stage j is complete for this wavefront once at most the S - 2 later stages are in
+    // flight; after the barrier it is complete for all, and every wavefront is done with
+    // slot (j - 1) % S, which the next issue refills
+    if (RES) {
+      // the stage loop unrolled over the unit's NST stages, so slices are indexed statically
+      for (int j0 = 0; j0 < total; j0 += NST) {
+#pragma unroll
+        for (int ks = 0; ks < (RES ? NST : 1); ++ks) {
+          const int j = j0 + ks;
+          wait_vm<C * (S - 2)>();
+          wg_barrier();
+          issue_w(a, sm, j + S - 1, total);
+          compute(j, ks, xa[0]);
+        }
+      }
+    } else {
+      for (int j0 = 0; j0 < total; j0 += S) {
+#pragma unroll
+        for (int q = 0; q < S; ++q) {
+          const int j = j0 + q;
+          if (j >= total) continue;
+          wait_vm<C * (S - 2)>();
+          wg_barrier();
+          issue_w(a, sm, j + S - 1, total);
+          issue_x(a, j + S - 1, xa[RES ? 0 : (q + S - 1) % S]);
+          compute(j, j % nst, xa[RES ? 0 : q]);
+        }
+      }
+    }
+    // the stages past the end are zero-size loads: nothing of this projection is in flight
+    // once they have returned
+  }
+};
+
+}  // namespace sk
+}  // namespace spec

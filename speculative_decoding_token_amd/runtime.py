@@ -222,7 +222,7 @@ class Engine:
         return B.spec_profile_read(self.ctx)
 
     def set_schedule(self, schedule: str):
-        """'step' (the default) or 'stream' (see spec_set_schedule)."""
+        """'step' (the default), 'stream' or 'forward' (see spec_set_schedule)."""
         B.spec_set_schedule(self.ctx, schedule)
 
     def use_graphs(self, enable: bool):

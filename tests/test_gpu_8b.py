@@ -21,7 +21,7 @@ def host_weights(w):
     return out
 
 
-@pytest.mark.parametrize("schedule", ["step", "stream"])
+@pytest.mark.parametrize("schedule", ["step", "stream", "forward"])
 @pytest.mark.parametrize("name,L,K,temp", [("qwen8b", 2048, 4, 0.0), ("qwen8b", 2048, 8, 1.0),
                                            ("qwen0p6b", 2047, 16, 1.0), ("qwen0p6b", 2047, 1, 0.0),
                                            ("qwen27b", 4096, 4, 0.0)])
@@ -53,6 +53,7 @@ def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
     kv = om.KVCache(spec, L + K + 2)
     kv.load_prefix(k.float().cpu().numpy(), v.float().cpu().numpy())
     ref = om.forward_tokens(spec, W, kv, [t0] + drafts)
+    assert eng.stats()["sync_timeouts"] == 0
     err = assert_rows_close(logits, ref, RTOL_BF16)
     print(f"{name} L={L} K={K} {schedule}: worst row error {err:.2e}")
     abs_err = np.abs(logits.astype(np.float64) - ref).max(axis=1)

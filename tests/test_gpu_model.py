@@ -223,12 +223,12 @@ def test_fused_and_standalone_norm_paths_bit_identical():
     assert_rows_close(logits[16].cpu().numpy(), ref, RTOL_BF16)
 
 
-@pytest.mark.parametrize("schedule", ["stream"])
+@pytest.mark.parametrize("schedule", ["stream", "forward"])
 def test_schedule_row_invariant_and_close_to_per_step(schedule):
-    """The streamed-projection schedule: rows 0..4 of verifies at K = 4, 8, 15 (5 to 16 rows)
-    are bit identical to each other and row 0 to the K = 0 forward (row-count invariance);
-    they agree with the per-row-tile schedule and with the oracle within the bf16
-    tolerance."""
+    """The streamed-projection and one-launch schedules: rows 0..4 of verifies at K = 4, 8, 15
+    (5 to 16 rows) are bit identical to each other and row 0 to the K = 0 forward (row-count
+    invariance); they agree with the per-row-tile schedule and with the oracle within the
+    bf16 tolerance; no grid barrier timed out."""
     shape = synth.ModelShape("wide", 2, 4096, 32, 8, 128, 1024, 1024, "bf16")
     w = synth.weights_to(synth.make_weights(shape, 4, std=0.02), "cuda")
     L = 130
@@ -242,7 +242,9 @@ def test_schedule_row_invariant_and_close_to_per_step(schedule):
         eng.load_prefix(0, 0, k.cuda(), v.cuda(), L)
         eng.set_last(torch.tensor([t0], dtype=torch.int32).cuda())
         d = torch.tensor([drafts[:K]], dtype=torch.int32).cuda() if K else None
-        return eng.cycle(1, K, 0, drafts=d, keep=True).logits[0]
+        out = eng.cycle(1, K, 0, drafts=d, keep=True).logits[0]
+        assert eng.stats()["sync_timeouts"] == 0
+        return out
 
     pers = {K: run(K, schedule) for K in (0, 4, 8, 15)}
     for K in (4, 8, 15):
