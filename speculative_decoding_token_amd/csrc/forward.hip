@@ -128,216 +128,250 @@ SPEC_DEVINL void embed_step(const FwdArgs& a, char* sm) {
 // keys and values (positions L .. L + mseq - 1) come from the QKV step's rows (read past the
 // L2): keys rotated, both rounded, used, and written to the cache by the group whose chunk
 // holds them.
-// Both groups of a workgroup pass the same barriers (inactive items included).
 template <int HD>
-SPEC_DEVINL void attn_item(const FwdArgs& a, int layer, char* gsm, int b, int kvh, int chunk, bool active) {
-  constexpr int C = ATTN_CHUNK;
-  constexpr int KP = HD + 8;
-  constexpr int VP = C + 8;
-  constexpr int HALF = HD / 2;
-  const int t = threadIdx.x & 255, lane = t & 63, wave = t >> 6;
-  const CacheView& cv = a.cache;
-  const int mseq = a.mseq, G = a.n_q / cv.n_kv;
-  const int L = a.len[b] + a.pos_off;
-  const int total = L + mseq;
-  const int c0 = chunk * C;
-  if (c0 >= total) active = false;
-  const int R = mseq * G, QT = (R + 15) / 16;
-  const int q_dim = a.n_q * HD, kv_dim = cv.n_kv * HD, qkv_ld = q_dim + 2 * kv_dim;
-  bf16_t* qs = (bf16_t*)gsm;       // [QT*16][KP]
-  bf16_t* ks = qs + QT * 16 * KP;  // [C][KP]
-  bf16_t* vt = ks + C * KP;        // [HD][VP]
-  const int64_t cbase = ((((int64_t)b * cv.n_layers + layer) * cv.n_kv + kvh) * cv.cap) * HD;
-  bf16_t* kc = (bf16_t*)cv.k + cbase;
-  bf16_t* vc = (bf16_t*)cv.v + cbase;
-  constexpr int NV = C * (HD / 8) / 256;
-  uint4 kreg[NV], vreg[NV];
-  if (active) {
-    const __amdgpu_buffer_rsrc_t vr = rsrc(vc, (uint32_t)((int64_t)cv.cap * HD * 2));
-    const __amdgpu_buffer_rsrc_t kr = rsrc(kc, (uint32_t)((int64_t)cv.cap * HD * 2));
+struct Attn {
+  static constexpr int C = ATTN_CHUNK;
+  static constexpr int KP = HD + 8;
+  static constexpr int VP = C + 8;
+  static constexpr int HALF = HD / 2;
+  static constexpr int NV = C * (HD / 8) / 256;  // 16-byte cache loads per thread and tensor
+
+  struct Item {
+    int b, kvh, chunk;
+    bool ok;
+  };
+  static SPEC_DEVINL Item item_of(const FwdArgs& a, int base) {
+    const int nkv = a.cache.n_kv;
+    const int items = (a.M / a.mseq) * nkv * a.nchunk;
+    const int gi = threadIdx.x >> 8;
+    const int it = base + blockIdx.x * ATT_GROUPS + gi;
+    Item r;
+    r.ok = it < items;
+    const int i = r.ok ? it : 0;
+    r.chunk = i % a.nchunk;
+    r.kvh = (i / a.nchunk) % nkv;
+    r.b = i / (a.nchunk * nkv);
+    if (r.chunk * C >= a.len[r.b] + a.pos_off + a.mseq) r.ok = false;  // past the last position
+    return r;
+  }
+  static SPEC_DEVINL int64_t cache_base(const FwdArgs& a, int layer, const Item& it) {
+    const CacheView& cv = a.cache;
+    return ((((int64_t)it.b * cv.n_layers + layer) * cv.n_kv + it.kvh) * cv.cap) * HD;
+  }
+  // cached keys and values of the item's chunk (positions past the cache clamp to its end;
+  // positions >= L are replaced after the load); nothing is read for an inactive item
+  static SPEC_DEVINL void load_kv(const FwdArgs& a, int layer, const Item& it, uint4 (&kreg)[NV], uint4 (&vreg)[NV]) {
+    const int t = threadIdx.x & 255;
+    const CacheView& cv = a.cache;
+    const int64_t cb = cache_base(a, layer, it);
+    const uint32_t bytes = it.ok ? (uint32_t)((int64_t)cv.cap * HD * 2) : 0u;
+    const __amdgpu_buffer_rsrc_t kr = rsrc((const bf16_t*)cv.k + cb, bytes);
+    const __amdgpu_buffer_rsrc_t vr = rsrc((const bf16_t*)cv.v + cb, bytes);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int idx = t + 256 * v;
-      const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
+      const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = it.chunk * C + j;
       const uint32_t off = (uint32_t)(min(p, cv.cap - 1) * HD + d8) * 2u;
       kreg[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
       vreg[v] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
     }
-    // query rows in batches of 8 loads per thread (one batch covers two query tiles)
-    constexpr int NQB = 8;
-    const int nq = (QT * 16 * HALF + 255) / 256;
-    for (int v0 = 0; v0 < nq; v0 += NQB) {
-      float qx0[NQB], qx1[NQB];
-      float2 qcs[NQB];
-#pragma unroll
-      for (int v = 0; v < NQB; ++v) {
-        const int idx = t + 256 * (v0 + v), d = idx % HALF;
-        const int r = min(idx / HALF, R - 1);
-        const int i = r / G, h = kvh * G + r % G;
-        const float* src = a.qkv + (int64_t)(b * mseq + i) * qkv_ld + h * HD;
-        qx0[v] = ld<true>(src + d);
-        qx1[v] = ld<true>(src + d + HALF);
-        qcs[v] = a.rope[(int64_t)(L + i) * HALF + d];
-      }
-#pragma unroll
-      for (int v = 0; v < NQB; ++v) {
-        const int idx = t + 256 * (v0 + v), r = idx / HALF, d = idx % HALF;
-        if (r < QT * 16) {
-          qs[r * KP + d] = r < R ? f32_to_bf16(qx0[v] * qcs[v].x - qx1[v] * qcs[v].y) : (bf16_t)0;
-          qs[r * KP + d + HALF] = r < R ? f32_to_bf16(qx1[v] * qcs[v].x + qx0[v] * qcs[v].y) : (bf16_t)0;
-        }
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int idx = t + 256 * v;
-      const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-      if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
-      else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
-      uint4 vv;
-      if (p < L) {
-        vv = vreg[v];
-      } else if (p < total) {
-        // a value of this pass: rounded here and cached
-        const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kv_dim + kvh * HD + d8;
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = ld<true>(src + e);
-        vv = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
-        *(uint4*)(vc + (int64_t)p * HD + d8) = vv;
-      } else {
-        vv = make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-      const int js = j ^ (((d8 >> 3) & 7) << 3);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(d8 + 2 * e) * VP + js] = (bf16_t)(w[e] & 0xFFFFu);
-        vt[(d8 + 2 * e + 1) * VP + js] = (bf16_t)(w[e] >> 16);
-      }
-    }
-    const int p0 = max(c0, L), p1 = min(c0 + C, total);
-    for (int idx = t; idx < (p1 - p0) * HALF; idx += 256) {
-      const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
-      const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kvh * HD;
-      const float x0 = ld<true>(src + d), x1 = ld<true>(src + d + HALF);
-      const float2 cs = a.rope[(int64_t)p * HALF + d];
-      const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
-      const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
-      ks[j * KP + d] = lo;
-      ks[j * KP + d + HALF] = hi;
-      kc[(int64_t)p * HD + d] = lo;
-      kc[(int64_t)p * HD + d + HALF] = hi;
-    }
   }
-  __syncthreads();
-  if (active) {
-    const int n = lane & 15, g = lane >> 4;
-    constexpr int DT = HD / 16;
-    const int wpt = min(QT == 1 ? 4 : (QT == 2 ? 2 : 1), DT);
-    const int part = wave % wpt;
-    const int dts = DT / wpt;
-    for (int qt = wave / wpt; qt < QT; qt += 4 / wpt) {
-      f32x4_t s[4];
+
+  static SPEC_DEVINL void item(const FwdArgs& a, int layer, char* gsm, const Item& it, const uint4 (&kreg)[NV],
+                               const uint4 (&vreg)[NV]) {
+    const int t = threadIdx.x & 255, lane = t & 63, wave = t >> 6;
+    const CacheView& cv = a.cache;
+    const int b = it.b, kvh = it.kvh, chunk = it.chunk;
+    const bool active = it.ok;
+    const int mseq = a.mseq, G = a.n_q / cv.n_kv;
+    const int L = a.len[b] + a.pos_off;
+    const int total = L + mseq;
+    const int c0 = chunk * C;
+    const int R = mseq * G, QT = (R + 15) / 16;
+    const int q_dim = a.n_q * HD, kv_dim = cv.n_kv * HD, qkv_ld = q_dim + 2 * kv_dim;
+    bf16_t* qs = (bf16_t*)gsm;       // [QT*16][KP]
+    bf16_t* ks = qs + QT * 16 * KP;  // [C][KP]
+    bf16_t* vt = ks + C * KP;        // [HD][VP]
+    const int64_t cb = cache_base(a, layer, it);
+    bf16_t* kc = (bf16_t*)cv.k + cb;
+    bf16_t* vc = (bf16_t*)cv.v + cb;
+    if (active) {
+      // query rows in batches of 8 loads per thread (one batch covers two query tiles)
+      constexpr int NQB = 8;
+      const int nq = (QT * 16 * HALF + 255) / 256;
+      for (int v0 = 0; v0 < nq; v0 += NQB) {
+        float qx0[NQB], qx1[NQB];
+        float2 qcs[NQB];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int v = 0; v < NQB; ++v) {
+          const int idx = t + 256 * (v0 + v), d = idx % HALF;
+          const int r = min(idx / HALF, R - 1);
+          const int i = r / G, h = kvh * G + r % G;
+          const float* src = a.qkv + (int64_t)(b * mseq + i) * qkv_ld + h * HD;
+          qx0[v] = ld<true>(src + d);
+          qx1[v] = ld<true>(src + d + HALF);
+          qcs[v] = a.rope[(int64_t)(L + i) * HALF + d];
+        }
 #pragma unroll
-        for (int stp = 0; stp < HD / 32; ++stp) {
-          const uint4 av = *(const uint4*)(ks + (kt * 16 + n) * KP + stp * 32 + 8 * g);
-          const uint4 bv = *(const uint4*)(qs + (qt * 16 + n) * KP + stp * 32 + 8 * g);
-          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                          __builtin_bit_cast(bf16x8_t, bv), s[kt], 0, 0, 0);
+        for (int v = 0; v < NQB; ++v) {
+          const int idx = t + 256 * (v0 + v), r = idx / HALF, d = idx % HALF;
+          if (r < QT * 16) {
+            qs[r * KP + d] = r < R ? f32_to_bf16(qx0[v] * qcs[v].x - qx1[v] * qcs[v].y) : (bf16_t)0;
+            qs[r * KP + d + HALF] = r < R ? f32_to_bf16(qx1[v] * qcs[v].x + qx0[v] * qcs[v].y) : (bf16_t)0;
+          }
         }
       }
-      const int r = qt * 16 + n;
-      const int pos = (r < R) ? L + r / G : -1;
-      float mx = -__builtin_inff();
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int v = 0; v < NV; ++v) {
+        const int idx = t + 256 * v;
+        const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
+        if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
+        else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
+        uint4 vv;
+        if (p < L) {
+          vv = vreg[v];
+        } else if (p < total) {
+          // a value of this pass: rounded here and cached
+          const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kv_dim + kvh * HD + d8;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = ld<true>(src + e);
+          vv = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
+          *(uint4*)(vc + (int64_t)p * HD + d8) = vv;
+        } else {
+          vv = make_uint4(0, 0, 0, 0);
+        }
+        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+        const int js = j ^ (((d8 >> 3) & 7) << 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vt[(d8 + 2 * e) * VP + js] = (bf16_t)(w[e] & 0xFFFFu);
+          vt[(d8 + 2 * e + 1) * VP + js] = (bf16_t)(w[e] >> 16);
+        }
+      }
+      const int p0 = max(c0, L), p1 = min(c0 + C, total);
+      for (int idx = t; idx < (p1 - p0) * HALF; idx += 256) {
+        const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
+        const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kvh * HD;
+        const float x0 = ld<true>(src + d), x1 = ld<true>(src + d + HALF);
+        const float2 cs = a.rope[(int64_t)p * HALF + d];
+        const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
+        const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
+        ks[j * KP + d] = lo;
+        ks[j * KP + d + HALF] = hi;
+        kc[(int64_t)p * HD + d] = lo;
+        kc[(int64_t)p * HD + d + HALF] = hi;
+      }
+    }
+    __syncthreads();
+    if (active) {
+      const int n = lane & 15, g = lane >> 4;
+      constexpr int DT = HD / 16;
+      const int wpt = min(QT == 1 ? 4 : (QT == 2 ? 2 : 1), DT);
+      const int part = wave % wpt;
+      const int dts = DT / wpt;
+      for (int qt = wave / wpt; qt < QT; qt += 4 / wpt) {
+        f32x4_t s[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int stp = 0; stp < HD / 32; ++stp) {
+            const uint4 av = *(const uint4*)(ks + (kt * 16 + n) * KP + stp * 32 + 8 * g);
+            const uint4 bv = *(const uint4*)(qs + (qt * 16 + n) * KP + stp * 32 + 8 * g);
+            s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                            __builtin_bit_cast(bf16x8_t, bv), s[kt], 0, 0, 0);
+          }
+        }
+        const int r = qt * 16 + n;
+        const int pos = (r < R) ? L + r / G : -1;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int p = c0 + kt * 16 + 4 * g + rr;
+            const float v = (p <= pos) ? s[kt][rr] * a.scale : -__builtin_inff();
+            s[kt][rr] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        uint32_t pk[4][2];
+        float l = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          float e[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float v = s[kt][rr];
+            const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : __expf(v - mx);
+            e[rr] = bf16_to_f32(f32_to_bf16(x));
+            l += e[rr];
+          }
+          pk[kt][0] = (uint32_t)f32_to_bf16(e[0]) | ((uint32_t)f32_to_bf16(e[1]) << 16);
+          pk[kt][1] = (uint32_t)f32_to_bf16(e[2]) | ((uint32_t)f32_to_bf16(e[3]) << 16);
+        }
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        bf16x8_t pa[2];
+#pragma unroll
+        for (int stp = 0; stp < 2; ++stp)
+          pa[stp] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * stp][0], pk[2 * stp][1], pk[2 * stp + 1][0],
+                                                            pk[2 * stp + 1][1]));
+        int rowoff[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int p = c0 + kt * 16 + 4 * g + rr;
-          const float v = (p <= pos) ? s[kt][rr] * a.scale : -__builtin_inff();
-          s[kt][rr] = v;
-          mx = fmaxf(mx, v);
+          const int r2 = qt * 16 + 4 * g + rr;
+          rowoff[rr] = -1;
+          if (r2 < R) {
+            const int i2 = r2 / G, h2 = kvh * G + r2 % G;
+            rowoff[rr] = (((b * mseq + i2) * a.n_q + h2) * a.nchunk + chunk) * (HD + 2);
+          }
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      uint32_t pk[4][2];
-      float l = 0.0f;
+        for (int dt = part * dts; dt < (part + 1) * dts; ++dt) {
+          f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const int dim = dt * 16 + n;
+          const int swz = ((dim >> 3) & 7) << 3;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float e[4];
+          for (int stp = 0; stp < 2; ++stp) {
+            const bf16_t* vrow = vt + dim * VP;
+            const uint2 x0 = *(const uint2*)(vrow + ((stp * 32 + 4 * g) ^ swz));
+            const uint2 x1 = *(const uint2*)(vrow + ((stp * 32 + 16 + 4 * g) ^ swz));
+            o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[stp],
+                                                        __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y)),
+                                                        o, 0, 0, 0);
+          }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float v = s[kt][rr];
-          const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : __expf(v - mx);
-          e[rr] = bf16_to_f32(f32_to_bf16(x));
-          l += e[rr];
+          for (int rr = 0; rr < 4; ++rr)
+            if (rowoff[rr] >= 0) st<true>(a.part + rowoff[rr] + dim, o[rr]);
         }
-        pk[kt][0] = (uint32_t)f32_to_bf16(e[0]) | ((uint32_t)f32_to_bf16(e[1]) << 16);
-        pk[kt][1] = (uint32_t)f32_to_bf16(e[2]) | ((uint32_t)f32_to_bf16(e[3]) << 16);
-      }
-      l += __shfl_xor(l, 16, 64);
-      l += __shfl_xor(l, 32, 64);
-      bf16x8_t pa[2];
-#pragma unroll
-      for (int stp = 0; stp < 2; ++stp)
-        pa[stp] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * stp][0], pk[2 * stp][1], pk[2 * stp + 1][0],
-                                                          pk[2 * stp + 1][1]));
-      int rowoff[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r2 = qt * 16 + 4 * g + rr;
-        rowoff[rr] = -1;
-        if (r2 < R) {
-          const int i2 = r2 / G, h2 = kvh * G + r2 % G;
-          rowoff[rr] = (((b * mseq + i2) * a.n_q + h2) * a.nchunk + chunk) * (HD + 2);
+        if (part == 0 && g == 0 && r < R) {
+          const int i = r / G, h = kvh * G + r % G;
+          float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
+          st<true>(P + HD, mx);
+          st<true>(P + HD + 1, l);
         }
-      }
-      for (int dt = part * dts; dt < (part + 1) * dts; ++dt) {
-        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int dim = dt * 16 + n;
-        const int swz = ((dim >> 3) & 7) << 3;
-#pragma unroll
-        for (int stp = 0; stp < 2; ++stp) {
-          const bf16_t* vrow = vt + dim * VP;
-          const uint2 x0 = *(const uint2*)(vrow + ((stp * 32 + 4 * g) ^ swz));
-          const uint2 x1 = *(const uint2*)(vrow + ((stp * 32 + 16 + 4 * g) ^ swz));
-          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[stp],
-                                                      __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y)),
-                                                      o, 0, 0, 0);
-        }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (rowoff[rr] >= 0) st<true>(a.part + rowoff[rr] + dim, o[rr]);
-      }
-      if (part == 0 && g == 0 && r < R) {
-        const int i = r / G, h = kvh * G + r % G;
-        float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
-        st<true>(P + HD, mx);
-        st<true>(P + HD + 1, l);
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-}
+};
 
 template <int HD>
-SPEC_DEVINL void attn_step(const FwdArgs& a, int layer, char* sm) {
-  const int nseq = a.M / a.mseq, nkv = a.cache.n_kv;
-  const int items = nseq * nkv * a.nchunk;
+SPEC_DEVINL void attn_step(const FwdArgs& a, int layer, char* sm, uint4 (&kreg)[Attn<HD>::NV],
+                           uint4 (&vreg)[Attn<HD>::NV]) {
+  using A = Attn<HD>;
+  const int nkv = a.cache.n_kv;
+  const int items = (a.M / a.mseq) * nkv * a.nchunk;
   const int G = a.n_q / nkv, QT = (a.mseq * G + 15) / 16;
-  const int gi = threadIdx.x >> 8;  // attention group of this thread
+  const int gi = threadIdx.x >> 8;
   char* gsm = sm + gi * attn_group_bytes(QT, HD);
   const int slots = gridDim.x * ATT_GROUPS;
   for (int base = 0; base < items; base += slots) {
-    const int item = base + blockIdx.x * ATT_GROUPS + gi;
-    const bool ok = gi < ATT_GROUPS && item < items;
-    const int it = ok ? item : 0;
-    const int chunk = it % a.nchunk, kvh = (it / a.nchunk) % nkv, b = it / (a.nchunk * nkv);
-    attn_item<HD>(a, layer, gsm, b, kvh, chunk, ok);
+    const typename A::Item it = A::item_of(a, base);
+    A::load_kv(a, layer, it, kreg, vreg);
+    A::item(a, layer, gsm, it, kreg, vreg);
   }
 }
 
@@ -505,6 +539,7 @@ __global__ __launch_bounds__(SNW * 64) void forward_kernel(FwdArgs a) {
   constexpr int P = RING - 1;  // weight stages issued ahead of a barrier
   Sync s{a.sync, 0u, a.trace, a.trace_cap};
   if (a.trace && threadIdx.x == 0 && a.trace_cap > 0) a.trace[(size_t)blockIdx.x * 2] = wall_clock64();
+  uint4 kreg[Attn<HD>::NV], vreg[Attn<HD>::NV];
   char* red = sm + RING * STAGE;  // the combine step's LDS, clear of the ring
   embed_step(a, sm);
   grid_sync(s, [&] { QKV::prefetch(qkv_args(a, 0), sm, P); });
@@ -512,15 +547,15 @@ __global__ __launch_bounds__(SNW * 64) void forward_kernel(FwdArgs a) {
   for (int l = 0; l < a.n_layers; ++l) {
     QKV::run(qkv_args(a, l), sm, P);
     grid_sync(s, [] {});
-    attn_step<HD>(a, l, sm);
+    attn_step<HD>(a, l, sm, kreg, vreg);
     grid_sync(s, [&] { OP::prefetch(o_args(a, l), sm, P); });
     combine_step<HD>(a, red);
     grid_sync(s, [] {});
     OP::run(o_args(a, l), sm, P);
     grid_sync(s, [&] { GU::prefetch(gu_args(a, l), sm, P); });
     GU::run(gu_args(a, l), sm, P);
-    grid_sync(s, [] {});
-    DN::run(down_args(a, l), sm, 0);
+    grid_sync(s, [&] { DN::prefetch(down_args(a, l), sm, P); });
+    DN::run(down_args(a, l), sm, P);
     if (l + 1 < a.n_layers) grid_sync(s, [&] { QKV::prefetch(qkv_args(a, l + 1), sm, P); });
     else if (a.logits) grid_sync(s, [&] { HEAD::prefetch(head_args(a), sm, P); });
   }
@@ -562,7 +597,11 @@ bool forward_supported(int M, int mseq, int d, int n_q, int n_kv, int hd, int ff
   return true;
 }
 
-size_t forward_sync_bytes() { return 11 * SYNC_SP * 4; }
+size_t forward_sync_bytes(int batch, int n_kv) {
+  (void)batch;
+  (void)n_kv;
+  return 11 * SYNC_SP * 4;
+}
 
 hipError_t forward_init(int* grid) {
   int dev = 0, ncu = 0;

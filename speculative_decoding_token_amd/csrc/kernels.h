@@ -232,7 +232,7 @@ hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_
 // ---- one persistent launch per forward (bf16 models, M <= 16 rows) ------------------
 // The rows, positions and buffers of forward(); x, y, ss, q/k staging, attention partials and
 // outputs and the SwiGLU product are the model's workspace buffers.  layers is a device copy
-// of the layer table.  sync: forward_sync_bytes() of device memory, zero before the first
+// of the layer table.  sync: forward_sync_bytes(batch, n_kv) of device memory, zero before the first
 // launch (its last word is a sticky error flag: non-zero once a barrier has timed out).
 struct FwdArgs {
   const spec_layer_weights* layers;
@@ -266,7 +266,10 @@ struct FwdArgs {
   int trace_cap;
 };
 bool forward_supported(int M, int mseq, int d, int n_q, int n_kv, int hd, int ffn, int vocab);
-size_t forward_sync_bytes();
+// barrier words and attention tickets for up to `batch` sequences of n_kv kv heads; the error
+// word is the 32-bit word at byte forward_error_offset()
+size_t forward_sync_bytes(int batch, int n_kv);
+constexpr size_t forward_error_offset() { return 10 * 32 * 4; }
 // per device: LDS limits; *grid = workgroups of one launch (one per compute unit, a multiple
 // of 8), 0 when the launch cannot be co-resident
 hipError_t forward_init(int* grid);

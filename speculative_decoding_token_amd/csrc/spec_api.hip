@@ -286,7 +286,7 @@ size_t layout(spec_ctx* c, void* ws) {
   c->hist = cv.take<int32_t>((size_t)B * c->hist_ld * 4);
   c->ndraft = cv.take<int32_t>(B * 4);
   c->match = cv.take<int32_t>(B * 8);
-  c->fsync = cv.take<unsigned>(forward_sync_bytes());
+  c->fsync = cv.take<unsigned>(forward_sync_bytes(B, std::max(g.target.n_kv_heads, c->draft.present ? g.draft.n_kv_heads : 0)));
   c->target.mseq_max = max_rows_per_seq(c->target.d, g.max_k, B);
   carve_model(c->target, cv, B, c->cap);
   if (c->draft.present) {
@@ -1281,7 +1281,7 @@ int spec_get_stats(spec_ctx* c, spec_stats* out) {
   out->drafts_accepted = h[2];
   out->emitted = h[3];
   unsigned err = 0;
-  HIPCHK(c, hipMemcpyAsync(&err, (const char*)c->fsync + forward_sync_bytes() - 32 * 4, sizeof err,
+  HIPCHK(c, hipMemcpyAsync(&err, (const char*)c->fsync + forward_error_offset(), sizeof err,
                            hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   out->sync_timeouts = err;

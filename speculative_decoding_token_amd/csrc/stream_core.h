@@ -231,8 +231,9 @@ struct Gemm {
     }
   }
 
-  // The first P <= S - 1 weight stages, issued ahead (before the barrier that precedes the
-  // projection, with resident inputs only: their loads must follow the barrier).
+  // The first P weight stages, issued ahead (before the barrier that precedes the
+  // projection): any P <= S - 1 with resident inputs, P = S - 1 with streamed inputs (whose
+  // slices of those stages are loaded after the barrier).
   static SPEC_DEVINL void prefetch(const StreamArgs& a, char* sm, int P) {
     const int total = total_stages(a);
     for (int j = 0; j < P; ++j) issue_w(a, sm, j, total);
@@ -309,6 +310,10 @@ struct Gemm {
     }
 
     uint4 xa[RES ? 1 : S][WSTEPS];
+    if (!RES && P > 0) {
+#pragma unroll
+      for (int j = 0; j < S - 1; ++j) issue_x(a, j, xa[RES ? 0 : j]);
+    }
     for (int j = P; j < S - 1; ++j) {
       issue_w(a, sm, j, total);
       if (!RES) issue_x(a, j, xa[RES ? 0 : j]);
@@ -455,12 +460,18 @@ struct Gemm {
         }
       }
     } else {
+      // after a prefetch the first slices follow the first S - 1 weight stages in issue
+      // order, so the first two waits count what was issued after slice 0 and slice 1
+      static_assert(S == 4, "the waits after a prefetch assume a ring of four");
+      const bool pre = P > 0;
       for (int j0 = 0; j0 < total; j0 += S) {
 #pragma unroll
         for (int q = 0; q < S; ++q) {
           const int j = j0 + q;
           if (j >= total) continue;
-          wait_vm<C * (S - 2)>();
+          if (pre && j == 0) wait_vm<2 * WSTEPS>();
+          else if (pre && j == 1) wait_vm<WSTEPS + C>();
+          else wait_vm<C * (S - 2)>();
           wg_barrier();
           issue_w(a, sm, j + S - 1, total);
           issue_x(a, j + S - 1, xa[RES ? 0 : (q + S - 1) % S]);
