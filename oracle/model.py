@@ -20,10 +20,15 @@ x += Wd . (silu(Wg n2) * (Wu n2)) with n2 = RMSNorm(x); logits = Wlm . RMSNorm(x
 RMSNorm eps 1e-6, rotate-half RoPE with theta 1e6, no biases, q-head h reads kv-head
 floor(h * n_kv / n_q), scale 1/sqrt(head_dim).
 
-Arithmetic is float64.  For a bf16 model the precision contract rounds to bfloat16 the
-normed activations, q, k and v (k and v are stored that way), the attention output and the
-SwiGLU product, and keeps the residual stream in float32; logits are float32.  An f32 model
-rounds nothing but the final logits to float32.
+Arithmetic is float64.  An RMSNorm that feeds a projection is taken in its folded form,
+W . RMSNorm(x) = (W . (x * g)) / rms(x) with rms(x) = sqrt(mean(x^2) + eps): the same map,
+with the projection reading the gain-multiplied row and its output scaled by 1/rms(x) (see
+``normed``).  For a bf16 model the precision contract rounds to bfloat16 the gain-multiplied
+rows x * g that the projections read, q, k and v (k and v are stored that way), the attention
+output and the SwiGLU product, and keeps the residual stream in float32; logits are float32.
+An f32 model rounds nothing but the final logits to float32.  The multi-token-prediction
+head's two input norms are plain RMSNorms (their rows are concatenated before the projection,
+so no single row scale exists).
 """
 from __future__ import annotations
 
@@ -86,6 +91,16 @@ def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     return x / np.sqrt(np.mean(x * x) + eps) * np.asarray(g, dtype=np.float64)
 
 
+def normed(x: np.ndarray, g: np.ndarray, eps: float, bf):
+    """RMSNorm in the form a projection consumes: (bf(x * g), 1 / rms(x)).  The projection of
+    the normed row is (W @ n) * s, the same as W @ RMSNorm(x) up to the rounding bf of the
+    gain-multiplied row."""
+    x = np.asarray(x, dtype=np.float64)
+    n = bf(x * np.asarray(g, dtype=np.float64))
+    s = 1.0 / np.sqrt(np.mean(x * x) + eps)
+    return n, s
+
+
 def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
     """Rotate-half RoPE on [n_heads, head_dim]: pair i with i + head_dim/2, angle
     pos * theta^(-2i/head_dim)."""
@@ -126,10 +141,10 @@ def decoder_layer(spec: Spec, lw: Dict[str, np.ndarray], x: np.ndarray, pos: int
     bf = round_bf16 if spec.bf16 else (lambda a: a)
     rs = round_f32 if spec.bf16 else (lambda a: a)
     hd = spec.head_dim
-    n1 = bf(rmsnorm(x, lw["attn_norm"], spec.rms_eps))
-    q = (_w(lw["wq"]) @ n1).reshape(spec.n_q_heads, hd)
-    k = (_w(lw["wk"]) @ n1).reshape(spec.n_kv_heads, hd)
-    v = (_w(lw["wv"]) @ n1).reshape(spec.n_kv_heads, hd)
+    n1, s1 = normed(x, lw["attn_norm"], spec.rms_eps, bf)
+    q = ((_w(lw["wq"]) @ n1) * s1).reshape(spec.n_q_heads, hd)
+    k = ((_w(lw["wk"]) @ n1) * s1).reshape(spec.n_kv_heads, hd)
+    v = ((_w(lw["wv"]) @ n1) * s1).reshape(spec.n_kv_heads, hd)
     q = bf(rope(q, pos, spec.rope_theta))
     k = bf(rope(k, pos, spec.rope_theta))
     v = bf(v)
@@ -138,9 +153,9 @@ def decoder_layer(spec: Spec, lw: Dict[str, np.ndarray], x: np.ndarray, pos: int
     o = attend(q, kv.k[l][:, :pos + 1], kv.v[l][:, :pos + 1], spec.n_kv_heads)
     o = bf(o.reshape(-1))
     x = rs(x + _w(lw["wo"]) @ o)
-    n2 = bf(rmsnorm(x, lw["ffn_norm"], spec.rms_eps))
-    g = _w(lw["wg"]) @ n2
-    u = _w(lw["wu"]) @ n2
+    n2, s2 = normed(x, lw["ffn_norm"], spec.rms_eps, bf)
+    g = (_w(lw["wg"]) @ n2) * s2
+    u = (_w(lw["wu"]) @ n2) * s2
     h = bf(silu(g) * u)
     x = rs(x + _w(lw["wd"]) @ h)
     return x
@@ -153,8 +168,8 @@ def forward_one(spec: Spec, W: Dict, kv: KVCache, pos: int, token: int):
     for l in range(spec.n_layers):
         x = decoder_layer(spec, W["layers"][l], x, pos, kv, l)
     bf = round_bf16 if spec.bf16 else (lambda a: a)
-    xf = bf(rmsnorm(x, W["final_norm"], spec.rms_eps))
-    logits = (_w(W["lm_head"]) @ xf).astype(np.float32)
+    xf, sf = normed(x, W["final_norm"], spec.rms_eps, bf)
+    logits = ((_w(W["lm_head"]) @ xf) * sf).astype(np.float32)
     return logits, x
 
 
@@ -203,6 +218,6 @@ def mtp_forward_one(spec: Spec, W: Dict, kv: KVCache, pos: int, h_prev: np.ndarr
     b = bf(rmsnorm(_w(W["embed"][token]), M["norm_e"], spec.rms_eps))
     x = rs(_w(M["w_proj"]) @ np.concatenate([a, b]))
     x = decoder_layer(spec, M, x, pos, kv, 0)
-    xf = bf(rmsnorm(x, M["final_norm"], spec.rms_eps))
-    logits = (_w(W["lm_head"]) @ xf).astype(np.float32)
+    xf, sf = normed(x, M["final_norm"], spec.rms_eps, bf)
+    logits = ((_w(W["lm_head"]) @ xf) * sf).astype(np.float32)
     return logits, x

@@ -14,7 +14,7 @@ import torch
 import torch.nn.functional as F
 
 from oracle import numerics
-from oracle.model import KVCache, Spec, attend, forward_tokens, rmsnorm, rope
+from oracle.model import KVCache, Spec, attend, forward_tokens, normed, rmsnorm, rope
 from speculative_decoding_token_amd import synth
 
 
@@ -35,6 +35,22 @@ def test_rmsnorm_matches_torch():
     g = rng.normal(1, 0.1, 257)
     ref = F.rms_norm(torch.from_numpy(x), (257,), torch.from_numpy(g), eps=1e-6).numpy()
     np.testing.assert_allclose(rmsnorm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_folded_rmsnorm_is_rmsnorm_before_the_projection():
+    # the folded form (W @ (x * g)) / rms(x) against torch's rms_norm followed by the product
+    rng = np.random.default_rng(11)
+    x = rng.normal(0, 3, 257)
+    g = rng.normal(1, 0.1, 257)
+    W = rng.normal(0, 0.02, (33, 257))
+    n, s = normed(x, g, 1e-6, lambda a: a)
+    ref = (torch.from_numpy(W) @ F.rms_norm(torch.from_numpy(x), (257,), torch.from_numpy(g), eps=1e-6)).numpy()
+    np.testing.assert_allclose((W @ n) * s, ref, rtol=1e-12, atol=1e-14)
+    # bf16 contract: the row the projection reads is the gain-multiplied row rounded to bf16
+    nb, sb = normed(x, g, 1e-6, numerics.round_bf16)
+    want = torch.from_numpy(x * g).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(nb, want)
+    assert sb == s
 
 
 def test_rope_closed_forms():
@@ -101,11 +117,18 @@ def torch_forward(spec: Spec, W, tokens, k_prefix=None, v_prefix=None, bf16=Fals
 
     x = w(W["embed"])[torch.as_tensor(tokens, dtype=torch.long)]
     mask = torch.ones(M, T, dtype=torch.bool).tril(diagonal=P)
+    def normed(x, g):
+        # f32: torch's rms_norm; bf16: the contract's folded form, the gain-multiplied row
+        # rounded to bf16 and the projection scaled by 1/rms(x) afterwards
+        if not bf16:
+            return F.rms_norm(x, (spec.d_model,), w(g), eps=spec.rms_eps), 1.0
+        return rb(x * w(g)), torch.rsqrt((x * x).mean(dim=-1, keepdim=True) + spec.rms_eps)
+
     for l, lw in enumerate(W["layers"]):
-        n1 = rb(F.rms_norm(x, (spec.d_model,), w(lw["attn_norm"]), eps=spec.rms_eps))
-        q = rb(rot((n1 @ w(lw["wq"]).T).view(M, nq, hd)))
-        k = rb(rot((n1 @ w(lw["wk"]).T).view(M, nkv, hd)))
-        v = rb((n1 @ w(lw["wv"]).T).view(M, nkv, hd))
+        n1, s1 = normed(x, lw["attn_norm"])
+        q = rb(rot(((n1 @ w(lw["wq"]).T) * s1).view(M, nq, hd)))
+        k = rb(rot(((n1 @ w(lw["wk"]).T) * s1).view(M, nkv, hd)))
+        v = rb(((n1 @ w(lw["wv"]).T) * s1).view(M, nkv, hd))
         kk, vv = k.transpose(0, 1), v.transpose(0, 1)
         if P:
             kk = torch.cat([torch.from_numpy(np.asarray(k_prefix[l], np.float64)), kk], dim=1)
@@ -115,11 +138,11 @@ def torch_forward(spec: Spec, W, tokens, k_prefix=None, v_prefix=None, bf16=Fals
         o = F.scaled_dot_product_attention(q.transpose(0, 1), kk, vv, attn_mask=mask)
         o = rb(o.transpose(0, 1).reshape(M, nq * hd))
         x = rf(x + o @ w(lw["wo"]).T)
-        n2 = rb(F.rms_norm(x, (spec.d_model,), w(lw["ffn_norm"]), eps=spec.rms_eps))
-        h = rb(F.silu(n2 @ w(lw["wg"]).T) * (n2 @ w(lw["wu"]).T))
+        n2, s2 = normed(x, lw["ffn_norm"])
+        h = rb(F.silu((n2 @ w(lw["wg"]).T) * s2) * ((n2 @ w(lw["wu"]).T) * s2))
         x = rf(x + h @ w(lw["wd"]).T)
-    xf = rb(F.rms_norm(x, (spec.d_model,), w(W["final_norm"]), eps=spec.rms_eps))
-    return (xf @ w(W["lm_head"]).T).to(torch.float32).numpy()
+    xf, sf = normed(x, W["final_norm"])
+    return ((xf @ w(W["lm_head"]).T) * sf).to(torch.float32).numpy()
 
 
 def tiny(seed=0):
