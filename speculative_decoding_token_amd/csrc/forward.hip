@@ -88,7 +88,7 @@ SPEC_DEVINL void grid_sync(Sync& s, F issue) {
 }
 
 // ---------------------------------------------------------------- embedding
-// Workgroup m < M gathers row m: x = E[token], y = x * gain of the first norm, and the row's
+// Workgroup m < M gathers row m: x = E[token], y = bf16(x * gain of the first norm), and the row's
 // sum of squares (each thread adds its columns t, t + 512, ... in order; then a xor
 // butterfly per wavefront and the wavefront sums in order).
 SPEC_DEVINL void embed_step(const FwdArgs& a, char* sm) {
@@ -104,7 +104,7 @@ SPEC_DEVINL void embed_step(const FwdArgs& a, char* sm) {
   for (int c = t; c < a.d; c += SNW * 64) {
     const float v = ok ? bf16_to_f32(row[c]) : __builtin_nanf("");
     st<true>(a.x + (int64_t)m * a.d + c, v);
-    st<true>(a.y + (int64_t)m * a.d + c, v * bf16_to_f32(g[c]));
+    st<true>((bf16_t*)a.y + (int64_t)m * a.d + c, f32_to_bf16(v * bf16_to_f32(g[c])));
     sq += v * v;
   }
 #pragma unroll
@@ -451,7 +451,7 @@ SPEC_DEVINL StreamArgs qkv_args(const FwdArgs& a, int l) {
   g.rows2 = a.kv_dim;
   g.K = a.d;
   g.nunits = (a.q_dim + 2 * a.kv_dim) / 16;
-  g.xres = a.y;
+  g.x = a.y;
   g.ss_in = a.ss;
   g.np_in = l == 0 ? 1 : a.d / 16;
   g.ss_ld = a.ss_ld;
@@ -484,7 +484,7 @@ SPEC_DEVINL StreamArgs gu_args(const FwdArgs& a, int l) {
   g.rows0 = a.ffn;
   g.K = a.d;
   g.nunits = a.ffn / 16;
-  g.xres = a.y;
+  g.x = a.y;
   g.ss_in = a.ss;
   g.np_in = a.d / 16;
   g.ss_ld = a.ss_ld;
@@ -515,7 +515,7 @@ SPEC_DEVINL StreamArgs head_args(const FwdArgs& a) {
   g.rows0 = a.vocab;
   g.K = a.d;
   g.nunits = a.vocab / 16;
-  g.xres = a.y;
+  g.x = a.y;
   g.ss_in = a.ss;
   g.np_in = a.d / 16;
   g.ss_ld = a.ss_ld;

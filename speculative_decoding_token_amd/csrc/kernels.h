@@ -96,15 +96,15 @@ struct GemmArgs {
   int rows[3];
   int K;
   const void* x;      // [M, K] model dtype (GEMM input as stored)
-  // fused RMSNorm input (bf16 path): when xres is set the GEMM input is
-  // bf16(xres * rsqrt(mean(xres^2) + eps) * gain), with the sum of squares of row m given as
-  // np_in partial sums ss_in[m * ss_ld + 0 .. np_in-1] added in order
-  const float* xres;
-  const void* gain;
+  // folded RMSNorm (bf16 path): when ss_in is set, x holds gain-multiplied rows bf16(r * g)
+  // of residual rows r, and result row m is scaled by 1/sqrt(mean + eps), mean = (the np_in
+  // partial sums of squares ss_in[m * ss_ld + 0 .. np_in-1], added in order) / K
   const float* ss_in;
   int np_in, ss_ld;
   float eps;
   float* ss_out;      // EPI_RESID: partial sums of squares of the updated rows, one per block
+  void* y_out;        // EPI_RESID (bf16, may be null): [M, ld] bf16(updated rows * y_gain)
+  const void* y_gain;
   RowMap rm;
   // outputs
   float* out;         // EPI_STORE / EPI_RESID: [M, ld]
@@ -135,20 +135,17 @@ constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions
 constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)
 
 hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStream_t st);
-// y (bf16 models, may be null): also writes the rows times gain (float32), the input of the
-// streamed projections' RMSNorm.
+// y (bf16 models, may be null): also writes bf16(rows * gain), the input of the first
+// projection (its RMSNorm folded in).
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        float* ss, int ss_ld, float* y, const void* gain, hipStream_t st);
+                        float* ss, int ss_ld, void* y, const void* gain, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, int M, int d,
                           void* y, hipStream_t st);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st);
-// The fused RMSNorm prologue keeps the M normalized rows in LDS: M * (K + 8) * 2 bytes,
-// used when it fits GEMM_NORM_LDS_MAX; otherwise launch_norm_apply writes them first.
-constexpr size_t GEMM_NORM_LDS_MAX = 64 * 1024;
-size_t gemm_norm_lds_bytes(int M, int K);
-hipError_t launch_norm_apply(const float* x, const void* gain, const float* ss, int np, int ss_ld, float eps,
-                             int M, int K, void* y, hipStream_t st);
+// y[m, k] = bf16(x[m, k] * gain[k]) for M rows of K (bf16 models): the input of a projection
+// of RMSNorm(x) when the producer of x did not leave it.
+hipError_t launch_gain_rows(const float* x, const void* gain, int M, int K, void* y, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_copy_rows(const int32_t* src, int src_ld, int32_t* dst, int n, hipStream_t st);
@@ -189,13 +186,12 @@ hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, 
 
 // ---- weight-streaming projections (bf16 models, M <= 16 rows) -------------------------
 // out[m, n] = sum_k W[n, k] x[m, k] with W streamed through an LDS ring by one workgroup per
-// compute unit (see stream.hip).  Epilogues as GemmArgs.  The input rows are either bf16
-// rows x [M, K], or (xres set) an RMSNorm: xres [M, K] holds the float32 residual rows
-// already multiplied by the norm's gain, row m's sum of squares is the np_in partials
-// ss_in[m * ss_ld + 0 ..] added in order, and the input is bf16(xres * rsqrt(mean + eps)).
+// compute unit (see stream.hip).  Epilogues as GemmArgs, and so is the folded RMSNorm: with
+// ss_in set, x holds bf16(r * g) of residual rows r and row m of the result is scaled by
+// 1/sqrt(mean + eps), the mean from the np_in partials ss_in[m * ss_ld + 0 ..] added in order.
 // EPI_RESID adds into out (row stride ld) and leaves, when set, ss_out[m * ss_ld + u] = the
-// sum of squares of the 16 updated columns of unit u, and y_out = the updated rows times
-// y_gain (the next norm's input).
+// sum of squares of the 16 updated columns of unit u, and y_out = bf16(updated rows * y_gain)
+// (the next projection's input).
 struct StreamArgs {
   // EPI_QKV / EPI_QKV_ROWS: W_q, W_k, W_v; EPI_SWIGLU: W_gate, W_up; else W.  Separate
   // members, not an array: an indexed member would move the block to scratch memory.
@@ -204,16 +200,15 @@ struct StreamArgs {
   const void* w2;
   int rows0, rows1, rows2;
   int K, nunits;      // nunits: row tiles of 16 (EPI_SWIGLU: gate/up tile pairs)
-  const void* x;      // [M, K] bf16 input rows (when xres is null)
-  const float* xres;  // normalized input: gain-multiplied residual rows and their partials
-  const float* ss_in;
+  const void* x;      // [M, K] bf16 input rows
+  const float* ss_in; // folded RMSNorm: partial sums of squares of the residual rows
   int np_in, ss_ld;
   float eps;
   int M;
   float* out;         // EPI_STORE / EPI_RESID: [M, ld]
   int ld;
   float* ss_out;      // EPI_RESID
-  float* y_out;       // EPI_RESID: [M, ld] updated rows times y_gain (bf16 [ld])
+  void* y_out;        // EPI_RESID: [M, ld] bf16(updated rows * y_gain)
   const void* y_gain;
   void* h;            // EPI_SWIGLU: [M, rows0] bf16
   float* q_stage;     // EPI_QKV
@@ -250,7 +245,7 @@ struct FwdArgs {
   CacheView cache;
   const float2* rope;
   float* x;       // [M][d] residual rows
-  float* y;       // [M][d] residual rows times the next norm's gain
+  void* y;        // [M][d] bf16(residual rows * the next norm's gain)
   float* ss;      // [M][ss_ld] sum-of-squares partials
   int ss_ld;
   float* qkv;     // [M][q_dim + 2 kv_dim] raw q, k, v rows

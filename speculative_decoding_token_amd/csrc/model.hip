@@ -32,12 +32,13 @@ __global__ void rope_table_kernel(float2* table, int cap, int hd, double theta) 
 // ---------------------------------------------------------------- embedding gather
 // Row m = (seq b, i): token first[b*first_ld] for i == 0, else rest[b*rest_ld + i-1].  Also
 // leaves the row's sum of squares in ss[m * ss_ld] (fixed reduction order) for the fused
-// RMSNorm of the first projection and, when y is set (bf16), the row times gain.
+// RMSNorm of the first projection and, when y is set (bf16), bf16(row * gain): that
+// projection's input.
 template <int DT>
 __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vocab,
                                                     const int32_t* first, int first_ld,
                                                     const int32_t* rest, int rest_ld, int mseq,
-                                                    float* x, float* ss, int ss_ld, float* y,
+                                                    float* x, float* ss, int ss_ld, bf16_t* y,
                                                     const bf16_t* gain) {
   using A = Act<DT>;
   __shared__ float red[256];
@@ -49,7 +50,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
   for (int c = t; c < d; c += blockDim.x) {
     const float v = ok ? A::load(row, c) : __builtin_nanf("");
     x[(int64_t)m * d + c] = v;
-    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = v * bf16_to_f32(gain[c]);
+    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
     sq += v * v;
   }
   red[t] = sq;
@@ -188,61 +189,39 @@ SPEC_DEVINL void gemm_epilogue(const GemmArgs& a, int mat, int m, int n, float v
 // B = 32 k x 16 token rows (the same k slice of x, zero for rows >= M).  The MFMA's 16x
 // padding of the token dimension costs nothing here: the pass is bound by streaming W.
 //
-// With NORM the input is the float32 residual stream, normalized on the fly: the block
-// first adds up the row's sum-of-squares partials (left by the previous residual update)
-// and each lane scales its 8 values by rsqrt(mean + eps) and the gain before rounding them
-// to bf16, so RMSNorm costs no launch and no extra pass over the activations.  A residual
-// epilogue leaves, per block, the sum of squares of its 16 updated columns of each row.
+// With NORM the RMSNorm in front of the projection is folded into it: W . RMSNorm(x) =
+// (W . (x * g)) / rms(x).  The input rows are bf16(x * g), left by the producer of the
+// residual x, and each result row is scaled by 1/sqrt(mean(x^2) + eps), the mean from the
+// row's sum-of-squares partials (left by the same producer).  The first partials of the
+// block's rows are loaded ahead of the weights, so their latency hides behind the stream.
+// A residual epilogue leaves, per block, the sum of squares of its 16 updated columns of each
+// row and, when asked, those columns times the next norm's gain, rounded to bf16.
 SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// RMSNorm pieces shared by the fused prologue and the stand-alone kernel, so both give the
-// same bits.  row_inv: one full wavefront adds the row's sum-of-squares partials (lane j takes
-// partials j, j+64, ... in order, then a fixed xor butterfly) and returns 1/sqrt(mean + eps).
-SPEC_DEVINL float row_inv(const float* ss, int np, int K, float eps, int lane) {
-  float acc = 0.0f;
-  for (int p = lane; p < np; p += 64) acc += ss[p];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  return 1.0f / sqrtf(acc / (float)K + eps);
-}
-// bf16(x * inv * gain) for 8 consecutive elements
-SPEC_DEVINL uint4 norm8(const float* x, const bf16_t* gain, float inv) {
-  const float4 x0 = *(const float4*)(x);
-  const float4 x1 = *(const float4*)(x + 4);
-  const uint4 gg = *(const uint4*)(gain);
-  return make_uint4(
-      pack_bf16x2(x0.x * inv * __uint_as_float(gg.x << 16), x0.y * inv * __uint_as_float(gg.x & 0xFFFF0000u)),
-      pack_bf16x2(x0.z * inv * __uint_as_float(gg.y << 16), x0.w * inv * __uint_as_float(gg.y & 0xFFFF0000u)),
-      pack_bf16x2(x1.x * inv * __uint_as_float(gg.z << 16), x1.y * inv * __uint_as_float(gg.z & 0xFFFF0000u)),
-      pack_bf16x2(x1.z * inv * __uint_as_float(gg.w << 16), x1.w * inv * __uint_as_float(gg.w & 0xFFFF0000u)));
-}
-
-// Stand-alone RMSNorm of bf16 models (rows too many for the fused prologue's LDS).
-__global__ __launch_bounds__(256) void norm_apply_kernel(const float* x, const void* gain, const float* ss,
-                                                         int np, int ss_ld, float eps, int K, bf16_t* y) {
-  __shared__ float s_inv;
-  const int m = blockIdx.x, t = threadIdx.x;
-  if (t < 64) {
-    const float iv = row_inv(ss + (int64_t)m * ss_ld, np, K, eps, t);
-    if (t == 0) s_inv = iv;
+// y[m, k] = bf16(x[m, k] * gain[k]): a projection's input rows when the producer of x left none.
+__global__ __launch_bounds__(256) void gain_rows_kernel(const float* x, const bf16_t* gain, int K, bf16_t* y) {
+  const int m = blockIdx.x;
+  for (int k = threadIdx.x * 2; k < K; k += 512) {
+    const float2 v = *(const float2*)(x + (int64_t)m * K + k);
+    *(uint32_t*)(y + (int64_t)m * K + k) =
+        pack_bf16x2(v.x * bf16_to_f32(gain[k]), v.y * bf16_to_f32(gain[k + 1]));
   }
-  __syncthreads();
-  const float iv = s_inv;
-  for (int k8 = t * 8; k8 < K; k8 += 256 * 8)
-    *(uint4*)(y + (int64_t)m * K + k8) = norm8(x + (int64_t)m * K + k8, (const bf16_t*)gain + k8, iv);
 }
 
+// Single-tile instances of 16 wavefronts are held to 64 VGPRs: two workgroups per compute
+// unit, so 384 or 512 tiles (QKV, output and down projections) run in one round.
 template <int EPI, int NT, bool NORM, int GEMM_NW>
-__global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
+__global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) ? 8 : 1) void gemm_bf16_kernel(
+    GemmArgs a) {
   // k-steps per load group: 8 KB of weights in flight per wave and tile either way
   constexpr int GEMM_U = (GEMM_NW == 16 || NT == 4) ? 4 : 8;
   constexpr int TILES = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int PSS = TILES == 2 ? 4 : 2;  // partials per lane loaded ahead (a row's first 64 * PSS)
   __shared__ f32x4_t red[GEMM_NW][TILES][NT][64];
   __shared__ float s_inv[16 * NT];
   __shared__ float s_sq[16 * NT][17];
-  extern __shared__ __attribute__((aligned(16))) bf16_t xs[];  // NORM: [M][K + 8] normalized rows
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int mat = 0, r0 = blockIdx.x * 16;
   if (EPI == EPI_QKV) {
@@ -256,8 +235,16 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
   const int K = a.K, nsteps = K >> 5, M = a.rm.M;
-  const int XP = K + 8;
   const int koff = 8 * (lane >> 4);
+  // row `wave`'s partials lane, lane + 64, ... (zero past the count: adding them changes nothing)
+  float pss[PSS];
+  if (NORM) {
+#pragma unroll
+    for (int q = 0; q < PSS; ++q) {
+      const int p = lane + 64 * q;
+      pss[q] = (wave < M && p < a.np_in) ? a.ss_in[(int64_t)wave * a.ss_ld + p] : 0.0f;
+    }
+  }
   const bf16_t* wp[TILES];
   wp[0] = (const bf16_t*)a.w[mat] + (int64_t)(r0 + (lane & 15)) * K + koff;
   if (TILES == 2) wp[TILES - 1] = (const bf16_t*)a.w[1] + (int64_t)(r0 + (lane & 15)) * K + koff;
@@ -267,7 +254,7 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int m = nt * 16 + (lane & 15);
     xv[nt] = m < M;
-    xrow[nt] = NORM ? (int64_t)(xv[nt] ? m : 0) * XP + koff : (int64_t)(xv[nt] ? m : 0) * K + koff;
+    xrow[nt] = (int64_t)(xv[nt] ? m : 0) * K + koff;
   }
   // first group of weights in flight before anything else
   uint4 wa[TILES][GEMM_U];
@@ -277,19 +264,6 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
       wa[t][u] = s < nsteps ? *(const uint4*)(wp[t] + (int64_t)s * 32) : make_uint4(0, 0, 0, 0);
-  }
-  if (NORM) {
-    for (int m = wave; m < M; m += GEMM_NW) {
-      const float iv = row_inv(a.ss_in + (int64_t)m * a.ss_ld, a.np_in, K, a.eps, lane);
-      if (lane == 0) s_inv[m] = iv;
-    }
-    __syncthreads();
-    const int per_row = K / 8;
-    for (int idx = threadIdx.x; idx < M * per_row; idx += GEMM_NW * 64) {
-      const int m = idx / per_row, k8 = (idx % per_row) * 8;
-      *(uint4*)(xs + m * XP + k8) = norm8(a.xres + (int64_t)m * K + k8, (const bf16_t*)a.gain + k8, s_inv[m]);
-    }
-    __syncthreads();
   }
 
   f32x4_t acc[TILES][NT];
@@ -305,13 +279,9 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
       const int s = s0 + u * GEMM_NW;
       const bool ok = s < nsteps;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (NORM)
-          xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)(xs + xrow[nt] + s * 32) : make_uint4(0, 0, 0, 0);
-        else
-          xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)((const bf16_t*)a.x + xrow[nt] + (int64_t)s * 32)
-                                     : make_uint4(0, 0, 0, 0);
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)((const bf16_t*)a.x + xrow[nt] + (int64_t)s * 32)
+                                   : make_uint4(0, 0, 0, 0);
     }
     // next group of weights while this one is multiplied
     uint4 wn[TILES][GEMM_U];
@@ -340,26 +310,45 @@ __global__ __launch_bounds__(GEMM_NW * 64) void gemm_bf16_kernel(GemmArgs a) {
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) red[wave][t][nt][lane] = acc[t][nt];
+  if (NORM) {
+    // 1/rms of each row: lane j adds the row's partials j, j + 64, ... in order, then a fixed
+    // xor butterfly; wave w takes rows w, w + GEMM_NW, ...
+    for (int r = wave; r < M; r += GEMM_NW) {
+      float sum = 0.0f;
+      int p0 = lane;
+      if (r == wave) {
+#pragma unroll
+        for (int q = 0; q < PSS; ++q) sum += pss[q];
+        p0 = lane + 64 * PSS;
+      }
+      for (int p = p0; p < a.np_in; p += 64) sum += a.ss_in[(int64_t)r * a.ss_ld + p];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) s_inv[r] = 1.0f / sqrtf(sum / (float)K + a.eps);
+    }
+  }
   __syncthreads();
 
   // D layout of the 16x16 MFMA: lane l holds column l%16 (token), rows 4*(l/16)+r (weight row)
   for (int e = threadIdx.x; e < NT * 256; e += GEMM_NW * 64) {
     const int nt = e >> 8, l = (e >> 2) & 63, r = e & 3;
-    float v[TILES];
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < GEMM_NW; ++w) s += red[w][t][nt][l][r];
-      v[t] = s;
-    }
     const int m = nt * 16 + (l & 15);
     const int n = r0 + 4 * (l >> 4) + r;
     if (m < M) {
+      float v[TILES];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < GEMM_NW; ++w) s += red[w][t][nt][l][r];
+        v[t] = NORM ? s * s_inv[m] : s;
+      }
       if (EPI == EPI_RESID) {
         const float xn = a.out[(int64_t)m * a.ld + n] + v[0];
         a.out[(int64_t)m * a.ld + n] = xn;
         s_sq[m][n - r0] = xn * xn;
+        if (a.y_out)
+          ((bf16_t*)a.y_out)[(int64_t)m * a.ld + n] = f32_to_bf16(xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
       } else {
         gemm_epilogue<SPEC_DTYPE_BF16, EPI>(a, mat, m, n, v[0], v[TILES - 1]);
       }
@@ -879,10 +868,10 @@ hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStr
 
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
-                        float* ss, int ss_ld, float* y, const void* gain, hipStream_t st) {
+                        float* ss, int ss_ld, void* y, const void* gain, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16)
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_BF16>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, y, (const bf16_t*)gain);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, (bf16_t*)y, (const bf16_t*)gain);
   else
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_F32>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
                        first_ld, rest, rest_ld, mseq, x, ss, ss_ld, nullptr, nullptr);
@@ -931,13 +920,12 @@ hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, i
 template <int EPI, bool NORM, int NW>
 static hipError_t gemm_bf16_nw(const GemmArgs& a, int blocks, hipStream_t st) {
   const int M = a.rm.M;
-  const size_t lds = NORM ? gemm_norm_lds_bytes(M, a.K) : 0;
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1, NORM, NW>), dim3(blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 1, NORM, NW>), dim3(blocks), dim3(NW * 64), 0, st, a);
   else if (M <= 32)
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2, NORM, NW>), dim3(blocks), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 2, NORM, NW>), dim3(blocks), dim3(NW * 64), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4, NORM, 8>), dim3(blocks), dim3(8 * 64), lds, st, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 4, NORM, 8>), dim3(blocks), dim3(8 * 64), 0, st, a);
   return hipGetLastError();
 }
 
@@ -946,11 +934,10 @@ static hipError_t gemm_bf16_nt(const GemmArgs& a, int blocks, hipStream_t st) {
   return blocks <= 1024 ? gemm_bf16_nw<EPI, NORM, 16>(a, blocks, st) : gemm_bf16_nw<EPI, NORM, 8>(a, blocks, st);
 }
 
-size_t gemm_norm_lds_bytes(int M, int K) { return (size_t)M * (K + 8) * 2; }
-
-hipError_t launch_norm_apply(const float* x, const void* gain, const float* ss, int np, int ss_ld, float eps,
-                             int M, int K, void* y, hipStream_t st) {
-  hipLaunchKernelGGL(norm_apply_kernel, dim3(M), dim3(256), 0, st, x, gain, ss, np, ss_ld, eps, K, (bf16_t*)y);
+hipError_t launch_gain_rows(const float* x, const void* gain, int M, int K, void* y, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  if (K % 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gain_rows_kernel, dim3(M), dim3(256), 0, st, x, (const bf16_t*)gain, K, (bf16_t*)y);
   return hipGetLastError();
 }
 
@@ -962,14 +949,15 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st) {
     const int blocks = rows / 16;
     // normalized inputs feed the QKV, gate/up and LM-head projections; the residual ones
     // (output and down projections) read the attention output / SwiGLU product as stored
+    const bool norm = a.ss_in != nullptr;
     switch (epi) {
       case EPI_STORE:
-        return a.xres ? gemm_bf16_nt<EPI_STORE, true>(a, blocks, st) : gemm_bf16_nt<EPI_STORE, false>(a, blocks, st);
-      case EPI_RESID: return gemm_bf16_nt<EPI_RESID, false>(a, blocks, st);
+        return norm ? gemm_bf16_nt<EPI_STORE, true>(a, blocks, st) : gemm_bf16_nt<EPI_STORE, false>(a, blocks, st);
+      case EPI_RESID: return norm ? hipErrorInvalidValue : gemm_bf16_nt<EPI_RESID, false>(a, blocks, st);
       case EPI_QKV:
-        return a.xres ? gemm_bf16_nt<EPI_QKV, true>(a, blocks, st) : gemm_bf16_nt<EPI_QKV, false>(a, blocks, st);
+        return norm ? gemm_bf16_nt<EPI_QKV, true>(a, blocks, st) : gemm_bf16_nt<EPI_QKV, false>(a, blocks, st);
       default:
-        return a.xres ? gemm_bf16_nt<EPI_SWIGLU, true>(a, blocks, st) : gemm_bf16_nt<EPI_SWIGLU, false>(a, blocks, st);
+        return norm ? gemm_bf16_nt<EPI_SWIGLU, true>(a, blocks, st) : gemm_bf16_nt<EPI_SWIGLU, false>(a, blocks, st);
     }
   }
   const int blocks = (rows + 3) / 4;

@@ -30,6 +30,8 @@ struct Model {
   size_t act = 4;
   CacheView cache{};
   float* x = nullptr;
+  // the input of the next projection of an RMSNorm: f32 models the normed rows; bf16 models
+  // bf16(rows * gain), the norm folded into the projection
   void* xn = nullptr;
   float* qst = nullptr;
   float* kst = nullptr;
@@ -38,7 +40,6 @@ struct Model {
   float* logits = nullptr;
   float* part = nullptr;
   float* ss = nullptr;  // [Mmax][d/16] partial sums of squares of the residual rows
-  float* y = nullptr;   // [Mmax][d] residual rows times the next RMSNorm's gain (streamed path)
   float* qkv = nullptr; // [Mmax][q_dim + 2 kv_dim] raw q, k, v rows (one-launch forward)
   spec_layer_weights* dev_layers = nullptr;  // device copy of the layer table (one-launch forward)
   float2* rope = nullptr;
@@ -265,7 +266,6 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.logits = cv.take<float>((size_t)m.Mmax * d.vocab * 4);
   m.part = cv.take<float>((size_t)m.Mmax * d.n_q_heads * m.nchunk * (d.head_dim + 2) * 4);
   m.ss = cv.take<float>((size_t)m.Mmax * (d.d_model / 16 + 1) * 4);
-  m.y = cv.take<float>((size_t)m.Mmax * d.d_model * 4);
   m.qkv = cv.take<float>((size_t)m.Mmax * (m.q_dim + 2 * m.kv_dim) * 4);
   m.dev_layers = cv.take<spec_layer_weights>((size_t)d.n_layers * sizeof(spec_layer_weights));
   m.rope = cv.take<float2>((size_t)cap * (d.head_dim / 2) * sizeof(float2));
@@ -376,13 +376,12 @@ int check_probs(spec_ctx* c, const spec_probs* p, const char* name, int need_cap
 
 int list_cap(const spec_sampler& s) { return s.temperature > 0.0f ? s.top_k : 1; }
 
-// RMSNorm input of a projection: bf16 models fuse it into the GEMM (few rows: each workgroup
-// normalizes them in its LDS prologue, which saves a launch) or run one stand-alone kernel
-// with the same arithmetic (more rows: redoing them in every workgroup costs more); f32
-// models run the plain RMSNorm kernel.  x / ss: residual rows and their np sum-of-squares
-// partials per row.
+// RMSNorm input of a projection.  bf16 models fold the norm into the projection: it reads
+// bf16(x * gain) and scales each result row by 1/rms(x) from the row's np sum-of-squares
+// partials ss; `ready` says that the producer of x already left bf16(x * gain) in m.xn,
+// otherwise one small kernel writes it.  f32 models run the plain RMSNorm kernel.
 int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const float* ss, int np,
-               const void* gain) {
+               const void* gain, bool ready) {
   const spec_model_desc& d = m.d;
   const int P = 16 * m.mi;
   if (d.dtype != SPEC_DTYPE_BF16) {
@@ -390,19 +389,14 @@ int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const 
     g.x = m.xn;
     return SPEC_OK;
   }
-  const int ss_ld = d.d_model / 16 + 1;
-  const bool in_lds = (int64_t)M * d.d_model <= 4096 && gemm_norm_lds_bytes(M, d.d_model) <= GEMM_NORM_LDS_MAX;
-  if (in_lds) {
-    g.xres = x;
-    g.gain = gain;
-    g.ss_in = ss;
-    g.np_in = np;
-    g.ss_ld = ss_ld;
-    g.eps = d.rms_eps;
-  } else {
-    LAUNCH(c, P + PROF_NORM, launch_norm_apply(x, gain, ss, np, ss_ld, d.rms_eps, M, d.d_model, m.xn, c->stream));
-    g.x = m.xn;
-  }
+  // bf16: the projection reads bf16(x * gain) and scales its rows by 1/rms(x); the residual
+  // epilogue (or the embedding) that produced x normally left those rows in m.xn already
+  if (!ready) LAUNCH(c, P + PROF_NORM, launch_gain_rows(x, gain, M, d.d_model, m.xn, c->stream));
+  g.x = m.xn;
+  g.ss_in = ss;
+  g.np_in = np;
+  g.ss_ld = d.d_model / 16 + 1;
+  g.eps = d.rms_eps;
   return SPEC_OK;
 }
 
@@ -436,7 +430,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.rows2 = m.kv_dim;
     g.K = d.d_model;
     g.nunits = (m.q_dim + 2 * m.kv_dim) / 16;
-    g.xres = m.y;
+    g.x = m.xn;
     g.ss_in = m.ss;
     g.np_in = np;
     g.ss_ld = ss_ld;
@@ -472,7 +466,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     o.ld = d.d_model;
     o.ss_out = m.ss;
     o.ss_ld = ss_ld;
-    o.y_out = m.y;
+    o.y_out = m.xn;
     o.y_gain = w.ffn_norm;
     LAUNCH(c, P + PROF_OPROJ, launch_stream_gemm(EPI_RESID, o, grid, c->stream));
     np = d.d_model / 16;
@@ -482,7 +476,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     gu.rows0 = d.d_ffn;
     gu.K = d.d_model;
     gu.nunits = d.d_ffn / 16;
-    gu.xres = m.y;
+    gu.x = m.xn;
     gu.ss_in = m.ss;
     gu.np_in = np;
     gu.ss_ld = ss_ld;
@@ -501,7 +495,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     dn.ld = d.d_model;
     dn.ss_out = m.ss;
     dn.ss_ld = ss_ld;
-    dn.y_out = m.y;
+    dn.y_out = m.xn;
     dn.y_gain = l + 1 < d.n_layers ? m.layers[l + 1].attn_norm : d.final_norm;
     LAUNCH(c, P + PROF_DOWN, launch_stream_gemm(EPI_RESID, dn, grid, c->stream));
   }
@@ -528,7 +522,7 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.rows[1] = m.kv_dim;
     g.rows[2] = m.kv_dim;
     g.K = d.d_model;
-    if (norm_input(c, m, g, M, m.x, m.ss, np, w.attn_norm)) return SPEC_E_HIP;
+    if (norm_input(c, m, g, M, m.x, m.ss, np, w.attn_norm, true)) return SPEC_E_HIP;
     g.rm = rm;
     g.q_stage = m.qst;
     g.k_stage = m.kst;
@@ -558,6 +552,8 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     o.ld = d.d_model;
     o.ss_out = fused ? m.ss : nullptr;
     o.ss_ld = ss_ld;
+    o.y_out = fused ? m.xn : nullptr;
+    o.y_gain = w.ffn_norm;
     LAUNCH(c, P + PROF_OPROJ, launch_gemm(dt, EPI_RESID, o, st));
     np = d.d_model / 16;
     GemmArgs gu{};
@@ -565,7 +561,7 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     gu.w[1] = w.wu;
     gu.rows[0] = d.d_ffn;
     gu.K = d.d_model;
-    if (norm_input(c, m, gu, M, m.x, m.ss, np, w.ffn_norm)) return SPEC_E_HIP;
+    if (norm_input(c, m, gu, M, m.x, m.ss, np, w.ffn_norm, true)) return SPEC_E_HIP;
     gu.rm = rm;
     gu.h = m.h;
     LAUNCH(c, P + PROF_GATEUP, launch_gemm(dt, EPI_SWIGLU, gu, st));
@@ -579,6 +575,8 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     dn.ld = d.d_model;
     dn.ss_out = fused ? m.ss : nullptr;
     dn.ss_ld = ss_ld;
+    dn.y_out = fused ? m.xn : nullptr;
+    dn.y_gain = l + 1 < d.n_layers ? m.layers[l + 1].attn_norm : d.final_norm;
     LAUNCH(c, P + PROF_DOWN, launch_gemm(dt, EPI_RESID, dn, st));
   }
   return SPEC_OK;
@@ -594,7 +592,7 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
     lm.rows0 = d.vocab;
     lm.K = d.d_model;
     lm.nunits = d.vocab / 16;
-    lm.xres = m.y;
+    lm.x = m.xn;
     lm.ss_in = ss;
     lm.np_in = np;
     lm.ss_ld = d.d_model / 16 + 1;
@@ -609,7 +607,8 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
   lm.w[0] = d.lm_head;
   lm.rows[0] = d.vocab;
   lm.K = d.d_model;
-  if (norm_input(c, m, lm, M, x, ss, np, d.final_norm)) return SPEC_E_HIP;
+  // rows of m.x come with bf16(x * final gain) from the last layer's residual epilogue
+  if (norm_input(c, m, lm, M, x, ss, np, d.final_norm, x == m.x)) return SPEC_E_HIP;
   lm.rm = rm;
   lm.out = logits;
   lm.ld = d.vocab;
@@ -654,7 +653,7 @@ int forward_one_launch(spec_ctx* c, Model& m, int B, int mseq, const int32_t* fi
   a.cache = m.cache;
   a.rope = m.rope;
   a.x = m.x;
-  a.y = m.y;
+  a.y = m.xn;
   a.ss = m.ss;
   a.ss_ld = d.d_model / 16 + 1;
   a.qkv = m.qkv;
@@ -680,9 +679,8 @@ int forward(spec_ctx* c, Model& m, int B, int mseq, const int32_t* first, int fi
   const bool fused = d.dtype == SPEC_DTYPE_BF16;
   const int ss_ld = d.d_model / 16 + 1;
   RowMap rm{M, mseq, c->len, pos_off};
-  const bool stream = use_stream(c, m, M);
   LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_embed(d.dtype, d.embed, d.d_model, d.vocab, first, first_ld, rest, rest_ld,
-                                                 M, mseq, m.x, fused ? m.ss : nullptr, ss_ld, stream ? m.y : nullptr,
+                                                 M, mseq, m.x, fused ? m.ss : nullptr, ss_ld, fused ? m.xn : nullptr,
                                                  m.layers[0].attn_norm, c->stream));
   int rc = run_layers(c, m, M, rm, 1);
   if (rc) return rc;
@@ -732,6 +730,8 @@ int mtp_layer(spec_ctx* c, int B, int R, const float* h, int64_t h_ss, const int
   g.ld = d.d_model;
   g.ss_out = fused ? m.ss : nullptr;
   g.ss_ld = d.d_model / 16 + 1;
+  g.y_out = fused ? m.xn : nullptr;
+  g.y_gain = m.layers[0].attn_norm;
   LAUNCH(c, 16 * m.mi + PROF_EMBED, launch_gemm(d.dtype, EPI_RESID, g, c->stream));
   return run_layers(c, m, M, rm, d.d_model / 16);
 }

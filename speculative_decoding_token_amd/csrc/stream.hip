@@ -80,7 +80,7 @@ hipError_t stream_init() {
 }
 
 hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_t st) {
-  if (!stream_supported(a.M, a.K, epi, a.xres != nullptr) || a.nunits < 1 || grid < 1) return hipErrorInvalidValue;
+  if (!stream_supported(a.M, a.K, epi, a.ss_in != nullptr) || a.nunits < 1 || grid < 1) return hipErrorInvalidValue;
   const void* k = select(epi, nst_of(epi, a.K));
   if (!k) return hipErrorInvalidValue;
   const int g = std::min(grid, a.nunits);

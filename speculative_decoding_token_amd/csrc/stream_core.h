@@ -15,18 +15,20 @@
 //   stages of consecutive units follow each other without a pause.
 // * The input rows (the B operand of the MFMA) are read once per workgroup into registers
 //   that stay resident: each wavefront keeps the k-slices it multiplies (K / 256 slices of 16
-//   bytes per lane).  RMSNorm is applied on the way in: the inputs of the QKV, gate/up and
-//   vocabulary projections are the float32 residual rows already multiplied by the norm's
-//   gain (written next to the residual by the projection or embedding that produced them),
-//   scaled by 1/sqrt(mean square + eps) from the sum-of-squares partials left with them and
-//   rounded to bf16, so no normalization pass exists.  Long reductions (the down projection,
-//   K = d_ffn) load their slices with each stage instead.
+//   bytes per lane).  Long reductions (the down projection, K = d_ffn) load their slices with
+//   each stage instead.
+// * RMSNorm is folded into the projections it feeds: W . RMSNorm(x) = (W . (x * g)) / rms(x).
+//   The QKV, gate/up and vocabulary projections read bf16(x * g), written next to the residual
+//   by the projection or embedding that produced x, and scale their results by
+//   1/sqrt(mean square + eps) from the sum-of-squares partials left with it, so no
+//   normalization pass exists.
 // * Each wavefront multiplies its k-steps of the stage with v_mfma_f32_16x16x32_bf16 (A = 16
 //   weight rows x 32 k read from LDS in the operand layout, B = the same 32 k of the 16 token
 //   rows, zero past M); the 8 partial tiles meet in LDS at the end of a unit.  The token
 //   dimension is padded to 16 at no cost: the kernel is bound by the weight stream.
 // * Residual projections add into the float32 residual stream and leave, per 16 columns and
-//   row, the sum of squares of the updated values and the values times the next norm's gain.
+//   row, the sum of squares of the updated values and the values times the next norm's gain
+//   rounded to bf16.
 //
 // A row's result depends only on that row (every reduction order is fixed by K and d
 // alone), so the rows of a K+1-row verify are bit-identical to one-row forwards.
@@ -172,9 +174,10 @@ SPEC_DEVINL const char* unit_rows(const StreamArgs& a, int u, int t, int* mat, i
 }
 
 // One projection over this workgroup's units (blockIdx.x, blockIdx.x + grid, ...).
-// EPI: epilogue.  NST > 0: K = NST stages, input slices resident in registers (normalized on
-// the way in when a.xres is set); NST == 0: any K of whole stages, bf16 input slices loaded
-// with each stage.  COH: activations cross workgroups inside the launch.
+// EPI: epilogue.  NST > 0: K = NST stages, input slices resident in registers; NST == 0: any
+// K of whole stages, bf16 input slices loaded with each stage.  With a.ss_in set the
+// projection folds in an RMSNorm (resident inputs only).  COH: activations cross workgroups
+// inside the launch.
 template <int EPI, int NST, bool COH>
 struct Gemm {
   static constexpr int TILES = EPI == EPI_SWIGLU ? 2 : 1;
@@ -250,62 +253,34 @@ struct Gemm {
     const uint32_t inv0 = red0 + RED_BYTES;
 
     // Resident input slices: slice (ks, i) holds k = ks * KS + (wave + 8 i) * 32 + 8 (lane /
-    // 16) .. + 7 of token row m (zero for m >= M).  Their loads (and the sum-of-squares
-    // partials of the rows) are issued before the remaining first weight stages; the slices
-    // are finished after.
-    constexpr int SSP = 8;   // partials per lane: np <= 512
-    constexpr int YC = 8;    // slices normalized per batch (bounds the float32 values in flight)
-    uint4 xres[XS];
+    // 16) .. + 7 of token row m (zero for m >= M).  Their loads, and those of the rows'
+    // sum-of-squares partials for a folded RMSNorm, are issued before the remaining first
+    // weight stages.
+    constexpr int SSP = 8;  // partials per lane: np <= 512
+    uint4 xin[XS];
     float pss[2][SSP];
-    const bool norm = RES && a.xres != nullptr;
-    const __amdgpu_buffer_rsrc_t yr = rsrc(a.xres, (uint32_t)(M * K * 4));
-    // float32 values of slices q0 .. q0 + YC - 1 (zero past the row count)
-    auto load_y = [&](int q0, float4 (&yv)[YC][2]) {
+    const bool norm = a.ss_in != nullptr;
+    if (norm) {
+      const __amdgpu_buffer_rsrc_t sr = rsrc(a.ss_in, (uint32_t)(M * a.ss_ld * 4));
 #pragma unroll
-      for (int qq = 0; qq < YC; ++qq) {
-        const int q = q0 + qq;
-        if (q >= XS) break;
-        const int ks = q / WSTEPS, i = q % WSTEPS;
-        const int k = ks * KS + (wave + SNW * i) * 32 + 8 * (lane >> 4);
-        const uint32_t off = m < M ? (uint32_t)(m * K + k) * 4u : 0x80000000u;
-        yv[qq][0] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(yr, off, 0, XP));
-        yv[qq][1] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(yr, off + 16u, 0, XP));
-      }
-    };
-    auto pack_y = [&](int q0, const float4 (&yv)[YC][2], float inv) {
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = wave + SNW * rr;
 #pragma unroll
-      for (int qq = 0; qq < YC; ++qq) {
-        const int q = q0 + qq;
-        if (q >= XS) break;
-        const float4 y0 = yv[qq][0], y1 = yv[qq][1];
-        xres[q] = make_uint4(pack_bf16(y0.x * inv, y0.y * inv), pack_bf16(y0.z * inv, y0.w * inv),
-                             pack_bf16(y1.x * inv, y1.y * inv), pack_bf16(y1.z * inv, y1.w * inv));
+        for (int t = 0; t < SSP; ++t) {
+          const int p = lane + 64 * t;
+          const uint32_t off = (r < M && p < a.np_in) ? (uint32_t)(r * a.ss_ld + p) * 4u : 0x80000000u;
+          pss[rr][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, XP));
+        }
       }
-    };
-    float4 y0v[YC][2];
+    }
     if (RES) {
-      if (norm) {
-        const __amdgpu_buffer_rsrc_t sr = rsrc(a.ss_in, (uint32_t)(M * a.ss_ld * 4));
+      const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
+      const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int r = wave + SNW * rr;
-#pragma unroll
-          for (int t = 0; t < SSP; ++t) {
-            const int p = lane + 64 * t;
-            const uint32_t off = (r < M && p < a.np_in) ? (uint32_t)(r * a.ss_ld + p) * 4u : 0x80000000u;
-            pss[rr][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, off, 0, XP));
-          }
-        }
-        load_y(0, y0v);
-      } else {
-        const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
-        const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
-#pragma unroll
-        for (int q = 0; q < XS; ++q) {
-          const int ks = q / WSTEPS, i = q % WSTEPS;
-          xres[q] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + (wave + SNW * i) * 32) * 2, XP));
-        }
+      for (int q = 0; q < XS; ++q) {
+        const int ks = q / WSTEPS, i = q % WSTEPS;
+        xin[q] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + (wave + SNW * i) * 32) * 2, XP));
       }
     }
 
@@ -319,28 +294,23 @@ struct Gemm {
       if (!RES) issue_x(a, j, xa[RES ? 0 : j]);
     }
 
+    // folded RMSNorm: 1/rms of each row (wavefront w handles rows w and w + 8; lane j adds
+    // partials j, j + 64, ... in order, then a fixed xor butterfly); thread e < 256 scales
+    // the results of token e / 16
+    float rinv = 1.0f;
     if (norm) {
-      // 1/rms of each row: wavefront w handles rows w and w + 8; lane j adds partials j,
-      // j + 64, ... in order, then a fixed xor butterfly
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int r = wave + SNW * rr;
-        float acc = 0.0f;
+        float sum = 0.0f;
 #pragma unroll
-        for (int t = 0; t < SSP; ++t) acc += pss[rr][t];
+        for (int t = 0; t < SSP; ++t) sum += pss[rr][t];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(acc / (float)K + a.eps));
+        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(sum / (float)K + a.eps));
       }
       wg_barrier();
-      const float inv = m < M ? lds_read_f32(inv0 + m * 4) : 0.0f;
-      pack_y(0, y0v, inv);
-#pragma unroll
-      for (int q0 = YC; q0 < XS; q0 += YC) {
-        float4 yv[YC][2];
-        load_y(q0, yv);
-        pack_y(q0, yv, inv);
-      }
+      if (threadIdx.x < 256 && (int)(threadIdx.x >> 4) < M) rinv = lds_read_f32(inv0 + (threadIdx.x >> 4) * 4);
     }
 
     f32x4_t acc[TILES];
@@ -373,7 +343,7 @@ struct Gemm {
 #pragma unroll
           for (int w = 0; w < SNW; ++w)
             sacc += __uint_as_float(r == 0 ? p[w].x : (r == 1 ? p[w].y : (r == 2 ? p[w].z : p[w].w)));
-          v[t] = sacc;
+          v[t] = norm ? sacc * rinv : sacc;
         }
         int mat, r0;
         (void)unit_rows<EPI>(a, u, 0, &mat, &r0);
@@ -385,7 +355,9 @@ struct Gemm {
             float* xp = a.out + (int64_t)mm * a.ld + n;
             xn = ld<COH>(xp) + v[0];
             st<COH>(xp, xn);
-            if (a.y_out) st<COH>(a.y_out + (int64_t)mm * a.ld + n, xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
+            if (a.y_out)
+              st<COH>((bf16_t*)a.y_out + (int64_t)mm * a.ld + n,
+                      f32_to_bf16(xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n])));
           }
           float sq = xn * xn;
 #pragma unroll
@@ -435,7 +407,7 @@ struct Gemm {
       lds_read4(ad[0], ad[1], ad[2], ad[3], wv[0], wv[1], wv[2], wv[3]);
 #pragma unroll
       for (int i = 0; i < WSTEPS; ++i) {
-        const uint4 b = RES ? xres[(RES ? ks : 0) * WSTEPS + i] : xb[i];
+        const uint4 b = RES ? xin[(RES ? ks : 0) * WSTEPS + i] : xb[i];
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[i * TILES + t]),
