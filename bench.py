@@ -9,7 +9,8 @@ and the one device-to-host read of the emitted tokens.
 
 Prints one JSON line: accepted (emitted) tokens per second over the timed steps, the
 verify pass's HBM bytes per second against the 8 TB/s peak, the roofline of the dominant
-kernel (the gate/up projection + SwiGLU of the target), a teacher-forced upper bound
+kernel (the gate/up projection + SwiGLU of the target; the forward kernel when the forward
+runs as one launch), a teacher-forced upper bound
 (drafts = the target's own greedy continuation, every draft accepted), and the CPU
 oracle timed on a bounded sample of the same cycle.
 """
@@ -59,18 +60,39 @@ def verify_bytes(shape, k, L):
     return w + kv_read + kv_write + logits + emb
 
 
-# HBM bytes per launch of the target gate/up kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
-# (scaled by a 1 GiB copy's readings), with the sha256 prefix of model.hip they were taken on:
-# the figure is reported only while that source is unchanged.
-GATE_UP_TRAFFIC = {"bytes": 202637312, "model_hip_sha256": "fd0426d14351706a"}
+# The dominant kernel of each schedule: the target's gate/up projection + SwiGLU (for the
+# one-launch forward, the forward kernel itself), and its HBM bytes per launch from rocprofv3
+# FETCH_SIZE / WRITE_SIZE (scaled by a 1 GiB copy's readings) with the sha256 prefix of the
+# sources that define it: the figure is reported only while those sources are unchanged.
+DOMINANT = {
+    "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
+                         "through an LDS ring, one workgroup per CU)",
+               "slot": "target.gate_up",
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 201951838, "sha256": "c695e44d9f9e0056"},
+    "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
+                       "per 16-row tile pair)",
+             "slot": "target.gate_up",
+             "sources": ["model.hip"], "traffic": None, "sha256": None},
+    "forward": {"kernel": "forward_kernel (the whole target forward of the verify as one launch)",
+                "slot": "target.forward", "sources": ["forward.hip", "stream_core.h"], "traffic": None,
+                "sha256": None},
+}
+REPS = 8  # back-to-back launches of the dominant kernel between the profiling events (the
+          # first REPS - 1 with other layers' weights, so none finds its weights cached)
 
 
-def gate_up_traffic():
+def sources_sha(names):
     import hashlib
-    path = os.path.join(ROOT, "speculative_decoding_token_amd", "csrc", "model.hip")
-    with open(path, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    return GATE_UP_TRAFFIC["bytes"] if sha == GATE_UP_TRAFFIC["model_hip_sha256"] else None
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_decoding_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_traffic(sched):
+    d = DOMINANT[sched]
+    return d["traffic"] if d["sha256"] and sources_sha(d["sources"]) == d["sha256"] else None
 
 
 def gate_up_bytes(shape, M):
@@ -170,8 +192,8 @@ def main():
 
     if args.no_graphs:
         eng.use_graphs(False)
-    if args.schedule:
-        eng.set_schedule(args.schedule)
+    sched = args.schedule or "stream"
+    eng.set_schedule(sched)
     reset()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -198,17 +220,25 @@ def main():
     vbytes = verify_bytes(tshape, K, L + args.warmup + 1)
     verify_gbs = vbytes / (verify_avg_ms * 1e-3) / 1e9
 
-    # per-kernel durations with events around every launch (separate steps)
+    # per-kernel durations with events around every launch (separate steps); the dominant
+    # kernel goes out REPS times back to back between its events (other layers' weights first),
+    # so its average carries one dispatch delay per REPS launches
+    dom = DOMINANT[sched]
     eng.profile(True)
+    if dom["slot"] != "target.forward":
+        eng.profile_repeat(dom["slot"], REPS)
     for _ in range(args.profile_steps):
         eng.cycle(1, K, rnd)
         rnd += 1
     prof = eng.profile_read() if args.profile_steps else {}
+    if dom["slot"] != "target.forward":
+        eng.profile_repeat(dom["slot"], 1)
     eng.profile(False)
-    gu = prof.get("target.gate_up", {"ms": float("nan"), "launches": 1})
-    gu_ms = gu["ms"] / gu["launches"]
-    gu_bytes = gate_up_bytes(tshape, K + 1)
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    dprof = prof.get(dom["slot"], {"ms": float("nan"), "launches": 1})
+    dom_ms = dprof["ms"] / dprof["launches"]
+    # the one-launch forward moves the whole verify's bytes (weights, cache, logits)
+    dom_bytes = gate_up_bytes(tshape, K + 1) if dom["slot"] == "target.gate_up" else vbytes
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     # teacher-forced upper bound: drafts = the target's own greedy continuation
     teacher = None
@@ -233,12 +263,16 @@ def main():
         "config": {"workload": f"8B-shape bf16 target verify K={K} + 0.6B-shape draft, batch 1, "
                                f"KV context {L}, {'sampled T=1 top_k 20 top_p 0.95' if args.sampled else 'greedy'}, "
                                f"random N(0,0.02) weights" + (f", {tshape.n_layers} layers" if args.layers else ""),
-                   "global_batch": 1, "seq_len": L, "k": K, "parallelism": "none (1 GPU)"},
+                   "global_batch": 1, "seq_len": L, "k": K, "schedule": sched, "parallelism": "none (1 GPU)"},
         "acceptance": accepted / (K * args.steps),
         "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
-        "roofline": {"bound": "hbm", "kernel": "target gate/up projection + SwiGLU (gemm_bf16_kernel<EPI_SWIGLU,1>)",
-                     "achieved": gu_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gu_gbs / PEAK_HBM_GBS,
-                     "traffic": gate_up_traffic(), "bytes_per_launch": gu_bytes, "avg_launch_ms": gu_ms},
+        "roofline": {"bound": "hbm", "kernel": dom["kernel"],
+                     "achieved": dom_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
+                     "traffic": dominant_traffic(sched), "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
+                     "timing": (f"HIP events on the context stream around {REPS} back-to-back launches (the first "
+                                f"{REPS - 1} with the next layers' weights, then the real one), "
+                                if dom["slot"] != "target.forward" else "HIP events around each launch, ")
+                               + f"{args.profile_steps} profiled steps after the timed ones"},
         "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
                     for k, v in prof.items()},
         "teacher_forced": teacher,

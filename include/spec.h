@@ -293,12 +293,20 @@ int spec_gate_update(spec_gate* g /*host*/, int32_t accepted, int32_t attempted)
 /* Profiling slots: slot = kernel class + 16 * model (model 0 = target, 1 = draft); classes
  * 0 embedding gather, 1 RMSNorm, 2 QKV projection, 3 attention (chunks + combine), 4 output
  * projection + residual, 5 gate/up projection + SwiGLU, 6 down projection + residual,
- * 7 LM head, 8 truncation, 9 draft sampling, 10 accept, 11 kv trim. */
+ * 7 LM head, 8 truncation, 9 draft sampling, 10 accept, 11 kv trim, 12 one-launch forward. */
 #define SPEC_PROF_SLOTS 32
 
 /* enable != 0: bracket every launch of the context with HIP events on its stream, filed by
  * slot (launches then go out one by one, not as a replayed graph).  0: stop. */
 int spec_profile(spec_ctx* ctx, int32_t enable);
+
+/* While profiling, each launch of the gate/up projection slot `slot` (5 target, 21 draft)
+ * goes out `reps` times back to back between its events (launches counts each): first with
+ * the weights of the following reps - 1 layers, so that no launch finds its weights in a
+ * cache, then the real one, which overwrites their output.  The average duration then carries
+ * one dispatch delay per reps launches instead of one per launch.  SPEC_E_INVAL for another
+ * slot or reps outside 1..64; reps = 1 turns it off. */
+int spec_profile_repeat(spec_ctx* ctx, int32_t slot, int32_t reps);
 
 /* Sums the recorded launches per slot: ms (host double [SPEC_PROF_SLOTS]) = total GPU time
  * between each launch's events, launches (host int64 [SPEC_PROF_SLOTS]) = launch count;
@@ -311,19 +319,20 @@ int spec_profile_read(spec_ctx* ctx, double* ms, int64_t* launches);
 int spec_use_graphs(spec_ctx* ctx, int32_t enable);
 
 /* Schedule of the forwards of bf16 models over at most 16 rows.
- *   SPEC_SCHED_STEP    (the default) one workgroup per 16-row tile of each projection,
- *                      RMSNorm fused into the projection or run as its own launch;
- *   SPEC_SCHED_STREAM  one launch per step, projections streaming their weights through an
- *                      LDS ring with one workgroup per compute unit; each residual projection
- *                      leaves the next RMSNorm's input, so no normalization launch is needed;
+ *   SPEC_SCHED_STEP    one launch per step, one workgroup per 16-row tile of each projection;
+ *   SPEC_SCHED_STREAM  (the default) one launch per step, projections streaming their weights
+ *                      through an LDS ring with one workgroup per compute unit;
  *   SPEC_SCHED_FORWARD the whole forward as one persistent (cooperative) launch of the
  *                      SPEC_SCHED_STREAM steps meeting at grid barriers, the next
  *                      projection's weights streaming while a barrier is awaited; draft_step
  *                      and verify_step are then launched directly, not replayed from graphs.
- * Shapes a schedule does not cover (reduction lengths that are not whole 1 KB stages, head
- * sizes other than 128 for SPEC_SCHED_FORWARD, the MTP head) fall back to the next simpler
- * one.  Schedules agree within the float tolerances, not bit for bit; each is row-count
- * invariant on its own.  Returns SPEC_E_INVAL for an unknown schedule. */
+ * In all three the RMSNorm is folded into the projection it feeds: the residual update (or
+ * the embedding) leaves bf16(x * gain) and the projection scales its result rows by 1/rms(x),
+ * so no normalization launch exists.  Shapes a schedule does not cover (reduction lengths
+ * that are not whole 1 KB stages, head sizes other than 128 for SPEC_SCHED_FORWARD, the MTP
+ * head) fall back to the next simpler one.  Schedules agree within the float tolerances, not
+ * bit for bit; each is row-count invariant on its own.  Returns SPEC_E_INVAL for an unknown
+ * schedule. */
 #define SPEC_SCHED_STEP 0
 #define SPEC_SCHED_STREAM 1
 #define SPEC_SCHED_FORWARD 2

@@ -34,7 +34,7 @@ EXPORTED = [
     "spec_prefill", "spec_set_last", "draft_step", "verify_step", "accept", "kv_trim",
     "spec_get_stats", "spec_get_lengths", "spec_truncate_scratch_size", "spec_truncate",
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
-    "spec_profile", "spec_profile_read", "spec_use_graphs", "spec_load_history",
+    "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
 ]
 PROF_SLOTS = 32
@@ -132,6 +132,7 @@ def lib(path: str = LIB_PATH):
         "spec_philox_uniforms": ([U64, P, I32, P, P], C.c_int),
         "spec_ngram_match": ([P, P, I32, I32, I32, I32, I32, P, P, P, P], C.c_int),
         "spec_profile": ([P, I32], C.c_int),
+        "spec_profile_repeat": ([P, I32, I32], C.c_int),
         "spec_profile_read": ([P, P, P], C.c_int),
         "spec_use_graphs": ([P, I32], C.c_int),
         "spec_set_schedule": ([P, I32], C.c_int),
@@ -338,6 +339,14 @@ def spec_ngram_match(ctx_tokens, lengths, batch: int, ld: int, k: int, n_min: in
 
 def spec_profile(ctx: int, enable: bool) -> None:
     _check(lib().spec_profile(ctx, int(enable)), ctx)
+
+
+def spec_profile_repeat(ctx: int, slot_name: str, reps: int) -> None:
+    """Repeat the launches of one profiling slot ('target.gate_up', ...) reps times back to
+    back between their events."""
+    model, cls = slot_name.split(".")
+    slot = PROF_CLASSES.index(cls) + (16 if model == "draft" else 0)
+    _check(lib().spec_profile_repeat(ctx, slot, reps), ctx)
 
 
 def spec_profile_read(ctx: int) -> Dict[str, Dict[str, float]]:

@@ -618,6 +618,23 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
     kreg[v] = *(const uint4*)(kc + (int64_t)pc * HD + d8);
     vreg[v] = *(const uint4*)(vc + (int64_t)pc * HD + d8);
   }
+  // the new keys of this chunk (positions p0 .. p1-1): the first NKH * 256 of their
+  // (position, pair) items are loaded here too, so the block waits for one round trip
+  const int p0 = max(c0, L), p1 = min(c0 + C, total), nnew = max(p1 - p0, 0) * HALF;
+  constexpr int NKH = 2;
+  float kx0[NKH], kx1[NKH];
+  float2 kcs[NKH];
+#pragma unroll
+  for (int v = 0; v < NKH; ++v) {
+    const int idx = t + 256 * v;
+    if (idx < nnew) {
+      const int p = p0 + idx / HALF, d = idx % HALF;
+      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
+      kx0[v] = src[d];
+      kx1[v] = src[d + HALF];
+      kcs[v] = a.rope[(int64_t)p * HALF + d];
+    }
+  }
 
   // query rows: every load of the thread first (ATTN_ROWS_MAX*HALF/256 slots), then the rotation
   {
@@ -662,18 +679,22 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   }
   // new keys in this chunk: rotate, round, use, and write to the cache
   {
-    const int p0 = max(c0, L), p1 = min(c0 + C, total);
-    for (int idx = t; idx < (p1 - p0) * HALF; idx += 256) {
+    auto put = [&](int idx, float x0, float x1, float2 cs) {
       const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
-      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
-      const float x0 = src[d], x1 = src[d + HALF];
-      const float2 cs = a.rope[(int64_t)p * HALF + d];
       const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
       const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
       ks[j * KP + d] = lo;
       ks[j * KP + d + HALF] = hi;
       kc[(int64_t)p * HD + d] = lo;
       kc[(int64_t)p * HD + d + HALF] = hi;
+    };
+#pragma unroll
+    for (int v = 0; v < NKH; ++v)
+      if (t + 256 * v < nnew) put(t + 256 * v, kx0[v], kx1[v], kcs[v]);
+    for (int idx = t + 256 * NKH; idx < nnew; idx += 256) {
+      const int p = p0 + idx / HALF, d = idx % HALF;
+      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
+      put(idx, src[d], src[d + HALF], a.rope[(int64_t)p * HALF + d]);
     }
   }
   __syncthreads();
@@ -774,10 +795,12 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 
 // Merges the chunks of one (row, head): weights exp(m_c - max) from one wavefront (every
 // chunk statistic loaded at once), then the weighted value sums with the chunks split over
-// 256/head_dim thread groups and added back in a fixed order.
+// 256/head_dim thread groups and added back in a fixed order.  Each thread's first values
+// are loaded before the weights are computed, so the merge waits for about one round trip.
 template <int DT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   using A = Act<DT>;
+  constexpr int NR = 32;  // chunk values per thread held in registers (the rest are loaded later)
   __shared__ float s_w[ATTN_MAX_CHUNKS];
   __shared__ float s_part[256];
   __shared__ float s_den;
@@ -788,6 +811,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int pos = a.rm.len[b] + a.rm.pos_off + i;
   const int nch = pos / ATTN_CHUNK + 1;
   const float* P = a.part + (int64_t)row * a.nchunk * (hd + 2);
+  const int groups = 256 / hd, g = t / hd, d = t % hd;
+  // this thread's values (chunks g, g + groups, ...) go out before the weights are known
+  float pv[NR];
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    const int c = g + groups * q;
+    pv[q] = c < nch ? P[c * (hd + 2) + d] : 0.0f;
+  }
   if (t < 64) {
     constexpr int PER = ATTN_MAX_CHUNKS / 64;
     float mc[PER], lc[PER];
@@ -816,10 +847,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     if (t == 0) s_den = den;
   }
   __syncthreads();
-  const int groups = 256 / hd, g = t / hd, d = t % hd;
   float o = 0.0f;
-#pragma unroll 8
-  for (int c = g; c < nch; c += groups) o += P[c * (hd + 2) + d] * s_w[c];
+#pragma unroll
+  for (int q = 0; q < NR; ++q) {
+    const int c = g + groups * q;
+    if (c < nch) o += pv[q] * s_w[c];
+  }
+  for (int c = g + groups * NR; c < nch; c += groups) o += P[c * (hd + 2) + d] * s_w[c];
   s_part[t] = o;
   __syncthreads();
   if (t < hd) {

@@ -58,6 +58,7 @@ enum ProfClass {
 struct ProfRec {
   int slot;
   hipEvent_t a, b;
+  int reps;  // back-to-back launches between the two events
 };
 
 // A captured launch sequence and the arguments it was captured with.
@@ -93,7 +94,7 @@ struct spec_ctx {
   int mtp_rows = 1;             // rows of the next catch-up (previous cycle's k + 1)
   // schedule of bf16 forwards over few rows (SPEC_SCHED_*) and the grid of the streamed
   // projections (one workgroup per compute unit)
-  int sched = SPEC_SCHED_STEP;
+  int sched = SPEC_SCHED_STREAM;
   int ncu = 0;
   int fgrid = 0;            // workgroups of the one-launch forward (0: not available)
   unsigned* fsync = nullptr;  // its barrier words
@@ -110,6 +111,7 @@ struct spec_ctx {
   uint32_t* round_dev = nullptr;  // the cycle's round, read by the draft sampling kernels
   // launch profiling (events around every launch; graphs are bypassed while it is on)
   bool prof = false;
+  int prof_rep_slot = -1, prof_reps = 1;  // spec_profile_repeat
   hipEvent_t prof_start = nullptr;
   std::vector<hipEvent_t> ev_free;
   std::vector<ProfRec> recs;
@@ -170,9 +172,30 @@ hipError_t take_event(spec_ctx* c, hipEvent_t* e) {
     if ((ctx)->prof) {                                                     \
       HIPCHK(ctx, take_event(ctx, &eb_));                                  \
       HIPCHK(ctx, hipEventRecord(eb_, (ctx)->stream));                     \
-      (ctx)->recs.push_back(ProfRec{(slot), ea_, eb_});                    \
+      (ctx)->recs.push_back(ProfRec{(slot), ea_, eb_, 1});                 \
     }                                                                      \
   } while (0)
+
+// LAUNCH for a launch that may be repeated under spec_profile_repeat: fn(r) issues repeat r
+// of reps (r = reps - 1 is the real one).
+#define LAUNCH_REP(ctx, slot, fn)                                                          \
+  do {                                                                                     \
+    hipEvent_t ea_ = nullptr, eb_ = nullptr;                                               \
+    const int reps_ = ((ctx)->prof && (slot) == (ctx)->prof_rep_slot) ? (ctx)->prof_reps : 1; \
+    if ((ctx)->prof) {                                                                     \
+      HIPCHK(ctx, take_event(ctx, &ea_));                                                  \
+      HIPCHK(ctx, hipEventRecord(ea_, (ctx)->stream));                                     \
+    }                                                                                      \
+    for (int r_ = 0; r_ < reps_; ++r_) HIPCHK(ctx, fn(r_, reps_));                         \
+    if ((ctx)->prof) {                                                                     \
+      HIPCHK(ctx, take_event(ctx, &eb_));                                                  \
+      HIPCHK(ctx, hipEventRecord(eb_, (ctx)->stream));                                     \
+      (ctx)->recs.push_back(ProfRec{(slot), ea_, eb_, reps_});                             \
+    }                                                                                      \
+  } while (0)
+
+// Layer of repeat r of reps of layer l's launch: the others first, l itself last.
+inline int rep_layer(int l, int r, int reps, int n_layers) { return (l + reps - 1 - r) % n_layers; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -483,7 +506,13 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     gu.eps = d.rms_eps;
     gu.M = M;
     gu.h = m.h;
-    LAUNCH(c, P + PROF_GATEUP, launch_stream_gemm(EPI_SWIGLU, gu, grid, c->stream));
+    auto gu_rep = [&](int r, int reps) {
+      StreamArgs g2 = gu;
+      g2.w0 = m.layers[rep_layer(l, r, reps, d.n_layers)].wg;
+      g2.w1 = m.layers[rep_layer(l, r, reps, d.n_layers)].wu;
+      return launch_stream_gemm(EPI_SWIGLU, g2, grid, c->stream);
+    };
+    LAUNCH_REP(c, P + PROF_GATEUP, gu_rep);
     StreamArgs dn{};
     dn.w0 = w.wd;
     dn.rows0 = d.d_model;
@@ -564,7 +593,13 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     if (norm_input(c, m, gu, M, m.x, m.ss, np, w.ffn_norm, true)) return SPEC_E_HIP;
     gu.rm = rm;
     gu.h = m.h;
-    LAUNCH(c, P + PROF_GATEUP, launch_gemm(dt, EPI_SWIGLU, gu, st));
+    auto gu_rep = [&](int r, int reps) {
+      GemmArgs g2 = gu;
+      g2.w[0] = m.layers[rep_layer(l, r, reps, d.n_layers)].wg;
+      g2.w[1] = m.layers[rep_layer(l, r, reps, d.n_layers)].wu;
+      return launch_gemm(dt, EPI_SWIGLU, g2, st);
+    };
+    LAUNCH_REP(c, P + PROF_GATEUP, gu_rep);
     GemmArgs dn{};
     dn.w[0] = w.wd;
     dn.rows[0] = d.d_model;
@@ -1223,6 +1258,16 @@ int spec_profile(spec_ctx* c, int32_t enable) {
   return SPEC_OK;
 }
 
+int spec_profile_repeat(spec_ctx* c, int32_t slot, int32_t reps) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  if (reps < 1 || reps > 64) return fail(c, SPEC_E_INVAL, "reps must be 1..64");
+  if (slot < 0 || slot >= SPEC_PROF_SLOTS || slot % 16 != PROF_GATEUP)
+    return fail(c, SPEC_E_INVAL, "only the gate/up slots can repeat");
+  c->prof_rep_slot = reps > 1 ? slot : -1;
+  c->prof_reps = reps;
+  return SPEC_OK;
+}
+
 int spec_profile_read(spec_ctx* c, double* ms, int64_t* launches) {
   if (need_ctx(c) || !ms || !launches) return SPEC_E_INVAL;
   HIPCHK(c, hipStreamSynchronize(c->stream));
@@ -1234,7 +1279,7 @@ int spec_profile_read(spec_ctx* c, double* ms, int64_t* launches) {
     float t = 0.0f;
     HIPCHK(c, hipEventElapsedTime(&t, r.a, r.b));
     ms[r.slot] += t;
-    launches[r.slot] += 1;
+    launches[r.slot] += r.reps;
     c->ev_free.push_back(r.a);
     c->ev_free.push_back(r.b);
   }

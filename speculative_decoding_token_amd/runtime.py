@@ -221,8 +221,11 @@ class Engine:
     def profile_read(self):
         return B.spec_profile_read(self.ctx)
 
+    def profile_repeat(self, slot_name: str, reps: int):
+        B.spec_profile_repeat(self.ctx, slot_name, reps)
+
     def set_schedule(self, schedule: str):
-        """'step' (the default), 'stream' or 'forward' (see spec_set_schedule)."""
+        """'step', 'stream' (the default) or 'forward' (see spec_set_schedule)."""
         B.spec_set_schedule(self.ctx, schedule)
 
     def use_graphs(self, enable: bool):
