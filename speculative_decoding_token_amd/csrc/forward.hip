@@ -19,8 +19,9 @@
 //
 // A barrier is a relaxed atomic arrival per workgroup after its stores have completed, a
 // counter per group of workgroups, a top counter and a release word.  Every wait is bounded
-// in time; once one has timed out the error word is set, every later wait is skipped and the
-// launch still drains (its results are then invalid, and the error is reported to the host).
+// in time; once one has timed out the error word is set, every later wait ends at once and
+// the launch still drains (its results are then invalid, and the error is reported to the
+// host).
 #include <algorithm>
 
 #include "stream_core.h"
@@ -33,6 +34,7 @@ using namespace sk;
 constexpr int SYNC_SP = 32;                          // words between barrier counters (128 bytes)
 constexpr unsigned long long WAIT_TICKS = 2000000;   // 20 ms of the 100 MHz constant clock
 constexpr int ATT_GROUPS = 2;                        // 4-wavefront attention groups per workgroup
+constexpr int FWD_LDS_BYTES = LDS_BYTES + 64;        // + the sequences' first positions (len + pos_off)
 
 __host__ __device__ inline int attn_group_bytes(int qt, int hd) {
   return 2 * (qt * 16 * (hd + 8) + ATTN_CHUNK * (hd + 8) + hd * (ATTN_CHUNK + 8));
@@ -60,20 +62,18 @@ SPEC_DEVINL void grid_sync(Sync& s, F issue) {
   unsigned* rel = s.w + 9 * SYNC_SP;
   unsigned* err = s.w + 10 * SYNC_SP;
   const bool lead = threadIdx.x == 0;
-  bool skip = false;
+  // every workgroup arrives at every barrier (the counts stay exact after a timeout); the
+  // error word is read only while waiting
   if (lead) {
-    skip = ld<true>(err) != 0u;
-    if (!skip) {
-      const unsigned gsize = gridDim.x / 8, grp = blockIdx.x & 7;
-      const unsigned a = __hip_atomic_fetch_add(s.w + grp * SYNC_SP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a == epoch * gsize - 1) {
-        const unsigned t = __hip_atomic_fetch_add(s.w + 8 * SYNC_SP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t == epoch * 8 - 1) st<true>(rel, epoch);
-      }
+    const unsigned gsize = gridDim.x / 8, grp = blockIdx.x & 7;
+    const unsigned a = __hip_atomic_fetch_add(s.w + grp * SYNC_SP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a == epoch * gsize - 1) {
+      const unsigned t = __hip_atomic_fetch_add(s.w + 8 * SYNC_SP, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == epoch * 8 - 1) st<true>(rel, epoch);
     }
   }
   issue();
-  if (lead && !skip) {
+  if (lead) {
     const unsigned long long t0 = wall_clock64();
     while (ld<true>(rel) < epoch) {
       if (wall_clock64() - t0 > WAIT_TICKS) {
@@ -140,7 +140,7 @@ struct Attn {
     int b, kvh, chunk;
     bool ok;
   };
-  static SPEC_DEVINL Item item_of(const FwdArgs& a, int base) {
+  static SPEC_DEVINL Item item_of(const FwdArgs& a, const int* s_len, int base) {
     const int nkv = a.cache.n_kv;
     const int items = (a.M / a.mseq) * nkv * a.nchunk;
     const int gi = threadIdx.x >> 8;
@@ -151,7 +151,7 @@ struct Attn {
     r.chunk = i % a.nchunk;
     r.kvh = (i / a.nchunk) % nkv;
     r.b = i / (a.nchunk * nkv);
-    if (r.chunk * C >= a.len[r.b] + a.pos_off + a.mseq) r.ok = false;  // past the last position
+    if (r.chunk * C >= s_len[r.b] + a.mseq) r.ok = false;  // past the last position
     return r;
   }
   static SPEC_DEVINL int64_t cache_base(const FwdArgs& a, int layer, const Item& it) {
@@ -161,7 +161,7 @@ struct Attn {
   // cached keys and values of the item's chunk (positions past the cache clamp to its end;
   // positions >= L are replaced after the load); nothing is read for an inactive item
   static SPEC_DEVINL void load_kv(const FwdArgs& a, int layer, const Item& it, uint4 (&kreg)[NV], uint4 (&vreg)[NV]) {
-    const int t = threadIdx.x & 255;
+    const int t = tid_here() & 255;
     const CacheView& cv = a.cache;
     const int64_t cb = cache_base(a, layer, it);
     const uint32_t bytes = it.ok ? (uint32_t)((int64_t)cv.cap * HD * 2) : 0u;
@@ -177,14 +177,15 @@ struct Attn {
     }
   }
 
-  static SPEC_DEVINL void item(const FwdArgs& a, int layer, char* gsm, const Item& it, const uint4 (&kreg)[NV],
+  static SPEC_DEVINL void item(const FwdArgs& a, const int* s_len, int layer, char* gsm, const Item& it,
+                               const uint4 (&kreg)[NV],
                                const uint4 (&vreg)[NV]) {
-    const int t = threadIdx.x & 255, lane = t & 63, wave = t >> 6;
+    const int t = tid_here() & 255, lane = t & 63, wave = t >> 6;
     const CacheView& cv = a.cache;
     const int b = it.b, kvh = it.kvh, chunk = it.chunk;
     const bool active = it.ok;
     const int mseq = a.mseq, G = a.n_q / cv.n_kv;
-    const int L = a.len[b] + a.pos_off;
+    const int L = s_len[b];
     const int total = L + mseq;
     const int c0 = chunk * C;
     const int R = mseq * G, QT = (R + 15) / 16;
@@ -196,6 +197,30 @@ struct Attn {
     bf16_t* kc = (bf16_t*)cv.k + cb;
     bf16_t* vc = (bf16_t*)cv.v + cb;
     if (active) {
+      // new keys and values of this chunk (positions p0 .. p1 - 1) from the QKV step's rows:
+      // the first NKH * 256 key pairs and NVH * 256 values go out with the query rows, so the
+      // group waits for one round trip
+      const int p0 = max(c0, L), p1 = min(c0 + C, total), nn = max(p1 - p0, 0);
+      constexpr int NKH = 2, NVH = 4;
+      float kx0[NKH], kx1[NKH], vx[NVH];
+      float2 kcs[NKH];
+      auto key_src = [&](int p) { return a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kvh * HD; };
+      auto val_src = [&](int p) { return a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kv_dim + kvh * HD; };
+#pragma unroll
+      for (int v = 0; v < NKH; ++v) {
+        const int idx = t + 256 * v;
+        if (idx < nn * HALF) {
+          const int p = p0 + idx / HALF, d = idx % HALF;
+          kx0[v] = ld<true>(key_src(p) + d);
+          kx1[v] = ld<true>(key_src(p) + d + HALF);
+          kcs[v] = a.rope[(int64_t)p * HALF + d];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < NVH; ++v) {
+        const int idx = t + 256 * v;
+        if (idx < nn * HD) vx[v] = ld<true>(val_src(p0 + idx / HD) + idx % HD);
+      }
       // query rows in batches of 8 loads per thread (one batch covers two query tiles)
       constexpr int NQB = 8;
       const int nq = (QT * 16 * HALF + 255) / 256;
@@ -221,26 +246,15 @@ struct Attn {
           }
         }
       }
+      // cached positions from the loads; positions past the end zero; new ones below
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const int idx = t + 256 * v;
         const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-        if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
-        else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
-        uint4 vv;
-        if (p < L) {
-          vv = vreg[v];
-        } else if (p < total) {
-          // a value of this pass: rounded here and cached
-          const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kv_dim + kvh * HD + d8;
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = ld<true>(src + e);
-          vv = make_uint4(pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]), pack_bf16(f[6], f[7]));
-          *(uint4*)(vc + (int64_t)p * HD + d8) = vv;
-        } else {
-          vv = make_uint4(0, 0, 0, 0);
-        }
+        if (p >= L && p < total) continue;
+        const uint4 kk = p < L ? kreg[v] : make_uint4(0, 0, 0, 0);
+        const uint4 vv = p < L ? vreg[v] : make_uint4(0, 0, 0, 0);
+        *(uint4*)(ks + j * KP + d8) = kk;
         const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
         const int js = j ^ (((d8 >> 3) & 7) << 3);
 #pragma unroll
@@ -249,19 +263,34 @@ struct Attn {
           vt[(d8 + 2 * e + 1) * VP + js] = (bf16_t)(w[e] >> 16);
         }
       }
-      const int p0 = max(c0, L), p1 = min(c0 + C, total);
-      for (int idx = t; idx < (p1 - p0) * HALF; idx += 256) {
+      // new keys: rotated, rounded, used and cached
+      auto put_key = [&](int idx, float x0, float x1, float2 cs) {
         const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
-        const float* src = a.qkv + (int64_t)(b * mseq + (p - L)) * qkv_ld + q_dim + kvh * HD;
-        const float x0 = ld<true>(src + d), x1 = ld<true>(src + d + HALF);
-        const float2 cs = a.rope[(int64_t)p * HALF + d];
         const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
         const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
         ks[j * KP + d] = lo;
         ks[j * KP + d + HALF] = hi;
         kc[(int64_t)p * HD + d] = lo;
         kc[(int64_t)p * HD + d + HALF] = hi;
+      };
+#pragma unroll
+      for (int v = 0; v < NKH; ++v)
+        if (t + 256 * v < nn * HALF) put_key(t + 256 * v, kx0[v], kx1[v], kcs[v]);
+      for (int idx = t + 256 * NKH; idx < nn * HALF; idx += 256) {
+        const int p = p0 + idx / HALF, d = idx % HALF;
+        put_key(idx, ld<true>(key_src(p) + d), ld<true>(key_src(p) + d + HALF), a.rope[(int64_t)p * HALF + d]);
       }
+      // new values: rounded, used (transposed, in the swizzled V^T layout) and cached
+      auto put_val = [&](int idx, float x) {
+        const int p = p0 + idx / HD, d = idx % HD, j = p - c0;
+        const bf16_t v16 = f32_to_bf16(x);
+        vt[d * VP + (j ^ (((d >> 3) & 7) << 3))] = v16;
+        vc[(int64_t)p * HD + d] = v16;
+      };
+#pragma unroll
+      for (int v = 0; v < NVH; ++v)
+        if (t + 256 * v < nn * HD) put_val(t + 256 * v, vx[v]);
+      for (int idx = t + 256 * NVH; idx < nn * HD; idx += 256) put_val(idx, ld<true>(val_src(p0 + idx / HD) + idx % HD));
     }
     __syncthreads();
     if (active) {
@@ -359,7 +388,7 @@ struct Attn {
 };
 
 template <int HD>
-SPEC_DEVINL void attn_step(const FwdArgs& a, int layer, char* sm, uint4 (&kreg)[Attn<HD>::NV],
+SPEC_DEVINL void attn_step(const FwdArgs& a, const int* s_len, int layer, char* sm, uint4 (&kreg)[Attn<HD>::NV],
                            uint4 (&vreg)[Attn<HD>::NV]) {
   using A = Attn<HD>;
   const int nkv = a.cache.n_kv;
@@ -369,19 +398,20 @@ SPEC_DEVINL void attn_step(const FwdArgs& a, int layer, char* sm, uint4 (&kreg)[
   char* gsm = sm + gi * attn_group_bytes(QT, HD);
   const int slots = gridDim.x * ATT_GROUPS;
   for (int base = 0; base < items; base += slots) {
-    const typename A::Item it = A::item_of(a, base);
+    const typename A::Item it = A::item_of(a, s_len, base);
     A::load_kv(a, layer, it, kreg, vreg);
-    A::item(a, layer, gsm, it, kreg, vreg);
+    A::item(a, s_len, layer, gsm, it, kreg, vreg);
   }
 }
 
 // ---------------------------------------------------------------- combine
 // Unit = (row m, q head h), one per 256-thread half of the workgroup: the chunk maxima and
 // weights exp(m_c - max) from one wavefront, the weighted value sums with the chunks split
-// over 256 / head_dim thread groups, added back in a fixed order.
+// over 256 / head_dim thread groups, added back in a fixed order.  Each thread's values go
+// out before the weights are known (coherent loads in a loop would wait for one another).
 template <int HD>
-SPEC_DEVINL void combine_step(const FwdArgs& a, char* red) {
-  const int half = threadIdx.x >> 8, t = threadIdx.x & 255;
+SPEC_DEVINL void combine_step(const FwdArgs& a, const int* s_len, char* red) {
+  const int txc = tid_here(), half = txc >> 8, t = txc & 255;
   float* s_w = (float*)red + half * (ATTN_MAX_CHUNKS + 257);
   float* s_part = s_w + ATTN_MAX_CHUNKS;
   float* s_den = s_part + 256;
@@ -392,9 +422,24 @@ SPEC_DEVINL void combine_step(const FwdArgs& a, char* red) {
     const int uu = ok ? u : 0;
     const int m = uu / a.n_q, h = uu % a.n_q;
     const int b = m / a.mseq, i = m % a.mseq;
-    const int pos = a.len[b] + a.pos_off + i;
+    const int pos = s_len[b] + i;
     const int nch = pos / ATTN_CHUNK + 1;
     const float* P = a.part + (int64_t)uu * a.nchunk * (HD + 2);
+    constexpr int GROUPS = 256 / HD;
+    constexpr int NR = 8;  // chunk values per thread loaded before the weights
+    const int g = t / HD, d = t % HD;
+    // coherent plain loads (not atomics), so that unrolled runs of them are all in flight
+    const __amdgpu_buffer_rsrc_t pr = rsrc(P, (uint32_t)(a.nchunk * (HD + 2) * 4));
+    auto pval = [&](int c) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pr, (uint32_t)(c * (HD + 2) + d) * 4u, 0,
+                                                                           CPOL_SC1));
+    };
+    float pv[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int c = g + GROUPS * q;
+      pv[q] = c < nch ? pval(c) : 0.0f;
+    }
     if (t < 64) {
       constexpr int PER = ATTN_MAX_CHUNKS / 64;
       float mc[PER], lc[PER];
@@ -423,10 +468,14 @@ SPEC_DEVINL void combine_step(const FwdArgs& a, char* red) {
       if (t == 0) *s_den = den;
     }
     __syncthreads();
-    constexpr int GROUPS = 256 / HD;
-    const int g = t / HD, d = t % HD;
     float o = 0.0f;
-    for (int c = g; c < nch; c += GROUPS) o += ld<true>(P + c * (HD + 2) + d) * s_w[c];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      const int c = g + GROUPS * q;
+      if (c < nch) o += pv[q] * s_w[c];
+    }
+#pragma unroll 8
+    for (int c = g + GROUPS * NR; c < nch; c += GROUPS) o += pval(c) * s_w[c];
     s_part[t] = o;
     __syncthreads();
     if (ok && t < HD) {
@@ -541,15 +590,19 @@ __global__ __launch_bounds__(SNW * 64) void forward_kernel(FwdArgs a) {
   if (a.trace && threadIdx.x == 0 && a.trace_cap > 0) a.trace[(size_t)blockIdx.x * 2] = wall_clock64();
   uint4 kreg[Attn<HD>::NV], vreg[Attn<HD>::NV];
   char* red = sm + RING * STAGE;  // the combine step's LDS, clear of the ring
+  // first position of each sequence, read once
+  int* s_len = (int*)(sm + LDS_BYTES);
+  if (threadIdx.x < (unsigned)(a.M / a.mseq)) s_len[threadIdx.x] = a.len[threadIdx.x] + a.pos_off;
+  __syncthreads();
   embed_step(a, sm);
   grid_sync(s, [&] { QKV::prefetch(qkv_args(a, 0), sm, P); });
 #pragma clang loop unroll(disable)
   for (int l = 0; l < a.n_layers; ++l) {
     QKV::run(qkv_args(a, l), sm, P);
     grid_sync(s, [] {});
-    attn_step<HD>(a, l, sm, kreg, vreg);
+    attn_step<HD>(a, s_len, l, sm, kreg, vreg);
     grid_sync(s, [&] { OP::prefetch(o_args(a, l), sm, P); });
-    combine_step<HD>(a, red);
+    combine_step<HD>(a, s_len, red);
     grid_sync(s, [] {});
     OP::run(o_args(a, l), sm, P);
     grid_sync(s, [&] { GU::prefetch(gu_args(a, l), sm, P); });
@@ -612,10 +665,10 @@ hipError_t forward_init(int* grid) {
                       fwd_ptr<5, 5, 128>()};
   int fit = 1 << 30;
   for (const void* k : ks) {
-    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, FWD_LDS_BYTES);
     if (e != hipSuccess) return e;
     int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, SNW * 64, LDS_BYTES);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k, SNW * 64, FWD_LDS_BYTES);
     if (e != hipSuccess) return e;
     fit = std::min(fit, nb);
   }
@@ -632,7 +685,7 @@ hipError_t launch_forward(const FwdArgs& a, int grid, hipStream_t st) {
   if (e != hipSuccess) return e;
   FwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel(k, dim3(grid), dim3(SNW * 64), args, (unsigned)LDS_BYTES, st);
+  return hipLaunchCooperativeKernel(k, dim3(grid), dim3(SNW * 64), args, (unsigned)FWD_LDS_BYTES, st);
 }
 
 }  // namespace spec

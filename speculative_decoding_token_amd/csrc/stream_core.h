@@ -144,6 +144,15 @@ SPEC_DEVINL uint64_t uni64(const void* p) {
   return ((uint64_t)hi << 32) | (uint64_t)lo;
 }
 
+// threadIdx.x as a value the compiler cannot move: everything derived from it is computed
+// where it is used (a persistent kernel would otherwise keep per-lane addresses of every step
+// live across the others)
+SPEC_DEVINL int tid_here() {
+  int v = (int)threadIdx.x;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 SPEC_DEVINL uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
@@ -203,7 +212,7 @@ struct Gemm {
   // is in the resource base; a stage past the end gets a resource of size 0, so its loads
   // touch no memory.
   static SPEC_DEVINL void issue_w(const StreamArgs& a, char* sm, int j, int total) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
     const int nst = stages_per_unit(a), K = RES ? NST * KS : a.K;
     const bool ok = j < total;
     const int u = (int)blockIdx.x + (j / nst) * (int)gridDim.x, ks = j % nst;
@@ -223,7 +232,7 @@ struct Gemm {
   }
   // The wavefront's bf16 input slices of stage j (streamed inputs).
   static SPEC_DEVINL void issue_x(const StreamArgs& a, int j, uint4 (&xb)[WSTEPS]) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
     const int K = a.K, ks = j % stages_per_unit(a), m = lane & 15;
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(a.M * K * 2));  // rows >= M: out of range
     const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
@@ -244,7 +253,7 @@ struct Gemm {
 
   // The projection; P weight stages were prefetched.
   static SPEC_DEVINL void run(const StreamArgs& a, char* sm, int P) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
     const int K = RES ? NST * KS : a.K, M = a.M, nst = stages_per_unit(a);
     const int total = total_stages(a);
     const int m = lane & 15;
@@ -310,7 +319,7 @@ struct Gemm {
         if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(sum / (float)K + a.eps));
       }
       wg_barrier();
-      if (threadIdx.x < 256 && (int)(threadIdx.x >> 4) < M) rinv = lds_read_f32(inv0 + (threadIdx.x >> 4) * 4);
+      if (tx < 256 && (tx >> 4) < M) rinv = lds_read_f32(inv0 + (tx >> 4) * 4);
     }
 
     f32x4_t acc[TILES];
@@ -328,8 +337,8 @@ struct Gemm {
         acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
       wg_barrier();
-      if (threadIdx.x < 256) {
-        const int e = threadIdx.x, mm = e >> 4, c = e & 15, ll = (c >> 2) * 16 + mm, r = c & 3;
+      if (tx < 256) {
+        const int e = tx, mm = e >> 4, c = e & 15, ll = (c >> 2) * 16 + mm, r = c & 3;
         float v[TILES];
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
