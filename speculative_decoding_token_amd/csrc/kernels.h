@@ -128,7 +128,13 @@ struct AttnArgs {
   float* part;         // [M*n_q][nchunk][hd+2]
   int nchunk;
   void* out;           // combine: [M, n_q*hd] model dtype
+  // bf16, head_dim 128: launches with at most ATTN_FEW_ROWS query rows per kv head run their
+  // chunks on the vector ALUs (attn_chunk_few_kernel) instead of 16-row MFMA tiles.  Set per
+  // model, so that all its forwards at those row counts take the same path.
+  int few;
 };
+
+constexpr int ATTN_FEW_ROWS = 4;
 
 constexpr int ATTN_CHUNK = 64;
 constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions

@@ -793,6 +793,210 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   }
 }
 
+// The same chunk for few query rows (R <= ATTN_FEW_ROWS, head_dim 128: a draft model at one or
+// two rows) on the vector ALUs, where 16-row MFMA tiles would be mostly padding.  K and V stay
+// in the cache layout in LDS.  Scores: thread t takes key t / 4 and the quarter t % 4 of the
+// head dimension (a sequential sum over its 32 dims, then the quarters added pairwise); the
+// chunk softmax per row as in the MFMA kernel (P rounded to bf16, the row sum of the rounded
+// values), reductions only for the R rows present; P V: wavefront w produces query row w, two
+// output dims per lane, keys in order.  Partials in the layout the combine kernel reads.
+__global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
+  constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2, QW = HD / 4;
+  constexpr int RM = ATTN_FEW_ROWS;
+  __shared__ __attribute__((aligned(16))) bf16_t ks[C * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t vs[C * KP];
+  __shared__ __attribute__((aligned(16))) float qf[RM][HD];
+  __shared__ __attribute__((aligned(16))) float ps[RM][C];
+  __shared__ float wred[2][4][RM];
+  const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const CacheView& cv = a.cache;
+  const int mseq = a.rm.mseq, G = a.n_q / cv.n_kv;
+  const int L = a.rm.len[b] + a.rm.pos_off;
+  const int total = L + mseq;
+  const int c0 = chunk * C;
+  if (c0 >= total) return;
+  const int R = mseq * G;
+  const int kv_dim = cv.n_kv * HD, q_dim = a.n_q * HD;
+  const int64_t cbase = ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap) * HD;
+  bf16_t* kc = (bf16_t*)cv.k + cbase;
+  const bf16_t* vc = (const bf16_t*)cv.v + cbase;
+  // every load first: cached K and V rows of the chunk (16 threads per 256-byte row), the
+  // query pair of this thread, and the first new-key pairs
+  constexpr int NV = C * (HD / 8) / 256;
+  uint4 kreg[NV], vreg[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int idx = t + 256 * v;
+    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8;
+    const int pc = min(c0 + j, cv.cap - 1);
+    kreg[v] = *(const uint4*)(kc + (int64_t)pc * HD + d8);
+    vreg[v] = *(const uint4*)(vc + (int64_t)pc * HD + d8);
+  }
+  const int qr = t / HALF, qd = t % HALF;  // query row and rotation pair of this thread
+  float qx0 = 0.f, qx1 = 0.f;
+  float2 qcs = make_float2(0.f, 0.f);
+  if (qr < R) {
+    const int i = qr / G, h = kvh * G + qr % G;
+    const float* src = a.q_stage + (int64_t)(b * mseq + i) * q_dim + h * HD;
+    qx0 = src[qd];
+    qx1 = src[qd + HALF];
+    qcs = a.rope[(int64_t)(L + i) * HALF + qd];
+  }
+  const int p0 = max(c0, L), p1 = min(c0 + C, total), nnew = max(p1 - p0, 0) * HALF;
+  constexpr int NKH = 2;
+  float kx0[NKH], kx1[NKH];
+  float2 kcs[NKH];
+#pragma unroll
+  for (int v = 0; v < NKH; ++v) {
+    const int idx = t + 256 * v;
+    if (idx < nnew) {
+      const int p = p0 + idx / HALF, d = idx % HALF;
+      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
+      kx0[v] = src[d];
+      kx1[v] = src[d + HALF];
+      kcs[v] = a.rope[(int64_t)p * HALF + d];
+    }
+  }
+  // staging: cached keys (new ones below), values (the QKV projection cached the new ones),
+  // zeros past the end; q rotated and rounded as the MFMA kernel does
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int idx = t + 256 * v;
+    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
+    if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
+    else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
+    *(uint4*)(vs + j * KP + d8) = p < total ? vreg[v] : make_uint4(0, 0, 0, 0);
+  }
+  if (qr < RM) {
+    qf[qr][qd] = qr < R ? bf16_to_f32(f32_to_bf16(qx0 * qcs.x - qx1 * qcs.y)) : 0.0f;
+    qf[qr][qd + HALF] = qr < R ? bf16_to_f32(f32_to_bf16(qx1 * qcs.x + qx0 * qcs.y)) : 0.0f;
+  }
+  {
+    auto put = [&](int idx, float x0, float x1, float2 cs) {
+      const int p = p0 + idx / HALF, d = idx % HALF, j = p - c0;
+      const bf16_t lo = f32_to_bf16(x0 * cs.x - x1 * cs.y);
+      const bf16_t hi = f32_to_bf16(x1 * cs.x + x0 * cs.y);
+      ks[j * KP + d] = lo;
+      ks[j * KP + d + HALF] = hi;
+      kc[(int64_t)p * HD + d] = lo;
+      kc[(int64_t)p * HD + d + HALF] = hi;
+    };
+#pragma unroll
+    for (int v = 0; v < NKH; ++v)
+      if (t + 256 * v < nnew) put(t + 256 * v, kx0[v], kx1[v], kcs[v]);
+    for (int idx = t + 256 * NKH; idx < nnew; idx += 256) {
+      const int p = p0 + idx / HALF, d = idx % HALF;
+      const float* src = a.k_stage + (int64_t)(b * mseq + (p - L)) * kv_dim + kvh * HD;
+      put(idx, src[d], src[d + HALF], a.rope[(int64_t)p * HALF + d]);
+    }
+  }
+  __syncthreads();
+
+  // scores of key j for every row
+  const int j = t >> 2, qq = t & 3;
+  float s[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) s[r] = 0.0f;
+#pragma unroll
+  for (int e8 = 0; e8 < QW / 8; ++e8) {
+    const int d0 = qq * QW + e8 * 8;
+    const uint4 kk = *(const uint4*)(ks + j * KP + d0);
+    const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
+    float kf[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kf[2 * e] = __uint_as_float(kw[e] << 16);
+      kf[2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r < R) {
+        const float4 q0 = *(const float4*)(&qf[r][d0]);
+        const float4 q1 = *(const float4*)(&qf[r][d0 + 4]);
+        s[r] += kf[0] * q0.x;
+        s[r] += kf[1] * q0.y;
+        s[r] += kf[2] * q0.z;
+        s[r] += kf[3] * q0.w;
+        s[r] += kf[4] * q1.x;
+        s[r] += kf[5] * q1.y;
+        s[r] += kf[6] * q1.z;
+        s[r] += kf[7] * q1.w;
+      }
+    }
+  }
+  // the quarters added pairwise (all four lanes of a key then hold the same sum), masked and
+  // scaled; the chunk maximum of each row from a butterfly over the wavefront's 16 keys and the
+  // four wavefronts' maxima
+  const int p = c0 + j;
+  float mx[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    mx[r] = -__builtin_inff();
+    if (r < R) {
+      float v = s[r];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      s[r] = p <= L + r / G ? v * a.scale : -__builtin_inff();
+      float m = s[r];
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      mx[r] = m;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) wred[0][wave][r] = mx[r];
+  }
+  __syncthreads();
+  // weights exp(s - max) rounded to bf16 (P of the MFMA kernel), their sums per wavefront
+  float lsum[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    lsum[r] = 0.0f;
+    if (r < R) {
+      const float m = fmaxf(fmaxf(wred[0][0][r], wred[0][1][r]), fmaxf(wred[0][2][r], wred[0][3][r]));
+      const float x = (m == -__builtin_inff() || s[r] == -__builtin_inff()) ? 0.0f : __expf(s[r] - m);
+      const float e = bf16_to_f32(f32_to_bf16(x));
+      if (qq == 0) ps[r][j] = e;
+      float l = qq == 0 ? e : 0.0f;
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
+      lsum[r] = l;
+      mx[r] = m;
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) wred[1][wave][r] = lsum[r];
+  }
+  __syncthreads();
+  // P V: wavefront w -> row w, lane -> dims 2 lane, 2 lane + 1, keys in order
+  const int r = wave;
+  if (r < R) {
+    float o0 = 0.0f, o1 = 0.0f;
+    const int d = 2 * lane;
+#pragma unroll 4
+    for (int jj = 0; jj < C; jj += 4) {
+      const float4 pw = *(const float4*)(&ps[r][jj]);
+      const float pv[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t vv = *(const uint32_t*)(vs + (jj + e) * KP + d);
+        o0 += pv[e] * __uint_as_float(vv << 16);
+        o1 += pv[e] * __uint_as_float(vv & 0xFFFF0000u);
+      }
+    }
+    const int i = r / G, h = kvh * G + r % G;
+    float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
+    *(float2*)(P + d) = make_float2(o0, o1);
+    if (lane == 0) {
+      P[HD] = mx[r];
+      P[HD + 1] = ((wred[1][0][r] + wred[1][1][r]) + wred[1][2][r]) + wred[1][3][r];
+    }
+  }
+}
+
 // Merges the chunks of one (row, head): weights exp(m_c - max) from one wavefront (every
 // chunk statistic loaded at once), then the weighted value sums with the chunks split over
 // 256/head_dim thread groups and added back in a fixed order.  Each thread's first values
@@ -1014,7 +1218,9 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16) {
     const int QT = (R + 15) / 16;
     const size_t lds2 = 2 * ((size_t)QT * 16 * (hd + 8) + (size_t)ATTN_CHUNK * (hd + 8) + (size_t)hd * (ATTN_CHUNK + 8));
-    if (QT <= 2) {
+    if (a.few && hd == 128 && R <= ATTN_FEW_ROWS) {
+      hipLaunchKernelGGL(attn_chunk_few_kernel, g1, dim3(256), 0, st, a);
+    } else if (QT <= 2) {
       if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 2>), g1, dim3(256), lds2, st, a);
       else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 2>), g1, dim3(256), lds2, st, a);
       else hipLaunchKernelGGL((attn_chunk_mfma_kernel<32, 2>), g1, dim3(256), lds2, st, a);

@@ -423,6 +423,17 @@ int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const 
   return SPEC_OK;
 }
 
+// Whether the attention of m runs its chunks on the vector ALUs: the draft model with head_dim
+// 128 and at most two q heads per kv head, so that its draft_step forwards (one or two rows)
+// have at most ATTN_FEW_ROWS query rows per kv head and all take the same path (a row's
+// results then do not depend on the row count; prefill chunks of more rows take the MFMA
+// kernel).
+bool attn_few(spec_ctx* c, const Model& m) {
+  const spec_model_desc& d = m.d;
+  return &m == &c->draft && d.dtype == SPEC_DTYPE_BF16 && d.head_dim == 128 &&
+         2 * (d.n_q_heads / d.n_kv_heads) <= ATTN_FEW_ROWS;
+}
+
 // Whether the forwards of m over M rows run on the weight-streaming projections: bf16,
 // at most 16 rows, reduction lengths in whole stages (normalized inputs: d in {1024, 2048,
 // 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
@@ -476,6 +487,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     at.scale = 1.0f / sqrtf((float)d.head_dim);
     at.part = m.part;
     at.nchunk = m.nchunk;
+    at.few = attn_few(c, m);
     at.out = m.attn;
     LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
     StreamArgs o{};
@@ -570,6 +582,7 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     a.part = m.part;
     a.nchunk = m.nchunk;
     a.out = m.attn;
+    a.few = attn_few(c, m);
     LAUNCH(c, P + PROF_ATTN, launch_attention(dt, a, st));
     GemmArgs o{};
     o.w[0] = w.wo;

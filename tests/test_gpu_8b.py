@@ -66,3 +66,64 @@ def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
             continue
         assert np.array_equal(gi, o.ids), i
         np.testing.assert_allclose(gp, o.probs, atol=4e-2 * float(o.probs.max()))
+
+
+@pytest.mark.parametrize("schedule", ["step", "stream", "forward"])
+@pytest.mark.parametrize("temp", [0.0, 1.0])
+def test_draft_model_first_draft_step(schedule, temp):
+    """The draft model's own path (one and two rows per forward, the vector-ALU attention
+    chunks of the step and stream schedules) at the 0.6B shape, 2 layers, a 1023-entry draft
+    cache: the K draft tokens and truncated q lists of one draft_step against the oracle's draft
+    forwards, each conditioned on the GPU's previous draft."""
+    dshape = synth.SHAPES["qwen0p6b"].with_layers(2)
+    L, K = 1024, 8
+    tw = synth.make_weights(dshape, 0, device="cuda")
+    # a wider weight scale than the workload's 0.02 spreads the logits, so that most greedy
+    # decisions are far from a tie
+    dw = synth.make_weights(dshape, 1, std=0.05, device="cuda")
+    tk, tv = synth.make_kv_prefix(dshape, L, 0, device="cuda")
+    dk, dv = synth.make_kv_prefix(dshape, L - 1, 1, device="cuda")
+    prev, last = (int(x) for x in synth.make_tokens(2, dshape.vocab, 9))
+    eng = runtime.Engine(dshape, tw, dshape, dw, temperature=temp, seed=5, max_ctx=L + 40, max_k=K)
+    eng.set_schedule(schedule)
+    eng.load_prefix(0, 0, tk, tv, L)
+    eng.load_prefix(1, 0, dk, dv, L - 1)
+    eng.set_last(torch.tensor([last], dtype=torch.int32, device="cuda"),
+                 torch.tensor([prev], dtype=torch.int32, device="cuda"))
+    from speculative_decoding_token_amd import binding as B
+    buf = eng.buffers(1, K)
+    with eng._enter():
+        B.draft_step(eng.ctx, 1, K, 0, buf["draft"], buf["q"])
+    torch.cuda.synchronize()
+    drafts = buf["draft"][0].cpu().tolist()
+    qlists = buf["q"].to_lists(K)
+    spec = om.Spec.from_shape(dshape)
+    W = host_weights(dw)
+    kv = om.KVCache(spec, L + K + 2)
+    kv.load_prefix(dk.float().cpu().numpy(), dv.float().cpu().numpy())
+    logits = om.forward_tokens(spec, W, kv, [prev, last])[-1]
+    checked = 0
+    for j in range(K):
+        o = osm.truncate(logits, temp, 20, 0.95)
+        gi, gp = qlists[j]
+        if temp == 0.0:
+            if o.gap_logit > 0.05:
+                assert drafts[j] == int(o.ids[0]), j
+                checked += 1
+        elif o.margin > 4e-2 and o.gap_logit > 0.05:
+            assert np.array_equal(gi, o.ids), j
+            np.testing.assert_allclose(gp, o.probs, atol=4e-2 * float(o.probs.max()))
+            checked += 1
+        else:
+            # the kept set is decided within the observed error: the lists share all but a few
+            # boundary ids, and the shared ids carry the same probabilities
+            common, ig, io = np.intersect1d(gi, o.ids, return_indices=True)
+            assert len(common) >= len(o.ids) - 3, j
+            a = gp[ig].astype(np.float64) / gp[ig].sum()
+            b = o.probs[io].astype(np.float64) / o.probs[io].sum()
+            np.testing.assert_allclose(a, b, atol=4e-2 * float(b.max()))
+            checked += 1
+        if j + 1 < K:
+            logits = om.forward_tokens(spec, W, kv, [drafts[j]])[-1]
+    print(f"draft step {schedule} T={temp}: {checked} of {K} decisions compared")
+    assert checked >= K // 2, "too few draft decisions far enough from a tie to compare"
