@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-graphs", action="store_true", help="plain launches instead of graph replays")
     ap.add_argument("--schedule", default=None, choices=["step", "stream", "forward"],
                     help="forward schedule of the bf16 models (default: the library's)")
+    ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -68,7 +69,7 @@ DOMINANT = {
     "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
-               "sources": ["stream_core.h", "stream.hip"], "traffic": 201951838, "sha256": "c695e44d9f9e0056"},
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 201972291, "sha256": "e5217649bee4cbfb"},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",
@@ -180,9 +181,11 @@ def main():
     tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
     start = synth.make_tokens(2, tshape.vocab, 0, tag="start")
+    SWEEP_K, SWEEP_REPS = (1, 2, 4, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
+    max_k = max(K, max(SWEEP_K))
     n_cycles = args.warmup + args.steps + args.profile_steps + 2
-    max_ctx = L + n_cycles * (K + 1) + 8
-    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=K)
+    max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + 8
+    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=max_k)
 
     def reset():
         eng.load_prefix(0, 0, tk, tv, L)
@@ -219,6 +222,19 @@ def main():
     verify_avg_ms = sum(verify_ms) / len(verify_ms)
     vbytes = verify_bytes(tshape, K, L + args.warmup + 1)
     verify_gbs = vbytes / (verify_avg_ms * 1e-3) / 1e9
+
+    # verify latency against K (the pass streams the same weights at any K up to 16 rows)
+    verify_vs_k = {}
+    if not args.no_k_sweep:
+        for k in SWEEP_K:
+            ms = []
+            for i in range(SWEEP_REPS):
+                eng.cycle(1, k, rnd, events=ev)
+                rnd += 1
+                if i > 0:  # the first cycle at a new K captures its graphs
+                    ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
+            vb = verify_bytes(tshape, k, L)
+            verify_vs_k[str(k)] = {"ms": sum(ms) / len(ms), "GBps": vb / (sum(ms) / len(ms) * 1e-3) / 1e9}
 
     # per-kernel durations with events around every launch (separate steps); the dominant
     # kernel goes out REPS times back to back between its events (other layers' weights first),
@@ -266,6 +282,7 @@ def main():
                    "global_batch": 1, "seq_len": L, "k": K, "schedule": sched, "parallelism": "none (1 GPU)"},
         "acceptance": accepted / (K * args.steps),
         "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
+        "verify_vs_k": verify_vs_k,
         "roofline": {"bound": "hbm", "kernel": dom["kernel"],
                      "achieved": dom_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
                      "traffic": dominant_traffic(sched), "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
