@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--k", type=int, default=4)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="sequences speculated together (each its own cache; default 1, the headline config)")
     ap.add_argument("--ctx", type=int, default=2048)
     ap.add_argument("--sampled", action="store_true", help="temperature 1, top_k 20, top_p 0.95")
     ap.add_argument("--profile-steps", type=int, default=3)
@@ -50,14 +52,15 @@ def parse():
     return ap.parse_args()
 
 
-def verify_bytes(shape, k, L):
-    """Algorithmic HBM bytes of one verify: weights once, cache read and written, logits."""
+def verify_bytes(shape, k, L, batch=1):
+    """Algorithmic HBM bytes of one verify: weights once, every sequence's cache read and
+    written, logits."""
     M = k + 1
     w = shape.streamed_params() * 2
-    kv_read = 2 * shape.n_layers * (L + M) * shape.kv_dim * 2
-    kv_write = 2 * shape.n_layers * M * shape.kv_dim * 2
-    logits = M * shape.vocab * 4
-    emb = M * shape.d_model * 2
+    kv_read = batch * 2 * shape.n_layers * (L + M) * shape.kv_dim * 2
+    kv_write = batch * 2 * shape.n_layers * M * shape.kv_dim * 2
+    logits = batch * M * shape.vocab * 4
+    emb = batch * M * shape.d_model * 2
     return w + kv_read + kv_write + logits + emb
 
 
@@ -180,18 +183,26 @@ def main():
     dw = synth.make_weights(dshape, 0, device="cuda")
     tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
-    start = synth.make_tokens(2, tshape.vocab, 0, tag="start")
     SWEEP_K, SWEEP_REPS = (1, 2, 4, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
     max_k = max(K, max(SWEEP_K))
     n_cycles = args.warmup + args.steps + args.profile_steps + 2
     max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + 8
-    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=max_k)
+    Bn = args.batch
+    if Bn > 1:
+        if Bn * (K + 1) > 16:
+            print("bench.py: batch x (K + 1) rows must stay within 16", file=sys.stderr)
+            sys.exit(2)
+        max_k = K  # no K sweep for a batch
+    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=max_k,
+                         max_batch=Bn)
+    starts = [synth.make_tokens(2, tshape.vocab, b, tag="start") for b in range(Bn)]
 
     def reset():
-        eng.load_prefix(0, 0, tk, tv, L)
-        eng.load_prefix(1, 0, dk, dv, L - 1)
-        eng.set_last(torch.tensor([int(start[1])], dtype=torch.int32, device="cuda"),
-                     torch.tensor([int(start[0])], dtype=torch.int32, device="cuda"))
+        for b in range(Bn):
+            eng.load_prefix(0, b, tk, tv, L)
+            eng.load_prefix(1, b, dk, dv, L - 1)
+        eng.set_last(torch.tensor([int(st[1]) for st in starts], dtype=torch.int32, device="cuda"),
+                     torch.tensor([int(st[0]) for st in starts], dtype=torch.int32, device="cuda"))
 
     if args.no_graphs:
         eng.use_graphs(False)
@@ -204,28 +215,28 @@ def main():
     ev = {}
     rnd = 0
     for _ in range(args.warmup):
-        eng.cycle(1, K, rnd)
+        eng.cycle(Bn, K, rnd)
         rnd += 1
     torch.cuda.synchronize()
     emitted = accepted = 0
     verify_ms = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        c = eng.cycle(1, K, rnd, events=ev)
-        emitted += len(c.tokens[0])
-        accepted += c.n[0]
+        c = eng.cycle(Bn, K, rnd, events=ev)
+        emitted += sum(len(t) for t in c.tokens)
+        accepted += sum(c.n)
         verify_ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
         rnd += 1
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     tok_s = emitted / elapsed
     verify_avg_ms = sum(verify_ms) / len(verify_ms)
-    vbytes = verify_bytes(tshape, K, L + args.warmup + 1)
+    vbytes = verify_bytes(tshape, K, L + args.warmup + 1, Bn)
     verify_gbs = vbytes / (verify_avg_ms * 1e-3) / 1e9
 
     # verify latency against K (the pass streams the same weights at any K up to 16 rows)
     verify_vs_k = {}
-    if not args.no_k_sweep:
+    if not args.no_k_sweep and Bn == 1:
         for k in SWEEP_K:
             ms = []
             for i in range(SWEEP_REPS):
@@ -244,7 +255,7 @@ def main():
     if dom["slot"] != "target.forward":
         eng.profile_repeat(dom["slot"], REPS)
     for _ in range(args.profile_steps):
-        eng.cycle(1, K, rnd)
+        eng.cycle(Bn, K, rnd)
         rnd += 1
     prof = eng.profile_read() if args.profile_steps else {}
     if dom["slot"] != "target.forward":
@@ -253,12 +264,12 @@ def main():
     dprof = prof.get(dom["slot"], {"ms": float("nan"), "launches": 1})
     dom_ms = dprof["ms"] / dprof["launches"]
     # the one-launch forward moves the whole verify's bytes (weights, cache, logits)
-    dom_bytes = gate_up_bytes(tshape, K + 1) if dom["slot"] == "target.gate_up" else vbytes
+    dom_bytes = gate_up_bytes(tshape, Bn * (K + 1)) if dom["slot"] == "target.gate_up" else vbytes
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     # teacher-forced upper bound: drafts = the target's own greedy continuation
     teacher = None
-    if not args.no_teacher and not args.sampled:
+    if not args.no_teacher and not args.sampled and Bn == 1:
         reset()
         n_tf = args.steps * (K + 1)
         plain, _ = eng.generate(n_tf + K + 1, 0)
@@ -276,11 +287,11 @@ def main():
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"8B-shape bf16 target verify K={K} + 0.6B-shape draft, batch 1, "
+        "config": {"workload": f"8B-shape bf16 target verify K={K} + 0.6B-shape draft, batch {Bn}, "
                                f"KV context {L}, {'sampled T=1 top_k 20 top_p 0.95' if args.sampled else 'greedy'}, "
                                f"random N(0,0.02) weights" + (f", {tshape.n_layers} layers" if args.layers else ""),
-                   "global_batch": 1, "seq_len": L, "k": K, "schedule": sched, "parallelism": "none (1 GPU)"},
-        "acceptance": accepted / (K * args.steps),
+                   "global_batch": Bn, "seq_len": L, "k": K, "schedule": sched, "parallelism": "none (1 GPU)"},
+        "acceptance": accepted / (K * args.steps * Bn),
         "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
         "verify_vs_k": verify_vs_k,
         "roofline": {"bound": "hbm", "kernel": dom["kernel"],
@@ -295,7 +306,7 @@ def main():
         "teacher_forced": teacher,
         "setup_s": setup_s,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and Bn == 1:
         out["cpu_baseline"] = cpu_baseline(tshape, dshape, tw, dw, K)
     print(json.dumps(out), flush=True)
 

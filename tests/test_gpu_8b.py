@@ -127,3 +127,35 @@ def test_draft_model_first_draft_step(schedule, temp):
             logits = om.forward_tokens(spec, W, kv, [drafts[j]])[-1]
     print(f"draft step {schedule} T={temp}: {checked} of {K} decisions compared")
     assert checked >= K // 2, "too few draft decisions far enough from a tie to compare"
+
+
+@pytest.mark.parametrize("schedule", ["step", "stream", "forward"])
+def test_full_shape_batched_verify_parity(schedule):
+    """Batched verify at the 8B shape (2 layers): three sequences with different cache lengths
+    (2048, 1990, 1500 positions) and their own drafts in one pass of 3 x (K+1) = 15 rows; every
+    row against the oracle's forward of its own sequence."""
+    shape = synth.SHAPES["qwen8b"].with_layers(2)
+    K, lens = 4, [2048, 1990, 1500]
+    Bn = len(lens)
+    w = synth.make_weights(shape, 0, device="cuda")
+    eng = runtime.Engine(shape, w, temperature=0.0, max_batch=Bn, max_ctx=max(lens) + 40, max_k=K)
+    eng.set_schedule(schedule)
+    prefixes = []
+    for b, L in enumerate(lens):
+        k, v = synth.make_kv_prefix(shape, L, 20 + b, device="cuda")
+        eng.load_prefix(0, b, k, v, L)
+        prefixes.append((k.float().cpu().numpy(), v.float().cpu().numpy()))
+    t0 = [int(x) for x in synth.make_tokens(Bn, shape.vocab, 17)]
+    eng.set_last(torch.tensor(t0, dtype=torch.int32, device="cuda"))
+    drafts = [[int(x) for x in synth.make_tokens(K, shape.vocab, 30 + b)] for b in range(Bn)]
+    c = eng.cycle(Bn, K, 0, drafts=torch.tensor(drafts, dtype=torch.int32, device="cuda"), keep=True)
+    logits = c.logits.cpu().numpy()
+    assert eng.stats()["sync_timeouts"] == 0
+    spec = om.Spec.from_shape(shape)
+    W = host_weights(w)
+    for b, L in enumerate(lens):
+        kv = om.KVCache(spec, L + K + 2)
+        kv.load_prefix(*prefixes[b])
+        ref = om.forward_tokens(spec, W, kv, [t0[b]] + drafts[b])
+        err = assert_rows_close(logits[b], ref, RTOL_BF16)
+        print(f"batched verify {schedule} seq {b} L={L}: worst row error {err:.2e}")
