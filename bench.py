@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--schedule", default=None, choices=["step", "stream", "forward"],
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
+    ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -283,6 +284,41 @@ def main():
                    "all_accepted": all(c.n[0] == K for c in cyc[:-1]),
                    "matches_plain": toks[0] == plain[0][:n_tf]}
 
+    # adaptive draft length (host controller spec_depth: +1 after a clean cycle, -1 after a
+    # rejection, K in [1, 8]) on the random draft, and with the target's own continuation as
+    # drafts (every cycle clean)
+    adaptive = None
+    if not args.no_adaptive and not args.sampled and Bn == 1:
+        from speculative_decoding_token_amd import binding as B
+        adaptive = {"rule": "K += 1 after a clean cycle, K -= 1 after a rejection, K in [1, 8], start K",
+                    "k_max": max_k}
+        n_ad = args.steps * (K + 1)
+        reset()
+        depth = B.Depth(K, 1, max_k, 1, 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, cyc = eng.generate(n_ad, K, rnd0=rnd, gate=depth)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        rnd += len(cyc)
+        ks = [len(c.drafts[0]) for c in cyc]
+        adaptive["draft_model"] = {"tok_s": n_ad / el, "cycles": len(cyc), "k_last": ks[-1],
+                                   "k_mean": sum(ks) / len(ks)}
+        if teacher is not None:
+            reset()
+            plain, _ = eng.generate(n_ad + max_k + 1, 0)
+            reset()
+            depth = B.Depth(K, 1, max_k, 1, 1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            toks, cyc = eng.generate(n_ad, K, rnd0=rnd, teacher=plain[0], gate=depth)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            rnd += len(cyc)
+            ks = [len(c.drafts[0]) for c in cyc]
+            adaptive["teacher_forced"] = {"tok_s": n_ad / el, "cycles": len(cyc), "k_last": ks[-1],
+                                          "k_mean": sum(ks) / len(ks), "matches_plain": toks[0] == plain[0][:n_ad]}
+
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
@@ -304,6 +340,7 @@ def main():
         "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
                     for k, v in prof.items()},
         "teacher_forced": teacher,
+        "adaptive_depth": adaptive,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline and Bn == 1:

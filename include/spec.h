@@ -288,6 +288,25 @@ int32_t spec_gate_choose(const spec_gate* g /*host*/);
 /* Folds one step's accepted / attempted drafts into alpha (nothing when attempted = 0). */
 int spec_gate_update(spec_gate* g /*host*/, int32_t accepted, int32_t attempted);
 
+/* ---- adaptive draft length (host) ----------------------------------------------------
+ * "Speculative decoding on Apple Silicon" (OptiQ docs), section "About depth": the heuristic
+ * that raises K after a cycle whose drafts were all accepted and lowers it after a cycle with
+ * a rejection.  The pages give no step sizes: K moves up by `up` and down by `down` drafts,
+ * within [k_min, k_max]; a cycle that drafted nothing leaves K unchanged.  Host-only state,
+ * no device work: the caller passes spec_depth_choose() as draft_step's / verify_step's k and
+ * reports each cycle's accepted count. */
+typedef struct spec_depth {
+  int32_t k, k_min, k_max, up, down;
+} spec_depth;
+
+/* SPEC_E_INVAL unless 0 <= k_min <= k0 <= k_max <= SPEC_MAX_K and up, down >= 0. */
+int spec_depth_init(spec_depth* d /*host*/, int32_t k0, int32_t k_min, int32_t k_max, int32_t up,
+                    int32_t down);
+/* The K of the next cycle (negative: invalid d). */
+int32_t spec_depth_choose(const spec_depth* d /*host*/);
+/* accepted of attempted drafts in the last cycle; SPEC_E_INVAL unless 0 <= accepted <= attempted. */
+int spec_depth_update(spec_depth* d /*host*/, int32_t accepted, int32_t attempted);
+
 /* ---- tracing ------------------------------------------------------------------------- */
 
 /* Profiling slots: slot = kernel class + 16 * model (model 0 = target, 1 = draft); classes

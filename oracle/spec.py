@@ -139,6 +139,31 @@ class MTPDraft:
         self.kv.trim(min(self.kv.length, new_len))
 
 
+class AdaptiveDepth:
+    """Adaptive draft length.  "Speculative decoding on Apple Silicon" (OptiQ docs), section
+    "About depth" (and "Qwen3.5 and Qwen3.6 MTP head reaches 1.4x...", section "Why K=1 wins
+    on Metal"): a heuristic that raises K after a cycle whose drafts were all accepted and
+    lowers it after a cycle with a rejection.  The pages give no step sizes; the reading takes
+    them as parameters (default one draft either way) and keeps K within [k_min, k_max].  A
+    cycle that drafted nothing leaves K as it is."""
+
+    def __init__(self, k0: int, k_min: int = 1, k_max: int = 8, up: int = 1, down: int = 1):
+        assert 0 <= k_min <= k0 <= k_max and up >= 0 and down >= 0
+        self.k, self.k_min, self.k_max, self.up, self.down = k0, k_min, k_max, up, down
+
+    def choose(self) -> int:
+        return self.k
+
+    def update(self, accepted: int, attempted: int) -> None:
+        assert 0 <= accepted <= attempted
+        if attempted == 0:
+            return
+        if accepted == attempted:
+            self.k = min(self.k_max, self.k + self.up)
+        else:
+            self.k = max(self.k_min, self.k - self.down)
+
+
 def one_hot(tok: int) -> TokenList:
     return TokenList(np.array([tok], dtype=np.int64), np.array([1.0], dtype=np.float32))
 
@@ -146,12 +171,13 @@ def one_hot(tok: int) -> TokenList:
 def run(target_spec: Spec, target_W: Dict, tkv: KVCache, t0: int, hist: List[int], n_new: int,
         K: int, sampler: Sampler, seed: int, draft=None, ngram: Optional[Dict] = None,
         hidden: Optional[Dict[int, np.ndarray]] = None, seq: int = 0,
-        teacher: Optional[Sequence[int]] = None) -> GenResult:
+        teacher: Optional[Sequence[int]] = None, depth: Optional[AdaptiveDepth] = None) -> GenResult:
     """Generate ``n_new`` tokens.  ``hist`` holds every token at positions < tkv.length plus
     t0 at position tkv.length.  ``draft`` is a DraftModel / MTPDraft or None; ``ngram`` a dict
     {n_min, max_match, gate: Gate|None}; ``teacher`` replaces the drafts by a known
     continuation: teacher[i] is the i-th generated token, so each cycle drafts the K entries
-    after the tokens emitted so far."""
+    after the tokens emitted so far.  ``depth`` (an AdaptiveDepth) picks each cycle's K for a
+    draft model or teacher and is told every cycle's outcome."""
     assert len(hist) == tkv.length + 1 and hist[-1] == t0
     out: List[int] = []
     cycles: List[CycleLog] = []
@@ -159,7 +185,7 @@ def run(target_spec: Spec, target_W: Dict, tkv: KVCache, t0: int, hist: List[int
     rnd = 0
     while len(out) < n_new:
         L = tkv.length
-        k = K
+        k = K = depth.choose() if depth is not None else K
         if ngram is not None:
             gate = ngram.get("gate")
             k = gate.choose() if gate is not None else K
@@ -205,6 +231,8 @@ def run(target_spec: Spec, target_W: Dict, tkv: KVCache, t0: int, hist: List[int
         acc += n
         if ngram is not None and ngram.get("gate") is not None:
             ngram["gate"].update(n, k)
+        if depth is not None:
+            depth.update(n, k)
         cycles.append(CycleLog(L, list(drafts), n, list(res.tokens), res.margin, gaps,
                                [ql.gap_logit for ql in qs], pm, [ql.margin for ql in qs]))
         out.extend(res.tokens)

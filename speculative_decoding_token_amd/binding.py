@@ -36,6 +36,7 @@ EXPORTED = [
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
     "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
+    "spec_depth_init", "spec_depth_choose", "spec_depth_update",
 ]
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
@@ -91,6 +92,11 @@ class spec_gate(C.Structure):
                 ("draft_cost", C.c_double), ("cost", C.c_double * (MAX_K + 1))]
 
 
+class spec_depth(C.Structure):
+    _fields_ = [("k", C.c_int32), ("k_min", C.c_int32), ("k_max", C.c_int32), ("up", C.c_int32),
+                ("down", C.c_int32)]
+
+
 class spec_stats(C.Structure):
     _fields_ = [("cycles", C.c_int64), ("drafts_attempted", C.c_int64),
                 ("drafts_accepted", C.c_int64), ("emitted", C.c_int64), ("sync_timeouts", C.c_int64)]
@@ -141,6 +147,9 @@ def lib(path: str = LIB_PATH):
         "spec_gate_init": ([C.POINTER(spec_gate), I32, C.POINTER(C.c_double), C.c_double, I32], C.c_int),
         "spec_gate_choose": ([C.POINTER(spec_gate)], C.c_int32),
         "spec_gate_update": ([C.POINTER(spec_gate), I32, I32], C.c_int),
+        "spec_depth_init": ([C.POINTER(spec_depth), I32, I32, I32, I32, I32], C.c_int),
+        "spec_depth_choose": ([C.POINTER(spec_depth)], C.c_int32),
+        "spec_depth_update": ([C.POINTER(spec_depth), I32, I32], C.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -378,6 +387,27 @@ def spec_set_schedule(ctx: int, schedule: str) -> None:
 
 def spec_use_graphs(ctx: int, enable: bool) -> None:
     _check(lib().spec_use_graphs(ctx, int(enable)), ctx)
+
+
+class Depth:
+    """Adaptive draft length of the library (host code): spec_depth_* on a spec_depth."""
+
+    def __init__(self, k0: int, k_min: int = 1, k_max: int = 8, up: int = 1, down: int = 1):
+        self.d = spec_depth()
+        rc = lib().spec_depth_init(C.byref(self.d), k0, k_min, k_max, up, down)
+        if rc:
+            raise SpecError(rc, "spec_depth_init")
+
+    def choose(self) -> int:
+        k = lib().spec_depth_choose(C.byref(self.d))
+        if k < 0:
+            raise SpecError(k, "spec_depth_choose")
+        return k
+
+    def update(self, accepted: int, attempted: int) -> None:
+        rc = lib().spec_depth_update(C.byref(self.d), accepted, attempted)
+        if rc:
+            raise SpecError(rc, "spec_depth_update")
 
 
 class Gate:

@@ -1393,6 +1393,26 @@ int spec_gate_update(spec_gate* g, int32_t accepted, int32_t attempted) {
   return SPEC_OK;
 }
 
+// ---------------------------------------------------------------- adaptive depth (host)
+int spec_depth_init(spec_depth* d, int32_t k0, int32_t k_min, int32_t k_max, int32_t up, int32_t down) {
+  if (!d || k_min < 0 || k0 < k_min || k_max < k0 || k_max > SPEC_MAX_K || up < 0 || down < 0) return SPEC_E_INVAL;
+  d->k = k0;
+  d->k_min = k_min;
+  d->k_max = k_max;
+  d->up = up;
+  d->down = down;
+  return SPEC_OK;
+}
+
+int32_t spec_depth_choose(const spec_depth* d) { return d ? d->k : SPEC_E_INVAL; }
+
+int spec_depth_update(spec_depth* d, int32_t accepted, int32_t attempted) {
+  if (!d || accepted < 0 || accepted > attempted) return SPEC_E_INVAL;
+  if (attempted == 0) return SPEC_OK;
+  d->k = accepted == attempted ? std::min(d->k_max, d->k + d->up) : std::max(d->k_min, d->k - d->down);
+  return SPEC_OK;
+}
+
 // ---------------------------------------------------------------- stateless
 int spec_truncate_scratch_size(int32_t rows, int32_t vocab, size_t* bytes) {
   if (!bytes || rows < 0 || vocab < 1) return SPEC_E_INVAL;

@@ -192,7 +192,8 @@ class Engine:
     def generate(self, n_new: int, k: int, batch: int = 1, rnd0: int = 0, keep: bool = False,
                  teacher: Optional[Sequence[int]] = None, gate: Optional["B.Gate"] = None):
         """Run cycles until every sequence emitted n_new tokens (batch 1 for ``teacher`` and
-        ``gate``).  ``gate`` (the n-gram acceptance gate) picks each cycle's k.
+        ``gate``).  ``gate`` (the n-gram acceptance gate B.Gate, or the adaptive draft length
+        B.Depth) picks each cycle's k and is told its outcome.
         Returns (tokens [batch][n_new], cycles)."""
         out = [[] for _ in range(batch)]
         cycles = []

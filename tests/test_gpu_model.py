@@ -9,6 +9,7 @@ import torch
 from oracle import model as om
 from oracle import spec as osp
 from oracle import sampling as osm
+from speculative_decoding_token_amd import binding as B
 from speculative_decoding_token_amd import runtime, synth
 from tests.helpers import RTOL_BF16, RTOL_F32, assert_rows_close
 
@@ -287,3 +288,41 @@ def test_tiny_batched_generation_parity(temperature):
         agree = cmp_streams(toks[b], ref, temperature == 0.0, 2e-4 * 2, 1e-4)
         assert agree >= N // 2, (b, agree)
     print(f"batched T={temperature}: accepted per sequence {accepted}")
+
+
+@pytest.mark.parametrize("temperature,same", [(0.0, False), (1.0, False), (0.0, True)])
+def test_tiny_adaptive_depth_generation_parity(temperature, same):
+    """Adaptive draft length (spec_depth, the library's host controller) driving draft_step /
+    verify_step: the per-cycle K and the token stream equal the oracle's run with the same rule,
+    up to a near-tie.  With the draft equal to the target every cycle is clean and K climbs to
+    its maximum; with the random draft it falls to its minimum."""
+    K0, N, KMIN, KMAX = 2, 48, 1, 6
+    eng, tw, dw = tiny_engine(temperature, draft_is_target=same)
+    p, pt = prompt_tensor()
+    eng.prefill(pt)
+    toks, cycles = eng.generate(N, K0, gate=B.Depth(K0, KMIN, KMAX, 1, 1))
+    dshape = TS if same else DS
+    tspec, dspec = om.Spec.from_shape(TS), om.Spec.from_shape(dshape)
+    tW, dW = synth.weights_to_numpy(tw), synth.weights_to_numpy(dw)
+    tkv = om.KVCache(tspec, 160)
+    osp.prefill(tspec, tW, tkv, [int(x) for x in p[:-1]])
+    d = osp.DraftModel(dspec, dW, 160)
+    osp.prefill(dspec, dW, d.kv, [int(x) for x in p[:-1]])
+    ref = osp.run(tspec, tW, tkv, int(p[-1]), [int(x) for x in p], N, K0, osp.Sampler(temperature, 20, 0.95),
+                  1234, draft=d, depth=osp.AdaptiveDepth(K0, KMIN, KMAX, 1, 1))
+    agree = cmp_streams(toks[0], ref, temperature == 0.0, 2e-4 * 2, 1e-4)
+    assert agree >= N // 2, agree
+    # the K of every cycle whose tokens lie before the first divergence
+    ks_gpu = [len(c.drafts[0]) for c in cycles]
+    ks_ref = [len(c.drafts) for c in ref.cycles]
+    done = 0
+    for i, c in enumerate(ref.cycles):
+        if done + len(c.tokens) > agree:
+            break
+        assert ks_gpu[i] == ks_ref[i], i
+        done += len(c.tokens)
+    print(f"adaptive depth T={temperature} same={same}: K per cycle {ks_gpu[:12]}")
+    if same:
+        assert max(ks_gpu) == KMAX
+    elif temperature == 0.0:
+        assert ks_gpu[-1] == KMIN
