@@ -136,6 +136,56 @@ def make_weights(shape: ModelShape, seed: int = 0, device: str = "cpu", tag: Opt
     return w
 
 
+# fp8 weights are drawn as such: each weight is an E4M3 code times a per-row float32 scale.
+# Codes are N(0, 1) values clipped to +-6.5, times FP8_UNIT, rounded to E4M3 by torch (so
+# magnitudes reach 416 of the format's 448 and the subnormal codes occur); each row's scale is
+# std / FP8_UNIT times U(0.75, 1.25), so rows differ and a weight is about N(0, std^2).
+FP8_UNIT = 64.0
+PROJ_TENSORS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def _fp8_codes(shape, s: int, device: str) -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(s)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    x.clamp_(-6.5, 6.5).mul_(FP8_UNIT)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _row_scales(rows: int, std: float, s: int, device: str) -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(s)
+    u = torch.rand((rows,), generator=g, device=device, dtype=torch.float32)
+    return (u * 0.5 + 0.75) * (std / FP8_UNIT)
+
+
+def make_weights_fp8(shape: ModelShape, seed: int = 0, device: str = "cpu", tag: Optional[str] = None,
+                     std: float = 0.02) -> Dict[str, object]:
+    """Like make_weights for a bf16 shape, with the seven projections of every layer and the
+    LM head (untied) as uint8 E4M3 code tensors [out, in] plus "<name>_scale" float32 [out]
+    row scales ("lm_head_scale" for the head).  Embedding and norm gains stay bf16."""
+    if shape.dtype != "bf16" or shape.tied or shape.mtp:
+        raise ValueError("fp8 weights: bf16 shapes with an untied LM head and no MTP layer")
+    tag = (tag or shape.name) + ":fp8"
+    V, d = shape.vocab, shape.d_model
+    layers = []
+    for l in range(shape.n_layers):
+        lw = {}
+        for name, shp in layer_shapes(shape).items():
+            if name.endswith("norm"):
+                lw[name] = torch.ones(shp, device=device, dtype=torch.bfloat16)
+            else:
+                lw[name] = _fp8_codes(shp, tensor_seed(seed, tag, l, name), device)
+                lw[name + "_scale"] = _row_scales(shp[0], std, tensor_seed(seed, tag, l, name + "_scale"), device)
+        layers.append(lw)
+    return {
+        "embed": _normal((V, d), std, tensor_seed(seed, tag, -1, "embed"), device, torch.bfloat16),
+        "lm_head": _fp8_codes((V, d), tensor_seed(seed, tag, -1, "lm_head"), device),
+        "lm_head_scale": _row_scales(V, std, tensor_seed(seed, tag, -1, "lm_head_scale"), device),
+        "final_norm": torch.ones((d,), device=device, dtype=torch.bfloat16),
+        "layers": layers,
+        "mtp": None,
+    }
+
+
 def make_mtp(shape: ModelShape, seed: int, device: str, tag: str, std: float = 0.02):
     """One extra decoder layer plus its input norms and the [d, 2d] input projection."""
     dt = _torch_dtype(shape.dtype)

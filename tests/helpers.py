@@ -34,3 +34,17 @@ def lists_equal(g_ids, g_p, o, prob_rtol):
     if len(g_ids) != len(o.ids) or not np.array_equal(np.asarray(g_ids), o.ids):
         return False
     return bool(np.all(np.abs(np.asarray(g_p, np.float64) - o.probs.astype(np.float64)) <= prob_rtol))
+
+
+def host_arrays(w):
+    """A weight dict of torch tensors (any device) as numpy: uint8 fp8 code tensors stay
+    uint8, every other tensor becomes float32 values; nested layer dicts are converted too."""
+    def conv(v):
+        if v is None:
+            return None
+        if v.dtype.is_floating_point:
+            return v.float().cpu().numpy()
+        return v.cpu().numpy()
+    out = {k: conv(v) for k, v in w.items() if k not in ("layers", "mtp")}
+    out["layers"] = [{k: conv(v) for k, v in lw.items()} for lw in w["layers"]]
+    return out
