@@ -13,6 +13,11 @@ kernel (the gate/up projection + SwiGLU of the target; the forward kernel when t
 runs as one launch), a teacher-forced upper bound
 (drafts = the target's own greedy continuation, every draft accepted), and the CPU
 oracle timed on a bounded sample of the same cycle.
+
+--weights fp8 runs the same cycle with the target's projections and LM head stored as OCP
+E4M3 codes with a float32 scale per output row (one byte per weight instead of two); the
+verify's bytes and the dominant kernel's bytes are then counted at that size, and the CPU
+baseline is left out.
 """
 from __future__ import annotations
 
@@ -48,16 +53,27 @@ def parse():
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="target projection weights: bf16, or OCP E4M3 codes with a float32 scale per row")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
 
 
-def verify_bytes(shape, k, L, batch=1):
+def weight_bytes(shape, fp8=False):
+    """Streamed weight bytes of one forward: bf16, or one byte per weight plus a float32
+    scale per output row."""
+    if not fp8:
+        return shape.streamed_params() * 2
+    rows = shape.n_layers * (shape.q_dim + 2 * shape.kv_dim + 2 * shape.d_model + 2 * shape.d_ffn) + shape.vocab
+    return shape.streamed_params() + 4 * rows
+
+
+def verify_bytes(shape, k, L, batch=1, fp8=False):
     """Algorithmic HBM bytes of one verify: weights once, every sequence's cache read and
     written, logits."""
     M = k + 1
-    w = shape.streamed_params() * 2
+    w = weight_bytes(shape, fp8)
     kv_read = batch * 2 * shape.n_layers * (L + M) * shape.kv_dim * 2
     kv_write = batch * 2 * shape.n_layers * M * shape.kv_dim * 2
     logits = batch * M * shape.vocab * 4
@@ -74,6 +90,10 @@ DOMINANT = {
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
                "sources": ["stream_core.h", "stream.hip"], "traffic": 201972291, "sha256": "e5217649bee4cbfb"},
+    "stream_fp8": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 4, 1> (target gate/up + SwiGLU over E4M3 weights "
+                             "with row scales, streamed through an LDS ring, one workgroup per CU)",
+                   "slot": "target.gate_up",
+                   "sources": ["stream_core.h", "stream.hip"], "traffic": None, "sha256": None},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",
@@ -95,14 +115,15 @@ def sources_sha(names):
     return h.hexdigest()[:16]
 
 
-def dominant_traffic(sched):
-    d = DOMINANT[sched]
+def dominant_traffic(key):
+    d = DOMINANT[key]
     return d["traffic"] if d["sha256"] and sources_sha(d["sources"]) == d["sha256"] else None
 
 
-def gate_up_bytes(shape, M):
+def gate_up_bytes(shape, M, fp8=False):
     d, f = shape.d_model, shape.d_ffn
-    return 2 * f * d * 2 + M * d * 2 + M * f * 2
+    w = 2 * f * d + 2 * f * 4 if fp8 else 2 * f * d * 2
+    return w + M * d * 2 + M * f * 2
 
 
 def cpu_baseline(tshape, dshape, tw, dw, K, t_layers=3, d_layers=4):
@@ -180,7 +201,8 @@ def main():
     L = args.ctx
     temp = 1.0 if args.sampled else 0.0
     t_setup = time.perf_counter()
-    tw = synth.make_weights(tshape, 0, device="cuda")
+    fp8 = args.weights == "fp8"
+    tw = synth.make_weights_fp8(tshape, 0, device="cuda") if fp8 else synth.make_weights(tshape, 0, device="cuda")
     dw = synth.make_weights(dshape, 0, device="cuda")
     tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
@@ -232,7 +254,7 @@ def main():
     elapsed = time.perf_counter() - t0
     tok_s = emitted / elapsed
     verify_avg_ms = sum(verify_ms) / len(verify_ms)
-    vbytes = verify_bytes(tshape, K, L + args.warmup + 1, Bn)
+    vbytes = verify_bytes(tshape, K, L + args.warmup + 1, Bn, fp8)
     verify_gbs = vbytes / (verify_avg_ms * 1e-3) / 1e9
 
     # verify latency against K (the pass streams the same weights at any K up to 16 rows)
@@ -245,13 +267,14 @@ def main():
                 rnd += 1
                 if i > 0:  # the first cycle at a new K captures its graphs
                     ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
-            vb = verify_bytes(tshape, k, L)
+            vb = verify_bytes(tshape, k, L, 1, fp8)
             verify_vs_k[str(k)] = {"ms": sum(ms) / len(ms), "GBps": vb / (sum(ms) / len(ms) * 1e-3) / 1e9}
 
     # per-kernel durations with events around every launch (separate steps); the dominant
     # kernel goes out REPS times back to back between its events (other layers' weights first),
     # so its average carries one dispatch delay per REPS launches
-    dom = DOMINANT[sched]
+    dom_key = "stream_fp8" if fp8 else sched  # fp8 weights run the streamed projections always
+    dom = DOMINANT[dom_key]
     eng.profile(True)
     if dom["slot"] != "target.forward":
         eng.profile_repeat(dom["slot"], REPS)
@@ -265,7 +288,7 @@ def main():
     dprof = prof.get(dom["slot"], {"ms": float("nan"), "launches": 1})
     dom_ms = dprof["ms"] / dprof["launches"]
     # the one-launch forward moves the whole verify's bytes (weights, cache, logits)
-    dom_bytes = gate_up_bytes(tshape, Bn * (K + 1)) if dom["slot"] == "target.gate_up" else vbytes
+    dom_bytes = gate_up_bytes(tshape, Bn * (K + 1), fp8) if dom["slot"] == "target.gate_up" else vbytes
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     # teacher-forced upper bound: drafts = the target's own greedy continuation
@@ -323,16 +346,18 @@ def main():
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"8B-shape bf16 target verify K={K} + 0.6B-shape draft, batch {Bn}, "
+        "config": {"workload": f"8B-shape {'fp8-weight (E4M3, row scales) ' if fp8 else ''}bf16 target verify "
+                               f"K={K} + 0.6B-shape draft, batch {Bn}, "
                                f"KV context {L}, {'sampled T=1 top_k 20 top_p 0.95' if args.sampled else 'greedy'}, "
                                f"random N(0,0.02) weights" + (f", {tshape.n_layers} layers" if args.layers else ""),
-                   "global_batch": Bn, "seq_len": L, "k": K, "schedule": sched, "parallelism": "none (1 GPU)"},
+                   "global_batch": Bn, "seq_len": L, "k": K, "schedule": "stream" if fp8 else sched,
+                   "target_weights": "fp8_e4m3_row" if fp8 else "bf16", "parallelism": "none (1 GPU)"},
         "acceptance": accepted / (K * args.steps * Bn),
         "verify": {"ms": verify_avg_ms, "bytes": vbytes, "GBps": verify_gbs, "frac_peak": verify_gbs / PEAK_HBM_GBS},
         "verify_vs_k": verify_vs_k,
         "roofline": {"bound": "hbm", "kernel": dom["kernel"],
                      "achieved": dom_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
-                     "traffic": dominant_traffic(sched), "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
+                     "traffic": dominant_traffic(dom_key), "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
                      "timing": (f"HIP events on the context stream around {REPS} back-to-back launches (the first "
                                 f"{REPS - 1} with the next layers' weights, then the real one), "
                                 if dom["slot"] != "target.forward" else "HIP events around each launch, ")
@@ -343,7 +368,7 @@ def main():
         "adaptive_depth": adaptive,
         "setup_s": setup_s,
     }
-    if not args.no_cpu_baseline and Bn == 1:
+    if not args.no_cpu_baseline and Bn == 1 and not fp8:
         out["cpu_baseline"] = cpu_baseline(tshape, dshape, tw, dw, K)
     print(json.dumps(out), flush=True)
 

@@ -56,6 +56,24 @@ extern "C" {
 #define SPEC_DTYPE_F32 0  /* weights, cache and GEMM inputs in float32                    */
 #define SPEC_DTYPE_BF16 1 /* bf16 weights and cache, bf16 GEMM inputs, fp32 accumulation  */
 
+/* Storage of the projection and LM-head weights (spec_model_desc.weights).  The pages' runs
+ * decode with quantized weights ("Speculative Decoding on Apple Silicon", section
+ * "Reproducing this"; "What is Speculative Decoding and How Does a Draft Model Work?", section
+ * "The demo, draft model on and off with two pairings"):
+ * a verify then reads fewer weight bytes per cycle.  The byte format here is the E4M3 type
+ * of the OCP 8-bit floating point specification, which gfx950 converts in hardware.  FP8_ROW
+ * models run the SPEC_SCHED_STREAM projections whatever the schedule; they need reduction
+ * lengths of 2048 or 4096 for the normalized projections (QKV, gate/up, LM head) and whole
+ * 2 KB stages for the rest, at most 16 rows per forward, and a drafter other than
+ * SPEC_DRAFT_MTP; else spec_init returns SPEC_E_UNSUPPORTED. */
+#define SPEC_WEIGHTS_NATIVE 0 /* in the model's dtype                                      */
+#define SPEC_WEIGHTS_FP8_ROW 1 /* bf16 models only: one byte per weight, an OCP FP8 E4M3
+                                  code (1 sign, 4 exponent bits of bias 7, 3 mantissa bits;
+                                  no infinities, S.1111.111 is NaN), and one float32 scale
+                                  per output row: weight[r][k] = decode(code[r][k]) * scale[r].
+                                  The embedding and the norm gains stay bf16; the LM head
+                                  must be its own tensor (not tied to the embedding). */
+
 #define SPEC_DRAFT_NONE 0  /* no drafter: verify_step at k = 0 is plain decoding          */
 #define SPEC_DRAFT_MODEL 1 /* a separate, smaller decoder with the same vocabulary         */
 #define SPEC_DRAFT_MTP 2   /* the target's own multi-token-prediction layer               */
@@ -83,6 +101,18 @@ typedef struct spec_layer_weights {
   const void* wd;        /* [d_model, d_ffn]               */
 } spec_layer_weights;
 
+/* Row scales of one layer's projections for SPEC_WEIGHTS_FP8_ROW (device float32 arrays,
+ * borrowed): one entry per output row of the matrix of the same name. */
+typedef struct spec_layer_scales {
+  const float* wq; /* [n_q_heads*head_dim]  */
+  const float* wk; /* [n_kv_heads*head_dim] */
+  const float* wv; /* [n_kv_heads*head_dim] */
+  const float* wo; /* [d_model]             */
+  const float* wg; /* [d_ffn]               */
+  const float* wu; /* [d_ffn]               */
+  const float* wd; /* [d_model]             */
+} spec_layer_scales;
+
 typedef struct spec_model_desc {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ffn, vocab;
   int32_t dtype;                    /* SPEC_DTYPE_*; every tensor of the model has it     */
@@ -92,6 +122,9 @@ typedef struct spec_model_desc {
   const void* lm_head;              /* [vocab, d_model]; may be the embed pointer (tied)   */
   const void* final_norm;           /* [d_model]                                           */
   const spec_layer_weights* layers; /* host array [n_layers]; copied by spec_init          */
+  int32_t weights;                  /* SPEC_WEIGHTS_*; zero-initialised descs are native   */
+  const float* lm_head_scale;       /* FP8_ROW: [vocab] row scales of lm_head              */
+  const spec_layer_scales* layer_scales; /* FP8_ROW: host array [n_layers]; copied      */
 } spec_model_desc;
 
 /* Multi-token-prediction layer: concat(RMSNorm(h_t), RMSNorm(E[x_{t+1}])) -> w_proj ->

@@ -24,6 +24,8 @@ SPEC_E_HIP = -5
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+WEIGHTS_NATIVE, WEIGHTS_FP8_ROW = 0, 1
+PROJ = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
 DRAFT_NONE, DRAFT_MODEL, DRAFT_MTP, DRAFT_NGRAM = 0, 1, 2, 3
 TOPK_MAX = 64
 MAX_K = 16
@@ -55,12 +57,18 @@ class spec_layer_weights(C.Structure):
                 ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "wg", "wu", "wd")]
 
 
+class spec_layer_scales(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in PROJ]
+
+
 class spec_model_desc(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ffn", C.c_int32),
                 ("vocab", C.c_int32), ("dtype", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("embed", C.c_void_p), ("lm_head", C.c_void_p),
-                ("final_norm", C.c_void_p), ("layers", C.POINTER(spec_layer_weights))]
+                ("final_norm", C.c_void_p), ("layers", C.POINTER(spec_layer_weights)),
+                ("weights", C.c_int32), ("lm_head_scale", C.c_void_p),
+                ("layer_scales", C.POINTER(spec_layer_scales))]
 
 
 class spec_mtp_desc(C.Structure):
@@ -191,14 +199,24 @@ def layer_struct(lw: Dict) -> spec_layer_weights:
 
 def model_desc(shape, w: Dict, keep: List) -> spec_model_desc:
     """spec_model_desc from a synth.ModelShape and a weight dict of device tensors.  The
-    ctypes layer array is appended to ``keep`` so it outlives the call that copies it."""
+    ctypes layer arrays are appended to ``keep`` so they outlive the call that copies them.
+    fp8 weights: ``w["lm_head_scale"]`` is present and each layer dict holds ``<name>_scale``
+    row-scale tensors beside the fp8 code tensors of wq .. wd."""
     arr = (spec_layer_weights * shape.n_layers)(*[layer_struct(lw) for lw in w["layers"]])
     keep.append(arr)
-    return spec_model_desc(
+    desc = spec_model_desc(
         shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
         shape.d_ffn, shape.vocab, DTYPE_BF16 if shape.dtype == "bf16" else DTYPE_F32,
         shape.rms_eps, shape.rope_theta, _ptr(w["embed"]), _ptr(w["lm_head"]),
         _ptr(w["final_norm"]), C.cast(arr, C.POINTER(spec_layer_weights)))
+    if "lm_head_scale" in w:
+        sc = (spec_layer_scales * shape.n_layers)(
+            *[spec_layer_scales(*[_ptr(lw[n + "_scale"]) for n in PROJ]) for lw in w["layers"]])
+        keep.append(sc)
+        desc.weights = WEIGHTS_FP8_ROW
+        desc.lm_head_scale = _ptr(w["lm_head_scale"])
+        desc.layer_scales = C.cast(sc, C.POINTER(spec_layer_scales))
+    return desc
 
 
 def mtp_desc(w: Dict) -> spec_mtp_desc:

@@ -204,6 +204,11 @@ struct StreamArgs {
   const void* w0;
   const void* w1;
   const void* w2;
+  // fp8 weights (wbytes 1): OCP e4m3 codes, the weight of row r being code * wNs[r]
+  const float* w0s;
+  const float* w1s;
+  const float* w2s;
+  int wbytes;         // 2: bf16 weights, 1: fp8 weights with row scales
   int rows0, rows1, rows2;
   int K, nunits;      // nunits: row tiles of 16 (EPI_SWIGLU: gate/up tile pairs)
   const void* x;      // [M, K] bf16 input rows
@@ -223,9 +228,12 @@ struct StreamArgs {
   int layer;
   RowMap rm;
 };
-// Whether M rows and reduction length K are covered: K in whole stages (1024; 512 for
-// SwiGLU); normalized inputs only for K in {1024, 2048, 4096, 5120}.
-bool stream_supported(int M, int K, int epi, bool norm);
+// Whether M rows and reduction length K are covered.  bf16 weights: K in whole stages (1024;
+// 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 4096, 5120}.  fp8 weights
+// (wbytes 1): stages of 2048 (1024 for SwiGLU), resident inputs for K in {2048, 4096}, streamed
+// inputs for the residual epilogue, and at most units_per_wg * tiles * 16 <= 1024 row scales
+// per workgroup.
+bool stream_supported(int M, int K, int epi, bool norm, int wbytes = 2, int units_per_wg = 1);
 size_t stream_lds_bytes();
 hipError_t stream_init();  // per device: LDS limit of the kernels
 hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_t st);

@@ -20,11 +20,14 @@ thread_local std::string g_init_error = "no error";
 constexpr int PREFILL_ROWS = 16;
 constexpr int GEMM_MAX_ROWS_BF16 = 64;
 constexpr int GEMM_MAX_ROWS_F32 = 32;
+constexpr int STREAM_MAX_ROWS = 16;  // fp8-weight models run the streamed projections only
 
 struct Model {
   int mi = 0;  // 0 target, 1 draft (profiling slot offset 16 * mi)
   spec_model_desc d{};
   std::vector<spec_layer_weights> layers;
+  std::vector<spec_layer_scales> scales;  // fp8 weights: row scales of each layer
+  bool fp8 = false;                       // SPEC_WEIGHTS_FP8_ROW
   bool present = false;
   int q_dim = 0, kv_dim = 0, mseq_max = 0, Mmax = 0, nchunk = 0;
   size_t act = 4;
@@ -212,6 +215,11 @@ struct Carver {
   }
 };
 
+int row_cap(const spec_model_desc& m) {
+  if (m.weights == SPEC_WEIGHTS_FP8_ROW) return STREAM_MAX_ROWS;
+  return m.dtype == SPEC_DTYPE_BF16 ? GEMM_MAX_ROWS_BF16 : GEMM_MAX_ROWS_F32;
+}
+
 int validate_model(const spec_model_desc& m, const char* name, int max_k, int max_batch, bool need_w) {
   if (m.n_layers < 1 || m.d_model < 16 || m.n_q_heads < 1 || m.n_kv_heads < 1 || m.head_dim < 2 ||
       m.d_ffn < 16 || m.vocab < 2)
@@ -220,6 +228,10 @@ int validate_model(const spec_model_desc& m, const char* name, int max_k, int ma
     return fail(nullptr, SPEC_E_INVAL, "%s: dtype %d", name, m.dtype);
   if (m.head_dim != 32 && m.head_dim != 64 && m.head_dim != 128)
     return fail(nullptr, SPEC_E_UNSUPPORTED, "%s: head_dim %d (32, 64 or 128)", name, m.head_dim);
+  if (m.weights != SPEC_WEIGHTS_NATIVE && m.weights != SPEC_WEIGHTS_FP8_ROW)
+    return fail(nullptr, SPEC_E_INVAL, "%s: weights %d", name, m.weights);
+  if (m.weights == SPEC_WEIGHTS_FP8_ROW && m.dtype != SPEC_DTYPE_BF16)
+    return fail(nullptr, SPEC_E_UNSUPPORTED, "%s: fp8 weights need a bf16 model", name);
   if (m.n_q_heads % m.n_kv_heads)
     return fail(nullptr, SPEC_E_INVAL, "%s: n_q_heads not a multiple of n_kv_heads", name);
   const int q = m.n_q_heads * m.head_dim, kv = m.n_kv_heads * m.head_dim;
@@ -231,7 +243,7 @@ int validate_model(const spec_model_desc& m, const char* name, int max_k, int ma
   const int G = m.n_q_heads / m.n_kv_heads;
   if ((max_k + 1) * G > ATTN_ROWS_MAX)
     return fail(nullptr, SPEC_E_UNSUPPORTED, "%s: (max_k+1) * q-heads-per-kv-head > %d", name, ATTN_ROWS_MAX);
-  const int rmax = m.dtype == SPEC_DTYPE_BF16 ? GEMM_MAX_ROWS_BF16 : GEMM_MAX_ROWS_F32;
+  const int rmax = row_cap(m);
   if (max_batch * (max_k + 1) > rmax)
     return fail(nullptr, SPEC_E_UNSUPPORTED, "%s: max_batch*(max_k+1) > %d rows", name, rmax);
   if (!(m.rms_eps >= 0.0f) || !(m.rope_theta > 0.0f))
@@ -243,6 +255,16 @@ int validate_model(const spec_model_desc& m, const char* name, int max_k, int ma
       const spec_layer_weights& w = m.layers[l];
       if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo || !w.ffn_norm || !w.wg || !w.wu || !w.wd)
         return fail(nullptr, SPEC_E_INVAL, "%s: null weight pointer in layer %d", name, l);
+    }
+    if (m.weights == SPEC_WEIGHTS_FP8_ROW) {
+      if (m.lm_head == m.embed)
+        return fail(nullptr, SPEC_E_UNSUPPORTED, "%s: fp8 weights need an untied LM head", name);
+      if (!m.lm_head_scale || !m.layer_scales) return fail(nullptr, SPEC_E_INVAL, "%s: null scale pointer", name);
+      for (int l = 0; l < m.n_layers; ++l) {
+        const spec_layer_scales& w = m.layer_scales[l];
+        if (!w.wq || !w.wk || !w.wv || !w.wo || !w.wg || !w.wu || !w.wd)
+          return fail(nullptr, SPEC_E_INVAL, "%s: null scale pointer in layer %d", name, l);
+      }
     }
   }
   return SPEC_OK;
@@ -259,7 +281,7 @@ int validate_sampler(const spec_sampler& s) {
 
 int max_rows_per_seq(const spec_model_desc& m, int max_k, int max_batch) {
   const int G = m.n_q_heads / m.n_kv_heads;
-  const int rmax = m.dtype == SPEC_DTYPE_BF16 ? GEMM_MAX_ROWS_BF16 : GEMM_MAX_ROWS_F32;
+  const int rmax = row_cap(m);
   int r = std::max(max_k + 1, PREFILL_ROWS);
   r = std::min(r, ATTN_ROWS_MAX / G);
   r = std::min(r, rmax / max_batch);
@@ -348,7 +370,10 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
   const int maxk = std::max(g.max_k, 1);
   rc = validate_model(g.target, "target", maxk, g.max_batch, false);
   if (rc) return rc;
+  if (g.target.weights == SPEC_WEIGHTS_FP8_ROW && g.draft_kind == SPEC_DRAFT_MTP)
+    return fail(nullptr, SPEC_E_UNSUPPORTED, "fp8 target weights with the MTP drafter");
   c->target.d = g.target;
+  c->target.fp8 = g.target.weights == SPEC_WEIGHTS_FP8_ROW;
   c->target.present = true;
   c->target.mi = 0;
   if (g.draft_kind == SPEC_DRAFT_MODEL) {
@@ -357,6 +382,7 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
     if (g.draft.vocab != g.target.vocab)
       return fail(nullptr, SPEC_E_INVAL, "draft vocab %d != target vocab %d", g.draft.vocab, g.target.vocab);
     c->draft.d = g.draft;
+    c->draft.fp8 = g.draft.weights == SPEC_WEIGHTS_FP8_ROW;
     c->draft.present = true;
     c->draft.mi = 1;
   } else if (g.draft_kind == SPEC_DRAFT_MTP) {
@@ -366,6 +392,8 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
     c->mtp.d.n_layers = 1;
     c->mtp.d.final_norm = g.mtp.final_norm;
     c->mtp.d.layers = nullptr;
+    c->mtp.d.weights = SPEC_WEIGHTS_NATIVE;
+    c->mtp.d.layer_scales = nullptr;
     c->mtp.present = true;
     c->mtp.mi = 1;
   } else if (g.draft_kind == SPEC_DRAFT_NGRAM) {
@@ -438,12 +466,27 @@ bool attn_few(spec_ctx* c, const Model& m) {
 // at most 16 rows, reduction lengths in whole stages (normalized inputs: d in {1024, 2048,
 // 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
 // gain-multiplied rows.
+bool stream_shapes(spec_ctx* c, const Model& m, int M) {
+  const spec_model_desc& d = m.d;
+  if (c->ncu < 1 || (m.q_dim + 2 * m.kv_dim) % 16 || d.d_ffn % 16 || d.vocab % 16 || d.d_model % 16) return false;
+  const int wb = m.fp8 ? 1 : 2;
+  // units per workgroup (the fp8 kernels keep that many tiles of row scales in LDS)
+  auto upw = [&](int nunits) {
+    const int g = std::min(c->ncu, nunits);
+    return (nunits + g - 1) / g;
+  };
+  return stream_supported(M, d.d_model, EPI_QKV, true, wb, upw((m.q_dim + 2 * m.kv_dim) / 16)) &&
+         stream_supported(M, d.d_model, EPI_SWIGLU, true, wb, upw(d.d_ffn / 16)) &&
+         stream_supported(M, m.q_dim, EPI_RESID, false, wb, upw(d.d_model / 16)) &&
+         stream_supported(M, d.d_ffn, EPI_RESID, false, wb, upw(d.d_model / 16)) &&
+         stream_supported(M, d.d_model, EPI_STORE, true, wb, upw(d.vocab / 16));
+}
+
+// fp8-weight models take these kernels under every schedule (no other kernel decodes fp8).
 bool use_stream(spec_ctx* c, const Model& m, int M) {
   const spec_model_desc& d = m.d;
-  if (c->sched != SPEC_SCHED_STREAM || c->ncu < 1 || d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp) return false;
-  return stream_supported(M, d.d_model, EPI_QKV, true) && stream_supported(M, d.d_model, EPI_SWIGLU, true) &&
-         stream_supported(M, m.q_dim, EPI_RESID, false) && stream_supported(M, d.d_ffn, EPI_RESID, false) &&
-         (m.q_dim + 2 * m.kv_dim) % 16 == 0 && d.d_ffn % 16 == 0 && d.vocab % 16 == 0;
+  if (d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp || (!m.fp8 && c->sched != SPEC_SCHED_STREAM)) return false;
+  return stream_shapes(c, m, M);
 }
 
 // The decoder layers of m on the streamed projections over the M rows in m.x (np
@@ -453,12 +496,19 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
   const int P = 16 * m.mi;
   const int grid = c->ncu;
   const int ss_ld = d.d_model / 16 + 1;
+  const int wb = m.fp8 ? 1 : 2;
+  const spec_layer_scales no_scales{};
   for (int l = 0; l < d.n_layers; ++l) {
     const spec_layer_weights& w = m.layers[l];
+    const spec_layer_scales& sc = m.fp8 ? m.scales[l] : no_scales;
     StreamArgs g{};
     g.w0 = w.wq;
     g.w1 = w.wk;
     g.w2 = w.wv;
+    g.w0s = sc.wq;
+    g.w1s = sc.wk;
+    g.w2s = sc.wv;
+    g.wbytes = wb;
     g.rows0 = m.q_dim;
     g.rows1 = m.kv_dim;
     g.rows2 = m.kv_dim;
@@ -492,6 +542,8 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
     StreamArgs o{};
     o.w0 = w.wo;
+    o.w0s = sc.wo;
+    o.wbytes = wb;
     o.rows0 = d.d_model;
     o.K = m.q_dim;
     o.nunits = d.d_model / 16;
@@ -508,6 +560,9 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     StreamArgs gu{};
     gu.w0 = w.wg;
     gu.w1 = w.wu;
+    gu.w0s = sc.wg;
+    gu.w1s = sc.wu;
+    gu.wbytes = wb;
     gu.rows0 = d.d_ffn;
     gu.K = d.d_model;
     gu.nunits = d.d_ffn / 16;
@@ -520,13 +575,20 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     gu.h = m.h;
     auto gu_rep = [&](int r, int reps) {
       StreamArgs g2 = gu;
-      g2.w0 = m.layers[rep_layer(l, r, reps, d.n_layers)].wg;
-      g2.w1 = m.layers[rep_layer(l, r, reps, d.n_layers)].wu;
+      const int lr = rep_layer(l, r, reps, d.n_layers);
+      g2.w0 = m.layers[lr].wg;
+      g2.w1 = m.layers[lr].wu;
+      if (m.fp8) {
+        g2.w0s = m.scales[lr].wg;
+        g2.w1s = m.scales[lr].wu;
+      }
       return launch_stream_gemm(EPI_SWIGLU, g2, grid, c->stream);
     };
     LAUNCH_REP(c, P + PROF_GATEUP, gu_rep);
     StreamArgs dn{};
     dn.w0 = w.wd;
+    dn.w0s = sc.wd;
+    dn.wbytes = wb;
     dn.rows0 = d.d_model;
     dn.K = d.d_ffn;
     dn.nunits = d.d_model / 16;
@@ -547,6 +609,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
 // row in m.ss for bf16 models), rows placed by rm.
 int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
   if (use_stream(c, m, M)) return run_layers_stream(c, m, M, rm, np);
+  if (m.fp8) return fail(c, SPEC_E_UNSUPPORTED, "fp8 weights over %d rows", M);
   const spec_model_desc& d = m.d;
   const hipStream_t st = c->stream;
   const int dt = d.dtype;
@@ -637,6 +700,8 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
   if (use_stream(c, m, M) && x == m.x && ss == m.ss) {
     StreamArgs lm{};
     lm.w0 = d.lm_head;
+    lm.w0s = m.fp8 ? d.lm_head_scale : nullptr;
+    lm.wbytes = m.fp8 ? 1 : 2;
     lm.rows0 = d.vocab;
     lm.K = d.d_model;
     lm.nunits = d.vocab / 16;
@@ -651,6 +716,7 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
     LAUNCH(c, 16 * m.mi + PROF_LMHEAD, launch_stream_gemm(EPI_STORE, lm, c->ncu, c->stream));
     return SPEC_OK;
   }
+  if (m.fp8) return fail(c, SPEC_E_UNSUPPORTED, "fp8 LM head outside the streamed projections");
   GemmArgs lm{};
   lm.w[0] = d.lm_head;
   lm.rows[0] = d.vocab;
@@ -667,7 +733,8 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
 // Whether the forward of m over B x mseq rows runs as one persistent launch.
 bool use_forward(spec_ctx* c, const Model& m, int B, int mseq) {
   const spec_model_desc& d = m.d;
-  if (c->sched != SPEC_SCHED_FORWARD || c->fgrid < 8 || d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp) return false;
+  if (c->sched != SPEC_SCHED_FORWARD || c->fgrid < 8 || d.dtype != SPEC_DTYPE_BF16 || &m == &c->mtp || m.fp8)
+    return false;
   if (B * mseq > c->fgrid) return false;
   return forward_supported(B * mseq, mseq, d.d_model, d.n_q_heads, d.n_kv_heads, d.head_dim, d.d_ffn, d.vocab);
 }
@@ -978,9 +1045,13 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
   }
   c->target.layers.assign(cfg->target.layers, cfg->target.layers + cfg->target.n_layers);
   c->target.d.layers = nullptr;
+  if (c->target.fp8) c->target.scales.assign(cfg->target.layer_scales, cfg->target.layer_scales + cfg->target.n_layers);
+  c->target.d.layer_scales = nullptr;
   if (c->draft.present) {
     c->draft.layers.assign(cfg->draft.layers, cfg->draft.layers + cfg->draft.n_layers);
     c->draft.d.layers = nullptr;
+    if (c->draft.fp8) c->draft.scales.assign(cfg->draft.layer_scales, cfg->draft.layer_scales + cfg->draft.n_layers);
+    c->draft.d.layer_scales = nullptr;
   }
   if (c->mtp.present) c->mtp.layers.assign(1, cfg->mtp.layer);
   const size_t need = layout(c, nullptr);
@@ -1014,6 +1085,13 @@ int spec_init(const spec_config* cfg, void* workspace, size_t ws_bytes, void* st
   if (e != hipSuccess) {
     delete c;
     return fail(nullptr, SPEC_E_HIP, "init kernels: %s", hipGetErrorString(e));
+  }
+  for (Model* m : {&c->target, &c->draft}) {
+    if (!m->present || !m->fp8 || stream_shapes(c, *m, m->Mmax)) continue;
+    const char* name = m == &c->target ? "target" : "draft";
+    delete c;
+    return fail(nullptr, SPEC_E_UNSUPPORTED,
+                "%s: fp8 weights need d_model in {2048, 4096}, other reductions in whole 2 KB stages", name);
   }
   *out = c;
   return SPEC_OK;

@@ -46,7 +46,9 @@ constexpr int STAGE = 32 * SEGP;              // one stage: 32 segments
 constexpr int RING = 4;                       // stages in the ring
 constexpr int RED_BYTES = SNW * 2 * 64 * 16;  // partial tiles of the 8 wavefronts (two tiles)
 constexpr int INV_BYTES = 16 * 4;             // 1/rms of the 16 token rows
-constexpr int LDS_BYTES = RING * STAGE + RED_BYTES + INV_BYTES;
+constexpr int SCALE_MAX = 1024;               // fp8 weights: row scales of a workgroup's units
+constexpr int SCALE_BYTES = SCALE_MAX * 4;
+constexpr int LDS_BYTES = RING * STAGE + RED_BYTES + INV_BYTES + SCALE_BYTES;
 constexpr int CPOL_SC1 = 16;                  // cache policy of coherent loads (device scope)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -157,9 +159,24 @@ SPEC_DEVINL uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Two fp8 (OCP e4m3) weights -> two bf16 in one word.  The hardware conversion gives the exact
+// float32 value; an e4m3 value has at most 4 significant bits, so its upper 16 bits are the
+// exact bf16.
+template <bool HI>
+SPEC_DEVINL uint32_t fp8x2_bf16(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xFFFF0000u);
+}
+// 16 fp8 weights (k = k0 .. k0 + 15 of one row) -> the bf16 A operands of k0 .. k0 + 7 (lo)
+// and k0 + 8 .. k0 + 15 (hi)
+SPEC_DEVINL void fp8x16_bf16(uint4 v, uint4& lo, uint4& hi) {
+  lo = make_uint4(fp8x2_bf16<false>(v.x), fp8x2_bf16<true>(v.x), fp8x2_bf16<false>(v.y), fp8x2_bf16<true>(v.y));
+  hi = make_uint4(fp8x2_bf16<false>(v.z), fp8x2_bf16<true>(v.z), fp8x2_bf16<false>(v.w), fp8x2_bf16<true>(v.w));
+}
+
 // First byte of the 16 weight rows of unit u in matrix t (SwiGLU: 0 gate, 1 up); for the QKV
-// projection the unit's rows may lie in W_q, W_k or W_v.
-template <int EPI>
+// projection the unit's rows may lie in W_q, W_k or W_v.  WB: bytes per weight.
+template <int EPI, int WB = 2>
 SPEC_DEVINL const char* unit_rows(const StreamArgs& a, int u, int t, int* mat, int* r0) {
   int m = 0, r = u * 16;
   if (EPI == EPI_QKV || EPI == EPI_QKV_ROWS) {
@@ -179,7 +196,26 @@ SPEC_DEVINL const char* unit_rows(const StreamArgs& a, int u, int t, int* mat, i
   // the pointers pass through readfirstlane before the select: a select of members would be
   // folded into an indexed load, which keeps the argument block in scratch memory
   const uint64_t w = m == 0 ? uni64(a.w0) : (m == 1 ? uni64(a.w1) : uni64(a.w2));
-  return (const char*)w + (int64_t)r * a.K * 2;
+  return (const char*)w + (int64_t)r * a.K * WB;
+}
+// Row scale of row r0 + c of unit u's matrix in tile t (fp8 weights); any lane's own unit.
+template <int EPI>
+SPEC_DEVINL float unit_scale(const StreamArgs& a, int u, int t, int c) {
+  int m = 0, r = u * 16;
+  if (EPI == EPI_QKV || EPI == EPI_QKV_ROWS) {
+    if (r >= a.rows0) {
+      r -= a.rows0;
+      m = 1;
+      if (r >= a.rows1) {
+        r -= a.rows1;
+        m = 2;
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    m = t;
+  }
+  const float* p = m == 0 ? a.w0s : (m == 1 ? a.w1s : a.w2s);
+  return p[r + c];
 }
 
 // One projection over this workgroup's units (blockIdx.x, blockIdx.x + grid, ...).
@@ -187,24 +223,34 @@ SPEC_DEVINL const char* unit_rows(const StreamArgs& a, int u, int t, int* mat, i
 // K of whole stages, bf16 input slices loaded with each stage.  With a.ss_in set the
 // projection folds in an RMSNorm (resident inputs only).  COH: activations cross workgroups
 // inside the launch.
-template <int EPI, int NST, bool COH>
+template <int EPI, int NST, bool COH, int WB = 2>
 struct Gemm {
   static constexpr int TILES = EPI == EPI_SWIGLU ? 2 : 1;
   static constexpr int S = RING;
-  static constexpr int KS = TILES == 1 ? 1024 : 512;  // k per stage
-  static constexpr int WSTEPS = KS / 32 / SNW;        // k-steps of 32 per wavefront and stage
-  static constexpr bool RES = NST > 0;                // resident input slices
-  static constexpr int C = 4 + (RES ? 0 : WSTEPS);    // vector memory instructions per wavefront and stage
-  static constexpr int XS = RES ? NST * WSTEPS : 1;   // resident slices per lane
-  static constexpr int XP = COH ? CPOL_SC1 : 0;       // cache policy of activation loads
-  static_assert(WSTEPS * TILES == 4, "four operand reads per wavefront and stage");
+  static constexpr int KSTEP = 2 / WB;                           // MFMA k-steps per 16-byte weight read
+  static constexpr int KS = (TILES == 1 ? 1024 : 512) * KSTEP;    // k per stage
+  static constexpr int WCH = 4 / TILES;                          // 64-byte row chunks per wavefront, tile and stage
+  static constexpr int NSL = WCH * KSTEP;                        // input slices per wavefront and stage
+  static constexpr bool RES = NST > 0;                           // resident input slices
+  static constexpr int C = 4 + (RES ? 0 : NSL);                  // vector memory instructions per wavefront and stage
+  static constexpr int XS = RES ? NST * NSL : 1;                 // resident slices per lane
+  static constexpr int XP = COH ? CPOL_SC1 : 0;                  // cache policy of activation loads
+  static_assert(WB == 2 || WB == 1, "bf16 or fp8 weights");
+  static_assert(!(COH && WB == 1), "fp8 weights: per-launch projections only");
+
+  // k of input slice (ks, i, sub) of wavefront `wave` (plus 8 KSTEP (lane / 16) per lane): chunk
+  // c = wave + 8 i holds k = c * 32 KSTEP + 8 KSTEP g .. of the stage, and for fp8 its two
+  // k-steps are the lanes' first and second 8 weights
+  static SPEC_DEVINL int slice_k(int ks, int i, int sub, int wave) {
+    return ks * KS + (wave + SNW * i) * 32 * KSTEP + 8 * sub;
+  }
+  static SPEC_DEVINL int my_units(const StreamArgs& a) {
+    const int nunits = a.nunits;
+    return nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  }
 
   static SPEC_DEVINL int stages_per_unit(const StreamArgs& a) { return RES ? NST : a.K / KS; }
-  static SPEC_DEVINL int total_stages(const StreamArgs& a) {
-    const int nunits = a.nunits;
-    const int myunits = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    return myunits * stages_per_unit(a);
-  }
+  static SPEC_DEVINL int total_stages(const StreamArgs& a) { return my_units(a) * stages_per_unit(a); }
 
   // Weights of stage j of this workgroup (unit blockIdx.x + (j / nst) * grid, k-range j % nst)
   // into ring slot j % S: four 1 KB segments per wavefront (segment s = wave + 8 i: row s % 16,
@@ -218,29 +264,30 @@ struct Gemm {
     const int u = (int)blockIdx.x + (j / nst) * (int)gridDim.x, ks = j % nst;
     char* buf = sm + (j % S) * STAGE;
     int mat, r0;
-    const char* base0 = unit_rows<EPI>(a, ok ? u : 0, 0, &mat, &r0);
-    const char* base1 = TILES == 2 ? unit_rows<EPI>(a, ok ? u : 0, 1, &mat, &r0) : base0;
-    const int64_t kofs = TILES == 1 ? ks * 2048 : ks * 1024;
+    const char* base0 = unit_rows<EPI, WB>(a, ok ? u : 0, 0, &mat, &r0);
+    const char* base1 = TILES == 2 ? unit_rows<EPI, WB>(a, ok ? u : 0, 1, &mat, &r0) : base0;
+    const int64_t kofs = TILES == 1 ? ks * 2048 : ks * 1024;  // a stage is 2 KB (1 KB) of each row
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = wave + SNW * i;
       const char* base = (TILES == 2 && (s >> 4)) ? base1 : base0;
-      const int64_t org = (int64_t)(s & 15) * K * 2 + kofs + (TILES == 1 ? (s >> 4) * 1024 : 0);
+      const int64_t org = (int64_t)(s & 15) * K * WB + kofs + (TILES == 1 ? (s >> 4) * 1024 : 0);
       const __amdgpu_buffer_rsrc_t r = rsrc(base + (ok ? org : 0), ok ? 0x7fffffffu : 0u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + s * SEGP), 16, (uint32_t)lane * 16u, 0, 0, 0);
     }
   }
   // The wavefront's bf16 input slices of stage j (streamed inputs).
-  static SPEC_DEVINL void issue_x(const StreamArgs& a, int j, uint4 (&xb)[WSTEPS]) {
+  static SPEC_DEVINL void issue_x(const StreamArgs& a, int j, uint4 (&xb)[NSL]) {
     const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
     const int K = a.K, ks = j % stages_per_unit(a), m = lane & 15;
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(a.M * K * 2));  // rows >= M: out of range
-    const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
+    const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 2u;
 #pragma unroll
-    for (int i = 0; i < WSTEPS; ++i) {
-      const int st = wave + SNW * i;
-      xb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + st * 32) * 2, XP));
-    }
+    for (int i = 0; i < WCH; ++i)
+#pragma unroll
+      for (int sub = 0; sub < KSTEP; ++sub)
+        xb[i * KSTEP + sub] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, slice_k(ks, i, sub, wave) * 2, XP));
   }
 
   // The first P weight stages, issued ahead (before the barrier that precedes the
@@ -284,16 +331,30 @@ struct Gemm {
     }
     if (RES) {
       const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
-      const uint32_t xoff = (uint32_t)(m * K + 8 * (lane >> 4)) * 2u;
+      const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 2u;
 #pragma unroll
       for (int q = 0; q < XS; ++q) {
-        const int ks = q / WSTEPS, i = q % WSTEPS;
+        const int ks = q / NSL, i = (q % NSL) / KSTEP, sub = q % KSTEP;
         xin[q] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (ks * KS + (wave + SNW * i) * 32) * 2, XP));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, slice_k(ks, i, sub, wave) * 2, XP));
+      }
+    }
+    // fp8 weights: the row scales of this workgroup's units (unit q, tile t, column c at
+    // (q * TILES + t) * 16 + c), loaded before the first weight stages, written to LDS below
+    const uint32_t scl0 = inv0 + INV_BYTES;
+    constexpr int NSC = WB == 1 ? SCALE_MAX / (SNW * 64) : 1;
+    float scv[NSC];
+    if (WB == 1) {
+      const int n_sc = my_units(a) * TILES * 16;
+#pragma unroll
+      for (int v = 0; v < NSC; ++v) {
+        const int e = tx + SNW * 64 * v;
+        const int q = e / (TILES * 16), t = (e / 16) % TILES, c = e % 16;
+        scv[v] = e < n_sc ? unit_scale<EPI>(a, (int)blockIdx.x + q * (int)gridDim.x, t, c) : 0.0f;
       }
     }
 
-    uint4 xa[RES ? 1 : S][WSTEPS];
+    uint4 xa[RES ? 1 : S][NSL];
     if (!RES && P > 0) {
 #pragma unroll
       for (int j = 0; j < S - 1; ++j) issue_x(a, j, xa[RES ? 0 : j]);
@@ -320,6 +381,11 @@ struct Gemm {
       }
       wg_barrier();
       if (tx < 256 && (tx >> 4) < M) rinv = lds_read_f32(inv0 + (tx >> 4) * 4);
+    }
+    if (WB == 1) {
+      // read at unit ends, after the first stage's barrier
+#pragma unroll
+      for (int v = 0; v < NSC; ++v) lds_write_f32(scl0 + (tx + SNW * 64 * v) * 4, scv[v]);
     }
 
     f32x4_t acc[TILES];
@@ -352,10 +418,11 @@ struct Gemm {
 #pragma unroll
           for (int w = 0; w < SNW; ++w)
             sacc += __uint_as_float(r == 0 ? p[w].x : (r == 1 ? p[w].y : (r == 2 ? p[w].z : p[w].w)));
-          v[t] = norm ? sacc * rinv : sacc;
+          const float sw = WB == 1 ? sacc * lds_read_f32(scl0 + (((u - (int)blockIdx.x) / (int)gridDim.x * TILES + t) * 16 + c) * 4) : sacc;
+          v[t] = norm ? sw * rinv : sw;
         }
         int mat, r0;
-        (void)unit_rows<EPI>(a, u, 0, &mat, &r0);
+        (void)unit_rows<EPI, WB>(a, u, 0, &mat, &r0);
         const int n = r0 + c;
         const bool live = mm < M;
         if (EPI == EPI_RESID) {
@@ -399,11 +466,11 @@ struct Gemm {
       // the partial tiles are written again only after the next stage's barrier
     };
 
-    auto compute = [&](int j, int ks, const uint4 (&xb)[WSTEPS]) {
+    auto compute = [&](int j, int ks, const uint4 (&xb)[NSL]) {
       const uint32_t buf = sm0 + (j % S) * STAGE;
       uint32_t ad[4];
 #pragma unroll
-      for (int i = 0; i < WSTEPS; ++i) {
+      for (int i = 0; i < WCH; ++i) {
         const int st = wave + SNW * i;
 #pragma unroll
         for (int t = 0; t < TILES; ++t) {
@@ -415,12 +482,24 @@ struct Gemm {
       uint4 wv[4];
       lds_read4(ad[0], ad[1], ad[2], ad[3], wv[0], wv[1], wv[2], wv[3]);
 #pragma unroll
-      for (int i = 0; i < WSTEPS; ++i) {
-        const uint4 b = RES ? xin[(RES ? ks : 0) * WSTEPS + i] : xb[i];
+      for (int i = 0; i < WCH; ++i) {
+        uint4 b[KSTEP];
 #pragma unroll
-        for (int t = 0; t < TILES; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[i * TILES + t]),
-                                                           __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+        for (int sub = 0; sub < KSTEP; ++sub) b[sub] = RES ? xin[((RES ? ks : 0) * WCH + i) * KSTEP + sub] : xb[i * KSTEP + sub];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          if (WB == 2) {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[i * TILES + t]),
+                                                             __builtin_bit_cast(bf16x8_t, b[0]), acc[t], 0, 0, 0);
+          } else {
+            uint4 lo, hi;
+            fp8x16_bf16(wv[i * TILES + t], lo, hi);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
+                                                             __builtin_bit_cast(bf16x8_t, b[0]), acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
+                                                             __builtin_bit_cast(bf16x8_t, b[KSTEP - 1]), acc[t], 0, 0, 0);
+          }
+        }
       }
       if (ks == nst - 1) finish_unit((int)blockIdx.x + (j / nst) * (int)gridDim.x);
     };
@@ -450,8 +529,8 @@ struct Gemm {
         for (int q = 0; q < S; ++q) {
           const int j = j0 + q;
           if (j >= total) continue;
-          if (pre && j == 0) wait_vm<2 * WSTEPS>();
-          else if (pre && j == 1) wait_vm<WSTEPS + C>();
+          if (pre && j == 0) wait_vm<2 * NSL>();
+          else if (pre && j == 1) wait_vm<NSL + C>();
           else wait_vm<C * (S - 2)>();
           wg_barrier();
           issue_w(a, sm, j + S - 1, total);

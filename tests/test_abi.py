@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) <= exported
 
 
-STRUCTS = ["spec_layer_weights", "spec_model_desc", "spec_mtp_desc", "spec_sampler", "spec_ngram_cfg",
+STRUCTS = ["spec_layer_weights", "spec_layer_scales", "spec_model_desc", "spec_mtp_desc", "spec_sampler", "spec_ngram_cfg",
            "spec_config", "spec_probs", "spec_stats", "spec_gate"]
 
 
@@ -95,6 +95,13 @@ def test_workspace_size_host_only():
     (lambda c: setattr(c.draft, "vocab", 1024), B.SPEC_E_INVAL),
     (lambda c: setattr(c, "draft_kind", 9), B.SPEC_E_INVAL),
     (lambda c: setattr(c, "max_batch", 8), B.SPEC_E_UNSUPPORTED),   # 8 x 9 rows > 64
+    (lambda c: setattr(c.target, "weights", 2), B.SPEC_E_INVAL),
+    (lambda c: (setattr(c.target, "weights", B.WEIGHTS_FP8_ROW), setattr(c.target, "dtype", B.DTYPE_F32)),
+     B.SPEC_E_UNSUPPORTED),
+    (lambda c: (setattr(c.target, "weights", B.WEIGHTS_FP8_ROW), setattr(c, "max_batch", 2)),
+     B.SPEC_E_UNSUPPORTED),                                           # fp8: 2 x 9 rows > 16
+    (lambda c: (setattr(c.target, "weights", B.WEIGHTS_FP8_ROW), setattr(c, "draft_kind", B.DRAFT_MTP)),
+     B.SPEC_E_UNSUPPORTED),
 ])
 def test_config_validation(mut, code):
     cfg, keep = host_cfg(synth.SHAPES["qwen8b"], synth.SHAPES["qwen0p6b"])
@@ -103,6 +110,16 @@ def test_config_validation(mut, code):
         B.spec_workspace_size(cfg)
     assert e.value.code == code
     assert B.spec_last_error(None) != ""
+
+
+def test_fp8_rows_cap_the_workspace():
+    t = synth.SHAPES["qwen8b"]
+    cfg, keep = host_cfg(t, max_k=6, max_batch=2)
+    native = B.spec_workspace_size(cfg)
+    cfg.target.weights = B.WEIGHTS_FP8_ROW
+    fp8 = B.spec_workspace_size(cfg)
+    # the same caches; activations (logits first) for 2 x 8 rows per forward instead of 2 x 16
+    assert 16 * t.vocab * 4 < native - fp8 < 16 * t.vocab * 4 + (32 << 20)
 
 
 def test_greedy_sampler_ignores_top_k():
