@@ -89,11 +89,11 @@ DOMINANT = {
     "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
-               "sources": ["stream_core.h", "stream.hip"], "traffic": 201972291, "sha256": "e5217649bee4cbfb"},
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 201975384, "sha256": "4be692ea973324b6"},
     "stream_fp8": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 4, 1> (target gate/up + SwiGLU over E4M3 weights "
                              "with row scales, streamed through an LDS ring, one workgroup per CU)",
                    "slot": "target.gate_up",
-                   "sources": ["stream_core.h", "stream.hip"], "traffic": None, "sha256": None},
+                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101529477, "sha256": "4be692ea973324b6"},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",
