@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                     help="target projection weights: bf16, or OCP E4M3 codes with a float32 scale per row")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-weight verify run of the default bench")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -220,12 +221,13 @@ def main():
                          max_batch=Bn)
     starts = [synth.make_tokens(2, tshape.vocab, b, tag="start") for b in range(Bn)]
 
-    def reset():
+    def reset(e=None):
+        e = e or eng
         for b in range(Bn):
-            eng.load_prefix(0, b, tk, tv, L)
-            eng.load_prefix(1, b, dk, dv, L - 1)
-        eng.set_last(torch.tensor([int(st[1]) for st in starts], dtype=torch.int32, device="cuda"),
-                     torch.tensor([int(st[0]) for st in starts], dtype=torch.int32, device="cuda"))
+            e.load_prefix(0, b, tk, tv, L)
+            e.load_prefix(1, b, dk, dv, L - 1)
+        e.set_last(torch.tensor([int(st[1]) for st in starts], dtype=torch.int32, device="cuda"),
+                   torch.tensor([int(st[0]) for st in starts], dtype=torch.int32, device="cuda"))
 
     if args.no_graphs:
         eng.use_graphs(False)
@@ -342,6 +344,37 @@ def main():
             adaptive["teacher_forced"] = {"tok_s": n_ad / el, "cycles": len(cyc), "k_last": ks[-1],
                                           "k_mean": sum(ks) / len(ks), "matches_plain": toks[0] == plain[0][:n_ad]}
 
+    # the same cycles with the target's weights as E4M3 codes + row scales (fp8 row of the
+    # next steps; not the headline): verify latency and rate at the fp8 byte count
+    fp8_run = None
+    if not fp8 and not args.no_fp8 and Bn == 1:
+        tw8 = synth.make_weights_fp8(tshape, 0, device="cuda")
+        eng8 = runtime.Engine(tshape, tw8, dshape, dw, temperature=temp, seed=0, max_ctx=max_ctx, max_k=K)
+        if args.no_graphs:
+            eng8.use_graphs(False)
+        reset(eng8)
+        r8 = 0
+        for _ in range(args.warmup):
+            eng8.cycle(1, K, r8)
+            r8 += 1
+        torch.cuda.synchronize()
+        ms8, n8 = [], 0
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            c = eng8.cycle(1, K, r8, events=ev)
+            n8 += sum(len(t) for t in c.tokens)
+            ms8.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
+            r8 += 1
+        torch.cuda.synchronize()
+        el8 = time.perf_counter() - t0
+        vb8 = verify_bytes(tshape, K, L + args.warmup + 1, 1, True)
+        v8 = sum(ms8) / len(ms8)
+        fp8_run = {"target_weights": "fp8_e4m3_row", "tok_s": n8 / el8, "verify_ms": v8, "verify_bytes": vb8,
+                   "verify_GBps": vb8 / (v8 * 1e-3) / 1e9, "frac_peak": vb8 / (v8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "verify_speedup_vs_bf16": verify_avg_ms / v8}
+        del eng8, tw8
+        torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
@@ -366,6 +399,7 @@ def main():
                     for k, v in prof.items()},
         "teacher_forced": teacher,
         "adaptive_depth": adaptive,
+        "fp8_weights": fp8_run,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline and Bn == 1 and not fp8:

@@ -131,3 +131,31 @@ def test_fp8_target_generation_parity(temperature):
     # rows of random weights are near-uniform over their top 20, so with bf16 rounding such a
     # tie comes within a few tokens; greedy streams must agree for at least half the run.
     assert agree >= (N // 2 if temperature == 0.0 else 1), agree
+
+
+def test_fp8_batched_verify_parity():
+    """fp8 weights under a batched verify: three sequences of the 2048-wide shape with caches
+    of 700, 333 and 64 positions and their own drafts in one pass of 3 x (K+1) = 15 rows; every
+    row against the oracle's forward of its own sequence."""
+    shape, K, lens = FP8_2048, 4, [700, 333, 64]
+    Bn = len(lens)
+    w = synth.make_weights_fp8(shape, 1, device="cuda")
+    eng = runtime.Engine(shape, w, temperature=0.0, max_batch=Bn, max_ctx=max(lens) + 40, max_k=K)
+    prefixes = []
+    for b, L in enumerate(lens):
+        k, v = synth.make_kv_prefix(shape, L, 40 + b, device="cuda")
+        eng.load_prefix(0, b, k, v, L)
+        prefixes.append((k.float().cpu().numpy(), v.float().cpu().numpy()))
+    t0 = [int(x) for x in synth.make_tokens(Bn, shape.vocab, 27)]
+    eng.set_last(torch.tensor(t0, dtype=torch.int32, device="cuda"))
+    drafts = [[int(x) for x in synth.make_tokens(K, shape.vocab, 50 + b)] for b in range(Bn)]
+    c = eng.cycle(Bn, K, 0, drafts=torch.tensor(drafts, dtype=torch.int32, device="cuda"), keep=True)
+    logits = c.logits.cpu().numpy()
+    spec = om.Spec.from_shape(shape)
+    W = oq.dequantize_model(host_arrays(w))
+    for b, L in enumerate(lens):
+        kv = om.KVCache(spec, L + K + 2)
+        kv.load_prefix(*prefixes[b])
+        ref = om.forward_tokens(spec, W, kv, [t0[b]] + drafts[b])
+        err = assert_rows_close(logits[b], ref, RTOL_BF16)
+        print(f"fp8 batched verify seq {b} L={L}: worst row error {err:.2e}")
