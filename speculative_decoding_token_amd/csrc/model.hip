@@ -437,6 +437,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 // row and head, the chunk's (max, sum of exp, weighted value sum); attn_combine merges the
 // chunks in order.  Chunks are fixed ranges of absolute positions, so a row's result does
 // not depend on how many rows the pass has.
+// A sequence length read as a vector load (the address passed through a VGPR), to be issued
+// before the loads that do not depend on it: vector loads complete in order, so waiting for
+// this one leaves those in flight, where a scalar load would be waited for together with the
+// kernel arguments before anything else is issued.
+SPEC_DEVINL int len_first(const int32_t* p) {
+  uint64_t v = (uint64_t)p;
+  asm volatile("" : "+v"(v));
+  return *(const __attribute__((address_space(1))) int32_t*)v;  // global, not flat
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
   using A = Act<DT>;
@@ -593,12 +603,10 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   const int lane = t & 63, wave = t >> 6;
   const CacheView& cv = a.cache;
   const int mseq = a.rm.mseq, G = a.n_q / cv.n_kv;
-  const int L = a.rm.len[b] + a.rm.pos_off;
-  const int total = L + mseq;
   const int c0 = chunk * C;
-  if (c0 >= total) return;
   const int R = mseq * G, QT = (R + 15) / 16;
   const int q_dim = a.n_q * HD, kv_dim = cv.n_kv * HD;
+  const int L = len_first(a.rm.len + b) + a.rm.pos_off;
   bf16_t* qs = (bf16_t*)smraw;   // [QT*16][KP]
   bf16_t* ks = qs + QT * 16 * KP;  // [C][KP]
   bf16_t* vt = ks + C * KP;        // [HD][VP]
@@ -606,7 +614,9 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   const int64_t cbase = ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap) * HD;
   bf16_t* kc = (bf16_t*)cv.k + cbase;
   const bf16_t* vc = (const bf16_t*)cv.v + cbase;
-  // cached keys and values, 16 bytes at a time, issued before anything else; zeros past the end
+  // cached keys and values, 16 bytes at a time, go out right behind the length (no address
+  // depends on it), so the two round trips overlap; zeros past the end are put in after the
+  // loads
   constexpr int NV = C * (HD / 8) / 256;
   uint4 kreg[NV], vreg[NV];
   // branch-free: addresses are clamped into the cache, out-of-range values zeroed after the load
@@ -618,6 +628,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
     kreg[v] = *(const uint4*)(kc + (int64_t)pc * HD + d8);
     vreg[v] = *(const uint4*)(vc + (int64_t)pc * HD + d8);
   }
+  const int total = L + mseq;
+  // (a chunk past the last position runs through with every key masked; no combine reads it)
   // the new keys of this chunk (positions p0 .. p1-1): the first NKH * 256 of their
   // (position, pair) items are loaded here too, so the block waits for one round trip
   const int p0 = max(c0, L), p1 = min(c0 + C, total), nnew = max(p1 - p0, 0) * HALF;
@@ -664,9 +676,11 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   for (int v = 0; v < NV; ++v) {
     const int idx = t + 256 * v;
     const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-    if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
-    else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
-    const uint4 vv = p < total ? vreg[v] : make_uint4(0, 0, 0, 0);
+    // value selects (a select of the two sources' addresses would put kreg in scratch memory)
+    const uint4 kz = make_uint4(0, 0, 0, 0);
+    const uint4 kk = p < L ? kreg[v] : kz;
+    if (p < L || p >= total) *(uint4*)(ks + j * KP + d8) = kk;
+    const uint4 vv = p < total ? vreg[v] : kz;
     const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
     // V^T rows d8..d8+7 are all in swizzle group d8/8: the key index is xor-ed with 8*(group&7),
     // which spreads the 16 lanes that write one key over 8 banks and keeps 8-key runs whole
