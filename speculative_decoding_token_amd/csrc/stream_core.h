@@ -214,8 +214,12 @@ SPEC_DEVINL float unit_scale(const StreamArgs& a, int u, int t, int c) {
   } else if (EPI == EPI_SWIGLU) {
     m = t;
   }
-  const float* p = m == 0 ? a.w0s : (m == 1 ? a.w1s : a.w2s);
-  return p[r + c];
+  // readfirstlane before the select, as in unit_rows: a select of members would become a load
+  // of the argument block, waited for before anything else
+  const uint64_t p = m == 0 ? uni64(a.w0s) : (m == 1 ? uni64(a.w1s) : uni64(a.w2s));
+  // a global load: a flat one could return out of order, and every wait behind it would then
+  // have to be for all loads (the weight stages in flight included)
+  return ((const __attribute__((address_space(1))) float*)p)[r + c];
 }
 
 // One projection over this workgroup's units (blockIdx.x, blockIdx.x + grid, ...).
