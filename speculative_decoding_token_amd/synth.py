@@ -186,6 +186,23 @@ def make_weights_fp8(shape: ModelShape, seed: int = 0, device: str = "cpu", tag:
     }
 
 
+def make_gdn_inputs(T: int, n_heads: int, d_k: int, d_v: int, seed: int = 0, device: str = "cpu"):
+    """Inputs of T tokens to one linear-attention layer and its committed state, float32:
+    q [T, H, d_k] ~ N(0, 1/d_k); k [T, H, d_k] uniform on the unit sphere (normalized normal
+    draws); v [T, H, d_v] ~ N(0, 1); decays alpha [T, H] ~ U(0.8, 1); write strengths
+    beta [T, H] ~ U(0.1, 0.9); state [H, d_v, d_k] ~ N(0, 0.3^2)."""
+    g = torch.Generator(device="cpu").manual_seed(tensor_seed(seed, "gdn", T, f"{n_heads}:{d_k}:{d_v}"))
+    q = torch.randn((T, n_heads, d_k), generator=g) / d_k ** 0.5
+    k = torch.randn((T, n_heads, d_k), generator=g)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn((T, n_heads, d_v), generator=g)
+    alpha = torch.rand((T, n_heads), generator=g) * 0.2 + 0.8
+    beta = torch.rand((T, n_heads), generator=g) * 0.8 + 0.1
+    state = torch.randn((n_heads, d_v, d_k), generator=g) * 0.3
+    return {n: t.to(device=device, dtype=torch.float32).contiguous()
+            for n, t in dict(q=q, k=k, v=v, alpha=alpha, beta=beta, state=state).items()}
+
+
 def make_mtp(shape: ModelShape, seed: int, device: str, tag: str, std: float = 0.02):
     """One extra decoder layer plus its input norms and the [d, 2d] input projection."""
     dt = _torch_dtype(shape.dtype)
