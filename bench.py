@@ -127,6 +127,39 @@ def gate_up_bytes(shape, M, fp8=False):
     return w + M * d * 2 + M * f * 2
 
 
+def gdn_state_run(torch, synth, B, K, reps=20, layers=48, H=32, dv=128):
+    """Linear-attention layer state under speculation (spec_gdn_commit_forward): one launch per
+    layer per cycle commits the previous verify's kept tokens (K+1, every draft accepted: the
+    most state work) and runs this verify's K+1 tokens.  `layers` states of H heads of
+    dv x 128 float32 (2 MB a layer at 32 x 128 x 128), launched back to back on one stream."""
+    T = 2 * (K + 1)
+    x = synth.make_gdn_inputs(T, H, 128, dv, seed=0, device="cuda")
+    states = x["state"].unsqueeze(0).repeat(layers, 1, 1, 1).contiguous()
+    out = torch.empty((K + 1, H, dv), device="cuda")
+    st = torch.cuda.current_stream()
+
+    def cycle():
+        for l in range(layers):
+            B.spec_gdn_commit_forward(H, 128, dv, states[l], x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                                      K + 1, K + 1, out, st)
+    cycle()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        cycle()
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
+    state_bytes = H * dv * 128 * 4
+    # state read and written, this call's token rows (q only for the forward half), outputs
+    nbytes = 2 * state_bytes + T * H * (128 + dv + 2) * 4 + (K + 1) * H * 128 * 4 + (K + 1) * H * dv * 4
+    return {"shape": f"{layers} layers x {H} heads x {dv} x 128 float32 state ({state_bytes / 2**20:.0f} MiB a layer)",
+            "tokens_per_launch": f"commit {K + 1} + forward {K + 1}", "us_per_layer": us, "bytes_per_layer": nbytes,
+            "GBps": nbytes / (us * 1e-6) / 1e9, "frac_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "timing": f"HIP events around {reps} cycles of {layers} back-to-back launches"}
+
+
 def cpu_baseline(tshape, dshape, tw, dw, K, t_layers=3, d_layers=4):
     """The oracle (numpy, fp64) timed on a bounded sample of one cycle at the full shapes:
     per model, a one-row forward through no layer (embedding, final norm, vocab head) and
@@ -375,6 +408,9 @@ def main():
         del eng8, tw8
         torch.cuda.empty_cache()
 
+    from speculative_decoding_token_amd import binding as SB
+    gdn_run = gdn_state_run(torch, synth, SB, K)
+
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
@@ -400,6 +436,7 @@ def main():
         "teacher_forced": teacher,
         "adaptive_depth": adaptive,
         "fp8_weights": fp8_run,
+        "linear_attention_state": gdn_run,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline and Bn == 1 and not fp8:

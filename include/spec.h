@@ -434,6 +434,32 @@ int spec_accept_lists(const int32_t* draft_tok /*device*/, const spec_probs* q,
                       int32_t* out_tok /*device*/, uint8_t* near_tie /*device or NULL*/,
                       void* stream);
 
+/* ---- linear-attention layer state under speculation ----------------------------------
+ * "Speculative Decoding on Apple Silicon: 119% Faster...", section "Why this needed a patch to
+ * mlx_lm at all": a linear-attention (Gated DeltaNet-style) layer of a hybrid model keeps one
+ * fixed-size recurrent state, so a rejected draft cannot be sliced off; the state from before
+ * the speculative forward is kept and the accepted tokens are run through the recurrence
+ * again.  The recurrence (the gated delta rule; the pages name the layer, not the formula),
+ * per head with a state S of d_v rows and d_k = 128 columns:
+ *   S <- alpha S (I - beta k k^T) + beta v k^T,   o = S q.
+ * One call does one cycle's state work: the first n_commit tokens (those the previous verify
+ * kept: its first input and its accepted drafts) are folded into the committed state, which is
+ * written back; then the next n_fwd tokens (this verify's inputs) run from it without changing
+ * it and give their outputs.  A call with n_fwd = 0 only commits; n_commit = 0 only runs.
+ * All buffers are device float32, token-major, caller-owned: q, k [T][n_heads][d_k],
+ * v [T][n_heads][d_v], alpha, beta [T][n_heads] with T = n_commit + n_fwd (q rows below
+ * n_commit are not read); state [n_heads][d_v][d_k] (in/out); out [n_fwd][n_heads][d_v].
+ * q and k come normalized and alpha, beta activated, as the layer's projections leave them.
+ * Returns SPEC_E_UNSUPPORTED unless d_k = 128 and d_v is a multiple of 32, SPEC_E_RANGE for
+ * more than SPEC_GDN_MAX_TOKENS tokens; asynchronous on stream (errors in spec_last_error(NULL)). */
+#define SPEC_GDN_MAX_TOKENS 64
+typedef struct spec_gdn_shape {
+  int32_t n_heads, d_k, d_v;
+} spec_gdn_shape;
+int spec_gdn_commit_forward(const spec_gdn_shape* shape, float* state, const float* q, const float* k,
+                            const float* v, const float* alpha, const float* beta, int32_t n_commit,
+                            int32_t n_fwd, float* out, void* stream);
+
 /* n uniforms of Philox4x32-10 under key `seed`: counters ctr (device uint32 [n, 4]) ->
  * out (device float32 [n]), u = (word0 >> 8) * 2^-24. */
 int spec_philox_uniforms(uint64_t seed, const uint32_t* ctr /*device*/, int32_t n,

@@ -38,8 +38,9 @@ EXPORTED = [
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
     "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
-    "spec_depth_init", "spec_depth_choose", "spec_depth_update",
+    "spec_depth_init", "spec_depth_choose", "spec_depth_update", "spec_gdn_commit_forward",
 ]
+GDN_MAX_TOKENS = 64
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",
                 "truncate", "sample", "accept", "kv_trim", "forward", "13", "14", "15"]
@@ -69,6 +70,10 @@ class spec_model_desc(C.Structure):
                 ("final_norm", C.c_void_p), ("layers", C.POINTER(spec_layer_weights)),
                 ("weights", C.c_int32), ("lm_head_scale", C.c_void_p),
                 ("layer_scales", C.POINTER(spec_layer_scales))]
+
+
+class spec_gdn_shape(C.Structure):
+    _fields_ = [("n_heads", C.c_int32), ("d_k", C.c_int32), ("d_v", C.c_int32)]
 
 
 class spec_mtp_desc(C.Structure):
@@ -144,6 +149,7 @@ def lib(path: str = LIB_PATH):
         "spec_accept_lists": ([P, C.POINTER(spec_probs), C.POINTER(spec_probs), I32, I32, I32, U64, U64,
                                P, P, P, P], C.c_int),
         "spec_philox_uniforms": ([U64, P, I32, P, P], C.c_int),
+        "spec_gdn_commit_forward": ([C.POINTER(spec_gdn_shape), P, P, P, P, P, P, I32, I32, P, P], C.c_int),
         "spec_ngram_match": ([P, P, I32, I32, I32, I32, I32, P, P, P, P], C.c_int),
         "spec_profile": ([P, I32], C.c_int),
         "spec_profile_repeat": ([P, I32, I32], C.c_int),
@@ -354,6 +360,15 @@ def spec_philox_uniforms(seed: int, ctr, n: int, out, stream=None) -> None:
     rc = lib().spec_philox_uniforms(seed, _ptr(ctr), n, _ptr(out), _stream(stream))
     if rc:
         raise SpecError(rc, "spec_philox_uniforms")
+
+
+def spec_gdn_commit_forward(n_heads: int, d_k: int, d_v: int, state, q, k, v, alpha, beta,
+                            n_commit: int, n_fwd: int, out, stream=None) -> None:
+    """Fold the first n_commit token rows into ``state`` (written back), then run the next n_fwd
+    rows from it into ``out`` (float32 device tensors, layouts as in include/spec.h)."""
+    shape = spec_gdn_shape(n_heads, d_k, d_v)
+    _check(lib().spec_gdn_commit_forward(C.byref(shape), _ptr(state), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), n_commit, n_fwd, _ptr(out), _stream(stream)))
 
 
 def spec_ngram_match(ctx_tokens, lengths, batch: int, ld: int, k: int, n_min: int, max_match: int,

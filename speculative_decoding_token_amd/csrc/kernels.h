@@ -136,6 +136,26 @@ struct AttnArgs {
 
 constexpr int ATTN_FEW_ROWS = 4;
 
+// Linear-attention (gated delta rule) state: gdn.hip.  Token-major rows: q, k [T][n_heads][128],
+// v [T][n_heads][d_v], alpha, beta [T][n_heads] with T = n_commit + n_fwd; state
+// [n_heads][d_v][128]; out [n_fwd][n_heads][d_v].  The first n_commit tokens are folded into
+// the state, which is written back; the next n_fwd run from it (unchanged) and give out.
+constexpr int GDN_DK = 128;
+constexpr int GDN_MAX_TOKENS = 64;
+struct GdnArgs {
+  float* state;
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* alpha;
+  const float* beta;
+  float* out;
+  int n_heads, d_v;
+  int n_commit, n_fwd;
+};
+hipError_t gdn_init();
+hipError_t launch_gdn(const GdnArgs& a, hipStream_t st);
+
 constexpr int ATTN_CHUNK = 64;
 constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions
 constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)

@@ -1,5 +1,6 @@
 // Host side of the C ABI: validation, workspace carving, the forward sequence of each
 // model, and the draft / verify / accept / trim state machine.  No device allocation.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -1544,6 +1545,43 @@ int spec_accept_lists(const int32_t* draft_tok, const spec_probs* q, const spec_
   a.out_tok = out_tok;
   a.near_tie = near_tie;
   return launch_accept(a, (hipStream_t)stream) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
+}
+
+static_assert(GDN_MAX_TOKENS == SPEC_GDN_MAX_TOKENS && GDN_DK == 128, "gdn limits");
+
+int spec_gdn_commit_forward(const spec_gdn_shape* shape, float* state, const float* q, const float* k,
+                            const float* v, const float* alpha, const float* beta, int32_t n_commit,
+                            int32_t n_fwd, float* out, void* stream) {
+  if (!shape) return fail(nullptr, SPEC_E_INVAL, "gdn: null shape");
+  if (shape->n_heads < 1 || shape->d_v < 1 || shape->d_k < 1 || n_commit < 0 || n_fwd < 0)
+    return fail(nullptr, SPEC_E_INVAL, "gdn: non-positive shape or negative token count");
+  if (shape->d_k != GDN_DK || shape->d_v % 32)
+    return fail(nullptr, SPEC_E_UNSUPPORTED, "gdn: d_k must be %d and d_v a multiple of 32", GDN_DK);
+  if (n_commit + n_fwd > GDN_MAX_TOKENS)
+    return fail(nullptr, SPEC_E_RANGE, "gdn: more than %d tokens in one call", GDN_MAX_TOKENS);
+  if (n_commit + n_fwd == 0) return SPEC_OK;
+  if (!state || !k || !v || !alpha || !beta || (n_fwd > 0 && (!q || !out)))
+    return fail(nullptr, SPEC_E_INVAL, "gdn: null pointer");
+  static std::atomic<bool> ready{false};
+  if (!ready.load()) {
+    const hipError_t e = gdn_init();
+    if (e != hipSuccess) return fail(nullptr, SPEC_E_HIP, "gdn init: %s", hipGetErrorString(e));
+    ready.store(true);
+  }
+  GdnArgs a{};
+  a.state = state;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.n_heads = shape->n_heads;
+  a.d_v = shape->d_v;
+  a.n_commit = n_commit;
+  a.n_fwd = n_fwd;
+  const hipError_t e = launch_gdn(a, (hipStream_t)stream);
+  return e == hipSuccess ? SPEC_OK : fail(nullptr, SPEC_E_HIP, "gdn launch: %s", hipGetErrorString(e));
 }
 
 int spec_philox_uniforms(uint64_t seed, const uint32_t* ctr, int32_t n, float* out, void* stream) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(decl) <= exported
 
 
-STRUCTS = ["spec_layer_weights", "spec_layer_scales", "spec_model_desc", "spec_mtp_desc", "spec_sampler", "spec_ngram_cfg",
+STRUCTS = ["spec_layer_weights", "spec_layer_scales", "spec_gdn_shape", "spec_model_desc", "spec_mtp_desc", "spec_sampler", "spec_ngram_cfg",
            "spec_config", "spec_probs", "spec_stats", "spec_gate"]
 
 
@@ -120,6 +120,25 @@ def test_fp8_rows_cap_the_workspace():
     fp8 = B.spec_workspace_size(cfg)
     # the same caches; activations (logits first) for 2 x 8 rows per forward instead of 2 x 16
     assert 16 * t.vocab * 4 < native - fp8 < 16 * t.vocab * 4 + (32 << 20)
+
+
+@pytest.mark.parametrize("shape,nc,nf,code", [
+    ((0, 128, 128), 1, 1, B.SPEC_E_INVAL),
+    ((4, 64, 128), 1, 1, B.SPEC_E_UNSUPPORTED),
+    ((4, 128, 48), 1, 1, B.SPEC_E_UNSUPPORTED),
+    ((4, 128, 128), 40, 25, B.SPEC_E_RANGE),
+    ((4, 128, 128), -1, 1, B.SPEC_E_INVAL),
+    ((4, 128, 128), 1, 1, B.SPEC_E_INVAL),   # null buffers
+])
+def test_gdn_argument_checks(shape, nc, nf, code):
+    # every case is rejected on the host before any HIP call
+    with pytest.raises(B.SpecError) as e:
+        B.spec_gdn_commit_forward(*shape, None, None, None, None, None, None, nc, nf, None, stream=0)
+    assert e.value.code == code
+
+
+def test_gdn_nothing_to_do_is_ok():
+    B.spec_gdn_commit_forward(4, 128, 128, None, None, None, None, None, None, 0, 0, None, stream=0)
 
 
 def test_greedy_sampler_ignores_top_k():
