@@ -295,8 +295,9 @@ struct FwdArgs {
   int trace_cap;
 };
 bool forward_supported(int M, int mseq, int d, int n_q, int n_kv, int hd, int ffn, int vocab);
-// barrier words and attention tickets for up to `batch` sequences of n_kv kv heads; the error
-// word is the 32-bit word at byte forward_error_offset()
+// bytes of the one-launch forward's barrier words (eight group counters, a top counter, a
+// release word, the error word at byte forward_error_offset()); the same for any batch and
+// n_kv, which the signature keeps for per-sequence words
 size_t forward_sync_bytes(int batch, int n_kv);
 constexpr size_t forward_error_offset() { return 10 * 32 * 4; }
 // per device: LDS limits; *grid = workgroups of one launch (one per compute unit, a multiple
