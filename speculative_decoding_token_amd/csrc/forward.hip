@@ -387,6 +387,15 @@ struct Attn {
   }
 };
 
+// The cached keys and values of a group's first item (positions before the new tokens, which
+// the QKV step does not touch) are loaded while the workgroup waits at the barrier before the
+// attention step: their round trip overlaps the barrier's.
+template <int HD>
+SPEC_DEVINL void attn_prefetch(const FwdArgs& a, const int* s_len, int layer, uint4 (&kreg)[Attn<HD>::NV],
+                               uint4 (&vreg)[Attn<HD>::NV]) {
+  Attn<HD>::load_kv(a, layer, Attn<HD>::item_of(a, s_len, 0), kreg, vreg);
+}
+
 template <int HD>
 SPEC_DEVINL void attn_step(const FwdArgs& a, const int* s_len, int layer, char* sm, uint4 (&kreg)[Attn<HD>::NV],
                            uint4 (&vreg)[Attn<HD>::NV]) {
@@ -399,7 +408,7 @@ SPEC_DEVINL void attn_step(const FwdArgs& a, const int* s_len, int layer, char* 
   const int slots = gridDim.x * ATT_GROUPS;
   for (int base = 0; base < items; base += slots) {
     const typename A::Item it = A::item_of(a, s_len, base);
-    A::load_kv(a, layer, it, kreg, vreg);
+    if (base > 0) A::load_kv(a, layer, it, kreg, vreg);  // the first item's came with the barrier
     A::item(a, s_len, layer, gsm, it, kreg, vreg);
   }
 }
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(SNW * 64) void forward_kernel(FwdArgs a) {
 #pragma clang loop unroll(disable)
   for (int l = 0; l < a.n_layers; ++l) {
     QKV::run(qkv_args(a, l), sm, P);
-    grid_sync(s, [] {});
+    grid_sync(s, [&] { attn_prefetch<HD>(a, s_len, l, kreg, vreg); });
     attn_step<HD>(a, s_len, l, sm, kreg, vreg);
     grid_sync(s, [&] { OP::prefetch(o_args(a, l), sm, P); });
     combine_step<HD>(a, s_len, red);
