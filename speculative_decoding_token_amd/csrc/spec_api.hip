@@ -1562,11 +1562,16 @@ int spec_gdn_commit_forward(const spec_gdn_shape* shape, float* state, const flo
   if (n_commit + n_fwd == 0) return SPEC_OK;
   if (!state || !k || !v || !alpha || !beta || (n_fwd > 0 && (!q || !out)))
     return fail(nullptr, SPEC_E_INVAL, "gdn: null pointer");
-  static std::atomic<bool> ready{false};
-  if (!ready.load()) {
-    const hipError_t e = gdn_init();
+  // the kernel's LDS limit is a per-device attribute: set it once on each device used
+  static std::atomic<bool> ready[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, SPEC_E_HIP, "gdn: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(nullptr, SPEC_E_UNSUPPORTED, "gdn: device %d", dev);
+  if (!ready[dev].load()) {
+    e = gdn_init();
     if (e != hipSuccess) return fail(nullptr, SPEC_E_HIP, "gdn init: %s", hipGetErrorString(e));
-    ready.store(true);
+    ready[dev].store(true);
   }
   GdnArgs a{};
   a.state = state;
@@ -1580,7 +1585,7 @@ int spec_gdn_commit_forward(const spec_gdn_shape* shape, float* state, const flo
   a.d_v = shape->d_v;
   a.n_commit = n_commit;
   a.n_fwd = n_fwd;
-  const hipError_t e = launch_gdn(a, (hipStream_t)stream);
+  e = launch_gdn(a, (hipStream_t)stream);
   return e == hipSuccess ? SPEC_OK : fail(nullptr, SPEC_E_HIP, "gdn launch: %s", hipGetErrorString(e));
 }
 
