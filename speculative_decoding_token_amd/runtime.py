@@ -25,6 +25,7 @@ class Cycle:
     logits: Optional[torch.Tensor] = None      # [batch, k+1, V] when kept
     p: Optional[list] = None                   # host lists when kept
     q: Optional[list] = None
+    verify_ms: Optional[float] = None          # Engine.run(time_verify=True)
 
 
 class Engine:
@@ -115,16 +116,26 @@ class Engine:
 
     # ---- one cycle
     def buffers(self, batch: int, k: int):
-        """Views of this batch's cycle buffers, sized once for max_k."""
+        """Views of this batch's cycle buffers, sized once for max_k.  The accepted counts,
+        near-tie flags, emitted tokens and drafts share one int32 device array (each region
+        256-byte aligned), so a cycle's results come back in one copy."""
         if getattr(self, "_buf_batch", None) != batch:
             dev, mk = "cuda", max(self.max_k, 1)
+            sizes = dict(n=batch, tie=(batch + 3) // 4, out=batch * (mk + 1), draft=batch * mk)
+            self._off, o = {}, 0
+            for name, sz in sizes.items():
+                self._off[name] = o
+                o += (sz + 63) // 64 * 64
+            self._dev = torch.zeros((o,), dtype=torch.int32, device=dev)
+            self._host = [torch.zeros((o,), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+            d, off = self._dev, self._off
             self._flat = dict(
-                draft=torch.zeros((batch * mk,), dtype=torch.int32, device=dev),
+                draft=d[off["draft"]: off["draft"] + batch * mk],
                 q=B.Probs(batch * mk, self.cap),
                 p=B.Probs(batch * (mk + 1), self.cap),
-                n=torch.zeros((batch,), dtype=torch.int32, device=dev),
-                out=torch.zeros((batch * (mk + 1),), dtype=torch.int32, device=dev),
-                tie=torch.zeros((batch,), dtype=torch.uint8, device=dev),
+                n=d[off["n"]: off["n"] + batch],
+                out=d[off["out"]: off["out"] + batch * (mk + 1)],
+                tie=d[off["tie"]: off["tie"] + sizes["tie"]].view(torch.uint8)[:batch],
             )
             self._buf_batch = batch
             self._logits = {}
@@ -133,13 +144,25 @@ class Engine:
         return dict(draft=f["draft"][: batch * kk].view(batch, kk), q=f["q"], p=f["p"], n=f["n"],
                     out=f["out"][: batch * (k + 1)].view(batch, k + 1), tie=f["tie"])
 
+    def _results(self, h: torch.Tensor, batch: int, k: int, kk: int) -> Cycle:
+        """A cycle's results from a host copy h of the packed array: k tokens verified per
+        sequence, drafts stored at row stride kk."""
+        off = self._off
+        n = h[off["n"]: off["n"] + batch].tolist()
+        tie = h[off["tie"]:].view(torch.uint8)[:batch].tolist()
+        out = h[off["out"]: off["out"] + batch * (k + 1)].view(batch, k + 1).tolist()
+        dr = h[off["draft"]: off["draft"] + batch * kk].view(batch, kk).tolist()
+        return Cycle(drafts=[row[:k] for row in dr], n=n, tokens=[out[b][: n[b] + 1] for b in range(batch)],
+                     near_tie=tie)
+
     def cycle(self, batch: int, k: int, rnd: int, drafts: Optional[torch.Tensor] = None,
               keep: bool = False, sync: bool = True, events: Optional[dict] = None) -> Optional[Cycle]:
         """draft_step (unless ``drafts`` are given) -> verify_step -> accept -> kv_trim.
         ``events``: a dict that receives (start, end) CUDA events of each call, recorded on
         the engine stream."""
         with self._enter():
-            return self._cycle(batch, k, rnd, drafts, keep, sync, events)
+            c = self._cycle(batch, k, rnd, drafts, keep, sync, events)
+            return c if sync else None
 
     def _mark(self, events, name, i):
         if events is not None:
@@ -149,6 +172,7 @@ class Engine:
 
     def _cycle(self, batch, k, rnd, drafts, keep, sync, events=None):
         buf = self.buffers(batch, k)
+        kk0 = max(k, 1)
         if k > 0:
             if drafts is None:
                 self._mark(events, "draft", 0)
@@ -177,16 +201,49 @@ class Engine:
         B.kv_trim(self.ctx, buf["n"], batch)
         self._mark(events, "accept", 1)
         if not sync:
-            return None
-        n = buf["n"].cpu().tolist()
-        out = buf["out"].cpu().tolist()
-        dr = buf["draft"].cpu().tolist() if k > 0 else [[] for _ in range(batch)]
-        c = Cycle(drafts=[row[:k] for row in dr], n=n,
-                  tokens=[out[b][: n[b] + 1] for b in range(batch)], near_tie=buf["tie"].cpu().tolist())
+            return k, kk0
+        h = self._host[0]
+        h.copy_(self._dev, non_blocking=True)
+        self.stream.synchronize()
+        c = self._results(h, batch, k, kk0)
         if keep:
             c.logits = logits.clone()
             c.p = buf["p"].to_lists(batch * (k + 1))
             c.q = buf["q"].to_lists(batch * k) if k > 0 else []
+        return c
+
+    def run(self, batch: int, k: int, rnd0: int, n_cycles: int, time_verify: bool = False) -> List[Cycle]:
+        """n_cycles cycles at a fixed k with the next cycle queued before the host reads the
+        current one: each cycle's packed results are copied to one of two pinned host arrays
+        behind its kernels, and the host parses cycle r while the device runs cycle r + 1.
+        Lengths and last tokens live on the device, so nothing of cycle r is needed to queue
+        cycle r + 1 (the n-gram drafter reads its match count back and is excluded).
+        ``time_verify`` stores each cycle's verify_step time (ms, events on the engine
+        stream) in Cycle.verify_ms.  Tokens are the same as n_cycles calls of ``cycle``."""
+        if self.drafter == "ngram" and k > 0:
+            raise ValueError("the n-gram drafter reads its match count back every cycle; use cycle()")
+        cycles: List[Cycle] = []
+        evs = [{}, {}] if time_verify else [None, None]
+        pending = None
+        with self._enter():
+            for r in range(n_cycles):
+                slot = r % 2
+                kv, kk = self._cycle(batch, k, rnd0 + r, None, False, False, evs[slot])
+                self._host[slot].copy_(self._dev, non_blocking=True)
+                done = torch.cuda.Event()
+                done.record(self.stream)
+                if pending is not None:
+                    cycles.append(self._collect(*pending))
+                pending = (slot, done, batch, kv, kk, evs[slot])
+            if pending is not None:
+                cycles.append(self._collect(*pending))
+        return cycles
+
+    def _collect(self, slot, done, batch, k, kk, ev):
+        done.synchronize()
+        c = self._results(self._host[slot], batch, k, kk)
+        if ev is not None:
+            c.verify_ms = ev["verify"][0].elapsed_time(ev["verify"][1])
         return c
 
     def generate(self, n_new: int, k: int, batch: int = 1, rnd0: int = 0, keep: bool = False,

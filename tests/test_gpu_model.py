@@ -326,3 +326,24 @@ def test_tiny_adaptive_depth_generation_parity(temperature, same):
         assert max(ks_gpu) == KMAX
     elif temperature == 0.0:
         assert ks_gpu[-1] == KMIN
+
+
+def test_pipelined_run_equals_cycle_by_cycle():
+    """Engine.run (cycle r + 1 queued before cycle r's tokens are read) emits the same
+    drafts, counts and tokens as cycle() called cycle by cycle, greedy and sampled, and
+    keeps going from the same device state afterwards."""
+    _, pt = prompt_tensor()
+    for temp in (0.0, 1.0):
+        a, _, _ = tiny_engine(temp)
+        b, _, _ = tiny_engine(temp)
+        a.prefill(pt)
+        b.prefill(pt)
+        ca = [a.cycle(1, 4, r) for r in range(9)]
+        cb = b.run(1, 4, 0, 9, time_verify=True)
+        assert [c.tokens for c in ca] == [c.tokens for c in cb]
+        assert [c.drafts for c in ca] == [c.drafts for c in cb]
+        assert [c.n for c in ca] == [c.n for c in cb]
+        assert [c.near_tie for c in ca] == [c.near_tie for c in cb]
+        assert all(c.verify_ms is not None and c.verify_ms > 0 for c in cb)
+        assert a.cycle(1, 2, 9).tokens == b.cycle(1, 2, 9).tokens
+        assert a.lengths(1) == b.lengths(1)
