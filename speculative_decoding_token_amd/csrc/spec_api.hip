@@ -1557,7 +1557,7 @@ int spec_gdn_commit_forward(const spec_gdn_shape* shape, float* state, const flo
     return fail(nullptr, SPEC_E_INVAL, "gdn: non-positive shape or negative token count");
   if (shape->d_k != GDN_DK || shape->d_v % 32)
     return fail(nullptr, SPEC_E_UNSUPPORTED, "gdn: d_k must be %d and d_v a multiple of 32", GDN_DK);
-  if (n_commit + n_fwd > GDN_MAX_TOKENS)
+  if (n_commit > GDN_MAX_TOKENS || n_fwd > GDN_MAX_TOKENS || n_commit + n_fwd > GDN_MAX_TOKENS)
     return fail(nullptr, SPEC_E_RANGE, "gdn: more than %d tokens in one call", GDN_MAX_TOKENS);
   if (n_commit + n_fwd == 0) return SPEC_OK;
   if (!state || !k || !v || !alpha || !beta || (n_fwd > 0 && (!q || !out)))

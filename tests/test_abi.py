@@ -127,6 +127,7 @@ def test_fp8_rows_cap_the_workspace():
     ((4, 64, 128), 1, 1, B.SPEC_E_UNSUPPORTED),
     ((4, 128, 48), 1, 1, B.SPEC_E_UNSUPPORTED),
     ((4, 128, 128), 40, 25, B.SPEC_E_RANGE),
+    ((4, 128, 128), 2**31 - 1, 1, B.SPEC_E_RANGE),   # no wrap of the token sum
     ((4, 128, 128), -1, 1, B.SPEC_E_INVAL),
     ((4, 128, 128), 1, 1, B.SPEC_E_INVAL),   # null buffers
 ])
