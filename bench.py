@@ -92,11 +92,11 @@ DOMINANT = {
     "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
-               "sources": ["stream_core.h", "stream.hip"], "traffic": 201975307, "sha256": "2de51eeff7a693eb"},
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 201963544, "sha256": "89d117fa1a7613cc"},
     "stream_fp8": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 4, 1> (target gate/up + SwiGLU over E4M3 weights "
                              "with row scales, streamed through an LDS ring, one workgroup per CU)",
                    "slot": "target.gate_up",
-                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101528415, "sha256": "2de51eeff7a693eb"},
+                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101514547, "sha256": "89d117fa1a7613cc"},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",

@@ -249,7 +249,7 @@ struct StreamArgs {
   RowMap rm;
 };
 // Whether M rows and reduction length K are covered.  bf16 weights: K in whole stages (1024;
-// 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 4096, 5120}.  fp8 weights
+// 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 3072, 4096, 5120}.  fp8 weights
 // (wbytes 1): stages of 2048 (1024 for SwiGLU), resident inputs for K in {2048, 4096}, streamed
 // inputs for the residual epilogue, and at most units_per_wg * tiles * 16 <= 1024 row scales
 // per workgroup.

@@ -465,7 +465,7 @@ bool attn_few(spec_ctx* c, const Model& m) {
 
 // Whether the forwards of m over M rows run on the weight-streaming projections: bf16,
 // at most 16 rows, reduction lengths in whole stages (normalized inputs: d in {1024, 2048,
-// 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
+// 3072, 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
 // gain-multiplied rows.
 bool stream_shapes(spec_ctx* c, const Model& m, int M) {
   const spec_model_desc& d = m.d;

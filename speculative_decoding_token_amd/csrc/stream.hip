@@ -18,7 +18,7 @@ const void* kptr() {
   return (const void*)stream_gemm_kernel<EPI, NST, WB>;
 }
 
-// Resident-slice variants: K = NST * KS for K in {1024, 2048, 4096, 5120} (bf16); fp8: K in
+// Resident-slice variants: K = NST * KS for K in {1024, 2048, 3072, 4096, 5120} (bf16); fp8: K in
 // {2048, 4096}, and streamed inputs only for the residual epilogue.
 int nst_of(int epi, int K, int wbytes) {
   const int ks = (epi == EPI_SWIGLU ? 512 : 1024) * (wbytes == 1 ? 2 : 1);
@@ -29,7 +29,7 @@ int nst_of(int epi, int K, int wbytes) {
     return epi == EPI_RESID ? 0 : -1;
   }
   const int k1 = K / 1024;
-  if (K % 1024 == 0 && (k1 == 1 || k1 == 2 || k1 == 4 || k1 == 5)) return n;
+  if (K % 1024 == 0 && k1 >= 1 && k1 <= 5) return n;
   return 0;
 }
 
@@ -39,6 +39,7 @@ const void* kernel_for(int nst) {
   switch (nst / T) {
     case 1: return kptr<EPI, T * 1>();
     case 2: return kptr<EPI, T * 2>();
+    case 3: return kptr<EPI, T * 3>();
     case 4: return kptr<EPI, T * 4>();
     case 5: return kptr<EPI, T * 5>();
     default: return nullptr;
@@ -90,7 +91,7 @@ size_t stream_lds_bytes() { return (size_t)sk::LDS_BYTES; }
 hipError_t stream_init() {
   const int lds = (int)stream_lds_bytes();
   for (int epi : {EPI_STORE, EPI_RESID, EPI_QKV, EPI_SWIGLU}) {
-    for (int k1 : {0, 1, 2, 4, 5}) {
+    for (int k1 : {0, 1, 2, 3, 4, 5}) {
       const void* k = select(epi, k1 * (epi == EPI_SWIGLU ? 2 : 1), 2);
       const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
       if (e != hipSuccess) return e;
