@@ -20,15 +20,11 @@ x += Wd . (silu(Wg n2) * (Wu n2)) with n2 = RMSNorm(x); logits = Wlm . RMSNorm(x
 RMSNorm eps 1e-6, rotate-half RoPE with theta 1e6, no biases, q-head h reads kv-head
 floor(h * n_kv / n_q), scale 1/sqrt(head_dim).
 
-Arithmetic is float64.  An RMSNorm that feeds a projection is taken in its folded form,
-W . RMSNorm(x) = (W . (x * g)) / rms(x) with rms(x) = sqrt(mean(x^2) + eps): the same map,
-with the projection reading the gain-multiplied row and its output scaled by 1/rms(x) (see
-``normed``).  For a bf16 model the precision contract rounds to bfloat16 the gain-multiplied
-rows x * g that the projections read, q, k and v (k and v are stored that way), the attention
-output and the SwiGLU product, and keeps the residual stream in float32; logits are float32.
-An f32 model rounds nothing but the final logits to float32.  The multi-token-prediction
-head's two input norms are plain RMSNorms (their rows are concatenated before the projection,
-so no single row scale exists).
+Arithmetic is float64.  For a bf16 model the precision contract rounds to bfloat16 the
+normed rows RMSNorm(x) * g that the projections read, q, k and v (k and v are stored that
+way), the attention output and the SwiGLU product, and keeps the residual stream in float32;
+softmax weights and logits are float32 quantities (computed in float64 here).  An f32 model
+rounds nothing but the final logits to float32.
 """
 from __future__ import annotations
 
@@ -52,11 +48,19 @@ class Spec:
     bf16: bool
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
+    # float32 arithmetic between the rounding points instead of float64: the same contract
+    # evaluated the way a float32 implementation would, to measure how far two correct
+    # evaluations of it drift apart (its bf16 rounding points amplify float32 rounding)
+    arith32: bool = False
 
     @staticmethod
-    def from_shape(s) -> "Spec":
+    def from_shape(s, arith32: bool = False) -> "Spec":
         return Spec(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.d_ffn,
-                    s.vocab, s.dtype == "bf16", s.rms_eps, s.rope_theta)
+                    s.vocab, s.dtype == "bf16", s.rms_eps, s.rope_theta, arith32)
+
+    @property
+    def dt(self):
+        return np.float32 if self.arith32 else np.float64
 
 
 class KVCache:
@@ -86,29 +90,20 @@ class KVCache:
         self.length = new_length
 
 
-def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
-    x = np.asarray(x, dtype=np.float64)
-    return x / np.sqrt(np.mean(x * x) + eps) * np.asarray(g, dtype=np.float64)
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float, dt=np.float64) -> np.ndarray:
+    x = np.asarray(x, dtype=dt)
+    return x / np.sqrt(np.mean(x * x) + dt(eps)) * np.asarray(g, dtype=dt)
 
 
-def normed(x: np.ndarray, g: np.ndarray, eps: float, bf):
-    """RMSNorm in the form a projection consumes: (bf(x * g), 1 / rms(x)).  The projection of
-    the normed row is (W @ n) * s, the same as W @ RMSNorm(x) up to the rounding bf of the
-    gain-multiplied row."""
-    x = np.asarray(x, dtype=np.float64)
-    n = bf(x * np.asarray(g, dtype=np.float64))
-    s = 1.0 / np.sqrt(np.mean(x * x) + eps)
-    return n, s
-
-
-def rope(x: np.ndarray, pos: int, theta: float) -> np.ndarray:
+def rope(x: np.ndarray, pos: int, theta: float, dt=np.float64) -> np.ndarray:
     """Rotate-half RoPE on [n_heads, head_dim]: pair i with i + head_dim/2, angle
     pos * theta^(-2i/head_dim)."""
     hd = x.shape[-1]
     half = hd // 2
     i = np.arange(half, dtype=np.float64)
     ang = float(pos) * theta ** (-2.0 * i / hd)
-    c, s = np.cos(ang), np.sin(ang)
+    c, s = np.cos(ang).astype(dt), np.sin(ang).astype(dt)
+    x = np.asarray(x, dtype=dt)
     a, b = x[..., :half], x[..., half:]
     return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
 
@@ -117,13 +112,14 @@ def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
-def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_kv: int) -> np.ndarray:
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_kv: int, dt=np.float64) -> np.ndarray:
     """One query position: q [n_q, hd]; k, v [n_kv, T, hd] (every visible key) -> [n_q, hd]."""
+    q, k, v = (np.asarray(a, dtype=dt) for a in (q, k, v))
     n_q, hd = q.shape
     out = np.empty_like(q)
     for h in range(n_q):
         kv = (h * n_kv) // n_q
-        s = k[kv] @ q[h] / np.sqrt(hd)
+        s = k[kv] @ q[h] / dt(np.sqrt(hd))
         s = s - s.max()
         w = np.exp(s)
         w = w / w.sum()
@@ -131,55 +127,68 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_kv: int) -> np.ndarray
     return out
 
 
-def _w(a) -> np.ndarray:
-    return np.asarray(a, dtype=np.float64)
+def _w(a, dt=np.float64) -> np.ndarray:
+    return np.asarray(a, dtype=dt)
 
 
 def decoder_layer(spec: Spec, lw: Dict[str, np.ndarray], x: np.ndarray, pos: int,
-                  kv: KVCache, l: int) -> np.ndarray:
-    """One layer for one token at ``pos``; appends this position's k, v to layer l."""
+                  kv: KVCache, l: int, trace: Optional[Dict] = None) -> np.ndarray:
+    """One layer for one token at ``pos``; appends this position's k, v to layer l.  With
+    ``trace`` (a dict) the layer's intermediate rows are recorded in it under their names."""
+    dt = spec.dt
     bf = round_bf16 if spec.bf16 else (lambda a: a)
-    rs = round_f32 if spec.bf16 else (lambda a: a)
+    rs = round_f32 if spec.bf16 and not spec.arith32 else (lambda a: a)
     hd = spec.head_dim
-    n1, s1 = normed(x, lw["attn_norm"], spec.rms_eps, bf)
-    q = ((_w(lw["wq"]) @ n1) * s1).reshape(spec.n_q_heads, hd)
-    k = ((_w(lw["wk"]) @ n1) * s1).reshape(spec.n_kv_heads, hd)
-    v = ((_w(lw["wv"]) @ n1) * s1).reshape(spec.n_kv_heads, hd)
-    q = bf(rope(q, pos, spec.rope_theta))
-    k = bf(rope(k, pos, spec.rope_theta))
-    v = bf(v)
+    x = np.asarray(x, dtype=dt)
+    n1 = bf(rmsnorm(x, lw["attn_norm"], spec.rms_eps, dt))
+    q_raw = _w(lw["wq"], dt) @ n1
+    k_raw = _w(lw["wk"], dt) @ n1
+    v = bf(_w(lw["wv"], dt) @ n1).reshape(spec.n_kv_heads, hd)
+    q = bf(rope(q_raw.reshape(spec.n_q_heads, hd), pos, spec.rope_theta, dt))
+    k = bf(rope(k_raw.reshape(spec.n_kv_heads, hd), pos, spec.rope_theta, dt))
     kv.k[l][:, pos] = k
     kv.v[l][:, pos] = v
-    o = attend(q, kv.k[l][:, :pos + 1], kv.v[l][:, :pos + 1], spec.n_kv_heads)
+    o = attend(q, kv.k[l][:, :pos + 1], kv.v[l][:, :pos + 1], spec.n_kv_heads, dt)
     o = bf(o.reshape(-1))
-    x = rs(x + _w(lw["wo"]) @ o)
-    n2, s2 = normed(x, lw["ffn_norm"], spec.rms_eps, bf)
-    g = (_w(lw["wg"]) @ n2) * s2
-    u = (_w(lw["wu"]) @ n2) * s2
+    x_mid = rs(x + _w(lw["wo"], dt) @ o)
+    n2 = bf(rmsnorm(x_mid, lw["ffn_norm"], spec.rms_eps, dt))
+    g = _w(lw["wg"], dt) @ n2
+    u = _w(lw["wu"], dt) @ n2
     h = bf(silu(g) * u)
-    x = rs(x + _w(lw["wd"]) @ h)
-    return x
+    x_out = rs(x_mid + _w(lw["wd"], dt) @ h)
+    if trace is not None:
+        trace.update(n1=n1, q_raw=q_raw, k_raw=k_raw, k=k.reshape(-1), v=v.reshape(-1), o=o,
+                     x_mid=x_mid, n2=n2, h=h, x_out=x_out)
+    return x_out
 
 
-def forward_one(spec: Spec, W: Dict, kv: KVCache, pos: int, token: int):
+def forward_one(spec: Spec, W: Dict, kv: KVCache, pos: int, token: int, trace: Optional[List] = None):
     """Single-token forward at ``pos``.  Returns (logits float32 [V], hidden float64 [d]) where
-    hidden is the last layer's residual output (before the final norm)."""
-    x = _w(W["embed"][token])
+    hidden is the last layer's residual output (before the final norm).  With ``trace`` (a
+    list) one dict of intermediate rows per layer is appended to it."""
+    x = _w(W["embed"][token], spec.dt)
     for l in range(spec.n_layers):
-        x = decoder_layer(spec, W["layers"][l], x, pos, kv, l)
+        tr = None if trace is None else {}
+        x = decoder_layer(spec, W["layers"][l], x, pos, kv, l, tr)
+        if trace is not None:
+            trace.append(tr)
     bf = round_bf16 if spec.bf16 else (lambda a: a)
-    xf, sf = normed(x, W["final_norm"], spec.rms_eps, bf)
-    logits = ((_w(W["lm_head"]) @ xf) * sf).astype(np.float32)
+    xf = bf(rmsnorm(x, W["final_norm"], spec.rms_eps, spec.dt))
+    logits = (_w(W["lm_head"], spec.dt) @ xf).astype(np.float32)
     return logits, x
 
 
-def forward_tokens(spec: Spec, W: Dict, kv: KVCache, tokens) -> np.ndarray:
+def forward_tokens(spec: Spec, W: Dict, kv: KVCache, tokens, traces: Optional[List] = None) -> np.ndarray:
     """Forward over ``tokens`` at positions kv.length, kv.length+1, ...: a plain loop of
-    single-token forwards.  Appends their k, v; returns float32 logits [M, V]."""
+    single-token forwards.  Appends their k, v; returns float32 logits [M, V].  With
+    ``traces`` (a list) each token's per-layer intermediates (a list of dicts) are appended."""
     out = []
     for t in tokens:
         pos = kv.length
-        logits, _ = forward_one(spec, W, kv, pos, int(t))
+        tr = None if traces is None else []
+        logits, _ = forward_one(spec, W, kv, pos, int(t), tr)
+        if traces is not None:
+            traces.append(tr)
         kv.length = pos + 1
         out.append(logits)
     return np.stack(out)
@@ -218,6 +227,6 @@ def mtp_forward_one(spec: Spec, W: Dict, kv: KVCache, pos: int, h_prev: np.ndarr
     b = bf(rmsnorm(_w(W["embed"][token]), M["norm_e"], spec.rms_eps))
     x = rs(_w(M["w_proj"]) @ np.concatenate([a, b]))
     x = decoder_layer(spec, M, x, pos, kv, 0)
-    xf, sf = normed(x, M["final_norm"], spec.rms_eps, bf)
-    logits = ((_w(W["lm_head"]) @ xf) * sf).astype(np.float32)
+    xf = bf(rmsnorm(x, M["final_norm"], spec.rms_eps))
+    logits = (_w(W["lm_head"]) @ xf).astype(np.float32)
     return logits, x

@@ -91,6 +91,17 @@ def _normal(shape, std: float, s: int, device: str, dtype: torch.dtype) -> torch
     return x.to(dtype)
 
 
+# RMSNorm gains are drawn per tensor from N(1, GAIN_STD^2), so that every gain multiply and the
+# choice of gain at each norm matter to the results.
+GAIN_STD = 0.1
+
+
+def _gain(n: int, s: int, device: str, dtype: torch.dtype) -> torch.Tensor:
+    g = torch.Generator(device=device).manual_seed(s)
+    x = torch.randn((n,), generator=g, device=device, dtype=torch.float32)
+    return x.mul_(GAIN_STD).add_(1.0).to(dtype)
+
+
 def layer_shapes(shape: ModelShape) -> Dict[str, tuple]:
     d, q, kv, f = shape.d_model, shape.q_dim, shape.kv_dim, shape.d_ffn
     return {
@@ -105,7 +116,7 @@ def make_layer(shape: ModelShape, seed: int, tag: str, layer: int, device: str =
     out = {}
     for name, shp in layer_shapes(shape).items():
         if name.endswith("norm"):
-            out[name] = torch.ones(shp, device=device, dtype=dt)
+            out[name] = _gain(shp[0], tensor_seed(seed, tag, layer, name), device, dt)
         else:
             out[name] = _normal(shp, std, tensor_seed(seed, tag, layer, name), device, dt)
     return out
@@ -113,7 +124,7 @@ def make_layer(shape: ModelShape, seed: int, tag: str, layer: int, device: str =
 
 def make_weights(shape: ModelShape, seed: int = 0, device: str = "cpu", tag: Optional[str] = None,
                  std: float = 0.02) -> Dict[str, object]:
-    """Random-init N(0, std) weights, RMSNorm gains 1, nn.Linear layout [out, in].
+    """Random-init N(0, std) weights, RMSNorm gains N(1, GAIN_STD^2), nn.Linear layout [out, in].
 
     Returns {"embed", "lm_head", "final_norm", "layers": [dict per layer], "mtp": dict|None}.
     With ``shape.tied`` the LM head is the embedding tensor itself (no copy).
@@ -127,7 +138,7 @@ def make_weights(shape: ModelShape, seed: int = 0, device: str = "cpu", tag: Opt
     w = {
         "embed": embed,
         "lm_head": lm_head,
-        "final_norm": torch.ones((d,), device=device, dtype=dt),
+        "final_norm": _gain(d, tensor_seed(seed, tag, -1, "final_norm"), device, dt),
         "layers": [make_layer(shape, seed, tag, l, device, std) for l in range(shape.n_layers)],
         "mtp": None,
     }
@@ -171,7 +182,7 @@ def make_weights_fp8(shape: ModelShape, seed: int = 0, device: str = "cpu", tag:
         lw = {}
         for name, shp in layer_shapes(shape).items():
             if name.endswith("norm"):
-                lw[name] = torch.ones(shp, device=device, dtype=torch.bfloat16)
+                lw[name] = _gain(shp[0], tensor_seed(seed, tag, l, name), device, torch.bfloat16)
             else:
                 lw[name] = _fp8_codes(shp, tensor_seed(seed, tag, l, name), device)
                 lw[name + "_scale"] = _row_scales(shp[0], std, tensor_seed(seed, tag, l, name + "_scale"), device)
@@ -180,7 +191,7 @@ def make_weights_fp8(shape: ModelShape, seed: int = 0, device: str = "cpu", tag:
         "embed": _normal((V, d), std, tensor_seed(seed, tag, -1, "embed"), device, torch.bfloat16),
         "lm_head": _fp8_codes((V, d), tensor_seed(seed, tag, -1, "lm_head"), device),
         "lm_head_scale": _row_scales(V, std, tensor_seed(seed, tag, -1, "lm_head_scale"), device),
-        "final_norm": torch.ones((d,), device=device, dtype=torch.bfloat16),
+        "final_norm": _gain(d, tensor_seed(seed, tag, -1, "final_norm"), device, torch.bfloat16),
         "layers": layers,
         "mtp": None,
     }
@@ -208,9 +219,8 @@ def make_mtp(shape: ModelShape, seed: int, device: str, tag: str, std: float = 0
     dt = _torch_dtype(shape.dtype)
     d = shape.d_model
     m = make_layer(shape, seed, tag + ":mtp", 0, device, std)
-    m["norm_h"] = torch.ones((d,), device=device, dtype=dt)
-    m["norm_e"] = torch.ones((d,), device=device, dtype=dt)
-    m["final_norm"] = torch.ones((d,), device=device, dtype=dt)
+    for name in ("norm_h", "norm_e", "final_norm"):
+        m[name] = _gain(d, tensor_seed(seed, tag + ":mtp", 0, name), device, dt)
     m["w_proj"] = _normal((d, 2 * d), std, tensor_seed(seed, tag + ":mtp", 0, "w_proj"), device, dt)
     return m
 

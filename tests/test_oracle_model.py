@@ -14,8 +14,9 @@ import torch
 import torch.nn.functional as F
 
 from oracle import numerics
-from oracle.model import KVCache, Spec, attend, forward_tokens, normed, rmsnorm, rope
+from oracle.model import KVCache, Spec, attend, forward_tokens, rmsnorm, rope
 from speculative_decoding_token_amd import synth
+from tests.torch_ref import torch_forward
 
 
 def test_round_bf16_matches_torch():
@@ -35,22 +36,6 @@ def test_rmsnorm_matches_torch():
     g = rng.normal(1, 0.1, 257)
     ref = F.rms_norm(torch.from_numpy(x), (257,), torch.from_numpy(g), eps=1e-6).numpy()
     np.testing.assert_allclose(rmsnorm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-14)
-
-
-def test_folded_rmsnorm_is_rmsnorm_before_the_projection():
-    # the folded form (W @ (x * g)) / rms(x) against torch's rms_norm followed by the product
-    rng = np.random.default_rng(11)
-    x = rng.normal(0, 3, 257)
-    g = rng.normal(1, 0.1, 257)
-    W = rng.normal(0, 0.02, (33, 257))
-    n, s = normed(x, g, 1e-6, lambda a: a)
-    ref = (torch.from_numpy(W) @ F.rms_norm(torch.from_numpy(x), (257,), torch.from_numpy(g), eps=1e-6)).numpy()
-    np.testing.assert_allclose((W @ n) * s, ref, rtol=1e-12, atol=1e-14)
-    # bf16 contract: the row the projection reads is the gain-multiplied row rounded to bf16
-    nb, sb = normed(x, g, 1e-6, numerics.round_bf16)
-    want = torch.from_numpy(x * g).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
-    assert np.array_equal(nb, want)
-    assert sb == s
 
 
 def test_rope_closed_forms():
@@ -88,61 +73,6 @@ def test_attend_single_key_and_gqa_vs_torch():
     vt = torch.from_numpy(v).repeat_interleave(4, dim=0)
     ref = F.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], kt, vt)[:, 0, :]
     np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
-
-
-def torch_forward(spec: Spec, W, tokens, k_prefix=None, v_prefix=None, bf16=False):
-    """Batched causal forward over all positions at once, from torch CPU operators."""
-    def w(a):
-        return torch.from_numpy(np.asarray(a, dtype=np.float64))
-
-    def rb(t):
-        return t.to(torch.float32).to(torch.bfloat16).to(torch.float64) if bf16 else t
-
-    def rf(t):
-        return t.to(torch.float32).to(torch.float64) if bf16 else t
-
-    P = 0 if k_prefix is None else k_prefix.shape[2]
-    M = len(tokens)
-    T = P + M
-    hd, nq, nkv = spec.head_dim, spec.n_q_heads, spec.n_kv_heads
-    pos = torch.arange(P, T, dtype=torch.float64)
-    inv = spec.rope_theta ** (-2.0 * torch.arange(hd // 2, dtype=torch.float64) / hd)
-    ang = pos[:, None] * inv[None, :]
-    cos, sin = torch.cos(ang), torch.sin(ang)
-
-    def rot(x):  # x [M, heads, hd]
-        a, b = x[..., : hd // 2], x[..., hd // 2:]
-        c, s = cos[:, None, :], sin[:, None, :]
-        return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
-
-    x = w(W["embed"])[torch.as_tensor(tokens, dtype=torch.long)]
-    mask = torch.ones(M, T, dtype=torch.bool).tril(diagonal=P)
-    def normed(x, g):
-        # f32: torch's rms_norm; bf16: the contract's folded form, the gain-multiplied row
-        # rounded to bf16 and the projection scaled by 1/rms(x) afterwards
-        if not bf16:
-            return F.rms_norm(x, (spec.d_model,), w(g), eps=spec.rms_eps), 1.0
-        return rb(x * w(g)), torch.rsqrt((x * x).mean(dim=-1, keepdim=True) + spec.rms_eps)
-
-    for l, lw in enumerate(W["layers"]):
-        n1, s1 = normed(x, lw["attn_norm"])
-        q = rb(rot(((n1 @ w(lw["wq"]).T) * s1).view(M, nq, hd)))
-        k = rb(rot(((n1 @ w(lw["wk"]).T) * s1).view(M, nkv, hd)))
-        v = rb(((n1 @ w(lw["wv"]).T) * s1).view(M, nkv, hd))
-        kk, vv = k.transpose(0, 1), v.transpose(0, 1)
-        if P:
-            kk = torch.cat([torch.from_numpy(np.asarray(k_prefix[l], np.float64)), kk], dim=1)
-            vv = torch.cat([torch.from_numpy(np.asarray(v_prefix[l], np.float64)), vv], dim=1)
-        kk = kk.repeat_interleave(nq // nkv, dim=0)
-        vv = vv.repeat_interleave(nq // nkv, dim=0)
-        o = F.scaled_dot_product_attention(q.transpose(0, 1), kk, vv, attn_mask=mask)
-        o = rb(o.transpose(0, 1).reshape(M, nq * hd))
-        x = rf(x + o @ w(lw["wo"]).T)
-        n2, s2 = normed(x, lw["ffn_norm"])
-        h = rb(F.silu((n2 @ w(lw["wg"]).T) * s2) * ((n2 @ w(lw["wu"]).T) * s2))
-        x = rf(x + h @ w(lw["wd"]).T)
-    xf, sf = normed(x, W["final_norm"])
-    return ((xf @ w(W["lm_head"]).T) * sf).to(torch.float32).numpy()
 
 
 def tiny(seed=0):
@@ -199,3 +129,16 @@ def test_causal_invariance_and_trim_rollback():
     forward_tokens(spec, W, kv3, prompt + [5, 6, 7])
     fresh = forward_tokens(spec, W, kv3, [42])
     assert np.array_equal(nxt, fresh)
+
+
+def test_float32_arithmetic_mode():
+    """Spec.arith32 evaluates the same contract in float32: on the float32 pair it agrees with
+    the float64 evaluation to float32 accuracy, and its intermediates are float32."""
+    spec, W = tiny()
+    spec32 = Spec.from_shape(synth.SHAPES["tiny_target"], arith32=True)
+    toks = synth.make_tokens(9, spec.vocab, 2)
+    a = forward_tokens(spec, W, KVCache(spec, 16), toks)
+    tr = []
+    b = forward_tokens(spec32, W, KVCache(spec32, 16), toks, tr)
+    assert np.abs(a - b).max() / np.abs(a).max() < 1e-5
+    assert tr[0][0]["h"].dtype == np.float32 and tr[-1][-1]["x_out"].dtype == np.float32
