@@ -180,7 +180,11 @@ typedef struct spec_stats {
   int64_t drafts_accepted;  /* sum of n                                        */
   int64_t emitted;          /* sum of n + 1                                    */
   int64_t sync_timeouts;    /* non-zero once a grid barrier of the one-launch forward timed
-                             * out (its results, and every later one, are invalid)   */
+                             * out (its results, and every later one, are invalid); the
+                             * calls that synchronize (spec_get_stats, spec_get_lengths, a
+                             * draft_step / verify_step that reads the lengths) then return
+                             * SPEC_E_HIP, and so does every later draft_step, verify_step,
+                             * accept and kv_trim of the context */
 } spec_stats;
 
 typedef struct spec_ctx spec_ctx;
@@ -284,14 +288,18 @@ int verify_step(spec_ctx* ctx, const int32_t* draft_tok /*device*/, int32_t batc
  * Writes n_acc (device int32 [batch], 0..k), out_tok (device int32 [batch, k+1], the first
  * n+1 entries valid: accepted drafts then the correction or bonus token), near_tie
  * (device uint8 [batch] of SPEC_FLAG_* bits, may be NULL), updates the device-side last
- * accepted token and the statistics.  Must follow a verify_step with the same k. */
+ * accepted token and the statistics.  A target row p_{j-1} with no entry (its logits held no
+ * finite value) stops the sequence at n = j - 1 kept drafts with SPEC_FLAG_BAD_ROW and -1 as
+ * its emitted token (the device-side last token becomes 0).  Must follow a verify_step with
+ * the same k. */
 int accept(spec_ctx* ctx, const int32_t* draft_tok /*device*/, const spec_probs* q,
            const spec_probs* p, int32_t batch, int32_t k, uint64_t round,
            int32_t* n_acc /*device*/, int32_t* out_tok /*device*/, uint8_t* near_tie);
 
 /* Rolls every cache back to the accepted prefix: L <- L + 1 + n_acc[b] (the last accepted
  * token and its n accepted drafts stay; the emitted last token is the next cycle's first
- * row).  Must follow accept.  n_acc: device int32 [batch]. */
+ * row).  Must follow accept.  n_acc: device int32 [batch], each value clamped to [0, k] of
+ * the cycle. */
 int kv_trim(spec_ctx* ctx, const int32_t* n_acc /*device*/, int32_t batch);
 
 /* ---- n-gram acceptance gate (host only) -------------------------------------------------
@@ -378,11 +386,12 @@ int spec_use_graphs(spec_ctx* ctx, int32_t enable);
  *                      SPEC_SCHED_STREAM steps meeting at grid barriers, the next
  *                      projection's weights streaming while a barrier is awaited; draft_step
  *                      and verify_step are then launched directly, not replayed from graphs.
- * In all three the RMSNorm is folded into the projection it feeds: the residual update (or
- * the embedding) leaves bf16(x * gain) and the projection scales its result rows by 1/rms(x),
- * so no normalization launch exists.  Shapes a schedule does not cover (reduction lengths
- * that are not whole 1 KB stages, head sizes other than 128 for SPEC_SCHED_FORWARD, the MTP
- * head) fall back to the next simpler one.  Schedules agree within the float tolerances, not
+ * In all three no normalization launch exists: the residual update (or the embedding) leaves
+ * the float32 rows x * gain and per-16-column sums of squares of x, and the projection that
+ * takes RMSNorm(x) * gain rounds (x * gain) / rms(x) to bf16 as it loads its input.  Shapes a
+ * schedule does not cover (reduction lengths that are not whole 1 KB stages, head sizes other
+ * than 128 or d_model above 4096 for SPEC_SCHED_FORWARD, the MTP head) fall back to the next
+ * simpler one.  Schedules agree within the float tolerances, not
  * bit for bit; each is row-count invariant on its own.  Returns SPEC_E_INVAL for an unknown
  * schedule. */
 #define SPEC_SCHED_STEP 0
@@ -403,6 +412,29 @@ int spec_get_stats(spec_ctx* ctx, spec_stats* out /*host*/);
 
 /* Reads the current cache length of each sequence (synchronizes the stream). */
 int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t batch);
+
+/* Diagnostics: copies the start of one of the context's activation buffers, as the last
+ * forward of that model left it, to dst (device, caller-owned; min(bytes, buffer size)
+ * bytes, enqueued on the context stream).  which: 0 target, 1 draft model, 2 MTP layer.
+ * Rows are the forward's rows (sequence-major), all float32 unless noted:
+ *   SPEC_BUF_RESIDUAL   [rows, d_model] residual stream after the last layer;
+ *   SPEC_BUF_NORM_INPUT [rows, d_model] the next RMSNorm input: x * gain (bf16 models) or the
+ *                       normed rows (f32 models);
+ *   SPEC_BUF_Q, _K      [rows, n_q_heads*head_dim], [rows, n_kv_heads*head_dim] the last
+ *                       layer's q and k before RoPE (per-launch schedules);
+ *   SPEC_BUF_ATTN       [rows, n_q_heads*head_dim] model dtype: the last layer's attention output;
+ *   SPEC_BUF_SWIGLU     [rows, d_ffn] model dtype: the last layer's SwiGLU product;
+ *   SPEC_BUF_CACHE_K,_V the whole cache, [max_batch, n_layers, n_kv_heads, capacity, head_dim]
+ *                       in the model dtype, capacity = max_ctx + max_k + 2. */
+#define SPEC_BUF_RESIDUAL 0
+#define SPEC_BUF_NORM_INPUT 1
+#define SPEC_BUF_Q 2
+#define SPEC_BUF_K 3
+#define SPEC_BUF_ATTN 4
+#define SPEC_BUF_SWIGLU 5
+#define SPEC_BUF_CACHE_K 6
+#define SPEC_BUF_CACHE_V 7
+int spec_debug_read(spec_ctx* ctx, int32_t which, int32_t buffer, void* dst /*device*/, size_t bytes);
 
 /* ---- stateless kernels (the accept workload on its own) ------------------------------ */
 

@@ -26,6 +26,43 @@ SPEC_DEVINL bf16_t f32_to_bf16(float f) {
   return (bf16_t)(u >> 16);
 }
 
+// Softmax weights of a 64-key attention chunk as A operands of the P V product on the bf16
+// MFMA.  Lane l holds query row l % 16 and, in s[kt][r], the score of key 16 kt + 4 (l / 16) + r
+// (already scaled, -inf where masked); mx is the row's chunk maximum.  P = exp(s - mx) stays
+// float32 up to the product: it is split into hi = bf16(P) and lo = bf16(P - hi) (P - hi is
+// exact in float32), so hi + lo carries P to a relative error below 2^-17.  The A operand of
+// 32-key step st holds keys 32 st + 4 g + (0..3) in slots 0-3 and 32 st + 16 + 4 g + (0..3) in
+// slots 4-7 (g = l / 16); pa[st][0] is the hi part, pa[st][1] the lo part.  Returns the row's
+// sum of P over the chunk: the lane's 16 values in order, then the four lane groups.
+SPEC_DEVINL float p_operands(const f32x4_t (&s)[4], float mx, bf16x8_t (&pa)[2][2]) {
+  uint32_t hi[4][2], lo[4][2];
+  float l = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    bf16_t h[4], r[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float v = s[kt][rr];
+      const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : expf(v - mx);
+      l += x;
+      h[rr] = f32_to_bf16(x);
+      r[rr] = f32_to_bf16(x - bf16_to_f32(h[rr]));
+    }
+    hi[kt][0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    hi[kt][1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    lo[kt][0] = (uint32_t)r[0] | ((uint32_t)r[1] << 16);
+    lo[kt][1] = (uint32_t)r[2] | ((uint32_t)r[3] << 16);
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    pa[st][0] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[2 * st][0], hi[2 * st][1], hi[2 * st + 1][0], hi[2 * st + 1][1]));
+    pa[st][1] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[2 * st][0], lo[2 * st][1], lo[2 * st + 1][0], lo[2 * st + 1][1]));
+  }
+  return l;
+}
+
 // Activation storage: bf16 models round GEMM inputs and the cache to bfloat16, f32
 // models keep float32.
 template <int DT> struct Act;

@@ -57,9 +57,9 @@ hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per
                          int32_t* tokens, int tok_ld, uint8_t* flags, hipStream_t st);
 hipError_t launch_set_u32(uint32_t* p, uint32_t v, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
-// len[b] += 1 + n_acc[b]; a second cache length (the MTP layer's) is first clamped to the
-// old len[b] + 1 when mlen is not null.
-hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen, hipStream_t st);
+// len[b] += 1 + n_acc[b] (n_acc[b] clamped to [0, k]); a second cache length (the MTP
+// layer's) is first clamped to the old len[b] + 1 when mlen is not null.
+hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int k, int32_t* mlen, hipStream_t st);
 // One-hot lists for rows b*k + j holding drafts[b*k + j].
 hipError_t launch_onehot(const int32_t* drafts, int rows, const spec_probs& q, hipStream_t st);
 // Token history [batch][ld]: hist[b][pos0 + i] = src[b * src_ld + i] for i < n.
@@ -96,14 +96,14 @@ struct GemmArgs {
   int rows[3];
   int K;
   const void* x;      // [M, K] model dtype (GEMM input as stored)
-  // folded RMSNorm (bf16 path): when ss_in is set, x holds gain-multiplied rows bf16(r * g)
-  // of residual rows r, and result row m is scaled by 1/sqrt(mean + eps), mean = (the np_in
-  // partial sums of squares ss_in[m * ss_ld + 0 .. np_in-1], added in order) / K
+  // RMSNorm input (bf16 path): when ss_in is set, x holds the float32 rows r * g of residual
+  // rows r and gain g, and the GEMM input row m is bf16((r * g) / sqrt(mean + eps)), mean =
+  // (the np_in partial sums of squares ss_in[m * ss_ld + 0 .. np_in-1], added in order) / K
   const float* ss_in;
   int np_in, ss_ld;
   float eps;
   float* ss_out;      // EPI_RESID: partial sums of squares of the updated rows, one per block
-  void* y_out;        // EPI_RESID (bf16, may be null): [M, ld] bf16(updated rows * y_gain)
+  void* y_out;        // EPI_RESID (bf16 models, may be null): [M, ld] float32 updated rows * y_gain
   const void* y_gain;
   RowMap rm;
   // outputs
@@ -161,16 +161,16 @@ constexpr int ATTN_MAX_CHUNKS = 256;  // contexts up to 16384 positions
 constexpr int ATTN_ROWS_MAX = 96;  // (tokens per sequence) x (q heads per kv head)
 
 hipError_t launch_rope_table(float2* table, int cap, int hd, float theta, hipStream_t st);
-// y (bf16 models, may be null): also writes bf16(rows * gain), the input of the first
-// projection (its RMSNorm folded in).
+// y (bf16 models, may be null): also writes the float32 rows * gain, the input of the first
+// projection before its 1/rms.
 hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_t* first,
                         int first_ld, const int32_t* rest, int rest_ld, int M, int mseq, float* x,
                         float* ss, int ss_ld, void* y, const void* gain, hipStream_t st);
 hipError_t launch_rmsnorm(int dtype, const float* x, const void* g, float eps, int M, int d,
                           void* y, hipStream_t st);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t st);
-// y[m, k] = bf16(x[m, k] * gain[k]) for M rows of K (bf16 models): the input of a projection
-// of RMSNorm(x) when the producer of x did not leave it.
+// y[m, k] = x[m, k] * gain[k] in float32 for M rows of K (bf16 models): the input of a
+// projection of RMSNorm(x) when the producer of x did not leave it.
 hipError_t launch_gain_rows(const float* x, const void* gain, int M, int K, void* y, hipStream_t st);
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 hipError_t launch_fill(void* p, size_t bytes, hipStream_t st);
@@ -212,12 +212,12 @@ hipError_t launch_copy_rows_f32(const float* src, int64_t src_ss, int R, int d, 
 
 // ---- weight-streaming projections (bf16 models, M <= 16 rows) -------------------------
 // out[m, n] = sum_k W[n, k] x[m, k] with W streamed through an LDS ring by one workgroup per
-// compute unit (see stream.hip).  Epilogues as GemmArgs, and so is the folded RMSNorm: with
-// ss_in set, x holds bf16(r * g) of residual rows r and row m of the result is scaled by
-// 1/sqrt(mean + eps), the mean from the np_in partials ss_in[m * ss_ld + 0 ..] added in order.
-// EPI_RESID adds into out (row stride ld) and leaves, when set, ss_out[m * ss_ld + u] = the
-// sum of squares of the 16 updated columns of unit u, and y_out = bf16(updated rows * y_gain)
-// (the next projection's input).
+// compute unit (see stream.hip).  Epilogues as GemmArgs, and so is the RMSNorm input: with
+// ss_in set, x holds the float32 rows r * g of residual rows r and the input row m is
+// bf16((r * g) / sqrt(mean + eps)), the mean from the np_in partials ss_in[m * ss_ld + 0 ..]
+// added in order.  EPI_RESID adds into out (row stride ld) and leaves, when set,
+// ss_out[m * ss_ld + u] = the sum of squares of the 16 updated columns of unit u, and y_out =
+// float32 updated rows * y_gain (the next projection's input before its 1/rms).
 struct StreamArgs {
   // EPI_QKV / EPI_QKV_ROWS: W_q, W_k, W_v; EPI_SWIGLU: W_gate, W_up; else W.  Separate
   // members, not an array: an indexed member would move the block to scratch memory.
@@ -231,15 +231,15 @@ struct StreamArgs {
   int wbytes;         // 2: bf16 weights, 1: fp8 weights with row scales
   int rows0, rows1, rows2;
   int K, nunits;      // nunits: row tiles of 16 (EPI_SWIGLU: gate/up tile pairs)
-  const void* x;      // [M, K] bf16 input rows
-  const float* ss_in; // folded RMSNorm: partial sums of squares of the residual rows
+  const void* x;      // [M, K] bf16 input rows, or float32 rows r * g with ss_in set
+  const float* ss_in; // RMSNorm input: partial sums of squares of the residual rows
   int np_in, ss_ld;
   float eps;
   int M;
   float* out;         // EPI_STORE / EPI_RESID: [M, ld]
   int ld;
   float* ss_out;      // EPI_RESID
-  void* y_out;        // EPI_RESID: [M, ld] bf16(updated rows * y_gain)
+  void* y_out;        // EPI_RESID: [M, ld] float32 updated rows * y_gain
   const void* y_gain;
   void* h;            // EPI_SWIGLU: [M, rows0] bf16
   float* q_stage;     // EPI_QKV
@@ -279,7 +279,7 @@ struct FwdArgs {
   CacheView cache;
   const float2* rope;
   float* x;       // [M][d] residual rows
-  void* y;        // [M][d] bf16(residual rows * the next norm's gain)
+  float* y;       // [M][d] residual rows * the next norm's gain
   float* ss;      // [M][ss_ld] sum-of-squares partials
   int ss_ld;
   float* qkv;     // [M][q_dim + 2 kv_dim] raw q, k, v rows

@@ -31,14 +31,14 @@ __global__ void rope_table_kernel(float2* table, int cap, int hd, double theta) 
 
 // ---------------------------------------------------------------- embedding gather
 // Row m = (seq b, i): token first[b*first_ld] for i == 0, else rest[b*rest_ld + i-1].  Also
-// leaves the row's sum of squares in ss[m * ss_ld] (fixed reduction order) for the fused
-// RMSNorm of the first projection and, when y is set (bf16), bf16(row * gain): that
-// projection's input.
+// leaves the row's sum of squares in ss[m * ss_ld] (fixed reduction order) for the RMSNorm of
+// the first projection and, when y is set (bf16), row * gain in float32: that projection's
+// input before its 1/rms.
 template <int DT>
 __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vocab,
                                                     const int32_t* first, int first_ld,
                                                     const int32_t* rest, int rest_ld, int mseq,
-                                                    float* x, float* ss, int ss_ld, bf16_t* y,
+                                                    float* x, float* ss, int ss_ld, float* y,
                                                     const bf16_t* gain) {
   using A = Act<DT>;
   __shared__ float red[256];
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
   for (int c = t; c < d; c += blockDim.x) {
     const float v = ok ? A::load(row, c) : __builtin_nanf("");
     x[(int64_t)m * d + c] = v;
-    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = f32_to_bf16(v * bf16_to_f32(gain[c]));
+    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = v * bf16_to_f32(gain[c]);
     sq += v * v;
   }
   red[t] = sq;
@@ -189,25 +189,21 @@ SPEC_DEVINL void gemm_epilogue(const GemmArgs& a, int mat, int m, int n, float v
 // B = 32 k x 16 token rows (the same k slice of x, zero for rows >= M).  The MFMA's 16x
 // padding of the token dimension costs nothing here: the pass is bound by streaming W.
 //
-// With NORM the RMSNorm in front of the projection is folded into it: W . RMSNorm(x) =
-// (W . (x * g)) / rms(x).  The input rows are bf16(x * g), left by the producer of the
-// residual x, and each result row is scaled by 1/sqrt(mean(x^2) + eps), the mean from the
-// row's sum-of-squares partials (left by the same producer).  The first partials of the
-// block's rows are loaded ahead of the weights, so their latency hides behind the stream.
-// A residual epilogue leaves, per block, the sum of squares of its 16 updated columns of each
-// row and, when asked, those columns times the next norm's gain, rounded to bf16.
+// With NORM the input is RMSNorm(x) * g with no pass of its own: the producer of the residual
+// x left the float32 rows x * g and the rows' sum-of-squares partials, the block adds the
+// partials into 1/sqrt(mean(x^2) + eps) before its main loop (their loads go out with the
+// first weights) and rounds (x * g) times it to bf16 as it loads each input slice.  A residual
+// epilogue leaves, per block, the sum of squares of its 16 updated columns of each row and,
+// when asked, those columns times the next norm's gain in float32.
 SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// y[m, k] = bf16(x[m, k] * gain[k]): a projection's input rows when the producer of x left none.
-__global__ __launch_bounds__(256) void gain_rows_kernel(const float* x, const bf16_t* gain, int K, bf16_t* y) {
+// y[m, k] = x[m, k] * gain[k] in float32: a projection's RMSNorm input rows when the producer
+// of x left none.
+__global__ __launch_bounds__(256) void gain_rows_kernel(const float* x, const bf16_t* gain, int K, float* y) {
   const int m = blockIdx.x;
-  for (int k = threadIdx.x * 2; k < K; k += 512) {
-    const float2 v = *(const float2*)(x + (int64_t)m * K + k);
-    *(uint32_t*)(y + (int64_t)m * K + k) =
-        pack_bf16x2(v.x * bf16_to_f32(gain[k]), v.y * bf16_to_f32(gain[k + 1]));
-  }
+  for (int k = threadIdx.x; k < K; k += 256) y[(int64_t)m * K + k] = x[(int64_t)m * K + k] * bf16_to_f32(gain[k]);
 }
 
 // Single-tile instances of 16 wavefronts are held to 64 VGPRs: two workgroups per compute
@@ -215,8 +211,9 @@ __global__ __launch_bounds__(256) void gain_rows_kernel(const float* x, const bf
 template <int EPI, int NT, bool NORM, int GEMM_NW>
 __global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) ? 8 : 1) void gemm_bf16_kernel(
     GemmArgs a) {
-  // k-steps per load group: 8 KB of weights in flight per wave and tile either way
-  constexpr int GEMM_U = (GEMM_NW == 16 || NT == 4) ? 4 : 8;
+  // k-steps per load group: 8 KB of weights in flight per wave and tile either way (halved for
+  // several token tiles of float32 RMSNorm inputs, whose slices take twice the registers)
+  constexpr int GEMM_U = ((GEMM_NW == 16 || NT == 4) ? 4 : 8) / ((NORM && NT >= 2) ? 2 : 1);
   constexpr int TILES = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int PSS = TILES == 2 ? 4 : 2;  // partials per lane loaded ahead (a row's first 64 * PSS)
   __shared__ f32x4_t red[GEMM_NW][TILES][NT][64];
@@ -272,6 +269,29 @@ __global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // RMSNorm input: 1/rms of each row (lane j adds the row's partials j, j + 64, ... in order,
+  // then a fixed xor butterfly; wave w takes rows w, w + GEMM_NW, ...), then per token tile
+  // the factor of this lane's row
+  float rv[NT];
+  if (NORM) {
+    for (int r = wave; r < M; r += GEMM_NW) {
+      float sum = 0.0f;
+      int p0 = lane;
+      if (r == wave) {
+#pragma unroll
+        for (int q = 0; q < PSS; ++q) sum += pss[q];
+        p0 = lane + 64 * PSS;
+      }
+      for (int p = p0; p < a.np_in; p += 64) sum += a.ss_in[(int64_t)r * a.ss_ld + p];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) s_inv[r] = 1.0f / sqrtf(sum / (float)K + a.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rv[nt] = xv[nt] ? s_inv[nt * 16 + (lane & 15)] : 0.0f;
+  }
+
   for (int s0 = wave; s0 < nsteps; s0 += GEMM_NW * GEMM_U) {
     uint4 xb[NT][GEMM_U];
 #pragma unroll
@@ -279,9 +299,21 @@ __global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) 
       const int s = s0 + u * GEMM_NW;
       const bool ok = s < nsteps;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)((const bf16_t*)a.x + xrow[nt] + (int64_t)s * 32)
-                                   : make_uint4(0, 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) {
+        if (NORM) {
+          const float* xp = (const float*)a.x + xrow[nt] + (int64_t)s * 32;
+          const uint4 lo = (ok && xv[nt]) ? *(const uint4*)xp : make_uint4(0, 0, 0, 0);
+          const uint4 hi = (ok && xv[nt]) ? *(const uint4*)(xp + 4) : make_uint4(0, 0, 0, 0);
+          const float r = rv[nt];
+          xb[nt][u] = make_uint4(pack_bf16x2(__uint_as_float(lo.x) * r, __uint_as_float(lo.y) * r),
+                                 pack_bf16x2(__uint_as_float(lo.z) * r, __uint_as_float(lo.w) * r),
+                                 pack_bf16x2(__uint_as_float(hi.x) * r, __uint_as_float(hi.y) * r),
+                                 pack_bf16x2(__uint_as_float(hi.z) * r, __uint_as_float(hi.w) * r));
+        } else {
+          xb[nt][u] = (ok && xv[nt]) ? *(const uint4*)((const bf16_t*)a.x + xrow[nt] + (int64_t)s * 32)
+                                     : make_uint4(0, 0, 0, 0);
+        }
+      }
     }
     // next group of weights while this one is multiplied
     uint4 wn[TILES][GEMM_U];
@@ -310,23 +342,6 @@ __global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) 
   for (int t = 0; t < TILES; ++t)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) red[wave][t][nt][lane] = acc[t][nt];
-  if (NORM) {
-    // 1/rms of each row: lane j adds the row's partials j, j + 64, ... in order, then a fixed
-    // xor butterfly; wave w takes rows w, w + GEMM_NW, ...
-    for (int r = wave; r < M; r += GEMM_NW) {
-      float sum = 0.0f;
-      int p0 = lane;
-      if (r == wave) {
-#pragma unroll
-        for (int q = 0; q < PSS; ++q) sum += pss[q];
-        p0 = lane + 64 * PSS;
-      }
-      for (int p = p0; p < a.np_in; p += 64) sum += a.ss_in[(int64_t)r * a.ss_ld + p];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      if (lane == 0) s_inv[r] = 1.0f / sqrtf(sum / (float)K + a.eps);
-    }
-  }
   __syncthreads();
 
   // D layout of the 16x16 MFMA: lane l holds column l%16 (token), rows 4*(l/16)+r (weight row)
@@ -341,14 +356,13 @@ __global__ __launch_bounds__(GEMM_NW * 64, (GEMM_NW == 16 && EPI != EPI_SWIGLU) 
         float s = 0.0f;
 #pragma unroll
         for (int w = 0; w < GEMM_NW; ++w) s += red[w][t][nt][l][r];
-        v[t] = NORM ? s * s_inv[m] : s;
+        v[t] = s;
       }
       if (EPI == EPI_RESID) {
         const float xn = a.out[(int64_t)m * a.ld + n] + v[0];
         a.out[(int64_t)m * a.ld + n] = xn;
         s_sq[m][n - r0] = xn * xn;
-        if (a.y_out)
-          ((bf16_t*)a.y_out)[(int64_t)m * a.ld + n] = f32_to_bf16(xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
+        if (a.y_out) ((float*)a.y_out)[(int64_t)m * a.ld + n] = xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]);
       } else {
         gemm_epilogue<SPEC_DTYPE_BF16, EPI>(a, mat, m, n, v[0], v[TILES - 1]);
       }
@@ -590,8 +604,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 // A-operand slots of the following P V product for two key tiles at once (with the key
 // order inside a 32-key step permuted the same way on the V side), so P never leaves the
 // registers.  V is staged transposed in LDS so that each lane's 8 keys are two 8-byte
-// reads.  P is rounded to bf16 for the product and the row sum uses the same rounded
-// values, so the weights of a row still sum to one.
+// reads.  P = exp(s - m) stays float32 up to the product: it enters the MFMA as the sum of
+// two bf16 operands (hi = bf16(P), lo = bf16(P - hi), 16 significant bits together, a
+// relative error below 2^-16), and the row sum adds the float32 values.
 template <int HD, int QTM>
 __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
   constexpr int C = ATTN_CHUNK;  // 64 keys
@@ -748,29 +763,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    uint32_t pk[4][2];  // P as packed bf16 pairs, per key tile
-    float l = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      float e[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float v = s[kt][rr];
-        const float x = (mx == -__builtin_inff() || v == -__builtin_inff()) ? 0.0f : __expf(v - mx);
-        e[rr] = bf16_to_f32(f32_to_bf16(x));
-        l += e[rr];
-      }
-      pk[kt][0] = (uint32_t)f32_to_bf16(e[0]) | ((uint32_t)f32_to_bf16(e[1]) << 16);
-      pk[kt][1] = (uint32_t)f32_to_bf16(e[2]) | ((uint32_t)f32_to_bf16(e[3]) << 16);
-    }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    // A operand of step st: slots 0-3 = keys 32st + 4g + (0..3), slots 4-7 = 32st + 16 + 4g + (0..3)
-    bf16x8_t pa[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-      pa[st] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * st][0], pk[2 * st][1], pk[2 * st + 1][0],
-                                                       pk[2 * st + 1][1]));
+    bf16x8_t pa[2][2];  // P = hi + lo, two bf16 operands per 32-key step
+    const float l = p_operands(s, mx, pa);
     // this lane's rows of the output tile: 4g + rr
     int rowoff[4];
 #pragma unroll
@@ -791,8 +785,9 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
         const bf16_t* vr = vt + dim * VP;
         const uint2 x0 = *(const uint2*)(vr + ((st * 32 + 4 * g) ^ swz));
         const uint2 x1 = *(const uint2*)(vr + ((st * 32 + 16 + 4 * g) ^ swz));
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[st], __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y)),
-                                                    o, 0, 0, 0);
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y));
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[st][0], vb, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[st][1], vb, o, 0, 0, 0);
       }
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
@@ -811,8 +806,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 // two rows) on the vector ALUs, where 16-row MFMA tiles would be mostly padding.  K and V stay
 // in the cache layout in LDS.  Scores: thread t takes key t / 4 and the quarter t % 4 of the
 // head dimension (a sequential sum over its 32 dims, then the quarters added pairwise); the
-// chunk softmax per row as in the MFMA kernel (P rounded to bf16, the row sum of the rounded
-// values), reductions only for the R rows present; P V: wavefront w produces query row w, two
+// chunk softmax per row in float32 as in the MFMA kernel, reductions only for the R rows
+// present; P V: wavefront w produces query row w, two
 // output dims per lane, keys in order.  Partials in the layout the combine kernel reads.
 __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
   constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2, QW = HD / 4;
@@ -963,15 +958,14 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
     for (int r = 0; r < RM; ++r) wred[0][wave][r] = mx[r];
   }
   __syncthreads();
-  // weights exp(s - max) rounded to bf16 (P of the MFMA kernel), their sums per wavefront
+  // weights exp(s - max) in float32, their sums per wavefront
   float lsum[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     lsum[r] = 0.0f;
     if (r < R) {
       const float m = fmaxf(fmaxf(wred[0][0][r], wred[0][1][r]), fmaxf(wred[0][2][r], wred[0][3][r]));
-      const float x = (m == -__builtin_inff() || s[r] == -__builtin_inff()) ? 0.0f : __expf(s[r] - m);
-      const float e = bf16_to_f32(f32_to_bf16(x));
+      const float e = (m == -__builtin_inff() || s[r] == -__builtin_inff()) ? 0.0f : expf(s[r] - m);
       if (qq == 0) ps[r][j] = e;
       float l = qq == 0 ? e : 0.0f;
 #pragma unroll
@@ -1123,7 +1117,7 @@ hipError_t launch_embed(int dtype, const void* E, int d, int vocab, const int32_
                         float* ss, int ss_ld, void* y, const void* gain, hipStream_t st) {
   if (dtype == SPEC_DTYPE_BF16)
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_BF16>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
-                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, (bf16_t*)y, (const bf16_t*)gain);
+                       first_ld, rest, rest_ld, mseq, x, ss, ss_ld, (float*)y, (const bf16_t*)gain);
   else
     hipLaunchKernelGGL(embed_kernel<SPEC_DTYPE_F32>, dim3(M), dim3(256), 0, st, E, d, vocab, first,
                        first_ld, rest, rest_ld, mseq, x, ss, ss_ld, nullptr, nullptr);
@@ -1189,7 +1183,7 @@ static hipError_t gemm_bf16_nt(const GemmArgs& a, int blocks, hipStream_t st) {
 hipError_t launch_gain_rows(const float* x, const void* gain, int M, int K, void* y, hipStream_t st) {
   if (M == 0) return hipSuccess;
   if (K % 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gain_rows_kernel, dim3(M), dim3(256), 0, st, x, (const bf16_t*)gain, K, (bf16_t*)y);
+  hipLaunchKernelGGL(gain_rows_kernel, dim3(M), dim3(256), 0, st, x, (const bf16_t*)gain, K, (float*)y);
   return hipGetLastError();
 }
 

@@ -466,19 +466,29 @@ __global__ void accept_kernel(AcceptArgs a) {
   uint8_t fl = 0;
   int n = kb;
   int emitted = -1;
+  bool stopped = false;  // a draft was rejected, or its target row was empty
   for (int j = 0; j < kb; ++j) {
     const int64_t pr = (int64_t)b * (k + 1) + j, qr = (int64_t)b * k + j;
     const int32_t* pid = a.p.ids + pr * a.p.cap;
     const float* pp = a.p.probs + pr * a.p.cap;
     const int pn = list_len(a.p, pr);
+    if (pn <= 0) {
+      // no distribution to test draft j against (its logits held no finite value): nothing
+      // from j on is kept and no token is emitted (-1 signals the bad row)
+      fl |= SPEC_FLAG_BAD_ROW;
+      n = j;
+      stopped = true;
+      break;
+    }
     if (a.greedy) {
-      const int am = pn > 0 ? list_argmax(pid, pp, pn) : -1;
+      const int am = list_argmax(pid, pp, pn);
       if (d[j] == am) {
         out[j] = d[j];
         continue;
       }
       n = j;
       emitted = am;
+      stopped = true;
       break;
     }
     const int32_t* qid = a.q.ids + qr * a.q.cap;
@@ -507,9 +517,10 @@ __global__ void accept_kernel(AcceptArgs a) {
     const float ur = philox_uniform(a.seed, 0u, a.round, (uint32_t)b, STREAM_RESIDUAL);
     emitted = (Z > 0.0f) ? sample_list(pid, r, pn, ur, &fl) : sample_list(pid, pp, pn, ur, &fl);
     n = j;
+    stopped = true;
     break;
   }
-  if (emitted < 0) {
+  if (!stopped) {
     // every draft kept: bonus token from the target row after the last draft
     const int64_t pr = (int64_t)b * (k + 1) + kb;
     const int32_t* pid = a.p.ids + pr * a.p.cap;
@@ -550,13 +561,14 @@ __global__ void accept_kernel(AcceptArgs a) {
 }
 
 // ---------------------------------------------------------------- kv trim
-__global__ void trim_kernel(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen) {
+// n_acc[b] is clamped to [0, k]: the host's bound on the lengths assumes at most k drafts kept.
+__global__ void trim_kernel(int32_t* len, const int32_t* n_acc, int batch, int k, int32_t* mlen) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   // the MTP layer keeps its entries up to the old last position: later ones were built from
   // its own hidden states rather than the target's
   if (mlen) mlen[b] = min(mlen[b], len[b] + 1);
-  len[b] += 1 + n_acc[b];
+  len[b] += 1 + min(max(n_acc[b], 0), k);
 }
 
 // ---------------------------------------------------------------- token history
@@ -702,8 +714,8 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int32_t* mlen, hipStream_t st) {
-  hipLaunchKernelGGL(trim_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, len, n_acc, batch, mlen);
+hipError_t launch_trim(int32_t* len, const int32_t* n_acc, int batch, int k, int32_t* mlen, hipStream_t st) {
+  hipLaunchKernelGGL(trim_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, len, n_acc, batch, k, mlen);
   return hipGetLastError();
 }
 

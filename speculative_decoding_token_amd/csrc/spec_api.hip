@@ -34,8 +34,8 @@ struct Model {
   size_t act = 4;
   CacheView cache{};
   float* x = nullptr;
-  // the input of the next projection of an RMSNorm: f32 models the normed rows; bf16 models
-  // bf16(rows * gain), the norm folded into the projection
+  // the input of the next projection of an RMSNorm, float32: f32 models the normed rows; bf16
+  // models rows * gain, which the projection scales by 1/rms and rounds to bf16 as it loads them
   void* xn = nullptr;
   float* qst = nullptr;
   float* kst = nullptr;
@@ -102,6 +102,7 @@ struct spec_ctx {
   int ncu = 0;
   int fgrid = 0;            // workgroups of the one-launch forward (0: not available)
   unsigned* fsync = nullptr;  // its barrier words
+  bool barrier_failed = false;  // a synchronizing call found the sticky barrier error word set
   unsigned long long* ftrace = nullptr;  // optional barrier timeline (spec_trace_forward)
   int ftrace_cap = 0;
   void* trunc = nullptr;
@@ -304,7 +305,7 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.cache.cap = cap;
   m.cache.hd = d.head_dim;
   m.x = cv.take<float>((size_t)m.Mmax * d.d_model * 4);
-  m.xn = cv.take<void>((size_t)m.Mmax * d.d_model * m.act);
+  m.xn = cv.take<void>((size_t)m.Mmax * d.d_model * 4);
   m.qst = cv.take<float>((size_t)m.Mmax * m.q_dim * 4);
   m.kst = cv.take<float>((size_t)m.Mmax * m.kv_dim * 4);
   m.attn = cv.take<void>((size_t)m.Mmax * m.q_dim * m.act);
@@ -428,10 +429,11 @@ int check_probs(spec_ctx* c, const spec_probs* p, const char* name, int need_cap
 
 int list_cap(const spec_sampler& s) { return s.temperature > 0.0f ? s.top_k : 1; }
 
-// RMSNorm input of a projection.  bf16 models fold the norm into the projection: it reads
-// bf16(x * gain) and scales each result row by 1/rms(x) from the row's np sum-of-squares
-// partials ss; `ready` says that the producer of x already left bf16(x * gain) in m.xn,
-// otherwise one small kernel writes it.  f32 models run the plain RMSNorm kernel.
+// RMSNorm input of a projection.  bf16 models have no normalization pass: the projection reads
+// the float32 rows x * gain and the row's np sum-of-squares partials ss, and rounds
+// (x * gain) / rms(x) to bf16 as it loads them; `ready` says that the producer of x already
+// left x * gain in m.xn, otherwise one small kernel writes it.  f32 models run the plain
+// RMSNorm kernel.
 int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const float* ss, int np,
                const void* gain, bool ready) {
   const spec_model_desc& d = m.d;
@@ -441,8 +443,8 @@ int norm_input(spec_ctx* c, Model& m, GemmArgs& g, int M, const float* x, const 
     g.x = m.xn;
     return SPEC_OK;
   }
-  // bf16: the projection reads bf16(x * gain) and scales its rows by 1/rms(x); the residual
-  // epilogue (or the embedding) that produced x normally left those rows in m.xn already
+  // bf16: the projection reads x * gain and the partials of x; the residual epilogue (or the
+  // embedding) that produced x normally left those rows in m.xn already
   if (!ready) LAUNCH(c, P + PROF_NORM, launch_gain_rows(x, gain, M, d.d_model, m.xn, c->stream));
   g.x = m.xn;
   g.ss_in = ss;
@@ -769,7 +771,7 @@ int forward_one_launch(spec_ctx* c, Model& m, int B, int mseq, const int32_t* fi
   a.cache = m.cache;
   a.rope = m.rope;
   a.x = m.x;
-  a.y = m.xn;
+  a.y = (float*)m.xn;
   a.ss = m.ss;
   a.ss_ld = d.d_model / 16 + 1;
   a.qkv = m.qkv;
@@ -854,6 +856,26 @@ int mtp_layer(spec_ctx* c, int B, int R, const float* h, int64_t h_ss, const int
 
 int need_ctx(spec_ctx* c) { return c ? SPEC_OK : SPEC_E_INVAL; }
 
+// After a call that synchronized the stream: the one-launch forward's sticky error word.  Once
+// it is set every result since the failed barrier is invalid, and every later cycle call of
+// the context fails.
+int read_barrier_error(spec_ctx* c) {
+  if (c->barrier_failed) return fail(c, SPEC_E_HIP, "a grid barrier of the one-launch forward timed out");
+  unsigned err = 0;
+  HIPCHK(c, hipMemcpyAsync(&err, (const char*)c->fsync + forward_error_offset(), sizeof err, hipMemcpyDeviceToHost,
+                           c->stream));
+  HIPCHK(c, hipStreamSynchronize(c->stream));
+  if (err) {
+    c->barrier_failed = true;
+    return fail(c, SPEC_E_HIP, "a grid barrier of the one-launch forward timed out");
+  }
+  return SPEC_OK;
+}
+int cycle_usable(spec_ctx* c) {
+  if (c->barrier_failed) return fail(c, SPEC_E_HIP, "a grid barrier of the one-launch forward timed out earlier");
+  return SPEC_OK;
+}
+
 // The host only knows bounds on the device lengths (an accept may keep 0..k drafts).  When
 // the upper bound leaves less than `need` free cache slots, read the exact lengths of the
 // first `batch` sequences (this synchronizes the stream) and tighten the bounds.
@@ -869,6 +891,7 @@ int ensure_room(spec_ctx* c, int batch, int need) {
   }
   c->len_lo = lo;
   c->len_hi = hi;
+  if (int rc = read_barrier_error(c)) return rc;
   if (c->len_hi + need > c->cap) return fail(c, SPEC_E_RANGE, "context would overflow the cache");
   return SPEC_OK;
 }
@@ -1222,6 +1245,7 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int32_t batch, int32_t P) {
 int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* draft_tok, spec_probs* q,
                int32_t* n_drafted) {
   if (need_ctx(c)) return SPEC_E_INVAL;
+  if (int rc = cycle_usable(c)) return rc;
   const int kind = c->cfg.draft_kind;
   if (kind == SPEC_DRAFT_NONE) return fail(c, SPEC_E_UNSUPPORTED, "no drafter configured");
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
@@ -1266,6 +1290,7 @@ int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* d
 int verify_step(spec_ctx* c, const int32_t* draft_tok, int32_t batch, int32_t k, float* logits_out,
                 spec_probs* p) {
   if (need_ctx(c)) return SPEC_E_INVAL;
+  if (int rc = cycle_usable(c)) return rc;
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
   if (k < 0 || k > c->cfg.max_k) return fail(c, SPEC_E_RANGE, "k %d not in 0..max_k", k);
   if (k > 0 && !draft_tok) return fail(c, SPEC_E_INVAL, "null draft_tok");
@@ -1296,6 +1321,7 @@ int verify_step(spec_ctx* c, const int32_t* draft_tok, int32_t batch, int32_t k,
 int accept(spec_ctx* c, const int32_t* draft_tok, const spec_probs* q, const spec_probs* p, int32_t batch,
            int32_t k, uint64_t round, int32_t* n_acc, int32_t* out_tok, uint8_t* near_tie) {
   if (need_ctx(c)) return SPEC_E_INVAL;
+  if (int rc = cycle_usable(c)) return rc;
   if (c->phase != VERIFIED) return fail(c, SPEC_E_STATE, "accept must follow verify_step");
   if (k != c->phase_k || batch != c->phase_batch) return fail(c, SPEC_E_STATE, "k / batch differ from the verify");
   if (!n_acc || !out_tok || (k > 0 && !draft_tok)) return fail(c, SPEC_E_INVAL, "null output");
@@ -1332,10 +1358,11 @@ int accept(spec_ctx* c, const int32_t* draft_tok, const spec_probs* q, const spe
 
 int kv_trim(spec_ctx* c, const int32_t* n_acc, int32_t batch) {
   if (need_ctx(c)) return SPEC_E_INVAL;
+  if (int rc = cycle_usable(c)) return rc;
   if (c->phase != ACCEPTED) return fail(c, SPEC_E_STATE, "kv_trim must follow accept");
   if (batch != c->phase_batch) return fail(c, SPEC_E_STATE, "batch differs from the cycle");
   if (!n_acc) return fail(c, SPEC_E_INVAL, "null n_acc");
-  LAUNCH(c, PROF_TRIM, launch_trim(c->len, n_acc, batch, c->mtp.present ? c->mtp_len : nullptr, c->stream));
+  LAUNCH(c, PROF_TRIM, launch_trim(c->len, n_acc, batch, c->phase_k, c->mtp.present ? c->mtp_len : nullptr, c->stream));
   c->len_lo += 1;
   c->len_hi += 1 + c->phase_k;
   c->mtp_rows = c->phase_k + 1;
@@ -1422,6 +1449,10 @@ int spec_get_stats(spec_ctx* c, spec_stats* out) {
                            hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
   out->sync_timeouts = err;
+  if (err) {
+    c->barrier_failed = true;
+    return fail(c, SPEC_E_HIP, "a grid barrier of the one-launch forward timed out");
+  }
   return SPEC_OK;
 }
 
@@ -1430,6 +1461,31 @@ int spec_get_lengths(spec_ctx* c, int32_t* lengths, int32_t batch) {
   if (batch < 1 || batch > c->cfg.max_batch) return fail(c, SPEC_E_RANGE, "batch %d", batch);
   HIPCHK(c, hipMemcpyAsync(lengths, c->len, sizeof(int32_t) * batch, hipMemcpyDeviceToHost, c->stream));
   HIPCHK(c, hipStreamSynchronize(c->stream));
+  return read_barrier_error(c);
+}
+
+int spec_debug_read(spec_ctx* c, int32_t which, int32_t buffer, void* dst, size_t bytes) {
+  if (need_ctx(c) || !dst) return SPEC_E_INVAL;
+  Model* m = which == 0 ? &c->target : (which == 1 ? &c->draft : (which == 2 ? &c->mtp : nullptr));
+  if (!m || !m->present) return fail(c, SPEC_E_INVAL, "no model %d", which);
+  const spec_model_desc& d = m->d;
+  const size_t rows = (size_t)m->Mmax;
+  const size_t cache = (size_t)c->cfg.max_batch * d.n_layers * d.n_kv_heads * c->cap * d.head_dim * m->act;
+  const void* src = nullptr;
+  size_t n = 0;
+  switch (buffer) {
+    case SPEC_BUF_RESIDUAL: src = m->x; n = rows * d.d_model * 4; break;
+    case SPEC_BUF_NORM_INPUT: src = m->xn; n = rows * d.d_model * 4; break;
+    case SPEC_BUF_Q: src = m->qst; n = rows * m->q_dim * 4; break;
+    case SPEC_BUF_K: src = m->kst; n = rows * m->kv_dim * 4; break;
+    case SPEC_BUF_ATTN: src = m->attn; n = rows * m->q_dim * m->act; break;
+    case SPEC_BUF_SWIGLU: src = m->h; n = rows * d.d_ffn * m->act; break;
+    case SPEC_BUF_CACHE_K: src = m->cache.k; n = cache; break;
+    case SPEC_BUF_CACHE_V: src = m->cache.v; n = cache; break;
+    default: return fail(c, SPEC_E_INVAL, "unknown buffer %d", buffer);
+  }
+  if (bytes < n) n = bytes;
+  HIPCHK(c, hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, c->stream));
   return SPEC_OK;
 }
 

@@ -17,18 +17,19 @@
 //   that stay resident: each wavefront keeps the k-slices it multiplies (K / 256 slices of 16
 //   bytes per lane).  Long reductions (the down projection, K = d_ffn) load their slices with
 //   each stage instead.
-// * RMSNorm is folded into the projections it feeds: W . RMSNorm(x) = (W . (x * g)) / rms(x).
-//   The QKV, gate/up and vocabulary projections read bf16(x * g), written next to the residual
-//   by the projection or embedding that produced x, and scale their results by
-//   1/sqrt(mean square + eps) from the sum-of-squares partials left with it, so no
-//   normalization pass exists.
+// * RMSNorm has no pass of its own.  The projection or embedding that produces a residual row x
+//   leaves next to it the float32 product x * g with the next norm's gain and, per 16 columns,
+//   the sum of squares of x.  The QKV, gate/up and vocabulary projections that consume the
+//   norm add those partials into 1/sqrt(mean square + eps) and round (x * g) times it to bf16
+//   as they load their resident input slices: the GEMM input is bf16(RMSNorm(x) * g), rounded
+//   where a plain normalization would round it.
 // * Each wavefront multiplies its k-steps of the stage with v_mfma_f32_16x16x32_bf16 (A = 16
 //   weight rows x 32 k read from LDS in the operand layout, B = the same 32 k of the 16 token
 //   rows, zero past M); the 8 partial tiles meet in LDS at the end of a unit.  The token
 //   dimension is padded to 16 at no cost: the kernel is bound by the weight stream.
 // * Residual projections add into the float32 residual stream and leave, per 16 columns and
 //   row, the sum of squares of the updated values and the values times the next norm's gain
-//   rounded to bf16.
+//   (float32).
 //
 // A row's result depends only on that row (every reduction order is fixed by K and d
 // alone), so the rows of a K+1-row verify are bit-identical to one-row forwards.
@@ -225,7 +226,7 @@ SPEC_DEVINL float unit_scale(const StreamArgs& a, int u, int t, int c) {
 // One projection over this workgroup's units (blockIdx.x, blockIdx.x + grid, ...).
 // EPI: epilogue.  NST > 0: K = NST stages, input slices resident in registers; NST == 0: any
 // K of whole stages, bf16 input slices loaded with each stage.  With a.ss_in set the
-// projection folds in an RMSNorm (resident inputs only).  COH: activations cross workgroups
+// projection takes an RMSNorm input (resident inputs only).  COH: activations cross workgroups
 // inside the launch.
 template <int EPI, int NST, bool COH, int WB = 2>
 struct Gemm {
@@ -314,12 +315,42 @@ struct Gemm {
 
     // Resident input slices: slice (ks, i) holds k = ks * KS + (wave + 8 i) * 32 + 8 (lane /
     // 16) .. + 7 of token row m (zero for m >= M).  Their loads, and those of the rows'
-    // sum-of-squares partials for a folded RMSNorm, are issued before the remaining first
-    // weight stages.
+    // sum-of-squares partials for an RMSNorm input, are issued before the remaining first
+    // weight stages.  An RMSNorm input is read as the float32 rows x * g (two 16-byte loads
+    // per slice) and rounded to bf16 once 1/rms of the row is known.
     constexpr int SSP = 8;  // partials per lane: np <= 512
+    // float32 slices in flight at once: all of them up to 16, else two halves (the second
+    // half's loads go out once the first half is converted), which bounds the registers
+    constexpr int XH = XS > 16 ? (XS + 1) / 2 : XS;
     uint4 xin[XS];
+    uint4 xf[RES ? XH : 1][2];
     float pss[2][SSP];
     const bool norm = a.ss_in != nullptr;
+    auto load_xf = [&](int q0) {
+      const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 4));
+      const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 4u;
+#pragma unroll
+      for (int v = 0; v < XH; ++v) {
+        const int q = q0 + v;
+        if (q >= XS) break;
+        const int ks = q / NSL, i = (q % NSL) / KSTEP, sub = q % KSTEP;
+        const int k4 = slice_k(ks, i, sub, wave) * 4;
+        xf[RES ? v : 0][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, k4, XP));
+        xf[RES ? v : 0][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, k4 + 16, XP));
+      }
+    };
+    auto convert_xf = [&](int q0, float rinv) {
+#pragma unroll
+      for (int v = 0; v < XH; ++v) {
+        const int q = q0 + v;
+        if (q >= XS) break;
+        const uint4 lo = xf[RES ? v : 0][0], hi = xf[RES ? v : 0][1];
+        xin[q] = make_uint4(pack_bf16(__uint_as_float(lo.x) * rinv, __uint_as_float(lo.y) * rinv),
+                            pack_bf16(__uint_as_float(lo.z) * rinv, __uint_as_float(lo.w) * rinv),
+                            pack_bf16(__uint_as_float(hi.x) * rinv, __uint_as_float(hi.y) * rinv),
+                            pack_bf16(__uint_as_float(hi.z) * rinv, __uint_as_float(hi.w) * rinv));
+      }
+    };
     if (norm) {
       const __amdgpu_buffer_rsrc_t sr = rsrc(a.ss_in, (uint32_t)(M * a.ss_ld * 4));
 #pragma unroll
@@ -334,13 +365,17 @@ struct Gemm {
       }
     }
     if (RES) {
-      const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
-      const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 2u;
+      if (norm) {
+        load_xf(0);
+      } else {
+        const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(M * K * 2));
+        const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 2u;
 #pragma unroll
-      for (int q = 0; q < XS; ++q) {
-        const int ks = q / NSL, i = (q % NSL) / KSTEP, sub = q % KSTEP;
-        xin[q] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, slice_k(ks, i, sub, wave) * 2, XP));
+        for (int q = 0; q < XS; ++q) {
+          const int ks = q / NSL, i = (q % NSL) / KSTEP, sub = q % KSTEP;
+          xin[q] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, slice_k(ks, i, sub, wave) * 2, XP));
+        }
       }
     }
     // fp8 weights: the row scales of this workgroup's units (unit q, tile t, column c at
@@ -368,10 +403,9 @@ struct Gemm {
       if (!RES) issue_x(a, j, xa[RES ? 0 : j]);
     }
 
-    // folded RMSNorm: 1/rms of each row (wavefront w handles rows w and w + 8; lane j adds
-    // partials j, j + 64, ... in order, then a fixed xor butterfly); thread e < 256 scales
-    // the results of token e / 16
-    float rinv = 1.0f;
+    // RMSNorm input: 1/rms of each row (wavefront w handles rows w and w + 8; lane j adds
+    // partials j, j + 64, ... in order, then a fixed xor butterfly), then the resident slices
+    // of token row m = lane % 16 become bf16((x * g) * 1/rms)
     if (norm) {
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
@@ -384,7 +418,14 @@ struct Gemm {
         if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(sum / (float)K + a.eps));
       }
       wg_barrier();
-      if (tx < 256 && (tx >> 4) < M) rinv = lds_read_f32(inv0 + (tx >> 4) * 4);
+      const float rinv = m < M ? lds_read_f32(inv0 + m * 4) : 0.0f;
+      if (RES) {
+        convert_xf(0, rinv);
+        if (XH < XS) {
+          load_xf(XH);
+          convert_xf(XH, rinv);
+        }
+      }
     }
     if (WB == 1) {
       // read at unit ends, after the first stage's barrier
@@ -422,8 +463,7 @@ struct Gemm {
 #pragma unroll
           for (int w = 0; w < SNW; ++w)
             sacc += __uint_as_float(r == 0 ? p[w].x : (r == 1 ? p[w].y : (r == 2 ? p[w].z : p[w].w)));
-          const float sw = WB == 1 ? sacc * lds_read_f32(scl0 + (((u - (int)blockIdx.x) / (int)gridDim.x * TILES + t) * 16 + c) * 4) : sacc;
-          v[t] = norm ? sw * rinv : sw;
+          v[t] = WB == 1 ? sacc * lds_read_f32(scl0 + (((u - (int)blockIdx.x) / (int)gridDim.x * TILES + t) * 16 + c) * 4) : sacc;
         }
         int mat, r0;
         (void)unit_rows<EPI, WB>(a, u, 0, &mat, &r0);
@@ -435,9 +475,7 @@ struct Gemm {
             float* xp = a.out + (int64_t)mm * a.ld + n;
             xn = ld<COH>(xp) + v[0];
             st<COH>(xp, xn);
-            if (a.y_out)
-              st<COH>((bf16_t*)a.y_out + (int64_t)mm * a.ld + n,
-                      f32_to_bf16(xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n])));
+            if (a.y_out) st<COH>((float*)a.y_out + (int64_t)mm * a.ld + n, xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
           }
           float sq = xn * xn;
 #pragma unroll

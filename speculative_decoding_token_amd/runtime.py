@@ -292,5 +292,14 @@ class Engine:
     def stats(self):
         return B.spec_get_stats(self.ctx)
 
+    def read_buffer(self, which: int, buffer: int, shape, dtype=torch.float32) -> torch.Tensor:
+        """A device copy of the start of one of the context's activation buffers (see
+        spec_debug_read), viewed as ``shape`` of ``dtype``."""
+        out = torch.empty(shape, dtype=dtype, device="cuda")
+        with self._enter():
+            B.spec_debug_read(self.ctx, which, buffer, out, out.numel() * out.element_size())
+        self.stream.synchronize()
+        return out
+
     def lengths(self, batch: int):
         return B.spec_get_lengths(self.ctx, batch)
