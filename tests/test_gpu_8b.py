@@ -9,23 +9,16 @@ import torch
 from oracle import model as om
 from oracle import sampling as osm
 from speculative_decoding_token_amd import runtime, synth
-from tests.helpers import RTOL_BF16, assert_rows_close
+from tests.helpers import RTOL_BF16, assert_rows_close, check_list_row, host_weights_f64
 
 pytestmark = pytest.mark.gpu
 
 
 def host_weights(w):
-    out = {"embed": w["embed"].float().cpu().numpy(), "final_norm": w["final_norm"].float().cpu().numpy()}
-    out["lm_head"] = out["embed"] if w["lm_head"] is w["embed"] else w["lm_head"].float().cpu().numpy()
-    out["layers"] = [{k: v.float().cpu().numpy() for k, v in lw.items()} for lw in w["layers"]]
-    return out
+    return host_weights_f64(w)
 
 
-@pytest.mark.parametrize("schedule", ["step", "stream", "forward"])
-@pytest.mark.parametrize("name,L,K,temp", [("qwen8b", 2048, 4, 0.0), ("qwen8b", 2048, 8, 1.0),
-                                           ("qwen0p6b", 2047, 16, 1.0), ("qwen0p6b", 2047, 1, 0.0),
-                                           ("qwen27b", 4096, 4, 0.0)])
-def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
+def two_layer_verify(name, L, K, temp, schedule):
     shape = synth.SHAPES[name].with_layers(2)
     w = synth.make_weights(shape, 0, device="cuda")
     k, v = synth.make_kv_prefix(shape, L, 0, device="cuda")
@@ -51,21 +44,32 @@ def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
     spec = om.Spec.from_shape(shape)
     W = host_weights(w)
     kv = om.KVCache(spec, L + K + 2)
-    kv.load_prefix(k.float().cpu().numpy(), v.float().cpu().numpy())
+    kv.load_prefix(k.double().cpu().numpy(), v.double().cpu().numpy())
     ref = om.forward_tokens(spec, W, kv, [t0] + drafts)
     assert eng.stats()["sync_timeouts"] == 0
     err = assert_rows_close(logits, ref, RTOL_BF16)
     print(f"{name} L={L} K={K} {schedule}: worst row error {err:.2e}")
     abs_err = np.abs(logits.astype(np.float64) - ref).max(axis=1)
-    for i in range(K + 1):
-        o = osm.truncate(ref[i], temp, 20, 0.95)
-        gi, gp = plists[i]
-        if o.gap_logit < 2 * abs_err[i] * (1.0 if temp == 0.0 else 1.0 / temp):
-            continue  # the boundary decision is within the observed logit error
-        if temp > 0 and o.margin < 4e-2:
-            continue
-        assert np.array_equal(gi, o.ids), i
-        np.testing.assert_allclose(gp, o.probs, atol=4e-2 * float(o.probs.max()))
+    kinds = [check_list_row(*plists[i], ref[i], abs_err[i], temp) for i in range(K + 1)]
+    checked = kinds.count("exact")
+    print(f"{name} L={L} K={K} {schedule}: {checked} of {K + 1} target lists compared whole, {kinds.count('partial')} around a decision within the error")
+    assert checked >= 1 or temp > 0, "no list far enough from a tie to compare whole"
+
+
+@pytest.mark.parametrize("schedule", ["step", "stream", "forward"])
+@pytest.mark.parametrize("name,L,K,temp", [("qwen8b", 2048, 4, 0.0), ("qwen8b", 2048, 8, 1.0),
+                                           ("qwen0p6b", 2047, 16, 1.0), ("qwen0p6b", 2047, 1, 0.0),
+                                           ("qwen27b", 4096, 4, 0.0)])
+def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
+    two_layer_verify(name, L, K, temp, schedule)
+
+
+@pytest.mark.parametrize("K,temp", [(1, 0.0), (2, 1.0), (8, 0.0), (16, 1.0)])
+def test_27b_shape_verify_k_sweep(K, temp):
+    """The 27B shape (d 5120, 40/8 heads, FFN 17408, a 4096-entry cache) at the other draft
+    lengths of its workload; K = 16 is 17 rows, past the streamed projections' 16, so that verify
+    runs the per-tile kernels."""
+    two_layer_verify("qwen27b", 4096, K, temp, "stream")
 
 
 @pytest.mark.parametrize("schedule", ["step", "stream", "forward"])

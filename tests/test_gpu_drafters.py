@@ -21,10 +21,11 @@ import torch
 from oracle import model as om
 from oracle import ngram as ong
 from oracle import sampling as osm
+from oracle import philox as oph
 from oracle import spec as osp
 from speculative_decoding_token_amd import binding as B
 from speculative_decoding_token_amd import runtime, synth
-from tests.helpers import RTOL_BF16, assert_rows_close
+from tests.helpers import RTOL_BF16, assert_rows_close, check_list_row, host_weights_f64, token_lists
 from tests.test_gpu_model import cmp_streams
 
 pytestmark = pytest.mark.gpu
@@ -227,3 +228,67 @@ def test_ngram_batch_two_per_sequence_counts():
             found_counts.add(len(rc.drafts))
             pos += len(rc.tokens)
     assert len(found_counts) > 1, found_counts
+
+
+@pytest.mark.parametrize("temperature", [0.0, 1.0])
+def test_ngram_9b_shape_8k_copy_stream(temperature):
+    """The n-gram workload at its size: the 9B shape (2 of its 32 layers, the full 151936-token
+    LM head) over an 8192-token copy-heavy stream as the context (a seeded cache prefix of
+    8191 positions, the stream as the token history), drafting up to 8 tokens per cycle with
+    the lookup, gate off.  Each GPU cycle is checked against the oracle run on the same history:
+    the lookup's drafts exactly, the verify's logits within the bf16 tolerance and its lists
+    (check_list_row), and the accepted count unless a decision lies within the logit error; the
+    oracle then follows the GPU's emitted tokens, so a near-tie never ends the comparison."""
+    shape = synth.SHAPES["qwen9b_mtp"].with_layers(2)
+    shape = dataclasses.replace(shape, mtp=False)
+    n_ctx, K, n_cycles = 8192, 8, 10
+    stream = synth.make_copy_stream(n_ctx, shape.vocab, seed=5)
+    # end the context inside a copy of an earlier window, so that the first lookup drafts
+    stream = np.concatenate([stream[:n_ctx - 24], stream[4000:4024]]).astype(np.int32)
+    L = n_ctx - 1
+    w = synth.make_weights(shape, 0, device="cuda")
+    k, v = synth.make_kv_prefix(shape, L, 0, device="cuda")
+    cap = n_ctx + K * n_cycles + 16
+    eng = runtime.Engine(shape, w, temperature=temperature, seed=21, max_ctx=cap, max_k=K, drafter="ngram",
+                         ngram=(3, 16))
+    eng.load_prefix(0, 0, k, v, L)
+    eng.load_history(0, torch.from_numpy(stream[:L].copy()).cuda())
+    eng.set_last(torch.tensor([int(stream[L])], dtype=torch.int32, device="cuda"))
+    spec = om.Spec.from_shape(shape)
+    W = host_weights_f64(w)
+    tkv = om.KVCache(spec, cap + K + 2)
+    tkv.load_prefix(k.double().cpu().numpy(), v.double().cpu().numpy())
+    hist = [int(t) for t in stream]
+    drafted = compared = excused = 0
+    for r in range(n_cycles):
+        c = eng.cycle(1, K, r, keep=True)
+        Lr = tkv.length
+        drafts, _, _ = ong.ngram_draft(hist, K, 3, 16)
+        assert c.drafts[0] == drafts, (r, c.drafts[0], drafts)
+        kk = len(drafts)
+        drafted += kk
+        rows = [hist[Lr]] + drafts
+        ref = om.forward_tokens(spec, W, tkv, rows)
+        got = c.logits[0][: kk + 1].cpu().numpy()
+        assert_rows_close(got, ref, RTOL_BF16)
+        abs_err = np.abs(got.astype(np.float64) - ref).max(axis=1)
+        for i in range(kk + 1):
+            compared += check_list_row(*c.p[i], ref[i], abs_err[i], temperature) == "exact"
+        # the accept rule on the GPU's own lists (one-hot drafts) and uniforms: exact
+        ps = token_lists(c.p[: kk + 1])
+        qs = [osp.one_hot(d) for d in drafts]
+        if temperature == 0.0:
+            res = osm.accept(drafts, qs, ps, True)
+        else:
+            ua = [oph.uniform(21, j, r, 0, 1) for j in range(1, kk + 1)]
+            res = osm.accept(drafts, qs, ps, False, ua, oph.uniform(21, 0, r, 0, 2))
+        if res.margin >= 1e-6:
+            assert c.n[0] == res.n and c.tokens[0] == res.tokens, (r, c.n[0], res.n, c.tokens[0], res.tokens)
+        else:
+            excused += 1
+        n = c.n[0]
+        tkv.trim(Lr + 1 + n)
+        hist.extend(int(t) for t in c.tokens[0])
+    print(f"9B-shape n-gram T={temperature}: {drafted} drafts over {n_cycles} cycles, {compared} target lists "
+          f"compared whole (the rest around a decision within the error), {excused} accept decisions at |u - p/q| < 1e-6")
+    assert drafted > 0 and (compared >= 1 or temperature > 0)

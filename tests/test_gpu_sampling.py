@@ -182,13 +182,20 @@ def accept_case(batch, K, sigma, greedy, seed, check_seqs):
 @pytest.mark.parametrize("K", [1, 2, 4, 8])
 @pytest.mark.parametrize("sigma", [0.5, 1.0, 2.0])
 def test_accept_workload_full_size(K, sigma):
-    n, excused = accept_case(64, K, sigma, False, seed=int(K * 10 + sigma * 4), check_seqs=range(0, 64, 16))
-    assert excused <= 1
+    """Every one of the 64 sequences re-derived by the oracle at K = 8, every fourth at the
+    smaller K; a sequence is excused only at a decision flagged within 1e-6."""
+    seqs = range(64) if K == 8 else range(0, 64, 4)
+    n, excused = accept_case(64, K, sigma, False, seed=int(K * 10 + sigma * 4), check_seqs=seqs)
+    print(f"accept workload K={K} sigma={sigma}: {len(seqs) - excused} of {len(seqs)} sequences compared, "
+          f"{excused} at a flagged near-tie")
+    assert excused <= max(1, len(seqs) // 32)
     assert n.min() >= 0 and n.max() <= K
 
 
-def test_accept_workload_greedy_full_size():
-    n, excused = accept_case(64, 4, 1.0, True, seed=5, check_seqs=range(0, 64, 8))
+@pytest.mark.parametrize("K", [4, 8])
+def test_accept_workload_greedy_full_size(K):
+    n, excused = accept_case(64, K, 1.0, True, seed=5 + K, check_seqs=range(64))
+    print(f"greedy accept workload K={K}: {64 - excused} of 64 sequences compared")
     assert excused == 0
 
 
@@ -221,3 +228,66 @@ def test_ngram_parity():
         d, ell, e = ong.ngram_draft(c, k, 3, 16)
         assert nf[b] == len(d) and list(drafts[b, :len(d)]) == d, b
         assert (match[b, 0], match[b, 1]) == ((ell, e) if d else (0, -1))
+
+
+def test_ngram_parity_copy_stream_8k_9b_vocab():
+    """The n-gram workload at its size: an 8192-token copy-heavy stream (40% copies of earlier
+    32-256-token windows, 60% uniform tokens over the 151936-token vocabulary), lookups at every
+    one of 64 cut points spread over it, each against the oracle's brute-force window search."""
+    V, n = 151936, 8192
+    stream = synth.make_copy_stream(n, V, seed=3)
+    cuts = np.linspace(64, n, 64).astype(np.int32)
+    batch, ld, k = len(cuts), n, 8
+    buf = np.zeros((batch, ld), np.int32)
+    for b, c in enumerate(cuts):
+        buf[b, :c] = stream[:c]
+    drafts = torch.empty((batch, k), dtype=torch.int32, device="cuda")
+    nf = torch.empty(batch, dtype=torch.int32, device="cuda")
+    match = torch.empty((batch, 2), dtype=torch.int32, device="cuda")
+    B.spec_ngram_match(torch.from_numpy(buf).cuda(), torch.from_numpy(cuts).cuda(), batch, ld, k, 3, 16,
+                       drafts, nf, match)
+    torch.cuda.synchronize()
+    drafts, nf, match = drafts.cpu().numpy(), nf.cpu().numpy(), match.cpu().numpy()
+    found = 0
+    for b, c in enumerate(cuts):
+        d, ell, e = ong.ngram_draft([int(x) for x in stream[:c]], k, 3, 16)
+        assert nf[b] == len(d) and list(drafts[b, :len(d)]) == d, b
+        assert (match[b, 0], match[b, 1]) == ((ell, e) if d else (0, -1)), b
+        found += len(d) > 0
+    print(f"8k n-gram lookups: {found} of {batch} cut points drafted")
+    assert found >= batch // 4
+
+
+@pytest.mark.parametrize("greedy", [True, False])
+def test_accept_stops_at_an_empty_target_row(greedy):
+    """A target row with no entry (its logits held no finite value) stops the sequence there:
+    the drafts before it are kept, no token is emitted (-1) and SPEC_FLAG_BAD_ROW is set, in
+    greedy and sampled mode; the drafts after it are never committed.  Sequence 1 has every row
+    and keeps every draft (each is its target row's only token)."""
+    K, batch, cap = 4, 2, 4
+    p = B.Probs(batch * (K + 1), cap)
+    q = B.Probs(batch * K, cap)
+    drafts = torch.tensor([[5, 6, 7, 8], [9, 10, 11, 12]], dtype=torch.int32, device="cuda")
+    for b in range(batch):
+        for j in range(K + 1):
+            r = b * (K + 1) + j
+            if b == 0 and j == 2:
+                continue  # empty row: count stays 0
+            tok = int(drafts[b, j]) if j < K else 99
+            p.ids[r, 0] = tok
+            p.probs[r, 0] = 1.0
+            p.count[r] = 1
+        for j in range(K):
+            r = b * K + j
+            q.ids[r, 0] = int(drafts[b, j])
+            q.probs[r, 0] = 1.0
+            q.count[r] = 1
+    n = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((batch, K + 1), -7, dtype=torch.int32, device="cuda")
+    tie = torch.zeros(batch, dtype=torch.uint8, device="cuda")
+    B.spec_accept_lists(drafts, q, p, batch, K, greedy, 3, 1, n, out, tie)
+    torch.cuda.synchronize()
+    n, out, tie = n.cpu().tolist(), out.cpu().tolist(), tie.cpu().tolist()
+    assert n[0] == 2 and out[0][:3] == [5, 6, -1], (n, out)
+    assert tie[0] & B.FLAG_BAD_ROW
+    assert n[1] == K and out[1] == [9, 10, 11, 12, 99] and not (tie[1] & B.FLAG_BAD_ROW), (n, out, tie)
