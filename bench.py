@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                     help="target projection weights: bf16, or OCP E4M3 codes with a float32 scale per row")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-weight verify run of the default bench")
+    ap.add_argument("--no-sampled", action="store_true", help="skip the sampled-cycle run of the default bench")
+    ap.add_argument("--no-accept-workload", action="store_true", help="skip the stand-alone accept workload")
+    ap.add_argument("--repeats", type=int, default=5, help="timed loops of --steps cycles (median and CV)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
     return ap.parse_args()
@@ -162,52 +165,122 @@ def gdn_state_run(torch, synth, B, K, reps=20, layers=48, H=32, dv=128):
             "timing": f"HIP events around {reps} cycles of {layers} back-to-back launches"}
 
 
-def cpu_baseline(tshape, dshape, tw, dw, K, t_layers=3, d_layers=4):
-    """The oracle (numpy, fp64) timed on a bounded sample of one cycle at the full shapes:
-    per model, a one-row forward through no layer (embedding, final norm, vocab head) and
-    a few single-row decoder layers, scaled to the model's layer count; a cycle at
-    acceptance 0 costs K+1 target rows and K draft rows for one emitted token."""
+def cpu_baseline(tshape, dshape, tw, dw, tk, tv, dk, dv, K, prev, last, seed=0):
+    """The oracle (numpy, float64 between the contract's rounding points) running the same
+    greedy cycle on the host: the draft model's K forwards (its first feeding the tokens at
+    positions L-1 and L, as on the GPU), the target's verify over K+1 rows, truncation, accept
+    and trim, on the same weights and cache prefixes.  One warm-up cycle, then one timed cycle.
+    The weights are widened to float64 once beforehand (host memory, outside the timing)."""
     import numpy as np
     import torch
     from oracle import model as om
+    from oracle import sampling as osm
+    from oracle import spec as osp
 
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas = 1
-    host = lambda t: t.float().cpu().numpy()
-    res, parts = {}, []
-    for name, shape, w, n_s in (("target", tshape, tw, t_layers), ("draft", dshape, dw, d_layers)):
-        W = {"embed": host(w["embed"]), "final_norm": host(w["final_norm"]),
-             "lm_head": host(w["lm_head"]), "layers": []}
-        spec0 = om.Spec.from_shape(shape.with_layers(0))
+    t_load = time.perf_counter()
+
+    def host(w):
+        conv = lambda t: t.detach().to("cpu").to(torch.float64).numpy()
+        out = {"embed": conv(w["embed"]), "final_norm": conv(w["final_norm"]),
+               "layers": [{k: conv(v) for k, v in lw.items()} for lw in w["layers"]]}
+        out["lm_head"] = out["embed"] if w["lm_head"] is w["embed"] else conv(w["lm_head"])
+        return out
+    tW, dW = host(tw), host(dw)
+    ts, ds = om.Spec.from_shape(tshape), om.Spec.from_shape(dshape)
+    L = tk.shape[2]
+    tkv = om.KVCache(ts, L + 2 * (K + 1) + 2)
+    tkv.load_prefix(tk.double().cpu().numpy(), tv.double().cpu().numpy())
+    draft = osp.DraftModel(ds, dW, L + 2 * (K + 1) + 2)
+    draft.kv.load_prefix(dk.double().cpu().numpy(), dv.double().cpu().numpy())
+    hist = [0] * (L - 1) + [int(prev), int(last)]
+    load_s = time.perf_counter() - t_load
+    sampler = osp.Sampler(0.0, 20, 0.95)
+    times = []
+    for rnd in range(2):
+        Lr = tkv.length
         t0 = time.perf_counter()
-        om.forward_one(spec0, W, om.KVCache(spec0, 2, n_layers=1), 0, 1)
-        t_head = time.perf_counter() - t0
-        del W
-        spec = om.Spec.from_shape(shape)
-        kv = om.KVCache(spec, 2, n_layers=n_s)
-        x = np.asarray(host(w["embed"][1]), dtype=np.float64)
-        t_lay = 0.0
-        for l in range(n_s):
-            lw = {k: host(v) for k, v in w["layers"][l].items()}
-            t0 = time.perf_counter()
-            x = om.decoder_layer(spec, lw, x, 0, kv, l)
-            t_lay += time.perf_counter() - t0
-            del lw
-        row = t_head + shape.n_layers * t_lay / n_s
-        res[name] = row
-        parts.append(f"{name}: head {t_head:.2f} s + {n_s} layers {t_lay:.2f} s -> row {row:.1f} s "
-                     f"({shape.n_layers} layers)")
-    cycle = (K + 1) * res["target"] + K * res["draft"]
+        drafts, qs = draft.propose(hist, Lr, K, sampler, seed, rnd)
+        t1 = time.perf_counter()
+        ref = om.forward_tokens(ts, tW, tkv, [hist[Lr]] + drafts)
+        ps = [osm.truncate(ref[i], 0.0, 20, 0.95) for i in range(K + 1)]
+        t2 = time.perf_counter()
+        res = osm.accept(drafts, qs, ps, True)
+        tkv.trim(Lr + 1 + res.n)
+        draft.trim(Lr + 1 + res.n)
+        hist.extend(res.tokens)
+        t3 = time.perf_counter()
+        times.append((t1 - t0, t2 - t1, t3 - t2, len(res.tokens)))
+    d_s, v_s, a_s, n_emit = times[-1]
+    cycle = d_s + v_s + a_s
     return {
-        "value": 1.0 / cycle, "unit": "tokens/s", "cores": blas, "kind": "oracle",
-        "sample": ("one row through embedding/final norm/vocab head and through the first few decoder "
-                   "layers of each model at the full shapes, scaled to all layers and to a K=%d cycle at "
-                   "acceptance 0 (K+1 target rows + K draft rows per emitted token); " % K) + "; ".join(parts),
-        "os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+        "value": n_emit / cycle, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+        "sample": (f"one full greedy K={K} cycle of the workload after one warm-up cycle: {K} draft forwards of "
+                   f"the {dshape.n_layers}-layer draft (the first over 2 rows), the {tshape.n_layers}-layer "
+                   f"target's verify over {K + 1} rows with truncation, accept and trim, numpy float64"),
+        "cycle_s": cycle, "draft_s": d_s, "verify_s": v_s, "accept_trim_s": a_s, "emitted": n_emit,
+        "warmup_cycle_s": sum(times[0][:3]), "weight_widening_s": load_s,
+        "os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "blas_threads": blas,
     }
+
+
+def accept_workload_run(torch, synth, B, batch=64, K=8, sigma=1.0, copies=3, reps=30, seed=0):
+    """The accept workload on its own: for `batch` sequences, truncation (T = 1, top_k 20,
+    top_p 0.95) of K + 1 target and K draft rows of bf16 logits over the 151936-token vocabulary,
+    the drafts sampled from q, and the accept rule with the residual resample; `copies` input
+    copies (together larger than the 256 MB memory-side cache) are rotated."""
+    V = 151936
+    t, d = synth.make_accept_logits(batch, K, V, sigma, seed=seed, device="cuda", copies=copies)
+    tl, dl = B.Probs(batch * (K + 1), 20), B.Probs(batch * K, 20)
+    nbytes = B.spec_truncate_scratch_size(batch * (K + 1), V)
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    drafts = torch.empty((batch, K), dtype=torch.int32, device="cuda")
+    n = torch.empty(batch, dtype=torch.int32, device="cuda")
+    out = torch.empty((batch, K + 1), dtype=torch.int32, device="cuda")
+    smp = B.sampler(1.0, 20, 0.95)
+    st = torch.cuda.current_stream()
+
+    def call(c, rnd, parts=None):
+        if parts is not None:
+            parts[0].record(st)
+        B.spec_truncate(t[c], B.DTYPE_BF16, batch * (K + 1), V, V, smp, tl, None, scratch, nbytes)
+        B.spec_truncate(d[c], B.DTYPE_BF16, batch * K, V, V, smp, dl, None, scratch, nbytes)
+        if parts is not None:
+            parts[1].record(st)
+        B.spec_sample(dl, batch, K, seed, rnd, 0, drafts)
+        B.spec_accept_lists(drafts, dl, tl, batch, K, False, seed, rnd, n, out, None)
+        if parts is not None:
+            parts[2].record(st)
+    for r in range(copies):
+        call(r, r)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for r in range(reps):
+        call(r % copies, r)
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tr, ac = [], []
+    for r in range(reps):
+        call(r % copies, r, ev)
+        torch.cuda.synchronize()
+        tr.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        ac.append(ev[1].elapsed_time(ev[2]) * 1e3)
+    nb = 2 * batch * (2 * K + 1) * V
+    acc = float(n.float().mean().item()) / K
+    return {"batch": batch, "k": K, "sigma": sigma, "vocab": V, "copies": copies,
+            "bytes_per_call": nb, "us_per_call": us, "GBps": nb / (us * 1e-6) / 1e9,
+            "frac_peak": nb / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "roofline_us": nb / (PEAK_HBM_GBS * 1e9) * 1e6,
+            "truncate_us": sorted(tr)[len(tr) // 2], "sample_accept_us": sorted(ac)[len(ac) // 2],
+            "acceptance_last_call": acc,
+            "timing": f"HIP events around {reps} calls back to back (rotating {copies} input copies); the "
+                      f"split into truncation and sample + accept is the median of single calls"}
 
 
 def main():
@@ -244,7 +317,7 @@ def main():
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
     SWEEP_K, SWEEP_REPS = (1, 2, 4, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
     max_k = max(K, max(SWEEP_K))
-    n_cycles = args.warmup + 2 * args.steps + args.profile_steps + 2  # timed run + the sync-loop rerun
+    n_cycles = args.warmup + (2 + args.repeats) * args.steps + args.profile_steps + 2  # timed runs + sync loop
     max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + 8
     Bn = args.batch
     if Bn > 1:
@@ -296,6 +369,20 @@ def main():
     torch.cuda.synchronize()
     sync_loop = {"tok_s": emitted_sync / (time.perf_counter() - t1),
                  "ms_per_step": (time.perf_counter() - t1) / args.steps * 1e3}
+    # repeats of the timed loop (the first one is the headline value)
+    rep_tok_s = [emitted / elapsed]
+    for _ in range(args.repeats - 1):
+        torch.cuda.synchronize()
+        tr0 = time.perf_counter()
+        cyc_r = eng.run(Bn, K, rnd, args.steps)
+        torch.cuda.synchronize()
+        rep_tok_s.append(sum(len(t) for c in cyc_r for t in c.tokens) / (time.perf_counter() - tr0))
+        rnd += args.steps
+    srt = sorted(rep_tok_s)
+    mean = sum(rep_tok_s) / len(rep_tok_s)
+    cv = (sum((x - mean) ** 2 for x in rep_tok_s) / len(rep_tok_s)) ** 0.5 / mean
+    repeats = {"tok_s": rep_tok_s, "median": srt[len(srt) // 2], "cv": cv,
+               "how": f"{len(rep_tok_s)} timed loops of {args.steps} cycles (the first is `value`)"}
     tok_s = emitted / elapsed
     verify_avg_ms = sum(verify_ms) / len(verify_ms)
     vbytes = verify_bytes(tshape, K, L + args.warmup + 1, Bn, fp8)
@@ -411,8 +498,30 @@ def main():
         del eng8, tw8
         torch.cuda.empty_cache()
 
+    # the same cycle under sampling (T = 1, top_k 20, top_p 0.95): a second context on the same
+    # weights
+    sampled = None
+    if not args.sampled and not fp8 and not args.no_sampled and Bn == 1:
+        engs = runtime.Engine(tshape, tw, dshape, dw, temperature=1.0, seed=0, max_ctx=max_ctx, max_k=K)
+        if args.no_graphs:
+            engs.use_graphs(False)
+        engs.set_schedule(sched)
+        reset(engs)
+        engs.run(1, K, 0, args.warmup)
+        torch.cuda.synchronize()
+        ts0 = time.perf_counter()
+        cs = engs.run(1, K, args.warmup, args.steps, time_verify=True)
+        torch.cuda.synchronize()
+        els = time.perf_counter() - ts0
+        sampled = {"sampler": "T=1 top_k 20 top_p 0.95, Philox uniforms", "tok_s": sum(len(t) for c in cs for t in c.tokens) / els,
+                   "ms_per_step": els / args.steps * 1e3, "verify_ms": sum(c.verify_ms for c in cs) / len(cs),
+                   "acceptance": sum(c.n[0] for c in cs) / (K * args.steps)}
+        del engs
+        torch.cuda.empty_cache()
+
     from speculative_decoding_token_amd import binding as SB
     gdn_run = gdn_state_run(torch, synth, SB, K)
+    accept_run = accept_workload_run(torch, synth, SB) if not args.no_accept_workload else None
 
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -429,7 +538,12 @@ def main():
         "verify_vs_k": verify_vs_k,
         "host_loop": {"timed": "one cycle queued ahead of the host's read of the previous cycle's tokens",
                       "sync_each_cycle": sync_loop},
+        "repeats": repeats,
+        "sampled": sampled,
         "roofline": {"bound": "hbm", "kernel": dom["kernel"],
+                     "verify_pass": {"GBps": verify_gbs, "frac": verify_gbs / PEAK_HBM_GBS, "ms": verify_avg_ms,
+                                     "bytes": vbytes, "note": "the whole verify_step (one graph launch): the "
+                                     "metric's figure; achieved/frac below are the dominant kernel's"},
                      "achieved": dom_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
                      "traffic": dominant_traffic(dom_key), "bytes_per_launch": dom_bytes, "avg_launch_ms": dom_ms,
                      "timing": (f"HIP events on the context stream around {REPS} back-to-back launches (the first "
@@ -442,10 +556,14 @@ def main():
         "adaptive_depth": adaptive,
         "fp8_weights": fp8_run,
         "linear_attention_state": gdn_run,
+        "accept_workload": accept_run,
+        "peak_device_memory_GB": torch.cuda.max_memory_allocated() / 1e9,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline and Bn == 1 and not fp8:
-        out["cpu_baseline"] = cpu_baseline(tshape, dshape, tw, dw, K)
+        del eng
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(tshape, dshape, tw, dw, tk, tv, dk, dv, K, starts[0][0], starts[0][1])
     print(json.dumps(out), flush=True)
 
 

@@ -425,7 +425,9 @@ int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t b
  *   SPEC_BUF_ATTN       [rows, n_q_heads*head_dim] model dtype: the last layer's attention output;
  *   SPEC_BUF_SWIGLU     [rows, d_ffn] model dtype: the last layer's SwiGLU product;
  *   SPEC_BUF_CACHE_K,_V the whole cache, [max_batch, n_layers, n_kv_heads, capacity, head_dim]
- *                       in the model dtype, capacity = max_ctx + max_k + 2. */
+ *                       in the model dtype, capacity = max_ctx + max_k + 2;
+ *   SPEC_BUF_LOGITS     [rows, vocab] the logits of the model's last forward that kept them in
+ *                       its own buffer (a draft forward; a verify without logits_out). */
 #define SPEC_BUF_RESIDUAL 0
 #define SPEC_BUF_NORM_INPUT 1
 #define SPEC_BUF_Q 2
@@ -434,6 +436,7 @@ int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t b
 #define SPEC_BUF_SWIGLU 5
 #define SPEC_BUF_CACHE_K 6
 #define SPEC_BUF_CACHE_V 7
+#define SPEC_BUF_LOGITS 8
 int spec_debug_read(spec_ctx* ctx, int32_t which, int32_t buffer, void* dst /*device*/, size_t bytes);
 
 /* ---- stateless kernels (the accept workload on its own) ------------------------------ */

@@ -41,7 +41,7 @@ EXPORTED = [
     "spec_depth_init", "spec_depth_choose", "spec_depth_update", "spec_gdn_commit_forward",
     "spec_debug_read",
 ]
-BUF_RESIDUAL, BUF_NORM_INPUT, BUF_Q, BUF_K, BUF_ATTN, BUF_SWIGLU, BUF_CACHE_K, BUF_CACHE_V = range(8)
+BUF_RESIDUAL, BUF_NORM_INPUT, BUF_Q, BUF_K, BUF_ATTN, BUF_SWIGLU, BUF_CACHE_K, BUF_CACHE_V, BUF_LOGITS = range(9)
 GDN_MAX_TOKENS = 64
 PROF_SLOTS = 32
 PROF_CLASSES = ["embed", "rmsnorm", "qkv", "attention", "o_proj", "gate_up", "down", "lm_head",

@@ -18,12 +18,14 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;    // one 16x16 MFMA 
 // ---- number formats ------------------------------------------------------------------
 SPEC_DEVINL float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// Round-to-nearest-even float32 -> bfloat16 on the bit pattern; NaN stays NaN.
-SPEC_DEVINL bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// Round-to-nearest-even float32 -> bfloat16 (gfx950's v_cvt_pk_bf16_f32, one instruction for
+// two values); NaN stays NaN.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+SPEC_DEVINL bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// Two values rounded to bfloat16, lo in the low half of the word.
+SPEC_DEVINL uint32_t bf16x2_pack(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Softmax weights of a 64-key attention chunk as A operands of the P V product on the bf16

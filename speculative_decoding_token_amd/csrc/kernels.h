@@ -258,6 +258,15 @@ size_t stream_lds_bytes();
 hipError_t stream_init();  // per device: LDS limit of the kernels
 hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_t st);
 
+// ---- vector-ALU projections of one or two rows (gemv.hip) ----------------------------
+// The streamed projections' arguments and epilogues, for M <= 2 rows and bf16 weights: RMSNorm
+// inputs (ss_in set, at most 128 partials per row) for QKV and the vocabulary projection with K
+// in {1024, 2048, 4096} and gate/up with K in {1024, 2048}; plain inputs for the residual
+// projections with K in {1024, 2048, 3072, 3584, 4096}.  One workgroup per unit of 16 rows
+// (a.nunits).
+bool gemv_supported(int M, int K, int epi, bool norm, int wbytes);
+hipError_t launch_gemv(int epi, const StreamArgs& a, hipStream_t st);
+
 // ---- one persistent launch per forward (bf16 models, M <= 16 rows) ------------------
 // The rows, positions and buffers of forward(); x, y, ss, q/k staging, attention partials and
 // outputs and the SwiGLU product are the model's workspace buffers.  layers is a device copy

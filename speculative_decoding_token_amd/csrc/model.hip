@@ -195,9 +195,7 @@ SPEC_DEVINL void gemm_epilogue(const GemmArgs& a, int mat, int m, int n, float v
 // first weights) and rounds (x * g) times it to bf16 as it loads each input slice.  A residual
 // epilogue leaves, per block, the sum of squares of its 16 updated columns of each row and,
 // when asked, those columns times the next norm's gain in float32.
-SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+SPEC_DEVINL uint32_t pack_bf16x2(float lo, float hi) { return bf16x2_pack(lo, hi); }
 
 // y[m, k] = x[m, k] * gain[k] in float32: a projection's RMSNorm input rows when the producer
 // of x left none.

@@ -30,6 +30,9 @@ struct Model {
   std::vector<spec_layer_scales> scales;  // fp8 weights: row scales of each layer
   bool fp8 = false;                       // SPEC_WEIGHTS_FP8_ROW
   bool present = false;
+  // one- and two-row forwards on the vector-ALU projections (the draft model: all its draft_step
+  // forwards take them, so its rows never depend on the row count)
+  bool gemv = false;
   int q_dim = 0, kv_dim = 0, mseq_max = 0, Mmax = 0, nchunk = 0;
   size_t act = 4;
   CacheView cache{};
@@ -387,6 +390,7 @@ int check_config(spec_ctx* c, const spec_config* cfg) {
     c->draft.fp8 = g.draft.weights == SPEC_WEIGHTS_FP8_ROW;
     c->draft.present = true;
     c->draft.mi = 1;
+    c->draft.gemv = true;
   } else if (g.draft_kind == SPEC_DRAFT_MTP) {
     // one extra decoder layer at the target's widths, its own final norm, the target's
     // embedding and LM head
@@ -485,6 +489,16 @@ bool stream_shapes(spec_ctx* c, const Model& m, int M) {
          stream_supported(M, d.d_model, EPI_STORE, true, wb, upw(d.vocab / 16));
 }
 
+// Whether the streamed-schedule forwards of m over M rows take the vector-ALU projections: a
+// model flagged for them (the draft), bf16 weights, at most 2 rows, and every projection shape
+// covered (RMSNorm inputs with at most 128 partials).
+bool use_gemv(const Model& m, int M) {
+  const spec_model_desc& d = m.d;
+  if (!m.gemv || m.fp8 || d.dtype != SPEC_DTYPE_BF16 || d.d_model / 16 > 128) return false;
+  return gemv_supported(M, d.d_model, EPI_QKV, true, 2) && gemv_supported(M, m.q_dim, EPI_RESID, false, 2) &&
+         gemv_supported(M, d.d_model, EPI_SWIGLU, true, 2) && gemv_supported(M, d.d_ffn, EPI_RESID, false, 2);
+}
+
 // fp8-weight models take these kernels under every schedule (no other kernel decodes fp8).
 bool use_stream(spec_ctx* c, const Model& m, int M) {
   const spec_model_desc& d = m.d;
@@ -501,6 +515,10 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
   const int ss_ld = d.d_model / 16 + 1;
   const int wb = m.fp8 ? 1 : 2;
   const spec_layer_scales no_scales{};
+  const bool gv = use_gemv(m, M);
+  auto proj = [&](int epi, const StreamArgs& a) {
+    return gv ? launch_gemv(epi, a, c->stream) : launch_stream_gemm(epi, a, grid, c->stream);
+  };
   for (int l = 0; l < d.n_layers; ++l) {
     const spec_layer_weights& w = m.layers[l];
     const spec_layer_scales& sc = m.fp8 ? m.scales[l] : no_scales;
@@ -528,7 +546,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.cache = m.cache;
     g.layer = l;
     g.rm = rm;
-    LAUNCH(c, P + PROF_QKV, launch_stream_gemm(EPI_QKV, g, grid, c->stream));
+    LAUNCH(c, P + PROF_QKV, proj(EPI_QKV, g));
     AttnArgs at{};
     at.q_stage = m.qst;
     at.k_stage = m.kst;
@@ -558,7 +576,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     o.ss_ld = ss_ld;
     o.y_out = m.xn;
     o.y_gain = w.ffn_norm;
-    LAUNCH(c, P + PROF_OPROJ, launch_stream_gemm(EPI_RESID, o, grid, c->stream));
+    LAUNCH(c, P + PROF_OPROJ, proj(EPI_RESID, o));
     np = d.d_model / 16;
     StreamArgs gu{};
     gu.w0 = w.wg;
@@ -585,7 +603,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
         g2.w0s = m.scales[lr].wg;
         g2.w1s = m.scales[lr].wu;
       }
-      return launch_stream_gemm(EPI_SWIGLU, g2, grid, c->stream);
+      return proj(EPI_SWIGLU, g2);
     };
     LAUNCH_REP(c, P + PROF_GATEUP, gu_rep);
     StreamArgs dn{};
@@ -603,7 +621,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     dn.ss_ld = ss_ld;
     dn.y_out = m.xn;
     dn.y_gain = l + 1 < d.n_layers ? m.layers[l + 1].attn_norm : d.final_norm;
-    LAUNCH(c, P + PROF_DOWN, launch_stream_gemm(EPI_RESID, dn, grid, c->stream));
+    LAUNCH(c, P + PROF_DOWN, proj(EPI_RESID, dn));
   }
   return SPEC_OK;
 }
@@ -1482,6 +1500,7 @@ int spec_debug_read(spec_ctx* c, int32_t which, int32_t buffer, void* dst, size_
     case SPEC_BUF_SWIGLU: src = m->h; n = rows * d.d_ffn * m->act; break;
     case SPEC_BUF_CACHE_K: src = m->cache.k; n = cache; break;
     case SPEC_BUF_CACHE_V: src = m->cache.v; n = cache; break;
+    case SPEC_BUF_LOGITS: src = m->logits; n = rows * d.vocab * 4; break;
     default: return fail(c, SPEC_E_INVAL, "unknown buffer %d", buffer);
   }
   if (bytes < n) n = bytes;

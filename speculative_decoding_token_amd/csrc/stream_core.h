@@ -156,9 +156,7 @@ SPEC_DEVINL int tid_here() {
   return v;
 }
 
-SPEC_DEVINL uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+SPEC_DEVINL uint32_t pack_bf16(float lo, float hi) { return bf16x2_pack(lo, hi); }
 
 // Two fp8 (OCP e4m3) weights -> two bf16 in one word.  The hardware conversion gives the exact
 // float32 value; an e4m3 value has at most 4 significant bits, so its upper 16 bits are the

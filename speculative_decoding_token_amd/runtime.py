@@ -93,26 +93,38 @@ class Engine:
         self.stream.wait_stream(torch.cuda.current_stream())
         return torch.cuda.stream(self.stream)
 
+    def _hold(self, *tensors):
+        """The library reads these caller tensors on the engine stream, after the call returns:
+        keep their memory from being reused by the caching allocator (which tracks only the
+        stream that allocated it) until that work has run."""
+        for t in tensors:
+            if t is not None and t.is_cuda:
+                t.record_stream(self.stream)
+
     def prefill(self, tokens: torch.Tensor):
         """tokens: int32 [batch, P] on the device."""
         with self._enter():
             b, P = tokens.shape
             B.spec_prefill(self.ctx, tokens, b, P)
+            self._hold(tokens)
 
     def load_prefix(self, which: int, seq: int, k: torch.Tensor, v: torch.Tensor, length: int):
         with self._enter():
             B.spec_load_kv(self.ctx, which, seq, k, v, length)
+            self._hold(k, v)
 
     def set_last(self, last_tok: torch.Tensor, prev_tok: Optional[torch.Tensor] = None,
                  hidden: Optional[torch.Tensor] = None):
         """hidden: float32 [batch, d] target hidden state at L-1 (the MTP drafter)."""
         with self._enter():
             B.spec_set_last(self.ctx, last_tok, prev_tok, hidden, last_tok.shape[0])
+            self._hold(last_tok, prev_tok, hidden)
 
     def load_history(self, seq: int, tokens: torch.Tensor):
         """Token history (int32, device) of sequence seq at positions 0..len-1."""
         with self._enter():
             B.spec_load_history(self.ctx, seq, tokens, int(tokens.numel()))
+            self._hold(tokens)
 
     # ---- one cycle
     def buffers(self, batch: int, k: int):
@@ -185,7 +197,9 @@ class Engine:
             else:
                 if not self.greedy:
                     raise ValueError("explicit drafts are supported with the greedy sampler")
-                buf["draft"].copy_(drafts.to(torch.int32))
+                d32 = drafts.to(torch.int32)
+                buf["draft"].copy_(d32)
+                self._hold(d32, drafts)
         logits = None
         if keep:
             logits = self._logits.get(k)

@@ -194,3 +194,54 @@ def test_0p6b_full_depth_draft_step(temp):
             l32 = om.forward_tokens(spec32, W, kv32, [drafts[j]])[-1]
     log(f"0.6B 28 layers draft_step T={temp}: {checked} of {K} draft decisions compared whole")
     assert checked >= 1 or temp > 0
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_0p6b_full_depth_draft_forward_logits(k):
+    """The k-th draft forward of a greedy draft_step (the first runs two rows, the tokens at L-1
+    and L; the later ones one row, the previous draft) of the 28-layer 0.6B-shape draft: its
+    logits row in the streamed schedule (the vector-ALU projections of one and two rows) and in
+    the per-tile schedule (the MFMA projections), against each other and against the oracle
+    fed the same drafts, beside the oracle's own float32 drift."""
+    ts = synth.SHAPES["qwen8b"].with_layers(1)
+    ds = synth.SHAPES["qwen0p6b"]
+    L = 2048
+    tw = synth.make_weights(ts, 0, device="cuda")
+    dw = synth.make_weights(ds, 1, device="cuda")
+    tk, tv = synth.make_kv_prefix(ts, L, 0, device="cuda")
+    dk, dv = synth.make_kv_prefix(ds, L - 1, 1, device="cuda")
+    prev, last = (int(x) for x in synth.make_tokens(2, ds.vocab, 9))
+    got, drafts = {}, {}
+    for sched in ("stream", "step"):
+        eng = runtime.Engine(ts, tw, ds, dw, temperature=0.0, seed=5, max_ctx=L + 40, max_k=k)
+        eng.set_schedule(sched)
+        eng.load_prefix(0, 0, tk, tv, L)
+        eng.load_prefix(1, 0, dk, dv, L - 1)
+        eng.set_last(torch.tensor([last], dtype=torch.int32, device="cuda"),
+                     torch.tensor([prev], dtype=torch.int32, device="cuda"))
+        buf = eng.buffers(1, k)
+        with eng._enter():
+            B.draft_step(eng.ctx, 1, k, 0, buf["draft"], buf["q"])
+        eng.stream.synchronize()
+        rows = 2 if k == 1 else 1
+        got[sched] = eng.read_buffer(1, B.BUF_LOGITS, (rows, ds.vocab)).cpu().numpy()[rows - 1]
+        drafts[sched] = buf["draft"][0].cpu().tolist()
+        eng.close()
+    spec, spec32 = om.Spec.from_shape(ds), om.Spec.from_shape(ds, arith32=True)
+    W = host_weights_f64(dw)
+    kh, vh = dk.double().cpu().numpy(), dv.double().cpu().numpy()
+    kv, kv32 = om.KVCache(spec, L + k + 4), om.KVCache(spec, L + k + 4)
+    kv.load_prefix(kh, vh)
+    kv32.load_prefix(kh, vh)
+    # the oracle fed the streamed schedule's drafts
+    toks = [prev, last] + drafts["stream"][: k - 1]
+    ref = om.forward_tokens(spec, W, kv, toks)[-1]
+    r32 = om.forward_tokens(spec32, W, kv32, toks)[-1]
+    e_stream = float(row_rel_err(got["stream"], ref))
+    e_step = float(row_rel_err(got["step"], ref))
+    drift = float(row_rel_err(r32, ref))
+    log(f"0.6B 28 layers, draft forward {k}: stream {e_stream:.2e}, step {e_step:.2e} (drafts "
+        f"{'equal' if drafts['stream'] == drafts['step'] else 'differ'}); oracle float32 drift {drift:.2e}")
+    assert e_stream <= max(RTOL_BF16, 2.0 * drift)
+    if drafts["stream"] == drafts["step"]:
+        assert e_step <= max(RTOL_BF16, 2.0 * drift)
