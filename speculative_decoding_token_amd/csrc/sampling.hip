@@ -5,10 +5,11 @@
 // draft and the verify side) runs in two launches:
 //   1. topk_segment: a workgroup per (row, segment of <= 16384 logits) finds the segment's
 //      exact top-k by the order (larger value, then lower id) from values held in
-//      registers: the k-th largest per-thread maximum bounds the answer from below, the
-//      elements at or above it are gathered into LDS and bitonic-sorted (a 64-step binary
-//      search on the key replaces the gather when more than 1024 elements qualify, e.g.
-//      on long runs of equal logits);
+//      registers: the k-th largest per-thread maximum of the raw values bounds the answer
+//      from below, the few elements at or above it are gathered into LDS and ranked exactly
+//      (a 64-step binary search on the key replaces the gather when more than 1024 elements
+//      qualify, e.g. on long runs of equal logits, or when the division by the temperature
+//      could tie the bound with the answer);
 //   2. truncate_finish: a wavefront per row merges the segment lists, then one lane does
 //      the float32 softmax, the top_p walk and the renormalization in the stated
 //      sequential order, and the lanes write the kept pairs in ascending id order.
@@ -24,7 +25,7 @@
 namespace spec {
 
 constexpr int TK_THREADS = 256;
-constexpr int TK_EPT = 32;                      // logits held per thread
+constexpr int TK_EPT = 64;                      // logits held per thread
 constexpr int TK_SEG = TK_THREADS * TK_EPT;     // longest segment
 constexpr int TK_CAND = 1024;                   // LDS candidate slots
 constexpr int FIN_THREADS = 256;
@@ -83,15 +84,52 @@ SPEC_DEVINL uint64_t wave_sort_desc(uint64_t v, int lane) {
 }
 
 // ---------------------------------------------------------------- 1. segment top-k
-// Output: the segment's ksel largest keys, descending, zero-padded.
+// Raw keys: an integer order of the stored bits (larger value, larger key; -0 just below +0;
+// NaN above +inf or below -inf by its sign), 16 bits for a bf16 value and 32 for a float32
+// one.  They bound the candidates only; the exact order is order_key's.
+constexpr uint32_t KEY16_NINF = 0x007Fu, KEY16_PINF = 0xFF80u;
+constexpr uint32_t KEY32_NINF = 0x007FFFFFu, KEY32_PINF = 0xFF800000u;
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// Two bf16 values packed in a word -> their two 16-bit keys, packed the same way.
+SPEC_DEVINL uint32_t raw_keys16x2(uint32_t w) {
+  const i16x2_t sgn = __builtin_bit_cast(i16x2_t, w) >> (i16x2_t){15, 15};
+  return w ^ (__builtin_bit_cast(uint32_t, sgn) | 0x80008000u);
+}
+SPEC_DEVINL uint32_t raw_key32(uint32_t u) {
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+// Inverse of the raw keys: the value as a float.
+SPEC_DEVINL float key16_value(uint32_t k) {
+  const uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
+SPEC_DEVINL float key32_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Output: the segment's ksel largest keys (order of value / T, then lower id), descending,
+// zero-padded.  Every thread holds TK_EPT logits and turns them into raw keys in place (bf16:
+// two per word, with packed 16-bit arithmetic), keeping its largest and smallest key.  In each
+// wavefront, a 16- or 32-step bitwise search over ballots finds the ceil(ksel / 4)-th largest
+// thread maximum; the smallest of the four is a bound that at least ksel logits reach.  Only
+// the logits reaching it go to LDS, with their ids, and are ordered exactly (value / T as an
+// IEEE float32 division, then id).  Every logit below the bound is at most the value whose key
+// precedes the bound's; after the division (which keeps the order of values but may make two
+// equal) that value must stay below the ksel-th candidate, else, or with more than TK_CAND
+// candidates, the segment is searched exhaustively.  NaN or +inf anywhere marks the row bad.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
-  constexpr int VW = (DT == SPEC_DTYPE_BF16) ? 8 : 4;  // elements per 16-byte load
+  constexpr bool BF = DT == SPEC_DTYPE_BF16;
+  constexpr int VW = BF ? 8 : 4;  // elements per 16-byte load
   constexpr int NV = TK_EPT / VW;
+  constexpr int KB = BF ? 16 : 32;  // key bits
   __shared__ uint64_t sk[TK_CAND];
-  __shared__ uint64_t s_wt[TK_THREADS / 64];
-  __shared__ int s_wcnt[TK_THREADS / 64];
-  __shared__ int s_bad, s_total;
+  __shared__ float s_cz[TK_CAND];
+  __shared__ int s_ci[TK_CAND];
+  __shared__ uint32_t s_wt[TK_THREADS / 64];
+  __shared__ int s_bad, s_n, s_slow, s_total;
   __shared__ unsigned long long s_count;
 
   const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
@@ -100,144 +138,181 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
   const int s1 = min(s0 + a.seg_len, a.vocab);
   const float T = a.temperature;
   const bool scale = T > 0.0f;
-  if (t == 0) s_bad = 0;
-
-  // all loads first, addresses clamped into the row
+  if (t == 0) {
+    s_bad = 0;
+    s_n = 0;
+    s_slow = 0;
+  }
+  // all loads first; elements past the segment hold -inf (never bad, lowest order) and are
+  // excluded by index wherever a candidate is taken
   const char* base = (const char*)a.logits;
   const int64_t rowoff = (int64_t)row * a.stride;
-  float x[TK_EPT];
+  uint32_t key[NV][4];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int i0 = s0 + (v * TK_THREADS + t) * VW;
     if (VEC) {
       const int ic = min(i0, a.vocab - VW);
-      if (DT == SPEC_DTYPE_BF16) {
-        const uint4 w = *(const uint4*)(base + (rowoff + ic) * 2);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[v * VW + 2 * e] = __uint_as_float(ww[e] << 16);
-          x[v * VW + 2 * e + 1] = __uint_as_float(ww[e] & 0xFFFF0000u);
-        }
-      } else {
-        const float4 w = *(const float4*)(base + (rowoff + ic) * 4);
-        x[v * VW + 0] = w.x; x[v * VW + 1] = w.y; x[v * VW + 2] = w.z; x[v * VW + 3] = w.w;
-      }
+      const uint4 r = *(const uint4*)(base + (rowoff + ic) * (BF ? 2 : 4));
+      key[v][0] = r.x;
+      key[v][1] = r.y;
+      key[v][2] = r.z;
+      key[v][3] = r.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        const int ic = min(i0 + e, a.vocab - 1);
-        x[v * VW + e] = (DT == SPEC_DTYPE_BF16) ? bf16_to_f32(((const bf16_t*)base)[rowoff + ic])
-                                                : ((const float*)base)[rowoff + ic];
+      for (int q = 0; q < 4; ++q) {
+        if (BF) {
+          const int ia = min(i0 + 2 * q, a.vocab - 1), ib = min(i0 + 2 * q + 1, a.vocab - 1);
+          const bf16_t* p = (const bf16_t*)base + rowoff;
+          key[v][q] = (uint32_t)p[ia] | ((uint32_t)p[ib] << 16);
+        } else {
+          key[v][q] = __float_as_uint(((const float*)base)[rowoff + min(i0 + q, a.vocab - 1)]);
+        }
       }
     }
   }
-  bool bad = false;
-  uint64_t tmax = 0;
 #pragma unroll
-  for (int v = 0; v < NV; ++v)
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = s0 + (v * TK_THREADS + t) * VW;
+    if (i0 + VW > s1) {
 #pragma unroll
-    for (int e = 0; e < VW; ++e) {
-      const int i = s0 + (v * TK_THREADS + t) * VW + e;
-      float z = x[v * VW + e];
-      if (i < s1) {
-        if (__builtin_isnan(z) || z == __builtin_inff()) bad = true;
-        if (scale) z = z / T;
-      } else {
-        z = __builtin_nanf("");  // outside the segment: never a candidate
-      }
-      x[v * VW + e] = z;
-      if (!__builtin_isnan(z)) {
-        const uint64_t k = order_key(z, (uint32_t)i);
-        tmax = k > tmax ? k : tmax;
-      }
+      for (int e = 0; e < VW; ++e)
+        if (i0 + e >= s1) {
+          if (BF) {
+            uint32_t& w = key[v][e >> 1];
+            w = (e & 1) ? ((w & 0xFFFFu) | 0xFF800000u) : ((w & 0xFFFF0000u) | 0xFF80u);
+          } else {
+            key[v][e] = 0xFF800000u;
+          }
+        }
     }
-  __syncthreads();
-  if (bad) atomicOr(&s_bad, 1);
-
-  // lower bound: each wave's ceil(ksel/4)-th largest thread maximum; the smallest of the
-  // four leaves at least ksel elements at or above it
+  }
+  // pass 1: raw keys in place; the thread's largest and smallest
+  uint32_t tmax, tmin;
+  if (BF) {
+    u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        key[v][q] = raw_keys16x2(key[v][q]);
+        const u16x2_t kv = __builtin_bit_cast(u16x2_t, key[v][q]);
+        mx = __builtin_elementwise_max(mx, kv);
+        mn = __builtin_elementwise_min(mn, kv);
+      }
+    tmax = mx.x > mx.y ? mx.x : mx.y;
+    tmin = mn.x < mn.y ? mn.x : mn.y;
+    if (tmax >= KEY16_PINF || tmin < KEY16_NINF) atomicOr(&s_bad, 1);  // +inf or NaN
+  } else {
+    tmax = 0;
+    tmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        key[v][q] = raw_key32(key[v][q]);
+        tmax = key[v][q] > tmax ? key[v][q] : tmax;
+        tmin = key[v][q] < tmin ? key[v][q] : tmin;
+      }
+    if (tmax >= KEY32_PINF || tmin < KEY32_NINF) atomicOr(&s_bad, 1);
+  }
+  // the bound: per wavefront the largest x that at least ceil(ksel/4) thread maxima reach,
+  // bit by bit from the top; the smallest over the four wavefronts
   const int kw = (a.ksel + 3) / 4;
-  const uint64_t srt = wave_sort_desc(tmax, lane);
-  const uint64_t wt = shfl_u64(srt, kw - 1);
+  uint32_t wt = 0;
+#pragma unroll
+  for (int b = KB - 1; b >= 0; --b) {
+    const uint32_t c = wt | (1u << b);
+    if (__popcll(__ballot(tmax >= c)) >= kw) wt = c;
+  }
   if (lane == 0) s_wt[wave] = wt;
   __syncthreads();
-  uint64_t tau = s_wt[0];
+  uint32_t tau = s_wt[0];
 #pragma unroll
   for (int w = 1; w < TK_THREADS / 64; ++w) tau = s_wt[w] < tau ? s_wt[w] : tau;
 
-  int cnt = 0;
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int e = 0; e < VW; ++e) {
-      const float z = x[v * VW + e];
-      const int i = s0 + (v * TK_THREADS + t) * VW + e;
-      if (!__builtin_isnan(z) && order_key(z, (uint32_t)i) >= tau) ++cnt;
-    }
-  // block exclusive scan of the counts: wave scan by shuffles, wave totals through LDS
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) s_wcnt[wave] = incl;
-  __syncthreads();
-  int woff = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < TK_THREADS / 64; ++w) {
-    if (w < wave) woff += s_wcnt[w];
-    total += s_wcnt[w];
-  }
-  uint64_t* out = a.part + ((int64_t)row * a.nseg + seg) * a.ksel;
-
-  if (total <= TK_CAND) {
-    int off = woff + incl - cnt;
+  auto elem_key = [&](int v, int e) -> uint32_t {
+    if (BF) return (e & 1) ? (key[v][e >> 1] >> 16) : (key[v][e >> 1] & 0xFFFFu);
+    return key[v][e];
+  };
+  auto elem_value = [&](int v, int e) -> float {
+    return BF ? key16_value(elem_key(v, e)) : key32_value(elem_key(v, e));
+  };
+  // candidates: the logits whose raw key reaches the bound
+  if (tmax >= tau) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
-        const float z = x[v * VW + e];
-        const int i = s0 + (v * TK_THREADS + t) * VW + e;
-        if (!__builtin_isnan(z)) {
-          const uint64_t k = order_key(z, (uint32_t)i);
-          if (k >= tau) sk[off++] = k;
+        if (elem_key(v, e) >= tau) {
+          const int i = s0 + (v * TK_THREADS + t) * VW + e;
+          if (i < s1) {
+            const int slot = atomicAdd(&s_n, 1);
+            if (slot < TK_CAND) {
+              s_cz[slot] = elem_value(v, e);
+              s_ci[slot] = i;
+            }
+          }
         }
       }
+  }
+  __syncthreads();
+  const int n = s_n;
+  // every logit under the bound is at most this value
+  const float below = tau == 0 ? 0.0f : (BF ? key16_value(tau - 1) : key32_value(tau - 1));
+  const float below_s = scale ? below / T : below;
+  uint64_t* out = a.part + ((int64_t)row * a.nseg + seg) * a.ksel;
+  if (n <= TK_CAND) {
+    // exact keys of the candidates, then the ksel largest by rank (keys are unique)
+    for (int c = t; c < n; c += TK_THREADS) {
+      float z = s_cz[c];
+      if (scale) z = z / T;
+      sk[c] = order_key(z, (uint32_t)s_ci[c]);
+    }
     __syncthreads();
-    if (total <= 256) {
-      // rank selection: a candidate's rank is the number of larger candidates (keys are unique)
-      for (int c = t; c < total; c += TK_THREADS) {
-        const uint64_t k = sk[c];
+    if (n <= TK_THREADS) {
+      if (t < n) {
+        const uint64_t k = sk[t];
         int rank = 0;
-        for (int o = 0; o < total; ++o) rank += sk[o] > k;
+        for (int o = 0; o < n; ++o) rank += sk[o] > k;
         if (rank < a.ksel) out[rank] = k;
+        if (tau != 0 && rank == min(a.ksel, n) - 1 && !(below_s < key_value(k))) s_slow = 1;
       }
+      for (int i = n + t; i < a.ksel; i += TK_THREADS) out[i] = 0;
     } else {
-      const int p2 = next_pow2(total);
-      for (int i = total + t; i < p2; i += TK_THREADS) sk[i] = 0;
+      const int p2 = next_pow2(n);
+      for (int i = n + t; i < p2; i += TK_THREADS) sk[i] = 0;
       __syncthreads();
       bitonic_desc<TK_THREADS>(sk, p2);
       for (int i = t; i < a.ksel; i += TK_THREADS) out[i] = sk[i];
+      if (t == 0 && tau != 0 && !(below_s < key_value(sk[min(a.ksel, n) - 1]))) s_slow = 1;
     }
-    for (int i = total + t; i < a.ksel; i += TK_THREADS) out[i] = 0;
+    __syncthreads();
   } else {
-    // exact ksel-th largest key by binary search over the 64-bit key space
+    if (t == 0) s_slow = 1;
+    __syncthreads();
+  }
+  if (s_slow) {
+    // exhaustive (rare: long runs of equal logits, or a division that makes the bound tie the
+    // answer): the exact ksel-th largest key by binary search over the 64-bit key space,
+    // reading the segment again rather than holding every key in registers
+    auto exact_key = [&](int i, bool* nan) -> uint64_t {
+      float z = BF ? bf16_to_f32(((const bf16_t*)base)[rowoff + i]) : ((const float*)base)[rowoff + i];
+      *nan = __builtin_isnan(z);
+      if (scale) z = z / T;
+      return order_key(z, (uint32_t)i);
+    };
     uint64_t lo = 0, hi = ~0ull;
     while (lo < hi) {
       const uint64_t mid = lo + (hi - lo) / 2 + 1;
       if (t == 0) s_count = 0;
       __syncthreads();
       int c = 0;
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int e = 0; e < VW; ++e) {
-          const float z = x[v * VW + e];
-          const int i = s0 + (v * TK_THREADS + t) * VW + e;
-          if (!__builtin_isnan(z) && order_key(z, (uint32_t)i) >= mid) ++c;
-        }
+      for (int i = s0 + t; i < s1; i += TK_THREADS) {
+        bool nan;
+        const uint64_t k = exact_key(i, &nan);
+        c += (!nan && k >= mid) ? 1 : 0;
+      }
       if (c) atomicAdd(&s_count, (unsigned long long)c);
       __syncthreads();
       const bool enough = s_count >= (unsigned long long)a.ksel;
@@ -247,20 +322,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
     if (t == 0) s_total = 0;
     for (int i = t; i < TK_CAND; i += TK_THREADS) sk[i] = 0;
     __syncthreads();
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        const float z = x[v * VW + e];
-        const int i = s0 + (v * TK_THREADS + t) * VW + e;
-        if (!__builtin_isnan(z)) {
-          const uint64_t k = order_key(z, (uint32_t)i);
-          if (k >= lo) {
-            const int slot = atomicAdd(&s_total, 1);
-            if (slot < TK_CAND) sk[slot] = k;
-          }
-        }
+    for (int i = s0 + t; i < s1; i += TK_THREADS) {
+      bool nan;
+      const uint64_t k = exact_key(i, &nan);
+      if (!nan && k >= lo) {
+        const int slot = atomicAdd(&s_total, 1);
+        if (slot < TK_CAND) sk[slot] = k;
       }
+    }
     __syncthreads();
     const int p2 = next_pow2(max(a.ksel, 2));
     bitonic_desc<TK_THREADS>(sk, p2);
@@ -270,97 +339,133 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
 }
 
 // ---------------------------------------------------------------- 2. finish
-// Merges the sorted segment lists by rank (a key's rank = its index in its own list plus
-// the number of larger keys in every other list, found by binary search), then lane 0
-// does the float32 softmax / top_p / renormalization in the stated sequential order.
+// Merges the sorted segment lists: the largest of the segments' ksel-th keys is a bound that
+// the row's ksel-th key reaches (that segment alone holds ksel keys at or above it), so only
+// keys at or above it are ranked, among themselves.  Then the float32 softmax, top_p cut and
+// renormalization: exponentials and divisions per lane, every running sum by one lane in the
+// stated sequential order.
 __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs a, spec_probs out,
                                                                       int out_rs, float top_p,
                                                                       uint8_t* flags) {
-  __shared__ uint64_t sk[FIN_SLOTS];
+  __shared__ uint64_t cand[FIN_SLOTS];
   __shared__ uint64_t top[SPEC_TOPK_MAX];
   __shared__ float s_p[SPEC_TOPK_MAX];
   __shared__ int s_id[SPEC_TOPK_MAX];
-  __shared__ int s_n, s_bad;
-  const int row = blockIdx.x, t = threadIdx.x;
+  __shared__ uint64_t s_theta;
+  __shared__ int s_n, s_nc, s_bad, s_keep;
+  __shared__ float s_S, s_Z;
+  __shared__ uint8_t s_fl;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int K = a.ksel, nk = a.nseg * K;
   const uint64_t* src = a.part + (int64_t)row * nk;
-  for (int i = t; i < nk; i += FIN_THREADS) sk[i] = src[i];
+  if (t < 64) {
+    // wave 0: the bound and the bad flags
+    uint64_t th = 0;
+    int bad = 0;
+    for (int s = lane; s < a.nseg; s += 64) {
+      const uint64_t v = src[s * K + K - 1];
+      th = v > th ? v : th;
+      bad |= a.bad[(int64_t)row * a.nseg + s];
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(th, m);
+      th = o > th ? o : th;
+    }
+    bad = __ballot(bad != 0) ? 1 : 0;
+    if (t == 0) {
+      s_theta = th;
+      s_bad = bad;
+      s_nc = 0;
+    }
+  }
   for (int i = t; i < K; i += FIN_THREADS) top[i] = 0;
-  if (t == 0) {
-    int b = 0;
-    for (int s = 0; s < a.nseg; ++s) b |= a.bad[(int64_t)row * a.nseg + s];
-    s_bad = b;
+  __syncthreads();
+  const uint64_t theta = s_theta;
+  for (int c = t; c < nk; c += FIN_THREADS) {
+    const uint64_t key = src[c];
+    if (key != 0 && key >= theta) cand[atomicAdd(&s_nc, 1)] = key;
   }
   __syncthreads();
-  for (int c = t; c < nk; c += FIN_THREADS) {
-    const uint64_t key = sk[c];
-    if (key == 0) continue;
-    const int own = c / K;
-    int rank = c % K;
-    for (int s = 0; s < a.nseg && rank < K; ++s) {
-      if (s == own) continue;
-      const uint64_t* l = sk + s * K;
-      int lo = 0, hi = K;  // first index whose key is smaller (empty slots are 0)
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (l[mid] > key) lo = mid + 1; else hi = mid;
-      }
-      rank += lo;
-    }
+  const int nc = s_nc;
+  for (int c = t; c < nc; c += FIN_THREADS) {
+    const uint64_t key = cand[c];
+    int rank = 0;
+    for (int o = 0; o < nc; ++o) rank += cand[o] > key;
     if (rank < K) top[rank] = key;
   }
   __syncthreads();
 
-  if (t == 0) {
-    uint8_t fl = 0;
-    int n = 0;
-    if (!s_bad) {
-      for (int i = 0; i < K; ++i) {
-        const uint64_t key = top[i];
-        if (key == 0) break;
-        const float zi = key_value(key);
-        if (zi == -__builtin_inff()) break;  // sorted: the rest is -inf or empty
-        s_id[n] = (int)key_id(key);
-        s_p[n] = zi;
-        ++n;
-      }
+  if (t < 64) {
+    // entries: the leading keys that are present and finite (sorted: the rest is -inf or empty)
+    bool ok = false;
+    float zi = 0.0f;
+    if (lane < K) {
+      const uint64_t key = top[lane];
+      zi = key_value(key);
+      ok = key != 0 && zi != -__builtin_inff();
     }
-    if (n == 0) {
-      fl |= SPEC_FLAG_BAD_ROW;
-    } else if (!(a.temperature > 0.0f)) {
-      n = 1;
+    const uint64_t okm = __ballot(ok);
+    int n = s_bad ? 0 : (~okm ? (int)__builtin_ctzll(~okm) : 64);
+    const bool sampled = a.temperature > 0.0f;
+    if (n > 0 && sampled && lane < n) {
+      s_id[lane] = (int)key_id(top[lane]);
+      s_p[lane] = expf(zi - key_value(top[0]));
+    } else if (n > 0 && !sampled && lane == 0) {
+      s_id[0] = (int)key_id(top[0]);
       s_p[0] = 1.0f;
-    } else {
-      const float m = s_p[0];
-      float S = 0.0f;
-      for (int i = 0; i < n; ++i) {
-        s_p[i] = expf(s_p[i] - m);
-        S = S + s_p[i];
-      }
-      for (int i = 0; i < n; ++i) s_p[i] = s_p[i] / S;
-      int nkeep = n;
-      if (top_p < 1.0f) {
-        float excl = 0.0f, excl_last = 0.0f;
-        nkeep = 0;
-        for (int i = 0; i < n; ++i) {
-          if (i > 0 && !(excl < top_p)) break;
-          excl_last = excl;
-          ++nkeep;
-          excl = excl + s_p[i];
-        }
-        float margin = __builtin_inff();
-        if (nkeep > 1) margin = fminf(margin, fabsf(excl_last - top_p));
-        if (nkeep < n) margin = fminf(margin, fabsf(excl - top_p));
-        if (margin < NEAR_TIE) fl |= SPEC_FLAG_TOPP_TIE;
-      }
-      float Z = 0.0f;
-      for (int i = 0; i < nkeep; ++i) Z = Z + s_p[i];
-      for (int i = 0; i < nkeep; ++i) s_p[i] = s_p[i] / Z;
-      n = nkeep;
     }
-    s_n = n;
-    out.count[(int64_t)row * out_rs] = n;
-    if (flags) flags[row] = fl;
+    if (n > 0 && !sampled) n = 1;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (n > 0 && sampled) {
+      if (lane == 0) {
+        float S = 0.0f;
+        for (int i = 0; i < n; ++i) S = S + s_p[i];
+        s_S = S;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      if (lane < n) s_p[lane] = s_p[lane] / s_S;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      if (lane == 0) {
+        uint8_t fl = 0;
+        int nkeep = n;
+        if (top_p < 1.0f) {
+          float excl = 0.0f, excl_last = 0.0f;
+          nkeep = 0;
+          for (int i = 0; i < n; ++i) {
+            if (i > 0 && !(excl < top_p)) break;
+            excl_last = excl;
+            ++nkeep;
+            excl = excl + s_p[i];
+          }
+          float margin = __builtin_inff();
+          if (nkeep > 1) margin = fminf(margin, fabsf(excl_last - top_p));
+          if (nkeep < n) margin = fminf(margin, fabsf(excl - top_p));
+          if (margin < NEAR_TIE) fl |= SPEC_FLAG_TOPP_TIE;
+        }
+        float Z = 0.0f;
+        for (int i = 0; i < nkeep; ++i) Z = Z + s_p[i];
+        s_Z = Z;
+        s_keep = nkeep;
+        s_fl = fl;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      n = s_keep;
+      if (lane < n) s_p[lane] = s_p[lane] / s_Z;
+    } else if (lane == 0) {
+      s_fl = n == 0 ? SPEC_FLAG_BAD_ROW : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    if (lane == 0) {
+      s_n = n;
+      out.count[(int64_t)row * out_rs] = n;
+      if (flags) flags[row] = s_fl;
+    }
   }
   __syncthreads();
   const int n = s_n;
@@ -454,78 +559,105 @@ SPEC_DEVINL int list_argmax(const int32_t* ids, const float* p, int n) {
   return ids[best];
 }
 
-__global__ void accept_kernel(AcceptArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.batch) return;
+// One wavefront per sequence.  The sequence's p rows (k + 1) and q rows (k) are first copied
+// to LDS in one burst; lane j then tests draft j (its probabilities under p and q, its uniform
+// and the ratio), the first rejected or empty row ends the run (a ballot), and lane 0 draws
+// the emitted token from the residual or the bonus row with the same sequential float32 sums
+// as a one-thread walk through the drafts.
+__global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
+  __shared__ int32_t s_pid[(SPEC_MAX_K + 1) * SPEC_TOPK_MAX];
+  __shared__ float s_pp[(SPEC_MAX_K + 1) * SPEC_TOPK_MAX];
+  __shared__ int32_t s_qid[SPEC_MAX_K * SPEC_TOPK_MAX];
+  __shared__ float s_qp[SPEC_MAX_K * SPEC_TOPK_MAX];
+  __shared__ float s_r[SPEC_TOPK_MAX];
+  __shared__ int s_pn[SPEC_MAX_K + 1], s_qn[SPEC_MAX_K], s_am[SPEC_MAX_K + 1];
+  const int b = blockIdx.x, lane = threadIdx.x;
   const int k = a.k;
   // drafts actually proposed for this sequence (an n-gram lookup may find fewer than k);
   // the rows past them are not tested and the bonus comes from row kb
   const int kb = a.kcap ? min(max(a.kcap[b], 0), k) : k;
   const int32_t* d = a.drafts + (int64_t)b * k;
   int32_t* out = a.out_tok + (int64_t)b * (k + 1);
-  uint8_t fl = 0;
-  int n = kb;
-  int emitted = -1;
-  bool stopped = false;  // a draft was rejected, or its target row was empty
-  for (int j = 0; j < kb; ++j) {
-    const int64_t pr = (int64_t)b * (k + 1) + j, qr = (int64_t)b * k + j;
-    const int32_t* pid = a.p.ids + pr * a.p.cap;
-    const float* pp = a.p.probs + pr * a.p.cap;
-    const int pn = list_len(a.p, pr);
+  const int pc = a.p.cap, qc = a.q.cap;
+  const int64_t p0 = (int64_t)b * (k + 1), q0 = (int64_t)b * k;
+  for (int i = lane; i < (k + 1) * pc; i += 64) {
+    s_pid[i] = a.p.ids[p0 * pc + i];
+    s_pp[i] = a.p.probs[p0 * pc + i];
+  }
+  if (lane <= k) s_pn[lane] = list_len(a.p, p0 + lane);
+  if (!a.greedy) {
+    for (int i = lane; i < k * qc; i += 64) {
+      s_qid[i] = a.q.ids[q0 * qc + i];
+      s_qp[i] = a.q.probs[q0 * qc + i];
+    }
+    if (lane < k) s_qn[lane] = list_len(a.q, q0 + lane);
+  }
+  __syncthreads();
+
+  // lane j: the test of draft j
+  bool stop = false, bad = false, tie = false;
+  int dj = 0;
+  if (lane < kb) {
+    dj = d[lane];
+    const int pn = s_pn[lane];
+    const int32_t* pid = s_pid + lane * pc;
+    const float* pp = s_pp + lane * pc;
     if (pn <= 0) {
       // no distribution to test draft j against (its logits held no finite value): nothing
       // from j on is kept and no token is emitted (-1 signals the bad row)
-      fl |= SPEC_FLAG_BAD_ROW;
-      n = j;
-      stopped = true;
-      break;
-    }
-    if (a.greedy) {
+      bad = stop = true;
+    } else if (a.greedy) {
       const int am = list_argmax(pid, pp, pn);
-      if (d[j] == am) {
-        out[j] = d[j];
-        continue;
-      }
-      n = j;
-      emitted = am;
-      stopped = true;
-      break;
+      s_am[lane] = am;
+      stop = dj != am;
+    } else {
+      const float pj = list_prob(pid, pp, pn, dj);
+      const float qj = list_prob(s_qid + lane * qc, s_qp + lane * qc, s_qn[lane], dj);
+      const float ratio = pj / qj;
+      const float u = philox_uniform(a.seed, (uint32_t)(lane + 1), a.round, (uint32_t)b, STREAM_ACCEPT);
+      tie = __builtin_isfinite(ratio) && fabsf(u - ratio) < NEAR_TIE;
+      stop = !(u < ratio);
     }
-    const int32_t* qid = a.q.ids + qr * a.q.cap;
-    const float* qp = a.q.probs + qr * a.q.cap;
-    const int qn = list_len(a.q, qr);
-    const float pj = list_prob(pid, pp, pn, d[j]);
-    const float qj = list_prob(qid, qp, qn, d[j]);
-    const float ratio = pj / qj;
-    const float u = philox_uniform(a.seed, (uint32_t)(j + 1), a.round, (uint32_t)b, STREAM_ACCEPT);
-    if (__builtin_isfinite(ratio) && fabsf(u - ratio) < NEAR_TIE) fl |= SPEC_FLAG_ACCEPT_TIE;
-    if (u < ratio) {
-      out[j] = d[j];
-      continue;
-    }
-    // residual max(0, p - q) over p's support, ascending ids (both lists are ascending)
-    float r[SPEC_TOPK_MAX];
-    float Z = 0.0f;
-    int qi = 0;
-    for (int i = 0; i < pn; ++i) {
-      while (qi < qn && qid[qi] < pid[i]) ++qi;
-      const float qv = (qi < qn && qid[qi] == pid[i]) ? qp[qi] : 0.0f;
-      const float diff = pp[i] - qv;
-      r[i] = diff > 0.0f ? diff : 0.0f;
-      Z = Z + r[i];
-    }
-    const float ur = philox_uniform(a.seed, 0u, a.round, (uint32_t)b, STREAM_RESIDUAL);
-    emitted = (Z > 0.0f) ? sample_list(pid, r, pn, ur, &fl) : sample_list(pid, pp, pn, ur, &fl);
-    n = j;
-    stopped = true;
-    break;
   }
-  if (!stopped) {
+  const uint64_t stops = __ballot(stop), bads = __ballot(bad);
+  const int n = stops ? (int)__builtin_ctzll(stops) : kb;  // drafts kept
+  uint8_t fl = __ballot(tie && lane <= n) ? SPEC_FLAG_ACCEPT_TIE : 0;
+  const bool bad_n = n < kb && ((bads >> n) & 1ull);
+  if (lane < n) out[lane] = dj;
+
+  // the residual max(0, p - q) over p's support of the rejecting row, one entry per lane
+  const bool resid = n < kb && !bad_n && !a.greedy;
+  if (resid) {
+    const int pn = s_pn[n];
+    if (lane < pn) {
+      const int id = s_pid[n * pc + lane];
+      const float qv = list_prob(s_qid + n * qc, s_qp + n * qc, s_qn[n], id);
+      const float diff = s_pp[n * pc + lane] - qv;
+      s_r[lane] = diff > 0.0f ? diff : 0.0f;
+    }
+  }
+  __syncthreads();
+  if (lane != 0) return;
+  int emitted;
+  if (n < kb) {
+    if (bad_n) {
+      fl |= SPEC_FLAG_BAD_ROW;
+      emitted = -1;
+    } else if (a.greedy) {
+      emitted = s_am[n];
+    } else {
+      const int pn = s_pn[n];
+      float Z = 0.0f;
+      for (int i = 0; i < pn; ++i) Z = Z + s_r[i];
+      const float ur = philox_uniform(a.seed, 0u, a.round, (uint32_t)b, STREAM_RESIDUAL);
+      emitted = (Z > 0.0f) ? sample_list(s_pid + n * pc, s_r, pn, ur, &fl)
+                           : sample_list(s_pid + n * pc, s_pp + n * pc, pn, ur, &fl);
+    }
+  } else {
     // every draft kept: bonus token from the target row after the last draft
-    const int64_t pr = (int64_t)b * (k + 1) + kb;
-    const int32_t* pid = a.p.ids + pr * a.p.cap;
-    const float* pp = a.p.probs + pr * a.p.cap;
-    const int pn = list_len(a.p, pr);
+    const int pn = s_pn[kb];
+    const int32_t* pid = s_pid + kb * pc;
+    const float* pp = s_pp + kb * pc;
     if (pn <= 0) {
       fl |= SPEC_FLAG_BAD_ROW;
       emitted = -1;
@@ -535,7 +667,6 @@ __global__ void accept_kernel(AcceptArgs a) {
       const float ur = philox_uniform(a.seed, 0u, a.round, (uint32_t)b, STREAM_RESIDUAL);
       emitted = sample_list(pid, pp, pn, ur, &fl);
     }
-    n = kb;
   }
   out[n] = emitted;
   a.n_acc[b] = n;
@@ -710,7 +841,11 @@ hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per
 
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(accept_kernel, dim3((a.batch + 63) / 64), dim3(64), 0, st, a);
+  // the kernel stages a sequence's lists in LDS sized for these limits
+  if (a.k < 0 || a.k > SPEC_MAX_K || a.p.cap < 1 || a.p.cap > SPEC_TOPK_MAX ||
+      (!a.greedy && a.k > 0 && (a.q.cap < 1 || a.q.cap > SPEC_TOPK_MAX)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3(a.batch), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -79,6 +79,25 @@ def test_truncate_parity(V, rows, dtype, samp):
     check_lists(out, flags, host, *samp)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("samp", [(0.7, 64, 0.5), (1.5, 20, 1.0), (1.0, 20, 0.95), (0.0, 20, 0.95)])
+def test_truncate_tied_and_adjacent_values(dtype, samp):
+    """Rows whose order is decided by ids or by the rounding of value / T: integer logits (long
+    runs of equal values, so that a segment holds a few hundred or thousands of candidates at
+    its bound) and 300 adjacent float32 values just under 2, which a division by 1.5 can make
+    equal; the lists must be the oracle's, ties broken by the lower id."""
+    V = 151936
+    rng = np.random.default_rng(11)
+    rows = [np.round(rng.normal(0, 1, V)), np.round(rng.normal(0, 2.5, V)), rng.normal(0, 0.1, V)]
+    pos = rng.choice(V, 300, replace=False)
+    rows[2][pos] = 2.0 - (np.arange(300) + 1) * 2.0 ** -23
+    x = torch.from_numpy(np.stack(rows).astype(np.float32))
+    x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    host = x.float().numpy()
+    out, flags = run_truncate(x.cuda(), *samp)
+    check_lists(out, flags, host, *samp)
+
+
 def test_truncate_edge_rows():
     V = 70000
     rows = []
