@@ -453,6 +453,20 @@ int spec_truncate(const void* logits /*device*/, int32_t dtype, int32_t rows, in
                   uint8_t* flags /*device or NULL*/, void* scratch /*device*/,
                   size_t scratch_bytes, void* stream);
 
+/* spec_truncate for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same results, with the partial lists in a fixed device array of SPEC_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on each GPU it runs on until the process ends.  Calls
+ * spec_truncate_scratch_size would size above that limit return SPEC_E_RANGE (e.g. 1088 rows of
+ * a 151936-token vocabulary need 5.6 MB).  The call allocates nothing; on its first call on a
+ * device it looks up that device's copy of the array (SPEC_E_HIP if that fails).  Every call on
+ * one GPU shares the array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  stream must belong to the current device. */
+#define SPEC_NOALLOC_SCRATCH_BYTES (8u << 20)
+int spec_truncate_noalloc(const void* logits /*device*/, int32_t dtype, int32_t rows, int32_t vocab,
+                          int64_t row_stride, const spec_sampler* s /*host*/, spec_probs* out,
+                          uint8_t* flags /*device or NULL*/, void* stream);
+
 /* Draws one token per row from lists (rows = batch*per_seq; row r is slot r%per_seq + 1
  * of sequence r/per_seq) with the uniform of counter (slot, round, seq, stream_id): ids
  * walked in ascending order, first running sum above u*Z.  tokens: device int32 [rows];

@@ -39,7 +39,7 @@ EXPORTED = [
     "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
     "spec_depth_init", "spec_depth_choose", "spec_depth_update", "spec_gdn_commit_forward",
-    "spec_debug_read",
+    "spec_debug_read", "spec_truncate_noalloc",
 ]
 BUF_RESIDUAL, BUF_NORM_INPUT, BUF_Q, BUF_K, BUF_ATTN, BUF_SWIGLU, BUF_CACHE_K, BUF_CACHE_V, BUF_LOGITS = range(9)
 GDN_MAX_TOKENS = 64
@@ -148,6 +148,8 @@ def lib(path: str = LIB_PATH):
         "spec_truncate_scratch_size": ([I32, I32, C.POINTER(SZ)], C.c_int),
         "spec_truncate": ([P, I32, I32, I32, I64, C.POINTER(spec_sampler), C.POINTER(spec_probs), P, P,
                            SZ, P], C.c_int),
+        "spec_truncate_noalloc": ([P, I32, I32, I32, I64, C.POINTER(spec_sampler), C.POINTER(spec_probs), P,
+                                   P], C.c_int),
         "spec_sample": ([C.POINTER(spec_probs), I32, I32, U64, U64, I32, P, P, P], C.c_int),
         "spec_accept_lists": ([P, C.POINTER(spec_probs), C.POINTER(spec_probs), I32, I32, I32, U64, U64,
                                P, P, P, P], C.c_int),
@@ -344,6 +346,17 @@ def spec_truncate(logits, dtype: int, rows: int, vocab: int, row_stride: int, s:
                              _ptr(flags), _ptr(scratch), scratch_bytes, _stream(stream))
     if rc:
         raise SpecError(rc, "spec_truncate")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def spec_truncate_noalloc(logits, dtype: int, rows: int, vocab: int, row_stride: int, s: spec_sampler,
+                          out: Probs, flags, stream=None) -> None:
+    rc = lib().spec_truncate_noalloc(_ptr(logits), dtype, rows, vocab, row_stride, C.byref(s),
+                                     C.byref(out.c), _ptr(flags), _stream(stream))
+    if rc:
+        raise SpecError(rc, "spec_truncate_noalloc")
 
 
 def spec_sample(lists: Probs, batch: int, per_seq: int, seed: int, rnd: int, stream_id: int, tokens,

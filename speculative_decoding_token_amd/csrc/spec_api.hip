@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1587,6 +1588,56 @@ int spec_truncate(const void* logits, int32_t dtype, int32_t rows, int32_t vocab
   if (rc) return rc;
   if (scratch_bytes < need) return SPEC_E_RANGE;
   return launch_truncate(logits, dtype, rows, vocab, row_stride, *s, *out, 1, flags, scratch,
+                         (hipStream_t)stream) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
+}
+
+// ---------------------------------------------------------------- truncation without allocation
+// The truncation's partial lists and flags live in this fixed device array instead of a caller
+// workspace.  Each device holds its own copy at its own address: host code never passes the
+// array's name to a kernel (on the host it names a stand-in, not device memory) but the
+// address hipGetSymbolAddress returns, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The current device's copy of `scratch`, looked up on the first call on that device.
+static int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_HIP;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return SPEC_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return SPEC_E_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+int spec_truncate_noalloc(const void* logits, int32_t dtype, int32_t rows, int32_t vocab,
+                          int64_t row_stride, const spec_sampler* s, spec_probs* out, uint8_t* flags,
+                          void* stream) {
+  if (!logits || !s || !out || rows < 0 || vocab < 1 || row_stride < vocab) return SPEC_E_INVAL;
+  if (dtype != SPEC_DTYPE_F32 && dtype != SPEC_DTYPE_BF16) return SPEC_E_INVAL;
+  int rc = validate_sampler(*s);
+  if (rc) return rc;
+  if (s->temperature > 0.0f && s->top_k > vocab) return SPEC_E_INVAL;
+  if (!out->ids || !out->probs || !out->count || out->cap < list_cap(*s)) return SPEC_E_INVAL;
+  size_t need = 0;
+  rc = truncate_scratch_bytes(rows, vocab, &need);
+  if (rc) return rc;
+  if (need > (size_t)SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_E_RANGE;
+  void* ptr = nullptr;
+  rc = noalloc_scratch(&ptr);
+  if (rc) return rc;
+  // every slot the kernels read is written first in the same call: nothing to clear
+  return launch_truncate(logits, dtype, rows, vocab, row_stride, *s, *out, 1, flags, ptr,
                          (hipStream_t)stream) == hipSuccess ? SPEC_OK : SPEC_E_HIP;
 }
 
