@@ -67,6 +67,22 @@ class GenResult:
     drafts_accepted: int
 
 
+def draft_confidence(ql: TokenList, d: int) -> np.float32:
+    """The draft model's confidence in its draft d: the probability its truncated list gives d
+    (float32, as the list holds it).  Greedy lists are one-hot, so every greedy draft has
+    confidence 1."""
+    hit = ql.probs[ql.ids == d]
+    return np.float32(hit[0]) if len(hit) else np.float32(0.0)
+
+
+def keeps_drafting(ql: TokenList, d: int, p_min: float) -> bool:
+    """The draft-probability control ("What is Speculative Decoding and How Does a Draft Model
+    Work?", section "The demo, draft model on and off with two pairings": drafting stops once
+    the draft model's confidence falls below the setting; 0 turns it off).  Reading: the draft
+    whose confidence is below p_min is not proposed, and neither is any later one."""
+    return not (p_min > 0.0) or bool(draft_confidence(ql, d) >= np.float32(p_min))
+
+
 class DraftModel:
     """External draft model: its own weights and cache."""
 
@@ -75,8 +91,9 @@ class DraftModel:
         self.kv = KVCache(spec, capacity)
 
     def propose(self, hist: List[int], L: int, K: int, sampler: Sampler, seed: int, rnd: int,
-                seq: int = 0):
-        """Feed history up to position L (t0), then K-1 of its own drafts."""
+                seq: int = 0, p_min: float = 0.0):
+        """Feed history up to position L (t0), then its own drafts: at most K, fewer when a
+        draft's confidence falls below p_min (keeps_drafting)."""
         logits = None
         while self.kv.length <= L:
             pos = self.kv.length
@@ -90,6 +107,8 @@ class DraftModel:
             else:
                 u = philox.uniform(seed, j, rnd, seq, philox.STREAM_DRAFT)
                 d, _ = sample(ql.ids, ql.probs, u)
+            if not keeps_drafting(ql, d, p_min):
+                break
             drafts.append(d)
             qs.append(ql)
             if j < K:
@@ -110,7 +129,7 @@ class MTPDraft:
         self.kv = KVCache(spec, capacity, n_layers=1)
         self.hidden = hidden    # target hidden state by position (shared with the loop)
 
-    def propose(self, hist, L, K, sampler, seed, rnd, seq=0):
+    def propose(self, hist, L, K, sampler, seed, rnd, seq=0, p_min=0.0):
         logits = h = None
         while self.kv.length <= L:
             pos = self.kv.length
@@ -125,6 +144,8 @@ class MTPDraft:
             else:
                 u = philox.uniform(seed, j, rnd, seq, philox.STREAM_DRAFT)
                 d, _ = sample(ql.ids, ql.probs, u)
+            if not keeps_drafting(ql, d, p_min):
+                break
             drafts.append(d)
             qs.append(ql)
             if j < K:
@@ -171,13 +192,19 @@ def one_hot(tok: int) -> TokenList:
 def run(target_spec: Spec, target_W: Dict, tkv: KVCache, t0: int, hist: List[int], n_new: int,
         K: int, sampler: Sampler, seed: int, draft=None, ngram: Optional[Dict] = None,
         hidden: Optional[Dict[int, np.ndarray]] = None, seq: int = 0,
-        teacher: Optional[Sequence[int]] = None, depth: Optional[AdaptiveDepth] = None) -> GenResult:
+        teacher: Optional[Sequence[int]] = None, depth: Optional[AdaptiveDepth] = None,
+        p_min: float = 0.0, min_draft: int = 0) -> GenResult:
     """Generate ``n_new`` tokens.  ``hist`` holds every token at positions < tkv.length plus
     t0 at position tkv.length.  ``draft`` is a DraftModel / MTPDraft or None; ``ngram`` a dict
     {n_min, max_match, gate: Gate|None}; ``teacher`` replaces the drafts by a known
     continuation: teacher[i] is the i-th generated token, so each cycle drafts the K entries
     after the tokens emitted so far.  ``depth`` (an AdaptiveDepth) picks each cycle's K for a
-    draft model or teacher and is told every cycle's outcome."""
+    draft model or teacher and is told every cycle's outcome.  ``p_min`` and ``min_draft`` are
+    the draft controls of "What is Speculative Decoding and How Does a Draft Model Work?",
+    section "The demo, draft model on and off with two pairings" (K is the most drafts): the
+    draft model / MTP head stops at the first draft below the draft probability p_min
+    (keeps_drafting), and a cycle with fewer drafts than min_draft (from a drafter, not a
+    teacher) checks none of them, which makes it a plain decoding step."""
     assert len(hist) == tkv.length + 1 and hist[-1] == t0
     out: List[int] = []
     cycles: List[CycleLog] = []
@@ -198,9 +225,12 @@ def run(target_spec: Spec, target_W: Dict, tkv: KVCache, t0: int, hist: List[int
             k = len(drafts)
             qs = [one_hot(d) for d in drafts]
         elif draft is not None and K > 0:
-            drafts, qs = draft.propose(hist, L, K, sampler, seed, rnd, seq)
+            drafts, qs = draft.propose(hist, L, K, sampler, seed, rnd, seq, p_min)
         else:
-            drafts, qs, k = [], [], 0
+            drafts, qs = [], []
+        if teacher is None and len(drafts) < min_draft:
+            drafts, qs = [], []
+        k = len(drafts)
         # verify: one target pass over [t0, d_1..d_k] at positions L..L+k
         rows = [hist[L]] + drafts
         ps, gaps, pm = [], [], []

@@ -154,3 +154,76 @@ def test_gate_choices():
     g2 = ngram.Gate(2, [1.0, 1.0, 1.0])
     g2.update(1, 2)
     assert g2.alpha == 0.75
+
+
+# ---------------------------------------------------------------- draft controls
+# "What is Speculative Decoding and How Does a Draft Model Work?", section "The demo, draft
+# model on and off with two pairings": max draft tokens (K), min draft tokens, and the draft
+# probability below which drafting stops.
+
+def draft_setup(seed=0, std=1.0):
+    """The tiny pair with a draft of wider weights, whose lists are peaked enough that its
+    confidences spread over (0, 1)."""
+    tspec, tW, dspec, _, prompt = setup(seed)
+    dW = synth.weights_to_numpy(synth.make_weights(synth.SHAPES["tiny_draft"], seed + 1, std=std))
+    return tspec, tW, dspec, dW, prompt
+
+
+def test_draft_probability_stops_at_the_first_unconfident_draft():
+    """propose with p_min returns the prefix of the same draws (p_min = 0) that ends before the
+    first draft whose list gives it less than p_min; checked for several thresholds against the
+    confidences read off the unstopped run's lists."""
+    tspec, tW, dspec, dW, prompt = draft_setup()
+    K, rnd, cap = 8, 3, 64
+    stops = set()
+    for p_min in (0.05, 0.2, 0.3, 0.6, 0.99):
+        full = DraftModel(dspec, dW, cap)
+        prefill(dspec, dW, full.kv, prompt[:-1])
+        d0, q0 = full.propose(list(prompt), len(prompt) - 1, K, SAMPLED, 1234, rnd)
+        conf = [float(q.probs[list(q.ids).index(d)]) for d, q in zip(d0, q0)]
+        want = next((j for j, c in enumerate(conf) if c < p_min), K)
+        cut = DraftModel(dspec, dW, cap)
+        prefill(dspec, dW, cut.kv, prompt[:-1])
+        d1, q1 = cut.propose(list(prompt), len(prompt) - 1, K, SAMPLED, 1234, rnd, p_min=p_min)
+        assert d1 == d0[:want]
+        assert all(np.array_equal(a.ids, b.ids) for a, b in zip(q1, q0))
+        # no forward past the last kept draft: the cache holds the prompt and the kept drafts
+        # that had a successor to draw
+        assert cut.kv.length == len(prompt) + min(want, K - 1)
+        stops.add(want)
+    assert len(stops) >= 3, stops  # the thresholds exercise different stopping points
+
+
+def test_draft_controls_that_check_nothing_reduce_to_plain_decoding():
+    """A cycle that checks no draft emits the target's own token from the same uniform as plain
+    decoding (K = 0): min_draft above K, or p_min = 1 with lists that never put all their mass
+    on one token, reproduce plain decoding token for token, greedy and sampled."""
+    for sampler in (GREEDY, SAMPLED):
+        plain = gen(0, sampler)
+        for kw in ({"min_draft": 5}, {"p_min": 1.0}):
+            if sampler is GREEDY and "p_min" in kw:
+                continue  # greedy lists are one-hot: confidence 1, never below p_min
+            tspec, tW, dspec, dW, prompt = setup(0)
+            cap = 16 + N_NEW + 20
+            tkv = KVCache(tspec, cap)
+            prefill(tspec, tW, tkv, prompt[:-1])
+            d = DraftModel(dspec, dW, cap)
+            prefill(dspec, dW, d.kv, prompt[:-1])
+            r = run(tspec, tW, tkv, prompt[-1], list(prompt), N_NEW, 4, sampler, 1234, draft=d, **kw)
+            assert r.tokens == plain.tokens, (sampler, kw)
+            assert r.drafts_attempted == 0
+
+
+def test_greedy_output_unchanged_by_min_draft():
+    """Greedy speculative output equals plain greedy decoding whatever the controls (the
+    greedy loop is lossless for any set of drafts checked)."""
+    plain = gen(0, GREEDY)
+    tspec, tW, dspec, dW, prompt = draft_setup()
+    for kw in ({"min_draft": 3}, {"min_draft": 2, "p_min": 0.5}):
+        cap = 16 + N_NEW + 20
+        tkv = KVCache(tspec, cap)
+        prefill(tspec, tW, tkv, prompt[:-1])
+        d = DraftModel(dspec, dW, cap)
+        prefill(dspec, dW, d.kv, prompt[:-1])
+        r = run(tspec, tW, tkv, prompt[-1], list(prompt), N_NEW, 4, GREEDY, 1234, draft=d, **kw)
+        assert r.tokens == plain.tokens
