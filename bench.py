@@ -516,6 +516,28 @@ def main():
         sampled = {"sampler": "T=1 top_k 20 top_p 0.95, Philox uniforms", "tok_s": sum(len(t) for c in cs for t in c.tokens) / els,
                    "ms_per_step": els / args.steps * 1e3, "verify_ms": sum(c.verify_ms for c in cs) / len(cs),
                    "acceptance": sum(c.n[0] for c in cs) / (K * args.steps)}
+        # the same sampled cycles with the draft-probability control: the draft stops at its
+        # first draft whose list gives it less than p_min, and the device skips the rest of
+        # the draft_step's forwards
+        if not args.no_adaptive:
+            ctl = {}
+            for p_min in (0.5,):
+                engs.set_draft_controls(p_min, 0)
+                reset(engs)
+                engs.run(1, K, 0, args.warmup)
+                st0 = engs.stats()
+                torch.cuda.synchronize()
+                ts0 = time.perf_counter()
+                cs = engs.run(1, K, args.warmup, args.steps)
+                torch.cuda.synchronize()
+                els = time.perf_counter() - ts0
+                st1 = engs.stats()
+                ctl[str(p_min)] = {"tok_s": sum(len(t) for c in cs for t in c.tokens) / els,
+                                   "ms_per_step": els / args.steps * 1e3,
+                                   "drafts_checked_per_cycle": (st1["drafts_attempted"] - st0["drafts_attempted"]) /
+                                                               (st1["cycles"] - st0["cycles"])}
+            engs.set_draft_controls(0.0, 0)
+            sampled["draft_probability"] = {"k_max": K, "runs": ctl}
         del engs
         torch.cuda.empty_cache()
 

@@ -439,6 +439,20 @@ int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t b
 #define SPEC_BUF_LOGITS 8
 int spec_debug_read(spec_ctx* ctx, int32_t which, int32_t buffer, void* dst /*device*/, size_t bytes);
 
+/* Draft controls ("What is Speculative Decoding and How Does a Draft Model Work?", section "The
+ * demo, draft model on and off with two pairings": the max draft tokens / min draft tokens /
+ * draft probability settings).  The k passed to draft_step is the most drafts.  p_min in
+ * [0, 1]: the draft model or MTP head stops proposing, for a sequence, at the first draft j whose
+ * list gives the drawn token a probability below p_min (drafts 1 .. j-1 are kept, draft j and
+ * later are not); once every sequence has stopped, the rest of the draft_step's forwards are
+ * skipped on the device (their launches return at once).  Greedy lists are one-hot, so under the
+ * greedy sampler p_min never stops a draft.  min_draft >= 0: a sequence whose kept drafts are
+ * fewer than min_draft has none of them checked (accept emits the target's own token at row 0).
+ * Both act on the next draft_step (the n-gram drafter: min_draft only).  Default 0, 0 (off).
+ * Only between cycles (SPEC_E_STATE otherwise); SPEC_E_INVAL for values out of range; a
+ * draft_step with p_min > 0 supports at most 64 sequences (SPEC_E_UNSUPPORTED). */
+int spec_draft_controls(spec_ctx* ctx, float p_min, int32_t min_draft);
+
 /* ---- stateless kernels (the accept workload on its own) ------------------------------ */
 
 /* Scratch bytes spec_truncate needs for `rows` rows of `vocab` logits. */

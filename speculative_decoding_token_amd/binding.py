@@ -39,7 +39,7 @@ EXPORTED = [
     "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
     "spec_depth_init", "spec_depth_choose", "spec_depth_update", "spec_gdn_commit_forward",
-    "spec_debug_read", "spec_truncate_noalloc",
+    "spec_debug_read", "spec_truncate_noalloc", "spec_draft_controls",
 ]
 BUF_RESIDUAL, BUF_NORM_INPUT, BUF_Q, BUF_K, BUF_ATTN, BUF_SWIGLU, BUF_CACHE_K, BUF_CACHE_V, BUF_LOGITS = range(9)
 GDN_MAX_TOKENS = 64
@@ -145,6 +145,7 @@ def lib(path: str = LIB_PATH):
         "spec_get_stats": ([P, C.POINTER(spec_stats)], C.c_int),
         "spec_get_lengths": ([P, P, I32], C.c_int),
         "spec_debug_read": ([P, I32, I32, P, SZ], C.c_int),
+        "spec_draft_controls": ([P, C.c_float, I32], C.c_int),
         "spec_truncate_scratch_size": ([I32, I32, C.POINTER(SZ)], C.c_int),
         "spec_truncate": ([P, I32, I32, I32, I64, C.POINTER(spec_sampler), C.POINTER(spec_probs), P, P,
                            SZ, P], C.c_int),
@@ -332,6 +333,10 @@ def spec_get_lengths(ctx: int, batch: int) -> List[int]:
 
 def spec_debug_read(ctx: int, which: int, buffer: int, dst, nbytes: int) -> None:
     _check(lib().spec_debug_read(ctx, which, buffer, _ptr(dst), nbytes), ctx)
+
+
+def spec_draft_controls(ctx: int, p_min: float, min_draft: int) -> None:
+    _check(lib().spec_draft_controls(ctx, p_min, min_draft), ctx)
 
 
 def spec_truncate_scratch_size(rows: int, vocab: int) -> int:

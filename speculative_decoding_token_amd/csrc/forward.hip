@@ -569,6 +569,7 @@ SPEC_DEVINL StreamArgs head_args(const FwdArgs& a) {
 template <int NSTD, int NSTQ, int HD>
 __global__ __launch_bounds__(SNW * 64) void forward_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
+  if (a.skip && *a.skip) return;  // every workgroup leaves before the first barrier
   using QKV = Gemm<EPI_QKV_ROWS, NSTD, true>;
   using OP = Gemm<EPI_RESID, NSTQ, true>;
   using GU = Gemm<EPI_SWIGLU, 2 * NSTD, true>;

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
   constexpr int K = NK * 512;
   __shared__ float s_out[T][16][GV_MAX_M];
   __shared__ float s_sq[GV_MAX_M][16];
+  if (a.skip && *a.skip) return;
   const int u = blockIdx.x, tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
   const int M = a.M;
 

@@ -15,10 +15,12 @@ struct TruncArgs {
   int nseg, seg_len;  // segments per row and their length (multiple of 8)
   uint64_t* part;     // [rows][nseg][ksel] keys, descending, 0 = empty
   uint8_t* bad;       // [rows][nseg]
+  const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
 };
 
 struct AcceptArgs {
   const int32_t* drafts;  // [batch, k]
+  int min_draft;          // fewer drafts than this (after kcap) are not tested at all
   spec_probs q, p;        // rows batch*k and batch*(k+1)
   int batch, k, greedy;
   uint64_t seed;
@@ -48,13 +50,27 @@ int truncate_scratch_bytes(int rows, int vocab, size_t* bytes);
 // Output row of input row r is r * out_rs.
 hipError_t launch_truncate(const void* logits, int dtype, int rows, int vocab, int64_t stride,
                            const spec_sampler& s, const spec_probs& out, int out_rs, uint8_t* flags,
-                           void* scratch, hipStream_t st);
+                           void* scratch, hipStream_t st, const uint32_t* skip = nullptr);
 // Row r = (seq r / per_seq, j = r % per_seq) reads list row r * list_rs and draws with slot
 // slot_base + j into tokens[seq * tok_ld + j].  The round is *rnd_ptr when rnd_ptr is not
 // null (device memory, so a captured launch can be replayed for a new round), else rnd.
 hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per_seq, int slot_base,
                          uint64_t seed, const uint32_t* rnd_ptr, uint32_t rnd, uint32_t stream_id,
                          int32_t* tokens, int tok_ld, uint8_t* flags, hipStream_t st);
+// Draft controls of a draft_step (one row per sequence, rows <= 64): `kept` holds the drafts each
+// sequence still proposes (k at the start); drawing draft j (slot j) from a list that gives it
+// less than p_min sets kept[seq] = j - 1 for a sequence still at k >= j, and once no sequence
+// proposes past draft j, *skip = 1 (the later draft forwards then do nothing).
+struct DraftCtl {
+  int32_t* kept;
+  uint32_t* skip;
+  float p_min;
+};
+hipError_t launch_sample_ctl(const spec_probs& lists, int list_rs, int rows, int slot, uint64_t seed,
+                             const uint32_t* rnd_ptr, uint32_t stream_id, int32_t* tokens, int tok_ld,
+                             const DraftCtl& ctl, hipStream_t st);
+// kept[b] = k for b < batch and *skip = 0: the start of a controlled draft_step.
+hipError_t launch_draft_ctl_init(int32_t* kept, int batch, int k, uint32_t* skip, hipStream_t st);
 hipError_t launch_set_u32(uint32_t* p, uint32_t v, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
 // len[b] += 1 + n_acc[b] (n_acc[b] clamped to [0, k]); a second cache length (the MTP
@@ -128,6 +144,7 @@ struct AttnArgs {
   float* part;         // [M*n_q][nchunk][hd+2]
   int nchunk;
   void* out;           // combine: [M, n_q*hd] model dtype
+  const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
   // bf16, head_dim 128: launches with at most ATTN_FEW_ROWS query rows per kv head run their
   // chunks on the vector ALUs (attn_chunk_few_kernel) instead of 16-row MFMA tiles.  Set per
   // model, so that all its forwards at those row counts take the same path.
@@ -247,6 +264,7 @@ struct StreamArgs {
   CacheView cache;
   int layer;
   RowMap rm;
+  const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
 };
 // Whether M rows and reduction length K are covered.  bf16 weights: K in whole stages (1024;
 // 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 3072, 4096, 5120}.  fp8 weights
@@ -302,6 +320,7 @@ struct FwdArgs {
   // workgroup arrives and when it leaves to trace[(e * grid + g) * 2 + {0, 1}] (e < trace_cap)
   unsigned long long* trace;
   int trace_cap;
+  const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
 };
 bool forward_supported(int M, int mseq, int d, int n_q, int n_kv, int hd, int ffn, int vocab);
 // bytes of the one-launch forward's barrier words (eight group counters, a top counter, a

@@ -461,6 +461,7 @@ SPEC_DEVINL int len_first(const int32_t* p) {
 
 template <int DT>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
+  if (a.skip && *a.skip) return;
   using A = Act<DT>;
   typedef typename A::T T;
   extern __shared__ float sm[];
@@ -607,6 +608,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 // relative error below 2^-16), and the row sum adds the float32 values.
 template <int HD, int QTM>
 __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
+  if (a.skip && *a.skip) return;
   constexpr int C = ATTN_CHUNK;  // 64 keys
   constexpr int KP = HD + 8;     // LDS pitch of q and K rows (bf16 elements)
   constexpr int VP = C + 8;      // LDS pitch of V^T rows
@@ -808,6 +810,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 // present; P V: wavefront w produces query row w, two
 // output dims per lane, keys in order.  Partials in the layout the combine kernel reads.
 __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
+  if (a.skip && *a.skip) return;
   constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2, QW = HD / 4;
   constexpr int RM = ATTN_FEW_ROWS;
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KP];
@@ -1009,6 +1012,7 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
 // are loaded before the weights are computed, so the merge waits for about one round trip.
 template <int DT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  if (a.skip && *a.skip) return;
   using A = Act<DT>;
   constexpr int NR = 32;  // chunk values per thread held in registers (the rest are loaded later)
   __shared__ float s_w[ATTN_MAX_CHUNKS];

@@ -132,6 +132,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
   __shared__ int s_bad, s_n, s_slow, s_total;
   __shared__ unsigned long long s_count;
 
+  if (a.skip && *a.skip) return;
   const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int s0 = seg * a.seg_len;
@@ -355,6 +356,7 @@ __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs 
   __shared__ int s_n, s_nc, s_bad, s_keep;
   __shared__ float s_S, s_Z;
   __shared__ uint8_t s_fl;
+  if (a.skip && *a.skip) return;
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int K = a.ksel, nk = a.nseg * K;
   const uint64_t* src = a.part + (int64_t)row * nk;
@@ -481,7 +483,8 @@ __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs 
 
 // ---------------------------------------------------------------- sampling from a list
 // First id (ascending) whose running sum exceeds u * Z; else the last id with mass.
-SPEC_DEVINL int sample_list(const int32_t* ids, const float* w, int n, float u, uint8_t* fl) {
+SPEC_DEVINL int sample_list(const int32_t* ids, const float* w, int n, float u, uint8_t* fl,
+                            int* picked = nullptr) {
   if (n <= 0) {
     *fl |= SPEC_FLAG_BAD_ROW;
     return -1;
@@ -517,6 +520,7 @@ SPEC_DEVINL int sample_list(const int32_t* ids, const float* w, int n, float u, 
   float margin = fabsf(c - thr);
   if (pick > 0) margin = fminf(margin, fabsf(cprev - thr));
   if (margin < NEAR_TIE) *fl |= SPEC_FLAG_SAMPLE_TIE;
+  if (picked) *picked = pick;
   return ids[pick];
 }
 
@@ -539,6 +543,54 @@ __global__ void sample_kernel(spec_probs lists, int list_rs, int rows, int per_s
   }
   tokens[(int64_t)seq * tok_ld + jj] = tok;
   if (flags) flags[r] = fl;
+}
+
+// Draft j of every sequence (one row each, rows <= 64, one wavefront) with the draft controls
+// of "What is Speculative Decoding and How Does a Draft Model Work?", section "The demo, draft
+// model on and off with two pairings" (the draft-probability setting): the draft model's
+// confidence in a draft is the probability its list gives the drawn token; below p_min the
+// sequence stops proposing before that draft.  Tokens are drawn exactly as sample_kernel draws
+// them, so that the lists and tokens of the drafts kept do not depend on the controls.
+__global__ __launch_bounds__(64) void sample_ctl_kernel(spec_probs lists, int list_rs, int rows, int slot,
+                                                        uint64_t seed, const uint32_t* rnd_ptr, uint32_t stream_id,
+                                                        int32_t* tokens, int tok_ld, DraftCtl ctl) {
+  const int r = threadIdx.x;
+  bool go = false;
+  if (r < rows) {
+    int kept = ctl.kept[r];
+    int tok = 0;
+    if (kept >= slot) {
+      // still proposing: draw draft `slot` from its list
+      const int64_t lr = (int64_t)r * list_rs;
+      const int n = min(lists.count[lr], lists.cap);
+      uint8_t fl = 0;
+      int pick = -1;
+      float conf = 0.0f;
+      tok = -1;
+      if (n > 0) {
+        const float u = philox_uniform(seed, (uint32_t)slot, *rnd_ptr, (uint32_t)r, stream_id);
+        tok = sample_list(lists.ids + lr * lists.cap, lists.probs + lr * lists.cap, n, u, &fl, &pick);
+        conf = lists.probs[lr * lists.cap + pick];
+      }
+      if (!(conf >= ctl.p_min)) {
+        kept = slot - 1;
+        ctl.kept[r] = kept;
+      }
+    }
+    // a sequence that stopped before this draft gets the placeholder id 0: a valid token, so
+    // that the forwards that still run over its rows (verify rows past its kept drafts, draft
+    // rows while other sequences go on) stay finite; those rows are never used
+    tokens[(int64_t)r * tok_ld] = tok;
+    go = kept > slot;  // this sequence goes on to draft slot + 1
+  }
+  const uint64_t any = __ballot(go);
+  if (r == 0 && any == 0) *ctl.skip = 1u;
+}
+
+__global__ void draft_ctl_init_kernel(int32_t* kept, int batch, int k, uint32_t* skip) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) kept[b] = k;
+  if (b == 0) *skip = 0u;
 }
 
 // ---------------------------------------------------------------- accept
@@ -575,7 +627,8 @@ __global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
   const int k = a.k;
   // drafts actually proposed for this sequence (an n-gram lookup may find fewer than k);
   // the rows past them are not tested and the bonus comes from row kb
-  const int kb = a.kcap ? min(max(a.kcap[b], 0), k) : k;
+  int kb = a.kcap ? min(max(a.kcap[b], 0), k) : k;
+  if (kb < a.min_draft) kb = 0;  // fewer drafts than the minimum worth checking: none
   const int32_t* d = a.drafts + (int64_t)b * k;
   int32_t* out = a.out_tok + (int64_t)b * (k + 1);
   const int pc = a.p.cap, qc = a.q.cap;
@@ -800,8 +853,9 @@ int truncate_scratch_bytes(int rows, int vocab, size_t* bytes) {
 
 hipError_t launch_truncate(const void* logits, int dtype, int rows, int vocab, int64_t stride,
                            const spec_sampler& s, const spec_probs& out, int out_rs, uint8_t* flags,
-                           void* scratch, hipStream_t st) {
+                           void* scratch, hipStream_t st, const uint32_t* skip) {
   TruncArgs a;
+  a.skip = skip;
   a.logits = logits;
   a.stride = stride;
   a.vocab = vocab;
@@ -836,6 +890,21 @@ hipError_t launch_sample(const spec_probs& lists, int list_rs, int rows, int per
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(sample_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, lists, list_rs, rows,
                      per_seq, slot_base, seed, rnd_ptr, rnd, stream_id, tokens, tok_ld, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_ctl(const spec_probs& lists, int list_rs, int rows, int slot, uint64_t seed,
+                             const uint32_t* rnd_ptr, uint32_t stream_id, int32_t* tokens, int tok_ld,
+                             const DraftCtl& ctl, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (rows > 64 || !rnd_ptr || !ctl.kept || !ctl.skip) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_ctl_kernel, dim3(1), dim3(64), 0, st, lists, list_rs, rows, slot, seed, rnd_ptr,
+                     stream_id, tokens, tok_ld, ctl);
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_ctl_init(int32_t* kept, int batch, int k, uint32_t* skip, hipStream_t st) {
+  hipLaunchKernelGGL(draft_ctl_init_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, kept, batch, k, skip);
   return hipGetLastError();
 }
 

@@ -51,6 +51,9 @@ struct Model {
   float* qkv = nullptr; // [Mmax][q_dim + 2 kv_dim] raw q, k, v rows (one-launch forward)
   spec_layer_weights* dev_layers = nullptr;  // device copy of the layer table (one-launch forward)
   float2* rope = nullptr;
+  // set while a controlled draft_step is enqueued: the launches of this model's forwards then
+  // do nothing once the word is non-zero (every sequence stopped proposing)
+  const uint32_t* skip = nullptr;
 };
 
 // IDLE: nothing to decode from yet; READY: a last token is set, the caches are trimmed;
@@ -92,6 +95,12 @@ struct spec_ctx {
   int32_t* ndraft = nullptr;    // [max_batch] drafts the n-gram lookup found
   int32_t* match = nullptr;     // [max_batch][2] n-gram match length and end
   bool ngram_cycle = false;     // this cycle's drafts came from the n-gram lookup
+  // draft controls (spec_draft_controls): the draft-probability threshold and the fewest drafts
+  // worth checking; the draft model / MTP drafter's kept counts live in ndraft
+  float p_min = 0.0f;
+  int min_draft = 0;
+  bool ctl_cycle = false;       // this cycle's draft_step ran with the controls
+  uint32_t* dskip = nullptr;    // non-zero once no sequence proposes further drafts
   // MTP drafter: its cache length, the target hidden rows it catches up from, the gathered
   // last row and its partials, the concatenated input rows
   int32_t* mtp_len = nullptr;
@@ -333,6 +342,7 @@ size_t layout(spec_ctx* c, void* ws) {
   c->prev_tok = cv.take<int32_t>(B * 4);
   c->stats = cv.take<int64_t>(4 * 8);
   c->round_dev = cv.take<uint32_t>(4);
+  c->dskip = cv.take<uint32_t>(4);
   c->hist_ld = c->cap + 1;
   c->hist = cv.take<int32_t>((size_t)B * c->hist_ld * 4);
   c->ndraft = cv.take<int32_t>(B * 4);
@@ -524,6 +534,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     const spec_layer_weights& w = m.layers[l];
     const spec_layer_scales& sc = m.fp8 ? m.scales[l] : no_scales;
     StreamArgs g{};
+    g.skip = m.skip;
     g.w0 = w.wq;
     g.w1 = w.wk;
     g.w2 = w.wv;
@@ -549,6 +560,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.rm = rm;
     LAUNCH(c, P + PROF_QKV, proj(EPI_QKV, g));
     AttnArgs at{};
+    at.skip = m.skip;
     at.q_stage = m.qst;
     at.k_stage = m.kst;
     at.cache = m.cache;
@@ -563,6 +575,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     at.out = m.attn;
     LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
     StreamArgs o{};
+    o.skip = m.skip;
     o.w0 = w.wo;
     o.w0s = sc.wo;
     o.wbytes = wb;
@@ -580,6 +593,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     LAUNCH(c, P + PROF_OPROJ, proj(EPI_RESID, o));
     np = d.d_model / 16;
     StreamArgs gu{};
+    gu.skip = m.skip;
     gu.w0 = w.wg;
     gu.w1 = w.wu;
     gu.w0s = sc.wg;
@@ -608,6 +622,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     };
     LAUNCH_REP(c, P + PROF_GATEUP, gu_rep);
     StreamArgs dn{};
+    dn.skip = m.skip;
     dn.w0 = w.wd;
     dn.w0s = sc.wd;
     dn.wbytes = wb;
@@ -656,6 +671,7 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.layer = l;
     LAUNCH(c, P + PROF_QKV, launch_gemm(dt, EPI_QKV, g, st));
     AttnArgs a{};
+    a.skip = m.skip;
     a.q_stage = m.qst;
     a.k_stage = m.kst;
     a.cache = m.cache;
@@ -721,6 +737,7 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
   const spec_model_desc& d = m.d;
   if (use_stream(c, m, M) && x == m.x && ss == m.ss) {
     StreamArgs lm{};
+    lm.skip = m.skip;
     lm.w0 = d.lm_head;
     lm.w0s = m.fp8 ? d.lm_head_scale : nullptr;
     lm.wbytes = m.fp8 ? 1 : 2;
@@ -765,6 +782,7 @@ int forward_one_launch(spec_ctx* c, Model& m, int B, int mseq, const int32_t* fi
                        const int32_t* rest, int rest_ld, int pos_off, float* logits) {
   const spec_model_desc& d = m.d;
   FwdArgs a{};
+  a.skip = m.skip;
   a.layers = m.dev_layers;
   a.n_layers = d.n_layers;
   a.d = d.d_model;
@@ -918,26 +936,51 @@ int ensure_room(spec_ctx* c, int batch, int need) {
 
 // The kernels of one draft_step: k forwards of the draft model at one row (two rows for
 // the first: the tokens at L-1 and L), each followed by truncation and a sampled draft.
+// Draws draft j of every sequence from its list row j - 1; with a draft-probability threshold
+// the controlled kernel also stops the sequences whose draft falls below it.
+int enqueue_draft_sample(spec_ctx* c, Model& m, int batch, int k, int j, int32_t* draft_tok, const spec_probs& q) {
+  const int P = 16 * m.mi;
+  if (c->p_min > 0.0f) {
+    LAUNCH(c, P + PROF_SAMPLE, launch_sample_ctl(offset_rows(q, j - 1), k, batch, j, c->cfg.seed, c->round_dev,
+                                                 STREAM_DRAFT, draft_tok + (j - 1), k,
+                                                 DraftCtl{c->ndraft, c->dskip, c->p_min}, c->stream));
+  } else {
+    LAUNCH(c, P + PROF_SAMPLE, launch_sample(offset_rows(q, j - 1), k, batch, 1, j, c->cfg.seed, c->round_dev,
+                                             0u, STREAM_DRAFT, draft_tok + (j - 1), k, nullptr, c->stream));
+  }
+  return SPEC_OK;
+}
+
+// With a draft-probability threshold the draft_step starts by setting every sequence's kept
+// count to k and clearing the stop word, and the model's launches check that word.
+struct DraftSkipScope {
+  Model& m;
+  DraftSkipScope(spec_ctx* c, Model& mm) : m(mm) { m.skip = c->p_min > 0.0f ? c->dskip : nullptr; }
+  ~DraftSkipScope() { m.skip = nullptr; }
+};
+
 int enqueue_draft(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_probs& q) {
   Model& m = c->draft;
   const spec_sampler& s = c->cfg.sampler;
   const int V = m.d.vocab;
   const int P = 16 * m.mi;
+  if (c->p_min > 0.0f) HIPCHK(c, launch_draft_ctl_init(c->ndraft, batch, k, c->dskip, c->stream));
+  DraftSkipScope scope(c, m);
   for (int j = 1; j <= k; ++j) {
     int rc;
     if (j == 1) {
       rc = forward(c, m, batch, 2, c->prev_tok, 1, c->last_tok, 1, -1, m.logits);
       if (rc) return rc;
       LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits + V, SPEC_DTYPE_F32, batch, V, 2 * (int64_t)V, s, q, k,
-                                                nullptr, c->trunc, c->stream));
+                                                nullptr, c->trunc, c->stream, m.skip));
     } else {
       rc = forward(c, m, batch, 1, draft_tok + (j - 2), k, nullptr, 0, j - 1, m.logits);
       if (rc) return rc;
       LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits, SPEC_DTYPE_F32, batch, V, V, s, offset_rows(q, j - 1), k,
-                                                nullptr, c->trunc, c->stream));
+                                                nullptr, c->trunc, c->stream, m.skip));
     }
-    LAUNCH(c, P + PROF_SAMPLE, launch_sample(offset_rows(q, j - 1), k, batch, 1, j, c->cfg.seed, c->round_dev,
-                                             0u, STREAM_DRAFT, draft_tok + (j - 1), k, nullptr, c->stream));
+    rc = enqueue_draft_sample(c, m, batch, k, j, draft_tok, q);
+    if (rc) return rc;
   }
   return SPEC_OK;
 }
@@ -956,6 +999,8 @@ int enqueue_draft_mtp(spec_ctx* c, int batch, int k, int32_t* draft_tok, const s
   const bool fused = m.d.dtype == SPEC_DTYPE_BF16;
   const int R = c->mtp_rows;
   const int64_t h_ss = (int64_t)(c->cfg.max_k + 1) * d;
+  if (c->p_min > 0.0f) HIPCHK(c, launch_draft_ctl_init(c->ndraft, batch, k, c->dskip, c->stream));
+  DraftSkipScope scope(c, m);
   for (int j = 1; j <= k; ++j) {
     int rc;
     if (j == 1) {
@@ -975,9 +1020,9 @@ int enqueue_draft_mtp(spec_ctx* c, int batch, int k, int32_t* draft_tok, const s
     rc = run_head(c, m, batch, rm, c->x1, c->ss1, d / 16, m.logits);
     if (rc) return rc;
     LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits, SPEC_DTYPE_F32, batch, V, V, s, offset_rows(q, j - 1), k,
-                                              nullptr, c->trunc, c->stream));
-    LAUNCH(c, P + PROF_SAMPLE, launch_sample(offset_rows(q, j - 1), k, batch, 1, j, c->cfg.seed, c->round_dev,
-                                             0u, STREAM_DRAFT, draft_tok + (j - 1), k, nullptr, c->stream));
+                                              nullptr, c->trunc, c->stream, m.skip));
+    rc = enqueue_draft_sample(c, m, batch, k, j, draft_tok, q);
+    if (rc) return rc;
   }
   return SPEC_OK;
 }
@@ -1203,6 +1248,7 @@ int spec_set_last(spec_ctx* c, const int32_t* last_tok, const int32_t* prev_tok,
     c->mtp_rows = 1;
   }
   c->ngram_cycle = false;
+  c->ctl_cycle = false;
   c->phase = READY;
   return SPEC_OK;
 }
@@ -1255,6 +1301,7 @@ int spec_prefill(spec_ctx* c, const int32_t* tokens, int32_t batch, int32_t P) {
   HIPCHK(c, launch_copy_rows(tokens + (P - 1), P, c->last_tok, batch, c->stream));
   if (P >= 2) HIPCHK(c, launch_copy_rows(tokens + (P - 2), P, c->prev_tok, batch, c->stream));
   c->ngram_cycle = false;
+  c->ctl_cycle = false;
   c->len_lo = c->len_hi = L0 + P - 1;
   c->started = true;
   c->phase = READY;
@@ -1279,6 +1326,7 @@ int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* d
   rc = ensure_room(c, batch, std::max(k, kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0) + 1);
   if (rc) return rc;
   const spec_probs qq = *q;
+  c->ctl_cycle = c->p_min > 0.0f || c->min_draft > 0;
   if (kind == SPEC_DRAFT_NGRAM) {
     rc = enqueue_draft_ngram(c, batch, k, draft_tok, qq);
     if (rc) return rc;
@@ -1290,9 +1338,14 @@ int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* d
     if (n_drafted) *n_drafted = mx;
     c->ngram_cycle = true;
   } else {
+    if (c->p_min > 0.0f && batch > 64) return fail(c, SPEC_E_UNSUPPORTED, "draft probability with more than 64 sequences");
     HIPCHK(c, launch_set_u32(c->round_dev, (uint32_t)round, c->stream));
+    uint32_t pbits = 0;
+    std::memcpy(&pbits, &c->p_min, sizeof pbits);
+    // the threshold is part of the captured launches (the controlled sampling kernel's argument)
     const void* key[8] = {draft_tok, qq.ids, qq.probs, qq.count, (const void*)(intptr_t)qq.cap,
-                          (const void*)(intptr_t)(kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0), nullptr, nullptr};
+                          (const void*)(intptr_t)(kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0),
+                          (const void*)(uintptr_t)pbits, nullptr};
     if (kind == SPEC_DRAFT_MTP)
       rc = run_graphed(c, 2, batch, k, key, [&]() { return enqueue_draft_mtp(c, batch, k, draft_tok, qq); });
     else
@@ -1323,7 +1376,10 @@ int verify_step(spec_ctx* c, const int32_t* draft_tok, int32_t batch, int32_t k,
   if (c->phase == DRAFTED && c->ngram_cycle && batch > 1 && k != c->phase_k)
     return fail(c, SPEC_E_INVAL, "n-gram drafts of a batch are verified at the drafted k (row stride)");
   if (c->phase == DRAFTED && k > c->phase_k) return fail(c, SPEC_E_INVAL, "k > drafted k");
-  if (c->phase == READY) c->ngram_cycle = false;
+  if (c->phase == READY) {
+    c->ngram_cycle = false;
+    c->ctl_cycle = false;
+  }
   rc = ensure_room(c, batch, k + 1);
   if (rc) return rc;
   const spec_probs pp = *p;
@@ -1366,7 +1422,11 @@ int accept(spec_ctx* c, const int32_t* draft_tok, const spec_probs* q, const spe
   a.last_tok = c->last_tok;
   a.prev_tok = c->prev_tok;
   a.stats = c->stats;
-  a.kcap = c->ngram_cycle ? c->ndraft : nullptr;
+  // drafts proposed per sequence: the n-gram lookup's count, or the draft model's / MTP
+  // head's kept count under a draft-probability threshold; then the minimum worth checking
+  const bool kept = c->ctl_cycle && c->p_min > 0.0f && c->cfg.draft_kind != SPEC_DRAFT_NGRAM;
+  a.kcap = (c->ngram_cycle || kept) ? c->ndraft : nullptr;
+  a.min_draft = c->ctl_cycle ? c->min_draft : 0;
   a.hist = c->hist;
   a.hist_ld = c->hist_ld;
   a.len = c->len;
@@ -1386,7 +1446,18 @@ int kv_trim(spec_ctx* c, const int32_t* n_acc, int32_t batch) {
   c->len_hi += 1 + c->phase_k;
   c->mtp_rows = c->phase_k + 1;
   c->ngram_cycle = false;
+  c->ctl_cycle = false;
   c->phase = READY;
+  return SPEC_OK;
+}
+
+int spec_draft_controls(spec_ctx* c, float p_min, int32_t min_draft) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  if (!(p_min >= 0.0f && p_min <= 1.0f)) return fail(c, SPEC_E_INVAL, "draft probability %g not in [0, 1]", p_min);
+  if (min_draft < 0) return fail(c, SPEC_E_INVAL, "min_draft < 0");
+  if (c->phase != IDLE && c->phase != READY) return fail(c, SPEC_E_STATE, "draft controls change between cycles");
+  c->p_min = p_min;
+  c->min_draft = min_draft;
   return SPEC_OK;
 }
 

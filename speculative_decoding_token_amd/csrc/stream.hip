@@ -10,6 +10,7 @@ namespace {
 template <int EPI, int NST, int WB>
 __global__ __launch_bounds__(sk::SNW * 64) void stream_gemm_kernel(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
+  if (a.skip && *a.skip) return;
   sk::Gemm<EPI, NST, false, WB>::run(a, sm, 0);
 }
 

@@ -296,6 +296,11 @@ class Engine:
     def profile_repeat(self, slot_name: str, reps: int):
         B.spec_profile_repeat(self.ctx, slot_name, reps)
 
+    def set_draft_controls(self, p_min: float = 0.0, min_draft: int = 0):
+        """Draft probability and min draft of the next cycles (see spec_draft_controls); the k
+        of each cycle is the most drafts."""
+        B.spec_draft_controls(self.ctx, p_min, min_draft)
+
     def set_schedule(self, schedule: str):
         """'step', 'stream' (the default) or 'forward' (see spec_set_schedule)."""
         B.spec_set_schedule(self.ctx, schedule)
