@@ -315,7 +315,7 @@ def main():
     dw = synth.make_weights(dshape, 0, device="cuda")
     tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
-    SWEEP_K, SWEEP_REPS = (1, 2, 4, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
+    SWEEP_K, SWEEP_REPS = (1, 2, 3, 4, 5, 6, 7, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
     max_k = max(K, max(SWEEP_K))
     n_cycles = args.warmup + (2 + args.repeats) * args.steps + args.profile_steps + 2  # timed runs + sync loop
     max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + 8
@@ -472,6 +472,30 @@ def main():
             ks = [len(c.drafts[0]) for c in cyc]
             adaptive["teacher_forced"] = {"tok_s": n_ad / el, "cycles": len(cyc), "k_last": ks[-1],
                                           "k_mean": sum(ks) / len(ks), "matches_plain": toks[0] == plain[0][:n_ad]}
+
+    # the cost gate (spec_gate: the K that maximizes the expected tokens per cycle, 1 + a + ... +
+    # a^K for the running acceptance a, over the cycle's cost) driven by this box's measured
+    # verify latency at every K and the measured draft step cost
+    if adaptive is not None and all(str(k) in verify_vs_k for k in range(max_k + 1)):
+        from speculative_decoding_token_amd import binding as B
+        vc = [verify_vs_k[str(k)]["ms"] for k in range(max_k + 1)]
+        draft_ms = max((elapsed / args.steps * 1e3 - verify_avg_ms) / K, 0.0)
+        gate = B.Gate(max_k, vc, draft_ms)
+        n_ad = args.steps * (K + 1)
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, cyc = eng.generate(n_ad, K, rnd0=rnd, gate=gate)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        rnd += len(cyc)
+        ks = [len(c.drafts[0]) for c in cyc]
+        adaptive["cost_gate"] = {"verify_ms_by_k": vc, "draft_step_ms": draft_ms, "tok_s": n_ad / el,
+                                 "cycles": len(cyc), "k_first": ks[0], "k_last": ks[-1],
+                                 "k_mean": sum(ks) / len(ks),
+                                 "note": "a cycle at K = 0 leaves the draft model's cache behind (it "
+                                         "catches up two rows per draft_step), which costs acceptance "
+                                         "only; the tokens are the target's"}
 
     # the same cycles with the target's weights as E4M3 codes + row scales (fp8 row of the
     # next steps; not the headline): verify latency and rate at the fp8 byte count

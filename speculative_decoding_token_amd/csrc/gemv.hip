@@ -37,7 +37,6 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
   constexpr int K = NK * 512;
   __shared__ float s_out[T][16][GV_MAX_M];
   __shared__ float s_sq[GV_MAX_M][16];
-  if (a.skip && *a.skip) return;
   const int u = blockIdx.x, tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
   const int M = a.M;
 
@@ -82,6 +81,9 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
         xb[m][c] = *(const uint4*)((const bf16_t*)a.x + (int64_t)m * K + (c * 64 + lane) * 8);
     }
   }
+  // a skipped draft launch leaves here; the check comes after the loads are issued so that
+  // the argument it reads is fetched with the others
+  if (a.skip && *a.skip) return;
   if (norm) {
     // 1/rms of each input row: lane j adds partials j, j + 64 in order, then the butterfly
 #pragma unroll

@@ -608,7 +608,6 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 // relative error below 2^-16), and the row sum adds the float32 values.
 template <int HD, int QTM>
 __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
-  if (a.skip && *a.skip) return;
   constexpr int C = ATTN_CHUNK;  // 64 keys
   constexpr int KP = HD + 8;     // LDS pitch of q and K rows (bf16 elements)
   constexpr int VP = C + 8;      // LDS pitch of V^T rows
@@ -663,6 +662,8 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
     }
   }
 
+  // a skipped draft launch leaves here, its argument fetched with the others
+  if (a.skip && *a.skip) return;
   // query rows: every load of the thread first (ATTN_ROWS_MAX*HALF/256 slots), then the rotation
   {
     constexpr int NQ = (QTM * 16 * HALF + 255) / 256;  // QTM: most query tiles this instance serves
@@ -810,7 +811,6 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 // present; P V: wavefront w produces query row w, two
 // output dims per lane, keys in order.  Partials in the layout the combine kernel reads.
 __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
-  if (a.skip && *a.skip) return;
   constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2, QW = HD / 4;
   constexpr int RM = ATTN_FEW_ROWS;
   __shared__ __attribute__((aligned(16))) bf16_t ks[C * KP];
@@ -868,6 +868,8 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
       kcs[v] = a.rope[(int64_t)p * HALF + d];
     }
   }
+  // a skipped draft launch leaves here, its argument fetched with the others
+  if (a.skip && *a.skip) return;
   // staging: cached keys (new ones below), values (the QKV projection cached the new ones),
   // zeros past the end; q rotated and rounded as the MFMA kernel does
 #pragma unroll
@@ -1012,7 +1014,6 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
 // are loaded before the weights are computed, so the merge waits for about one round trip.
 template <int DT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  if (a.skip && *a.skip) return;
   using A = Act<DT>;
   constexpr int NR = 32;  // chunk values per thread held in registers (the rest are loaded later)
   __shared__ float s_w[ATTN_MAX_CHUNKS];
@@ -1033,6 +1034,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int c = g + groups * q;
     pv[q] = c < nch ? P[c * (hd + 2) + d] : 0.0f;
   }
+  if (a.skip && *a.skip) return;  // a skipped draft launch (argument fetched with the others)
   if (t < 64) {
     constexpr int PER = ATTN_MAX_CHUNKS / 64;
     float mc[PER], lc[PER];

@@ -132,7 +132,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
   __shared__ int s_bad, s_n, s_slow, s_total;
   __shared__ unsigned long long s_count;
 
-  if (a.skip && *a.skip) return;
   const int row = blockIdx.y, seg = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int s0 = seg * a.seg_len;
@@ -172,6 +171,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_segment_kernel(TruncArgs a) {
       }
     }
   }
+  if (a.skip && *a.skip) return;  // a skipped draft launch (argument fetched with the others)
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int i0 = s0 + (v * TK_THREADS + t) * VW;
