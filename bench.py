@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--repeats", type=int, default=5, help="timed loops of --steps cycles (median and CV)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM counter calibration)")
+    ap.add_argument("--accept-workload-only", action="store_true",
+                    help="only run the stand-alone accept workload (64 sequences, K = 8) and print its figures")
     return ap.parse_args()
 
 
@@ -95,11 +97,11 @@ DOMINANT = {
     "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
-               "sources": ["stream_core.h", "stream.hip"], "traffic": 201963544, "sha256": "89d117fa1a7613cc"},
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 202326171, "sha256": "0a5b067d9f9fed62"},
     "stream_fp8": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 4, 1> (target gate/up + SwiGLU over E4M3 weights "
                              "with row scales, streamed through an LDS ring, one workgroup per CU)",
                    "slot": "target.gate_up",
-                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101514547, "sha256": "89d117fa1a7613cc"},
+                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101880139, "sha256": "0a5b067d9f9fed62"},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",
@@ -286,11 +288,16 @@ def accept_workload_run(torch, synth, B, batch=64, K=8, sigma=1.0, copies=3, rep
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              f"(multi-GPU sharding is design-only)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sharding across "
+              f"GPUs is described, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     from speculative_decoding_token_amd import runtime, synth
+
+    if args.accept_workload_only:
+        from speculative_decoding_token_amd import binding as SB
+        print(json.dumps({"accept_workload": accept_workload_run(torch, synth, SB)}), flush=True)
+        return
 
     if args.calibrate_copy:
         n = 1 << 30

@@ -360,6 +360,8 @@ __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs 
   const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
   const int K = a.ksel, nk = a.nseg * K;
   const uint64_t* src = a.part + (int64_t)row * nk;
+  // this thread's first key goes out together with wave 0's loads of the bound
+  const uint64_t key0 = t < nk ? src[t] : 0;
   if (t < 64) {
     // wave 0: the bound and the bad flags
     uint64_t th = 0;
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs 
   __syncthreads();
   const uint64_t theta = s_theta;
   for (int c = t; c < nk; c += FIN_THREADS) {
-    const uint64_t key = src[c];
+    const uint64_t key = c == t ? key0 : src[c];
     if (key != 0 && key >= theta) cand[atomicAdd(&s_nc, 1)] = key;
   }
   __syncthreads();
@@ -633,18 +635,48 @@ __global__ __launch_bounds__(64) void accept_kernel(AcceptArgs a) {
   int32_t* out = a.out_tok + (int64_t)b * (k + 1);
   const int pc = a.p.cap, qc = a.q.cap;
   const int64_t p0 = (int64_t)b * (k + 1), q0 = (int64_t)b * k;
-  for (int i = lane; i < (k + 1) * pc; i += 64) {
-    s_pid[i] = a.p.ids[p0 * pc + i];
-    s_pp[i] = a.p.probs[p0 * pc + i];
-  }
-  if (lane <= k) s_pn[lane] = list_len(a.p, p0 + lane);
-  if (!a.greedy) {
-    for (int i = lane; i < k * qc; i += 64) {
-      s_qid[i] = a.q.ids[q0 * qc + i];
-      s_qp[i] = a.q.probs[q0 * qc + i];
+  // every load of the lists first (a loop that stores each value before the next load would
+  // wait one round trip per 64 entries), then the LDS stores
+  constexpr int NP = SPEC_MAX_K + 1, NQ = SPEC_MAX_K;  // 64-entry rounds at most
+  const int np = (k + 1) * pc, nq = a.greedy ? 0 : k * qc;
+  int32_t vid[NP], wid[NQ];
+  float vp[NP], wp[NQ];
+#pragma unroll
+  for (int r = 0; r < NP; ++r) {
+    const int i = lane + 64 * r;
+    if (i < np) {
+      vid[r] = a.p.ids[p0 * pc + i];
+      vp[r] = a.p.probs[p0 * pc + i];
     }
-    if (lane < k) s_qn[lane] = list_len(a.q, q0 + lane);
   }
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) {
+    const int i = lane + 64 * r;
+    if (i < nq) {
+      wid[r] = a.q.ids[q0 * qc + i];
+      wp[r] = a.q.probs[q0 * qc + i];
+    }
+  }
+  const int pn_l = lane <= k ? list_len(a.p, p0 + lane) : 0;
+  const int qn_l = (!a.greedy && lane < k) ? list_len(a.q, q0 + lane) : 0;
+#pragma unroll
+  for (int r = 0; r < NP; ++r) {
+    const int i = lane + 64 * r;
+    if (i < np) {
+      s_pid[i] = vid[r];
+      s_pp[i] = vp[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) {
+    const int i = lane + 64 * r;
+    if (i < nq) {
+      s_qid[i] = wid[r];
+      s_qp[i] = wp[r];
+    }
+  }
+  if (lane <= k) s_pn[lane] = pn_l;
+  if (!a.greedy && lane < k) s_qn[lane] = qn_l;
   __syncthreads();
 
   // lane j: the test of draft j
