@@ -9,12 +9,17 @@ and the one device-to-host read of the emitted tokens.  The timed host loop keep
 cycle queued while it reads the previous cycle's tokens; the same cycles with a wait after
 each one are reported beside it.
 
-Prints one JSON line: accepted (emitted) tokens per second over the timed steps, the
-verify pass's HBM bytes per second against the 8 TB/s peak, the roofline of the dominant
-kernel (the gate/up projection + SwiGLU of the target; the forward kernel when the forward
-runs as one launch), a teacher-forced upper bound
-(drafts = the target's own greedy continuation, every draft accepted), and the CPU
-oracle timed on a bounded sample of the same cycle.
+Prints one JSON line: accepted (emitted) tokens per second over the timed steps (the first of
+`--repeats` timed loops; all of them with their median and coefficient of variation under
+`repeats`), the verify pass's HBM bytes per second against the 8 TB/s peak and its latency at
+every K from 0 to 8, the roofline of the dominant kernel (the gate/up projection + SwiGLU of the
+target; the forward kernel when the forward runs as one launch) with its HBM traffic from the
+recorded rocprofv3 counters, a teacher-forced upper bound (drafts = the target's own greedy
+continuation, every draft accepted), the same cycle sampled (T = 1, top_k 20, top_p 0.95) with
+and without the draft-probability control, the adaptive draft length and the cost gate, the
+fp8-weight cycle, the linear-attention state step, the stand-alone accept workload (64
+sequences, K = 8, the 151936-token vocabulary) against its roofline, and the CPU oracle timed
+on one full greedy cycle of the workload after a warm-up cycle.
 
 --weights fp8 runs the same cycle with the target's projections and LM head stored as OCP
 E4M3 codes with a float32 scale per output row (one byte per weight instead of two); the
