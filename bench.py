@@ -45,7 +45,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--k", type=int, default=4)
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences speculated together (each its own cache; default 1, the headline config)")
@@ -362,6 +362,11 @@ def main():
     eng.run(Bn, K, rnd, args.warmup)
     rnd += args.warmup
     torch.cuda.synchronize()
+    # no garbage-collector pass inside the timed loops (a pass over the process's objects can
+    # stall the host loop for tens of ms); collected before each loop instead
+    import gc
+    gc.collect()
+    gc.disable()
     # timed: the host loop keeps one cycle queued ahead (Engine.run); every cycle's tokens
     # are read back to the host inside the timed region
     t0 = time.perf_counter()
@@ -385,11 +390,15 @@ def main():
     rep_tok_s = [emitted / elapsed]
     for _ in range(args.repeats - 1):
         torch.cuda.synchronize()
+        gc.enable()
+        gc.collect()
+        gc.disable()
         tr0 = time.perf_counter()
         cyc_r = eng.run(Bn, K, rnd, args.steps)
         torch.cuda.synchronize()
         rep_tok_s.append(sum(len(t) for c in cyc_r for t in c.tokens) / (time.perf_counter() - tr0))
         rnd += args.steps
+    gc.enable()
     srt = sorted(rep_tok_s)
     mean = sum(rep_tok_s) / len(rep_tok_s)
     cv = (sum((x - mean) ** 2 for x in rep_tok_s) / len(rep_tok_s)) ** 0.5 / mean
@@ -576,6 +585,13 @@ def main():
             sampled["draft_probability"] = {"k_max": K, "runs": ctl}
         del engs
         torch.cuda.empty_cache()
+
+    # the adaptive draft length's three parts in one place: the depth controller, the cost gate
+    # (greedy engine) and the draft-probability control (sampled engine: greedy lists are one-hot)
+    if adaptive is not None and sampled is not None and "draft_probability" in sampled:
+        adaptive["draft_probability"] = dict(sampled.pop("draft_probability"),
+                                             sampler="T=1 top_k 20 top_p 0.95 (the sampled engine)",
+                                             without_control_tok_s=sampled["tok_s"])
 
     from speculative_decoding_token_amd import binding as SB
     gdn_run = gdn_state_run(torch, synth, SB, K)
