@@ -263,7 +263,11 @@ int spec_set_last(spec_ctx* ctx, const int32_t* last_tok /*device*/,
  * SPEC_DRAFT_MTP: the first forward of the cycle catches the MTP layer up on the positions
  * the target verified since its last draft (rows built from the target's hidden states of
  * the previous verify, or of the start), so every cycle of that drafter starts with
- * draft_step; the draft logits come from the target's LM head. */
+ * draft_step; the draft logits come from the target's LM head.
+ * With a draft probability set (spec_draft_controls) a draft model / MTP sequence may stop
+ * before k drafts: its draft_tok entries past the kept ones hold the placeholder id 0 (or the
+ * unconfident draft that stopped it), its q rows past them are unspecified, and accept tests
+ * only the kept drafts; *n_drafted is still k. */
 int draft_step(spec_ctx* ctx, int32_t batch, int32_t k, uint64_t round,
                int32_t* draft_tok /*device*/, spec_probs* q /*host struct of device ptrs*/,
                int32_t* n_drafted /*host, may be NULL*/);
@@ -290,8 +294,10 @@ int verify_step(spec_ctx* ctx, const int32_t* draft_tok /*device*/, int32_t batc
  * (device uint8 [batch] of SPEC_FLAG_* bits, may be NULL), updates the device-side last
  * accepted token and the statistics.  A target row p_{j-1} with no entry (its logits held no
  * finite value) stops the sequence at n = j - 1 kept drafts with SPEC_FLAG_BAD_ROW and -1 as
- * its emitted token (the device-side last token becomes 0).  Must follow a verify_step with
- * the same k. */
+ * its emitted token (the device-side last token becomes 0).  After a draft_step with draft
+ * controls, each sequence is tested on its kept drafts only (none when they are fewer than
+ * min_draft), the bonus coming from the row after them.  Must follow a verify_step with the
+ * same k. */
 int accept(spec_ctx* ctx, const int32_t* draft_tok /*device*/, const spec_probs* q,
            const spec_probs* p, int32_t batch, int32_t k, uint64_t round,
            int32_t* n_acc /*device*/, int32_t* out_tok /*device*/, uint8_t* near_tie);

@@ -575,8 +575,10 @@ __global__ __launch_bounds__(64) void sample_ctl_kernel(spec_probs lists, int li
         conf = lists.probs[lr * lists.cap + pick];
       }
       if (!(conf >= ctl.p_min)) {
+        // not proposed (an empty list, from logits with no finite value, stops here too)
         kept = slot - 1;
         ctl.kept[r] = kept;
+        if (tok < 0) tok = 0;
       }
     }
     // a sequence that stopped before this draft gets the placeholder id 0: a valid token, so
