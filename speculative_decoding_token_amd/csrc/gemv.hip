@@ -50,7 +50,8 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
     for (int i = 0; i < GV_RW; ++i) {
       const char* row = base + (int64_t)(GV_RW * wave + i) * K * 2;
 #pragma unroll
-      for (int c = 0; c < NK; ++c) w[t][i][c] = *(const uint4*)(row + (int64_t)(c * 64 + lane) * 16);
+      for (int c = 0; c < NK; ++c)
+        w[t][i][c] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const __attribute__((address_space(1))) sk::u32x4_t*)(row + (int64_t)(c * 64 + lane) * 16)));
     }
   }
   // inputs: bf16 rows, or float32 rows x * g of an RMSNorm input with its partials
