@@ -112,6 +112,8 @@ hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_
   const int g = std::min(grid, a.nunits);
   const int wb = a.wbytes == 1 ? 1 : 2;
   if (!stream_supported(a.M, a.K, epi, a.ss_in != nullptr, wb, (a.nunits + g - 1) / g)) return hipErrorInvalidValue;
+  // resident inputs: the residual projections take bf16 rows, the others an RMSNorm input
+  if (nst_of(epi, a.K, wb) > 0 && (a.ss_in != nullptr) != (epi != EPI_RESID)) return hipErrorInvalidValue;
   if (wb == 1 && (!a.w0s || (epi == EPI_SWIGLU && !a.w1s) || (epi == EPI_QKV && (!a.w1s || !a.w2s))))
     return hipErrorInvalidValue;
   const void* k = select(epi, nst_of(epi, a.K, wb), wb);

@@ -571,8 +571,8 @@ struct Gemm {
     if constexpr (LAZY) {
       // input slices interleaved with the first S - 1 weight stages; the first unit's stage j
       // waits for its weights and slices only (the loads issued after them stay in flight),
-      // and its slices become bf16 after that stage's barrier.  One body per input kind, so
-      // that neither kind's loads are outstanding, as far as the compiler can tell, in the other.
+      // and its slices become bf16 after that stage's barrier.  The input kind is fixed per
+      // instance, so that the compiler's own waits see only that kind's loads.
       auto lazy = [&](auto nc) {
         constexpr bool NORM = decltype(nc)::value;
         if (NORM) load_pss();
@@ -606,8 +606,9 @@ struct Gemm {
           });
         }
       };
-      if (norm) lazy(std::true_type{});
-      else lazy(std::false_type{});
+      // per-launch projections: the residual ones take bf16 rows, the others an RMSNorm input
+      // (the launcher checks it)
+      lazy(std::bool_constant<EPI != EPI_RESID>{});
       j00 = NST;
     } else {
       if (norm) load_pss();
