@@ -265,6 +265,10 @@ struct StreamArgs {
   int layer;
   RowMap rm;
   const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
+  // EPI_QKV, per-launch projections: when > 0, the chunk count of the attention launch that
+  // follows (grid nchunk x n_kv x batch), whose cached rows of this layer the workgroups with
+  // one unit fewer than the others touch before they end (a pre-read, nothing is written)
+  int pf_nchunk;
 };
 // Whether M rows and reduction length K are covered.  bf16 weights: K in whole stages (1024;
 // 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 3072, 4096, 5120}.  fp8 weights

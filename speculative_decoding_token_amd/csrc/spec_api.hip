@@ -558,6 +558,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.cache = m.cache;
     g.layer = l;
     g.rm = rm;
+    g.pf_nchunk = m.nchunk;  // the attention launch below: grid (nchunk, n_kv, batch)
     LAUNCH(c, P + PROF_QKV, proj(EPI_QKV, g));
     AttnArgs at{};
     at.skip = m.skip;
