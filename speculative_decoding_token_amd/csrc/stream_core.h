@@ -265,6 +265,14 @@ struct Gemm {
   }
 
   static SPEC_DEVINL int stages_per_unit(const StreamArgs& a) { return RES ? NST : a.K / KS; }
+  // The k range (stage of the unit) that stage j of this workgroup reads.  Streamed inputs:
+  // workgroup w walks its unit's stages from w mod nst on, so that the workgroups streaming at
+  // the same time do not all read the same columns of their rows, whose addresses differ by
+  // whole units (down 24.4 -> 23.8 us a launch at the 8B shape).  Resident inputs keep the
+  // order, which their statically indexed slices follow.
+  static SPEC_DEVINL int kstage(int j, int nst) {
+    return RES ? j % nst : (j % nst + (int)blockIdx.x) % nst;
+  }
   static SPEC_DEVINL int total_stages(const StreamArgs& a) { return my_units(a) * stages_per_unit(a); }
 
   // Weights of stage j of this workgroup (unit blockIdx.x + (j / nst) * grid, k-range j % nst)
@@ -277,7 +285,7 @@ struct Gemm {
     const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
     const int nst = stages_per_unit(a), K = RES ? NST * KS : a.K;
     const bool ok = j < total;
-    const int u = (int)blockIdx.x + (j / nst) * (int)gridDim.x, ks = j % nst;
+    const int u = (int)blockIdx.x + (j / nst) * (int)gridDim.x, ks = kstage(j, nst);
     char* buf = sm + (j % S) * STAGE;
     int mat, r0;
     const char* base0 = unit_rows<EPI, WB>(a, ok ? u : 0, 0, &mat, &r0);
@@ -295,7 +303,7 @@ struct Gemm {
   // The wavefront's bf16 input slices of stage j (streamed inputs).
   static SPEC_DEVINL void issue_x(const StreamArgs& a, int j, uint4 (&xb)[NSL]) {
     const int tx = tid_here(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-    const int K = a.K, ks = j % stages_per_unit(a), m = lane & 15;
+    const int K = a.K, ks = kstage(j, stages_per_unit(a)), m = lane & 15;
     const __amdgpu_buffer_rsrc_t xr = rsrc(a.x, (uint32_t)(a.M * K * 2));  // rows >= M: out of range
     const uint32_t xoff = (uint32_t)(m * K + 8 * KSTEP * (lane >> 4)) * 2u;
 #pragma unroll
