@@ -40,6 +40,29 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
   const int u = blockIdx.x, tx = threadIdx.x, lane = tx & 63, wave = tx >> 6;
   const int M = a.M;
 
+  // The epilogue's thread e < 16 M takes column ec = e % 16 of the unit for input row em = e / 16.
+  // Its operands from memory (the residual and the next norm's gain, the cache position of a
+  // value row) are loaded here, ahead of the weights, so that the epilogue waits for no second
+  // round trip after the products.
+  const int e = tx, em = e >> 4, ec = e & 15;
+  const bool live = e < 16 * M;
+  int mat = 0, r0 = 0;
+  (void)sk::unit_rows<EPI, 2>(a, u, 0, &mat, &r0);
+  const int n = r0 + ec;
+  // Every thread loads (the others from row 0, unused), and the values are kept as loaded, so
+  // that no branch or arithmetic puts a wait for them ahead of the weight loads.
+  float res = 0.0f;
+  bf16_t gain_b = 0;
+  int vlen = 0;
+  if (EPI == EPI_RESID) {
+    // without a next norm the gain load reads the residual's own first bytes, unused
+    const float* res_p = a.out + (int64_t)(live ? em : 0) * a.ld + n;
+    res = *res_p;
+    gain_b = *(a.y_out ? (const bf16_t*)a.y_gain + n : (const bf16_t*)res_p);
+  }
+  // (sequence em / mseq of row em < 2 is em >= mseq: no integer division ahead of the weights)
+  if (EPI == EPI_QKV && mat == 2) vlen = a.rm.len[live && em >= a.rm.mseq ? 1 : 0];
+
   // weights: rows r0 + 4 wave + i of each tile, pieces c of 16 bytes
   uint4 w[T][GV_RW][NK];
 #pragma unroll
@@ -127,19 +150,14 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
       }
   }
   __syncthreads();
-  // epilogue: thread e < 16 M takes column c = e % 16 of the unit for input row m = e / 16
-  const int e = tx, m = e >> 4, c = e & 15;
-  const bool live = e < 16 * M;
-  int mat = 0, r0 = 0;
-  (void)sk::unit_rows<EPI, 2>(a, u, 0, &mat, &r0);
-  const int n = r0 + c;
+  // epilogue
+  const int m = em, c = ec;
   if (EPI == EPI_RESID) {
     float xn = 0.0f;
     if (live) {
-      float* xp = a.out + (int64_t)m * a.ld + n;
-      xn = *xp + s_out[0][c][m];
-      *xp = xn;
-      if (a.y_out) ((float*)a.y_out)[(int64_t)m * a.ld + n] = xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]);
+      xn = res + s_out[0][c][m];
+      a.out[(int64_t)m * a.ld + n] = xn;
+      if (a.y_out) ((float*)a.y_out)[(int64_t)m * a.ld + n] = xn * bf16_to_f32(gain_b);
       s_sq[m][c] = xn * xn;
     }
     if (a.ss_out) {
@@ -165,7 +183,7 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
       } else {
         const CacheView& cv = a.cache;
         const int b = m / a.rm.mseq;
-        const int pos = a.rm.len[b] + a.rm.pos_off + m % a.rm.mseq;
+        const int pos = vlen + a.rm.pos_off + m % a.rm.mseq;
         const int kvh = n / cv.hd, dd = n % cv.hd;
         const int64_t idx = ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap + pos) * cv.hd + dd;
         ((bf16_t*)cv.v)[idx] = f32_to_bf16(v);
