@@ -41,17 +41,40 @@ __global__ __launch_bounds__(256) void embed_kernel(const void* E, int d, int vo
                                                     float* x, float* ss, int ss_ld, float* y,
                                                     const bf16_t* gain) {
   using A = Act<DT>;
-  __shared__ float red[256];
+  constexpr int NT = 256, NV = 16;  // threads; elements a thread loads before its first store
+  __shared__ float red[NT];
   const int m = blockIdx.x, b = m / mseq, i = m % mseq, t = threadIdx.x;
   const int tok = (i == 0) ? first[(int64_t)b * first_ld] : rest[(int64_t)b * rest_ld + i - 1];
   const bool ok = tok >= 0 && tok < vocab;
   const typename A::T* row = (const typename A::T*)E + (int64_t)(ok ? tok : 0) * d;
+  const bool gy = DT == SPEC_DTYPE_BF16 && y;
+  // without y the gain loads read the row's own first bytes, unused
+  const bf16_t* gp = gy ? gain : (const bf16_t*)row;
+  // Thread t takes elements t, t + NT, ...: all NV loads of a group (embedding and gain, at
+  // clamped indices, with no branch or arithmetic between them) go out before its stores, so
+  // a row of up to NT * NV elements waits for one round trip after the token id, not one per
+  // element group.
   float sq = 0.0f;
-  for (int c = t; c < d; c += blockDim.x) {
-    const float v = ok ? A::load(row, c) : __builtin_nanf("");
-    x[(int64_t)m * d + c] = v;
-    if (DT == SPEC_DTYPE_BF16 && y) y[(int64_t)m * d + c] = v * bf16_to_f32(gain[c]);
-    sq += v * v;
+  for (int c0 = 0; c0 < d; c0 += NT * NV) {
+    typename A::T v[NV];
+    bf16_t g[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int c = min(c0 + t + NT * q, d - 1);
+      v[q] = row[c];
+      g[q] = gp[c];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load of the group ahead of the stores
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int c = c0 + t + NT * q;
+      if (c < d) {
+        const float val = ok ? A::load(v, q) : __builtin_nanf("");
+        x[(int64_t)m * d + c] = val;
+        if (gy) y[(int64_t)m * d + c] = val * bf16_to_f32(g[q]);
+        sq += val * val;
+      }
+    }
   }
   red[t] = sq;
   __syncthreads();
@@ -80,11 +103,34 @@ __global__ __launch_bounds__(256) void mtp_input_kernel(MtpInArgs a) {
   const int tok = a.tok[(int64_t)b * a.tok_ld + (a.tok_pos ? a.tok_pos[b] : 0) + i];
   const bool ok = tok >= 0 && tok < a.vocab;
   const T* e = (const T*)a.embed + (int64_t)(ok ? tok : 0) * d;
+  const T* gh = (const T*)a.norm_h;
+  const T* ge = (const T*)a.norm_e;
+  // Thread t takes elements t, t + NT, ...; the loads of a group of NV of them (both rows and,
+  // when the whole row is one group, both gains) go out together, ahead of any arithmetic.
+  constexpr int NT = 256, NV = 16;
+  const bool one = d <= NT * NV;  // then the values stay in registers for the second pass
+  float hv[NV];
+  T ev[NV], ghv[NV], gev[NV];
   float sh = 0.0f, se = 0.0f;
-  for (int c = t; c < d; c += 256) {
-    const float x = h[c], y = A::load(e, c);
-    sh += x * x;
-    se += y * y;
+  for (int c0 = 0; c0 < d; c0 += NT * NV) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int c = min(c0 + t + NT * q, d - 1);
+      hv[q] = h[c];
+      ev[q] = e[c];
+      if (one) {
+        ghv[q] = gh[c];
+        gev[q] = ge[c];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+      if (c0 + t + NT * q < d) {
+        const float x = hv[q], y = A::load(ev, q);
+        sh += x * x;
+        se += y * y;
+      }
   }
   red[0][t] = sh;
   red[1][t] = se;
@@ -99,11 +145,26 @@ __global__ __launch_bounds__(256) void mtp_input_kernel(MtpInArgs a) {
   const float ih = 1.0f / sqrtf(red[0][0] / (float)d + a.eps);
   const float ie = ok ? 1.0f / sqrtf(red[1][0] / (float)d + a.eps) : __builtin_nanf("");
   T* o = (T*)a.out + (int64_t)m * 2 * d;
-  const T* gh = (const T*)a.norm_h;
-  const T* ge = (const T*)a.norm_e;
-  for (int c = t; c < d; c += 256) {
-    A::store(o, c, h[c] * ih * A::load(gh, c));
-    A::store(o, d + c, A::load(e, c) * ie * A::load(ge, c));
+  for (int c0 = 0; c0 < d; c0 += NT * NV) {
+    if (!one) {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) {
+        const int c = min(c0 + t + NT * q, d - 1);
+        hv[q] = h[c];
+        ev[q] = e[c];
+        ghv[q] = gh[c];
+        gev[q] = ge[c];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      const int c = c0 + t + NT * q;
+      if (c < d) {
+        A::store(o, c, hv[q] * ih * A::load(ghv, q));
+        A::store(o, d + c, A::load(ev, q) * ie * A::load(gev, q));
+      }
+    }
   }
 }
 
