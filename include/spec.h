@@ -433,7 +433,13 @@ int spec_get_lengths(spec_ctx* ctx, int32_t* lengths /*host [batch]*/, int32_t b
  *   SPEC_BUF_CACHE_K,_V the whole cache, [max_batch, n_layers, n_kv_heads, capacity, head_dim]
  *                       in the model dtype, capacity = max_ctx + max_k + 2;
  *   SPEC_BUF_LOGITS     [rows, vocab] the logits of the model's last forward that kept them in
- *                       its own buffer (a draft forward; a verify without logits_out). */
+ *                       its own buffer (a verify without logits_out; the MTP head's last
+ *                       forward).  A draft model's draft_step over `batch` sequences keeps the
+ *                       logits of each of its forwards: forward 1 (two rows a sequence) in rows
+ *                       2b and 2b + 1, forward j >= 2 in row j * batch + b; draft j (1-based) of
+ *                       sequence b was drawn from row 2b + 1 (j = 1) or j * batch + b (j >= 2).
+ *                       The buffer holds max(rows of one forward, (max_k + 1) * max_batch) rows
+ *                       for the draft model. */
 #define SPEC_BUF_RESIDUAL 0
 #define SPEC_BUF_NORM_INPUT 1
 #define SPEC_BUF_Q 2

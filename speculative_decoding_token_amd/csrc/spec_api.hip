@@ -35,6 +35,7 @@ struct Model {
   // forwards take them, so its rows never depend on the row count)
   bool gemv = false;
   int q_dim = 0, kv_dim = 0, mseq_max = 0, Mmax = 0, nchunk = 0;
+  int logit_rows = 0;  // rows of `logits`: Mmax, or for the draft model (max_k + 1) per sequence
   size_t act = 4;
   CacheView cache{};
   float* x = nullptr;
@@ -303,7 +304,7 @@ int max_rows_per_seq(const spec_model_desc& m, int max_k, int max_batch) {
   return std::max(r, max_k + 1);
 }
 
-void carve_model(Model& m, Carver& cv, int B, int cap) {
+void carve_model(Model& m, Carver& cv, int B, int cap, int logit_rows = 0) {
   const spec_model_desc& d = m.d;
   m.act = d.dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   m.q_dim = d.n_q_heads * d.head_dim;
@@ -323,7 +324,8 @@ void carve_model(Model& m, Carver& cv, int B, int cap) {
   m.kst = cv.take<float>((size_t)m.Mmax * m.kv_dim * 4);
   m.attn = cv.take<void>((size_t)m.Mmax * m.q_dim * m.act);
   m.h = cv.take<void>((size_t)m.Mmax * d.d_ffn * m.act);
-  m.logits = cv.take<float>((size_t)m.Mmax * d.vocab * 4);
+  m.logit_rows = std::max(m.Mmax, logit_rows);
+  m.logits = cv.take<float>((size_t)m.logit_rows * d.vocab * 4);
   m.part = cv.take<float>((size_t)m.Mmax * d.n_q_heads * m.nchunk * (d.head_dim + 2) * 4);
   m.ss = cv.take<float>((size_t)m.Mmax * (d.d_model / 16 + 1) * 4);
   m.qkv = cv.take<float>((size_t)m.Mmax * (m.q_dim + 2 * m.kv_dim) * 4);
@@ -352,7 +354,9 @@ size_t layout(spec_ctx* c, void* ws) {
   carve_model(c->target, cv, B, c->cap);
   if (c->draft.present) {
     c->draft.mseq_max = std::max(2, max_rows_per_seq(c->draft.d, 1, B));
-    carve_model(c->draft, cv, B, c->cap);
+    // a draft_step keeps every forward's logits: forward 1 in rows 0 .. 2B-1, forward j >= 2
+    // in rows jB .. jB + B - 1
+    carve_model(c->draft, cv, B, c->cap, (g.max_k + 1) * B);
   }
   if (c->mtp.present) {
     const int d = c->mtp.d.d_model;
@@ -967,6 +971,8 @@ int enqueue_draft(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_
   const int P = 16 * m.mi;
   if (c->p_min > 0.0f) HIPCHK(c, launch_draft_ctl_init(c->ndraft, batch, k, c->dskip, c->stream));
   DraftSkipScope scope(c, m);
+  // each forward keeps its logits in rows of its own (forward 1: 0 .. 2 batch - 1; forward j:
+  // j batch .. j batch + batch - 1), which the context's logits buffer holds up to max_k
   for (int j = 1; j <= k; ++j) {
     int rc;
     if (j == 1) {
@@ -975,9 +981,10 @@ int enqueue_draft(spec_ctx* c, int batch, int k, int32_t* draft_tok, const spec_
       LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits + V, SPEC_DTYPE_F32, batch, V, 2 * (int64_t)V, s, q, k,
                                                 nullptr, c->trunc, c->stream, m.skip));
     } else {
-      rc = forward(c, m, batch, 1, draft_tok + (j - 2), k, nullptr, 0, j - 1, m.logits);
+      float* lg = m.logits + (size_t)j * batch * V;
+      rc = forward(c, m, batch, 1, draft_tok + (j - 2), k, nullptr, 0, j - 1, lg);
       if (rc) return rc;
-      LAUNCH(c, P + PROF_TRUNC, launch_truncate(m.logits, SPEC_DTYPE_F32, batch, V, V, s, offset_rows(q, j - 1), k,
+      LAUNCH(c, P + PROF_TRUNC, launch_truncate(lg, SPEC_DTYPE_F32, batch, V, V, s, offset_rows(q, j - 1), k,
                                                 nullptr, c->trunc, c->stream, m.skip));
     }
     rc = enqueue_draft_sample(c, m, batch, k, j, draft_tok, q);
@@ -1573,7 +1580,7 @@ int spec_debug_read(spec_ctx* c, int32_t which, int32_t buffer, void* dst, size_
     case SPEC_BUF_SWIGLU: src = m->h; n = rows * d.d_ffn * m->act; break;
     case SPEC_BUF_CACHE_K: src = m->cache.k; n = cache; break;
     case SPEC_BUF_CACHE_V: src = m->cache.v; n = cache; break;
-    case SPEC_BUF_LOGITS: src = m->logits; n = rows * d.vocab * 4; break;
+    case SPEC_BUF_LOGITS: src = m->logits; n = (size_t)m->logit_rows * d.vocab * 4; break;
     default: return fail(c, SPEC_E_INVAL, "unknown buffer %d", buffer);
   }
   if (bytes < n) n = bytes;

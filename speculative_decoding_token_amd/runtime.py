@@ -320,5 +320,13 @@ class Engine:
         self.stream.synchronize()
         return out
 
+    def draft_logits(self, batch: int, k: int) -> torch.Tensor:
+        """[k, batch, vocab] float32: the draft model's logits row that draft j + 1 of each
+        sequence was drawn from in the last draft_step over ``batch`` sequences and ``k`` drafts
+        (see SPEC_BUF_LOGITS)."""
+        rows = self.read_buffer(1, B.BUF_LOGITS, ((k + 1) * batch, self.draft_shape.vocab))
+        first = rows[: 2 * batch].view(batch, 2, -1)[:, 1]
+        return torch.stack([first] + [rows[j * batch:(j + 1) * batch] for j in range(2, k + 1)])
+
     def lengths(self, batch: int):
         return B.spec_get_lengths(self.ctx, batch)

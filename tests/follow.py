@@ -9,8 +9,6 @@ decision; then the oracle takes the GPU's accepted tokens and trims its caches a
 Lists are compared against the oracle's within the float error of their logits; the discrete
 steps that read them (drafting, accepting) are checked exactly on the GPU's own lists, where
 only a margin below 1e-6 excuses a difference."""
-import dataclasses
-
 import numpy as np
 import torch
 
@@ -23,36 +21,31 @@ from tests.helpers import assert_rows_close, check_list_row, token_lists
 def follow_cycles(eng, n_cycles, K, tspec, tW, tkv, dspec, dW, dkv, hist, temperature, seed, rtol):
     """Runs n_cycles GPU cycles of k = K drafts and checks each.  hist: the token history up to
     and including the last accepted token (position tkv.length).  Checks:
-    * the draft model's lists against the oracle's draft forwards fed the GPU's previous drafts
-      (check_list_row; the error band of a draft row is twice the contract's float32 drift on
-      it, the oracle's float32 and float64 logits), and each draft token against a draw from the
-      GPU's own list with the same uniform (the argmax under greedy sampling);
+    * the draft model's logits (each draft forward's row, read back after the cycle) within rtol
+      of the oracle's draft forwards fed the GPU's previous drafts, its lists against the
+      oracle's (check_list_row, within the row's measured logit error, as for the verify), and
+      each draft token against a draw from the GPU's own list with the same uniform (the argmax
+      under greedy sampling);
     * the verify's logits within rtol and its lists (check_list_row);
     * the accept decision: the oracle's rule on the GPU's own lists and uniforms gives the GPU's
       accepted count and tokens exactly, unless |u - p/q| or a sampling step lies within 1e-6.
     Returns counts of the checks."""
-    dspec32 = dataclasses.replace(dspec, arith32=True)
-    dkv32 = om.KVCache(dspec32, len(dkv.k[0][0]))
-    for l in range(len(dkv.k)):
-        dkv32.k[l][:] = dkv.k[l]
-        dkv32.v[l][:] = dkv.v[l]
-    dkv32.length = dkv.length
     cnt = dict(draft_lists_exact=0, draft_lists_partial=0, drafts=0, verify_lists_exact=0, verify_lists_partial=0,
                accepts=0, accepts_at_tie=0)
     for r in range(n_cycles):
         c = eng.cycle(1, K, r, keep=True)
         L = tkv.length
         gd = [int(t) for t in c.drafts[0]]
+        dlg = eng.draft_logits(1, K)[:, 0].cpu().numpy().astype(np.float64)
         # draft model: feed the history it has not consumed, then the GPU's drafts one by one
-        lg = lg32 = None
+        lg = None
         while dkv.length <= L:
             pos = dkv.length
             lg, _ = om.forward_one(dspec, dW, dkv, pos, hist[pos])
-            lg32, _ = om.forward_one(dspec32, dW, dkv32, pos, hist[pos])
-            dkv.length = dkv32.length = pos + 1
+            dkv.length = pos + 1
         for j in range(K):
-            band = 2.0 * float(np.abs(lg32.astype(np.float64) - lg).max())
-            kind = check_list_row(*c.q[j], lg, band, temperature)
+            assert_rows_close(dlg[j][None], lg[None], rtol, "draft logits")
+            kind = check_list_row(*c.q[j], lg, float(np.abs(dlg[j] - lg).max()), temperature)
             cnt["draft_lists_" + kind] += 1
             gq = token_lists([c.q[j]])[0]
             if temperature <= 0:
@@ -64,8 +57,7 @@ def follow_cycles(eng, n_cycles, K, tspec, tW, tkv, dspec, dW, dkv, hist, temper
             if j + 1 < K:
                 pos = dkv.length
                 lg, _ = om.forward_one(dspec, dW, dkv, pos, gd[j])
-                lg32, _ = om.forward_one(dspec32, dW, dkv32, pos, gd[j])
-                dkv.length = dkv32.length = pos + 1
+                dkv.length = pos + 1
         # verify over the GPU's drafts
         ref = om.forward_tokens(tspec, tW, tkv, [hist[L]] + gd)
         got = c.logits[0].cpu().numpy()
@@ -89,6 +81,5 @@ def follow_cycles(eng, n_cycles, K, tspec, tW, tkv, dspec, dW, dkv, hist, temper
         for kvc in (tkv,):
             kvc.trim(L + 1 + n)
         dkv.trim(min(dkv.length, L + 1 + n))
-        dkv32.trim(min(dkv32.length, L + 1 + n))
         hist.extend(int(t) for t in c.tokens[0])
     return cnt

@@ -147,9 +147,11 @@ def test_8b_full_depth_verify(verify_8b, temp):
 def test_0p6b_full_depth_draft_step(temp):
     """One draft_step of K = 8 at the 0.6B draft shape (28 layers, tied 151936-token head, a
     2047-entry draft cache): each draft decision against the oracle's draft forward
-    conditioned on the GPU's previous drafts.  A decision is compared unless its deciding
-    margin lies within twice the contract's own float32 drift on that row (the float32 and
-    float64 oracle logits of the same forward)."""
+    conditioned on the GPU's previous drafts.  Each draft's logits row (read back after the
+    step) lies within the bf16 tolerance of the oracle's, or twice the contract's own float32
+    drift on that row (the float32 and float64 oracle logits of the same forward) where that
+    is larger; a decision is compared unless its deciding margin lies within twice the row's
+    measured logit error."""
     ts = synth.SHAPES["qwen8b"].with_layers(1)
     ds = synth.SHAPES["qwen0p6b"]
     L, K = 2048, 8
@@ -170,6 +172,7 @@ def test_0p6b_full_depth_draft_step(temp):
     eng.stream.synchronize()
     drafts = buf["draft"][0].cpu().tolist()
     qlists = buf["q"].to_lists(K)
+    dlg = eng.draft_logits(1, K)[:, 0].cpu().numpy().astype(np.float64)
     spec, spec32 = om.Spec.from_shape(ds), om.Spec.from_shape(ds, arith32=True)
     W = host_weights_f64(dw)
     kh, vh = dk.double().cpu().numpy(), dv.double().cpu().numpy()
@@ -180,15 +183,17 @@ def test_0p6b_full_depth_draft_step(temp):
     l32 = om.forward_tokens(spec32, W, kv32, [prev, last])[-1]
     checked = 0
     for j in range(K):
-        drift = float(np.abs(l32.astype(np.float64) - logits).max())
+        drift = float(row_rel_err(l32, logits))
+        assert row_rel_err(dlg[j], logits) <= max(RTOL_BF16, 2.0 * drift), j
+        err = float(np.abs(dlg[j] - logits).max())
         o = osm.truncate(logits, temp, 20, 0.95)
         gi, gp = qlists[j]
         if temp == 0.0:
-            if o.gap_logit > 2 * drift:
+            if o.gap_logit > 2 * err:
                 assert drafts[j] == int(o.ids[0]), j
                 checked += 1
         else:
-            checked += check_list_row(gi, gp, logits, drift, temp) == "exact"
+            checked += check_list_row(gi, gp, logits, err, temp) == "exact"
         if j + 1 < K:
             logits = om.forward_tokens(spec, W, kv, [drafts[j]])[-1]
             l32 = om.forward_tokens(spec32, W, kv32, [drafts[j]])[-1]
@@ -223,8 +228,7 @@ def test_0p6b_full_depth_draft_forward_logits(k):
         with eng._enter():
             B.draft_step(eng.ctx, 1, k, 0, buf["draft"], buf["q"])
         eng.stream.synchronize()
-        rows = 2 if k == 1 else 1
-        got[sched] = eng.read_buffer(1, B.BUF_LOGITS, (rows, ds.vocab)).cpu().numpy()[rows - 1]
+        got[sched] = eng.draft_logits(1, k)[k - 1, 0].cpu().numpy()
         drafts[sched] = buf["draft"][0].cpu().tolist()
         eng.close()
     spec, spec32 = om.Spec.from_shape(ds), om.Spec.from_shape(ds, arith32=True)
