@@ -865,19 +865,32 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 }
 
 // The same chunk for few query rows (R <= ATTN_FEW_ROWS, head_dim 128: a draft model at one or
-// two rows) on the vector ALUs, where 16-row MFMA tiles would be mostly padding.  K and V stay
-// in the cache layout in LDS.  Scores: thread t takes key t / 4 and the quarter t % 4 of the
-// head dimension (a sequential sum over its 32 dims, then the quarters added pairwise); the
-// chunk softmax per row in float32 as in the MFMA kernel, reductions only for the R rows
-// present; P V: wavefront w produces query row w, two
-// output dims per lane, keys in order.  Partials in the layout the combine kernel reads.
+// two rows) on the vector ALUs, where 16-row MFMA tiles would be mostly padding.  The cached
+// keys and values stay in the registers they are loaded into: thread t holds rows
+// j = t / 16 + 16 v (v < 4) of the chunk, dims 8 (t % 16) .. + 7.  Only the query rows and the
+// chunk's new keys (rotated here) pass through LDS.  Scores: each thread's 8-dim products in
+// order, then summed over the 16 threads of a row by a fixed butterfly; the chunk softmax per
+// row in float32 (maximum over the chunk, then exp(s - max)); P V: each thread's products over
+// its four keys, summed over the four rows of threads of a wavefront and then over the four
+// wavefronts in order.  Partials in the layout the combine kernel reads.
+SPEC_DEVINL float few_sum16(float x) {
+  // xor 1 and 2 within a quad, then the two quads of each half row and the two half rows:
+  // every lane of a row of 16 ends with the same sum
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
 __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
-  constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2, QW = HD / 4;
+  constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2;
   constexpr int RM = ATTN_FEW_ROWS;
-  __shared__ __attribute__((aligned(16))) bf16_t ks[C * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t vs[C * KP];
+  constexpr int NV = C * (HD / 8) / 256;  // key rows a thread holds
+  static_assert(NV == 4, "four key rows a thread: one per row of 16 threads of a wavefront");
+  __shared__ __attribute__((aligned(16))) bf16_t ks[C * KP];  // the new keys' rows only
   __shared__ __attribute__((aligned(16))) float qf[RM][HD];
-  __shared__ __attribute__((aligned(16))) float ps[RM][C];
+  __shared__ __attribute__((aligned(16))) float opart[4][RM][HD];
   __shared__ float wred[2][4][RM];
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -894,12 +907,11 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
   const bf16_t* vc = (const bf16_t*)cv.v + cbase;
   // every load first: cached K and V rows of the chunk (16 threads per 256-byte row), the
   // query pair of this thread, and the first new-key pairs
-  constexpr int NV = C * (HD / 8) / 256;
+  const int d8 = (t & 15) * 8;
   uint4 kreg[NV], vreg[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int idx = t + 256 * v;
-    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8;
+    const int j = (t >> 4) + 16 * v;
     const int pc = min(c0 + j, cv.cap - 1);
     kreg[v] = *(const uint4*)(kc + (int64_t)pc * HD + d8);
     vreg[v] = *(const uint4*)(vc + (int64_t)pc * HD + d8);
@@ -931,16 +943,8 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
   }
   // a skipped draft launch leaves here, its argument fetched with the others
   if (a.skip && *a.skip) return;
-  // staging: cached keys (new ones below), values (the QKV projection cached the new ones),
-  // zeros past the end; q rotated and rounded as the MFMA kernel does
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int idx = t + 256 * v;
-    const int j = idx / (HD / 8), d8 = (idx % (HD / 8)) * 8, p = c0 + j;
-    if (p < L) *(uint4*)(ks + j * KP + d8) = kreg[v];
-    else if (p >= total) *(uint4*)(ks + j * KP + d8) = make_uint4(0, 0, 0, 0);
-    *(uint4*)(vs + j * KP + d8) = p < total ? vreg[v] : make_uint4(0, 0, 0, 0);
-  }
+  // staging: q rotated and rounded as the MFMA kernel does; the new keys rotated, rounded and
+  // written to LDS and to the cache
   if (qr < RM) {
     qf[qr][qd] = qr < R ? bf16_to_f32(f32_to_bf16(qx0 * qcs.x - qx1 * qcs.y)) : 0.0f;
     qf[qr][qd + HALF] = qr < R ? bf16_to_f32(f32_to_bf16(qx1 * qcs.x + qx0 * qcs.y)) : 0.0f;
@@ -966,55 +970,46 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // scores of key j for every row
-  const int j = t >> 2, qq = t & 3;
-  float s[RM];
+  // this thread's keys: cached ones as loaded, new ones from LDS, none past the end (their
+  // values zero, so that a stale row never meets a zero weight)
 #pragma unroll
-  for (int r = 0; r < RM; ++r) s[r] = 0.0f;
+  for (int v = 0; v < NV; ++v) {
+    const int j = (t >> 4) + 16 * v, p = c0 + j;
+    if (p >= L && p < total) kreg[v] = *(const uint4*)(ks + j * KP + d8);
+    if (p >= total) vreg[v] = make_uint4(0, 0, 0, 0);
+  }
+  float kf[NV][8];
 #pragma unroll
-  for (int e8 = 0; e8 < QW / 8; ++e8) {
-    const int d0 = qq * QW + e8 * 8;
-    const uint4 kk = *(const uint4*)(ks + j * KP + d0);
-    const uint32_t kw[4] = {kk.x, kk.y, kk.z, kk.w};
-    float kf[8];
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t kw[4] = {kreg[v].x, kreg[v].y, kreg[v].z, kreg[v].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = __uint_as_float(kw[e] << 16);
-      kf[2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
-    }
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      if (r < R) {
-        const float4 q0 = *(const float4*)(&qf[r][d0]);
-        const float4 q1 = *(const float4*)(&qf[r][d0 + 4]);
-        s[r] += kf[0] * q0.x;
-        s[r] += kf[1] * q0.y;
-        s[r] += kf[2] * q0.z;
-        s[r] += kf[3] * q0.w;
-        s[r] += kf[4] * q1.x;
-        s[r] += kf[5] * q1.y;
-        s[r] += kf[6] * q1.z;
-        s[r] += kf[7] * q1.w;
-      }
+      kf[v][2 * e] = __uint_as_float(kw[e] << 16);
+      kf[v][2 * e + 1] = __uint_as_float(kw[e] & 0xFFFF0000u);
     }
   }
-  // the quarters added pairwise (all four lanes of a key then hold the same sum), masked and
-  // scaled; the chunk maximum of each row from a butterfly over the wavefront's 16 keys and the
-  // four wavefronts' maxima
-  const int p = c0 + j;
-  float mx[RM];
+  // scores, masked and scaled; the chunk maximum of each row over this thread's four keys, the
+  // four rows of threads of the wavefront and the four wavefronts
+  float s[NV][RM], mx[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     mx[r] = -__builtin_inff();
     if (r < R) {
-      float v = s[r];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      s[r] = p <= L + r / G ? v * a.scale : -__builtin_inff();
-      float m = s[r];
+      const float4 q0 = *(const float4*)(&qf[r][d8]);
+      const float4 q1 = *(const float4*)(&qf[r][d8 + 4]);
+      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-      for (int o = 4; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      mx[r] = m;
+      for (int v = 0; v < NV; ++v) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += kf[v][e] * qv[e];
+        acc = few_sum16(acc);
+        const int p = c0 + (t >> 4) + 16 * v;
+        s[v][r] = p <= L + r / G ? acc * a.scale : -__builtin_inff();
+        mx[r] = fmaxf(mx[r], s[v][r]);
+      }
+      mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 16, 64));
+      mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 32, 64));
     }
   }
   if (lane == 0) {
@@ -1022,48 +1017,63 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
     for (int r = 0; r < RM; ++r) wred[0][wave][r] = mx[r];
   }
   __syncthreads();
-  // weights exp(s - max) in float32, their sums per wavefront
-  float lsum[RM];
+  // weights exp(s - max) in float32; P V over this thread's keys in order and the weight sums,
+  // then over the wavefront's four rows of threads
+  float o[RM][8], lsum[RM];
+  float vf[NV][8];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t vw[4] = {vreg[v].x, vreg[v].y, vreg[v].z, vreg[v].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vf[v][2 * e] = __uint_as_float(vw[e] << 16);
+      vf[v][2 * e + 1] = __uint_as_float(vw[e] & 0xFFFF0000u);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     lsum[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[r][e] = 0.0f;
     if (r < R) {
       const float m = fmaxf(fmaxf(wred[0][0][r], wred[0][1][r]), fmaxf(wred[0][2][r], wred[0][3][r]));
-      const float e = (m == -__builtin_inff() || s[r] == -__builtin_inff()) ? 0.0f : expf(s[r] - m);
-      if (qq == 0) ps[r][j] = e;
-      float l = qq == 0 ? e : 0.0f;
-#pragma unroll
-      for (int o = 4; o < 64; o <<= 1) l += __shfl_xor(l, o, 64);
-      lsum[r] = l;
       mx[r] = m;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const float w = (m == -__builtin_inff() || s[v][r] == -__builtin_inff()) ? 0.0f : expf(s[v][r] - m);
+        lsum[r] += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] += w * vf[v][e];
+      }
+#pragma unroll
+      for (int o2 = 16; o2 < 64; o2 <<= 1) {
+        lsum[r] += __shfl_xor(lsum[r], o2, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[r][e] += __shfl_xor(o[r][e], o2, 64);
+      }
     }
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+      if (r < R) {
+        *(float4*)(&opart[wave][r][d8]) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+        *(float4*)(&opart[wave][r][d8 + 4]) = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+      }
   }
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < RM; ++r) wred[1][wave][r] = lsum[r];
   }
   __syncthreads();
-  // P V: wavefront w -> row w, lane -> dims 2 lane, 2 lane + 1, keys in order
-  const int r = wave;
-  if (r < R) {
-    float o0 = 0.0f, o1 = 0.0f;
-    const int d = 2 * lane;
-#pragma unroll 4
-    for (int jj = 0; jj < C; jj += 4) {
-      const float4 pw = *(const float4*)(&ps[r][jj]);
-      const float pv[4] = {pw.x, pw.y, pw.z, pw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t vv = *(const uint32_t*)(vs + (jj + e) * KP + d);
-        o0 += pv[e] * __uint_as_float(vv << 16);
-        o1 += pv[e] * __uint_as_float(vv & 0xFFFF0000u);
-      }
-    }
+  // the four wavefronts' partials added in order: thread t takes (row, dim) pairs t, t + 256
+  for (int idx = t; idx < R * HD; idx += 256) {
+    const int r = idx / HD, d = idx % HD;
     const int i = r / G, h = kvh * G + r % G;
     float* P = a.part + ((int64_t)((b * mseq + i) * a.n_q + h) * a.nchunk + chunk) * (HD + 2);
-    *(float2*)(P + d) = make_float2(o0, o1);
-    if (lane == 0) {
-      P[HD] = mx[r];
+    P[d] = ((opart[0][r][d] + opart[1][r][d]) + opart[2][r][d]) + opart[3][r][d];
+    if (d == 0) {
+      P[HD] = fmaxf(fmaxf(wred[0][0][r], wred[0][1][r]), fmaxf(wred[0][2][r], wred[0][3][r]));
       P[HD + 1] = ((wred[1][0][r] + wred[1][1][r]) + wred[1][2][r]) + wred[1][3][r];
     }
   }

@@ -1,0 +1,67 @@
+"""The draft model's few-row attention chunks (one or two rows per forward, head_dim 128)
+against a float64 attention over the GPU's own inputs.
+
+"What is Speculative Decoding and How Does a Draft Model Work?", section "#1": the draft
+proposes its tokens one forward at a time, each attending over the whole cache.  After a
+draft_step the test reads back the last forward's raw queries, the draft cache (keys rotated
+and rounded by the kernels, values stored by the QKV projection) and the attention output,
+rotates and rounds the queries as the precision contract does (oracle.model.rope, bf16), and
+evaluates the attention of every query row over the keys at or below its position in float64
+(oracle.model.attend).  The GPU output is that value rounded to bf16 after float32 sums: every
+element lies within one bf16 step of the rounded float64 value, and only a small share (those
+within float32 error of a rounding midpoint) may differ at all.  A dropped, doubled or
+misplaced key, a wrong mask or a wrong merge of the chunks moves whole rows by far more.  The
+cache holds 300 positions before the forwards, so they span several 64-key chunks with a
+ragged last one; K = 1 ends on the two-row catch-up forward (rows at L - 1 and L), K = 3 on a
+one-row forward at L + 2."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle.numerics import round_bf16
+from speculative_decoding_token_amd import binding as B
+from speculative_decoding_token_amd import runtime, synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_draft_attention_against_float64(K):
+    dshape = synth.SHAPES["qwen0p6b"].with_layers(1)
+    L, max_ctx = 301, 340
+    n_q, n_kv, hd = dshape.n_q_heads, dshape.n_kv_heads, dshape.head_dim
+    tw = synth.make_weights(dshape, 0, device="cuda")
+    dw = synth.make_weights(dshape, 1, std=0.05, device="cuda")
+    tk, tv = synth.make_kv_prefix(dshape, L, 0, device="cuda")
+    dk, dv = synth.make_kv_prefix(dshape, L - 1, 1, device="cuda")
+    prev, last = (int(x) for x in synth.make_tokens(2, dshape.vocab, 9))
+    eng = runtime.Engine(dshape, tw, dshape, dw, temperature=0.0, seed=5, max_ctx=max_ctx, max_k=K)
+    eng.set_schedule("stream")
+    eng.load_prefix(0, 0, tk, tv, L)
+    eng.load_prefix(1, 0, dk, dv, L - 1)
+    eng.set_last(torch.tensor([last], dtype=torch.int32, device="cuda"),
+                 torch.tensor([prev], dtype=torch.int32, device="cuda"))
+    buf = eng.buffers(1, K)
+    with eng._enter():
+        B.draft_step(eng.ctx, 1, K, 0, buf["draft"], buf["q"])
+    torch.cuda.synchronize()
+    rows = 2 if K == 1 else 1
+    pos = [L - 1, L] if K == 1 else [L + K - 1]
+    q_raw = eng.read_buffer(1, B.BUF_Q, (rows, n_q * hd)).double().cpu().numpy()
+    o_gpu = eng.read_buffer(1, B.BUF_ATTN, (rows, n_q * hd), torch.bfloat16).double().cpu().numpy()
+    cap = max_ctx + K + 2
+    ck = eng.read_buffer(1, B.BUF_CACHE_K, (n_kv, cap, hd), torch.bfloat16).double().cpu().numpy()
+    cv = eng.read_buffer(1, B.BUF_CACHE_V, (n_kv, cap, hd), torch.bfloat16).double().cpu().numpy()
+    spec = om.Spec.from_shape(dshape)
+    for i, p in enumerate(pos):
+        q = round_bf16(om.rope(q_raw[i].reshape(n_q, hd), p, spec.rope_theta))
+        o_ref = round_bf16(om.attend(q, ck[:, :p + 1], cv[:, :p + 1], n_kv).reshape(-1))
+        got = o_gpu[i]
+        # one bf16 step of each reference element (8 significant bits)
+        step = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 7)
+        worst = float(np.max(np.abs(got - o_ref) / step))
+        differ = float(np.mean(got != o_ref))
+        print(f"K={K} row {i} at {p}: worst {worst:.2f} bf16 steps, {differ:.4f} of elements differ")
+        assert worst <= 1.0, (i, worst)
+        assert differ <= 0.02, (i, differ)
