@@ -28,6 +28,50 @@ SPEC_DEVINL uint32_t bf16x2_pack(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// ---- wavefront reductions without LDS -------------------------------------------------------
+// The quad swaps (lane l with l ^ 1, then l ^ 2) and the half-row and row mirrors (DPP) pair the
+// lanes within each row of 16; the gfx950 permlane swaps exchange rows 0 <-> 1 and 2 <-> 3 (lane
+// l with l ^ 16) and the two halves of the wavefront (l with l ^ 32).  At every step both
+// partners already hold one value per group of lanes, so each adds (or takes the larger of) the
+// same two values and every lane of the row (of the wavefront) ends with the same result, with
+// no LDS round trip.  Callers keep every lane of the wavefront active.
+template <int CTRL>
+SPEC_DEVINL float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+SPEC_DEVINL float xor16_sum(float x) {  // x[l] + x[l ^ 16]
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+SPEC_DEVINL float xor32_sum(float x) {  // x[l] + x[l ^ 32]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+SPEC_DEVINL float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+SPEC_DEVINL float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+SPEC_DEVINL float row16_sum(float x) {  // over each row of 16 lanes
+  x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
+SPEC_DEVINL float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));
+  x = fmaxf(x, dpp_f32<0x4E>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  return x;
+}
+SPEC_DEVINL float wave_sum(float x) { return xor32_sum(xor16_sum(row16_sum(x))); }
+SPEC_DEVINL float wave_max(float x) { return xor32_max(xor16_max(row16_max(x))); }
+
 // Softmax weights of a 64-key attention chunk as A operands of the P V product on the bf16
 // MFMA.  Lane l holds query row l % 16 and, in s[kt][r], the score of key 16 kt + 4 (l / 16) + r
 // (already scaled, -inf where masked); mx is the row's chunk maximum.  P = exp(s - mx) stays
@@ -55,8 +99,7 @@ SPEC_DEVINL float p_operands(const f32x4_t (&s)[4], float mx, bf16x8_t (&pa)[2][
     lo[kt][0] = (uint32_t)r[0] | ((uint32_t)r[1] << 16);
     lo[kt][1] = (uint32_t)r[2] | ((uint32_t)r[3] << 16);
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = xor32_sum(xor16_sum(l));
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     pa[st][0] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[2 * st][0], hi[2 * st][1], hi[2 * st + 1][0], hi[2 * st + 1][1]));

@@ -15,10 +15,10 @@
 //   rows x * g, and each wavefront adds the rows' sum-of-squares partials into 1/rms itself (no
 //   workgroup barrier before the arithmetic) and rounds (x * g) / rms to bf16, the contract's
 //   rounding point;
-// * float32 products summed per lane in k order, then across the wavefront by a fixed xor
-//   butterfly; the 16 results per row and tile meet in LDS for the epilogues of the streamed
-//   projections (residual add with sum-of-squares partials and the next norm's x * g, SwiGLU,
-//   q / k staging and the value rows into the cache).
+// * float32 products summed per lane in k order, then across the wavefront by a fixed
+//   butterfly of DPP and permlane moves (no LDS); the 16 results per row and tile meet in LDS
+//   for the epilogues of the streamed projections (residual add with sum-of-squares partials
+//   and the next norm's x * g, SwiGLU, q / k staging and the value rows into the cache).
 //
 // A row's result depends only on that row, so a two-row forward computes each row exactly as a
 // one-row forward does.
@@ -109,13 +109,11 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
   // the argument it reads is fetched with the others
   if (a.skip && *a.skip) return;
   if (norm) {
-    // 1/rms of each input row: lane j adds partials j, j + 64 in order, then the butterfly
+    // 1/rms of each input row: lane j adds partials j, j + 64 in order, then the wavefront sum
 #pragma unroll
     for (int m = 0; m < GV_MAX_M; ++m) {
       if (m >= M) break;
-      float sum = ps[NORM ? m : 0][0] + ps[NORM ? m : 0][1];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      const float sum = wave_sum(ps[NORM ? m : 0][0] + ps[NORM ? m : 0][1]);
       const float rinv = 1.0f / sqrtf(sum / (float)K + a.eps);
 #pragma unroll
       for (int c = 0; c < NK; ++c) {
@@ -144,8 +142,7 @@ __global__ __launch_bounds__(GV_WAVES * 64) void gemv_kernel(StreamArgs a) {
             acc = fmaf(__uint_as_float(wv[e] & 0xFFFF0000u), __uint_as_float(xv[e] & 0xFFFF0000u), acc);
           }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        acc = wave_sum(acc);
         if (lane == 0) s_out[t][GV_RW * wave + i][m] = acc;
       }
   }

@@ -823,8 +823,7 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
         s[kt][rr] = v;
         mx = fmaxf(mx, v);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor32_max(xor16_max(mx));
     bf16x8_t pa[2][2];  // P = hi + lo, two bf16 operands per 32-key step
     const float l = p_operands(s, mx, pa);
     // this lane's rows of the output tile: 4g + rr
@@ -873,16 +872,6 @@ __global__ __launch_bounds__(256) void attn_chunk_mfma_kernel(AttnArgs a) {
 // row in float32 (maximum over the chunk, then exp(s - max)); P V: each thread's products over
 // its four keys, summed over the four rows of threads of a wavefront and then over the four
 // wavefronts in order.  Partials in the layout the combine kernel reads.
-SPEC_DEVINL float few_sum16(float x) {
-  // xor 1 and 2 within a quad, then the two quads of each half row and the two half rows:
-  // every lane of a row of 16 ends with the same sum
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
-  return x;
-}
-
 __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
   constexpr int HD = 128, C = ATTN_CHUNK, KP = HD + 8, HALF = HD / 2;
   constexpr int RM = ATTN_FEW_ROWS;
@@ -1003,13 +992,12 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += kf[v][e] * qv[e];
-        acc = few_sum16(acc);
+        acc = row16_sum(acc);
         const int p = c0 + (t >> 4) + 16 * v;
         s[v][r] = p <= L + r / G ? acc * a.scale : -__builtin_inff();
         mx[r] = fmaxf(mx[r], s[v][r]);
       }
-      mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 16, 64));
-      mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], 32, 64));
+      mx[r] = xor32_max(xor16_max(mx[r]));
     }
   }
   if (lane == 0) {
@@ -1045,12 +1033,9 @@ __global__ __launch_bounds__(256) void attn_chunk_few_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[r][e] += w * vf[v][e];
       }
+      lsum[r] = xor32_sum(xor16_sum(lsum[r]));
 #pragma unroll
-      for (int o2 = 16; o2 < 64; o2 <<= 1) {
-        lsum[r] += __shfl_xor(lsum[r], o2, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[r][e] += __shfl_xor(o[r][e], o2, 64);
-      }
+      for (int e = 0; e < 8; ++e) o[r][e] = xor32_sum(xor16_sum(o[r][e]));
     }
   }
   if (lane < 16) {
@@ -1117,8 +1102,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       lc[q] = c < nch ? P[c * (hd + 2) + hd + 1] : 0.0f;
       mx = fmaxf(mx, mc[q]);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_max(mx);
     float den = 0.0f;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -1129,8 +1113,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
         den += lc[q] * w;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    den = wave_sum(den);
     if (t == 0) s_den = den;
   }
   __syncthreads();

@@ -441,7 +441,7 @@ struct Gemm {
       }
     };
     // RMSNorm input: 1/rms of each row into LDS (wavefront w handles rows w and w + 8; lane j
-    // adds partials j, j + 64, ... in order, then a fixed xor butterfly); after a barrier the
+    // adds partials j, j + 64, ... in order, then the fixed wavefront sum); after a barrier the
     // resident slices of token row m = lane % 16 become bf16((x * g) * 1/rms)
     auto rms_to_lds = [&]() {
 #pragma unroll
@@ -450,8 +450,7 @@ struct Gemm {
         float sum = 0.0f;
 #pragma unroll
         for (int t = 0; t < SSP; ++t) sum += pss[rr][t];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        sum = wave_sum(sum);
         if (lane == 0 && r < M) lds_write_f32(inv0 + r * 4, 1.0f / sqrtf(sum / (float)K + a.eps));
       }
     };
@@ -483,7 +482,7 @@ struct Gemm {
     // Unit end: the 8 partial tiles meet in LDS.  Thread e < 256 takes token mm = e / 16 and
     // column c = e % 16 of the unit; in the D layout of the 16x16 MFMA that element is held
     // by lane (c / 4) * 16 + mm, entry c % 4.  The 16 columns of a token are 16 adjacent
-    // lanes, so the residual epilogue adds their squares with a fixed butterfly.
+    // lanes, so the residual epilogue adds their squares with a fixed row-of-16 sum (DPP).
     auto finish_unit = [&](int q) {  // q: the workgroup's q-th unit
       const int u = unit_of(a, q);
 #pragma unroll
@@ -521,9 +520,7 @@ struct Gemm {
             st<COH>(xp, xn);
             if (a.y_out) st<COH>((float*)a.y_out + (int64_t)mm * a.ld + n, xn * bf16_to_f32(((const bf16_t*)a.y_gain)[n]));
           }
-          float sq = xn * xn;
-#pragma unroll
-          for (int o = 8; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+          const float sq = row16_sum(xn * xn);
           if (live && c == 0 && a.ss_out) st<COH>(a.ss_out + (int64_t)mm * a.ss_ld + u, sq);
         } else if (live) {
           if (EPI == EPI_STORE) {
