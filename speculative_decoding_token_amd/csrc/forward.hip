@@ -89,8 +89,8 @@ SPEC_DEVINL void grid_sync(Sync& s, F issue) {
 
 // ---------------------------------------------------------------- embedding
 // Workgroup m < M gathers row m: x = E[token], y = x * gain of the first norm, and the row's
-// sum of squares (each thread adds its columns t, t + 512, ... in order; then a xor
-// butterfly per wavefront and the wavefront sums in order).
+// sum of squares (each thread adds its columns t, t + 512, ... in order; then a fixed sum per
+// wavefront by DPP and permlane moves, and the wavefront sums in order).
 SPEC_DEVINL void embed_step(const FwdArgs& a, char* sm) {
   const int m = blockIdx.x;
   if (m >= a.M) return;
@@ -107,8 +107,7 @@ SPEC_DEVINL void embed_step(const FwdArgs& a, char* sm) {
     st<true>(a.y + (int64_t)m * a.d + c, v * bf16_to_f32(g[c]));
     sq += v * v;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  sq = wave_sum(sq);
   float* red = (float*)sm;
   if (lane == 0) red[wave] = sq;
   __syncthreads();
@@ -324,8 +323,7 @@ struct Attn {
             s[kt][rr] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = xor32_max(xor16_max(mx));
         bf16x8_t pa[2][2];
         const float l = p_operands(s, mx, pa);
         int rowoff[4];
@@ -440,8 +438,7 @@ SPEC_DEVINL void combine_step(const FwdArgs& a, const int* s_len, char* red) {
         lc[q] = c < nch ? ld<true>(P + c * (HD + 2) + HD + 1) : 0.0f;
         mx = fmaxf(mx, mc[q]);
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      mx = wave_max(mx);
       float den = 0.0f;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -452,8 +449,7 @@ SPEC_DEVINL void combine_step(const FwdArgs& a, const int* s_len, char* red) {
           den += lc[q] * w;
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+      den = wave_sum(den);
       if (t == 0) *s_den = den;
     }
     __syncthreads();

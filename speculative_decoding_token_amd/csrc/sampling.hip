@@ -58,29 +58,26 @@ SPEC_DEVINL int next_pow2(int x) {
   return p;
 }
 
-SPEC_DEVINL uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+// The largest 64-bit key of the wavefront in every lane: the moves of wave_max (common.h) applied
+// to both halves of the key.
+template <int CTRL>
+SPEC_DEVINL uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
   return ((uint64_t)hi << 32) | lo;
 }
-SPEC_DEVINL uint64_t shfl_u64(uint64_t v, int src) {
-  const uint32_t lo = __shfl((uint32_t)v, src, 64), hi = __shfl((uint32_t)(v >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Sorts one key per lane of a wavefront, descending: afterwards lane j holds the j-th largest.
-SPEC_DEVINL uint64_t wave_sort_desc(uint64_t v, int lane) {
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, j);
-      const bool up = (lane & j) == 0;          // lower partner of the pair
-      const bool desc = (lane & k) == 0;        // this run sorts descending
-      const bool keep_max = (up == desc);
-      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-    }
-  }
-  return v;
+SPEC_DEVINL uint64_t wave_max_u64(uint64_t v) {
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0xB1>(v));
+  v = mx(v, dpp_u64<0x4E>(v));
+  v = mx(v, dpp_u64<0x141>(v));
+  v = mx(v, dpp_u64<0x140>(v));
+  const auto l16 = __builtin_amdgcn_permlane16_swap((int)(uint32_t)v, (int)(uint32_t)v, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), false, false);
+  v = mx(((uint64_t)(uint32_t)h16[0] << 32) | (uint32_t)l16[0], ((uint64_t)(uint32_t)h16[1] << 32) | (uint32_t)l16[1]);
+  const auto l32 = __builtin_amdgcn_permlane32_swap((int)(uint32_t)v, (int)(uint32_t)v, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), false, false);
+  return mx(((uint64_t)(uint32_t)h32[0] << 32) | (uint32_t)l32[0], ((uint64_t)(uint32_t)h32[1] << 32) | (uint32_t)l32[1]);
 }
 
 // ---------------------------------------------------------------- 1. segment top-k
@@ -371,11 +368,7 @@ __global__ __launch_bounds__(FIN_THREADS) void truncate_finish_kernel(TruncArgs 
       th = v > th ? v : th;
       bad |= a.bad[(int64_t)row * a.nseg + s];
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(th, m);
-      th = o > th ? o : th;
-    }
+    th = wave_max_u64(th);
     bad = __ballot(bad != 0) ? 1 : 0;
     if (t == 0) {
       s_theta = th;
