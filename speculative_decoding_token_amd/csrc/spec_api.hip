@@ -757,7 +757,12 @@ int run_head(spec_ctx* c, Model& m, int M, RowMap rm, const float* x, const floa
     lm.M = M;
     lm.out = logits;
     lm.ld = d.vocab;
-    LAUNCH(c, 16 * m.mi + PROF_LMHEAD, launch_stream_gemm(EPI_STORE, lm, c->ncu, c->stream));
+    // the draft's one or two rows take the vector-ALU kernel: a workgroup per 16 vocabulary rows
+    // (9496 at 151936), many resident per CU, instead of the ring's per-unit cross-wavefront
+    // reduction every 32 KB stage (0.6B tied table: 52.4 -> 48.1 us by events)
+    const bool gv = use_gemv(m, M) && gemv_supported(M, d.d_model, EPI_STORE, true, 2);
+    LAUNCH(c, 16 * m.mi + PROF_LMHEAD,
+           gv ? launch_gemv(EPI_STORE, lm, c->stream) : launch_stream_gemm(EPI_STORE, lm, c->ncu, c->stream));
     return SPEC_OK;
   }
   if (m.fp8) return fail(c, SPEC_E_UNSUPPORTED, "fp8 LM head outside the streamed projections");
