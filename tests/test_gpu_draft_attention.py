@@ -10,10 +10,10 @@ evaluates the attention of every query row over the keys at or below its positio
 (oracle.model.attend).  The GPU output is that value rounded to bf16 after float32 sums: every
 element lies within one bf16 step of the rounded float64 value, and only a small share (those
 within float32 error of a rounding midpoint) may differ at all.  A dropped, doubled or
-misplaced key, a wrong mask or a wrong merge of the chunks moves whole rows by far more.  The
-cache holds 300 positions before the forwards, so they span several 64-key chunks with a
-ragged last one; K = 1 ends on the two-row catch-up forward (rows at L - 1 and L), K = 3 on a
-one-row forward at L + 2."""
+misplaced key, a wrong mask or a wrong merge of the chunks moves whole rows by far more.  With
+300 cached positions the forwards span five 64-key chunks with a ragged last one; with 2600,
+41 chunks, the length of the workload's contexts and more.  K = 1 ends on the two-row catch-up
+forward (rows at L - 1 and L), K = 3 on a one-row forward at L + 2."""
 import numpy as np
 import pytest
 import torch
@@ -26,10 +26,10 @@ from speculative_decoding_token_amd import runtime, synth
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("K", [1, 3])
-def test_draft_attention_against_float64(K):
+@pytest.mark.parametrize("K,L", [(1, 301), (3, 301), (1, 2601), (3, 2601)])
+def test_draft_attention_against_float64(K, L):
     dshape = synth.SHAPES["qwen0p6b"].with_layers(1)
-    L, max_ctx = 301, 340
+    max_ctx = L + 39
     n_q, n_kv, hd = dshape.n_q_heads, dshape.n_kv_heads, dshape.head_dim
     tw = synth.make_weights(dshape, 0, device="cuda")
     dw = synth.make_weights(dshape, 1, std=0.05, device="cuda")
@@ -62,6 +62,6 @@ def test_draft_attention_against_float64(K):
         step = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 7)
         worst = float(np.max(np.abs(got - o_ref) / step))
         differ = float(np.mean(got != o_ref))
-        print(f"K={K} row {i} at {p}: worst {worst:.2f} bf16 steps, {differ:.4f} of elements differ")
+        print(f"K={K} L={L} row {i} at {p}: worst {worst:.2f} bf16 steps, {differ:.4f} of elements differ")
         assert worst <= 1.0, (i, worst)
         assert differ <= 0.02, (i, differ)
