@@ -18,8 +18,10 @@ recorded rocprofv3 counters, a teacher-forced upper bound (drafts = the target's
 continuation, every draft accepted), the same cycle sampled (T = 1, top_k 20, top_p 0.95) with
 and without the draft-probability control, the adaptive draft length and the cost gate, the
 fp8-weight cycle, the linear-attention state step, the stand-alone accept workload (64
-sequences, K = 8, the 151936-token vocabulary) against its roofline, and the CPU oracle timed
-on one full greedy cycle of the workload after a warm-up cycle.
+sequences, K = 8, the 151936-token vocabulary) against its roofline, the draft's one- and
+two-row projections on the vector ALUs against the MFMA weight-streaming kernels (per-launch
+times at M = 1 and 2 and the whole draft_step), and the CPU oracle timed on one full greedy
+cycle of the workload after a warm-up cycle.
 
 --weights fp8 runs the same cycle with the target's projections and LM head stored as OCP
 E4M3 codes with a float32 scale per output row (one byte per weight instead of two); the
@@ -59,6 +61,8 @@ def parse():
     ap.add_argument("--schedule", default=None, choices=["step", "stream", "forward"],
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
+    ap.add_argument("--no-crossover", action="store_true",
+                    help="skip the draft projections' vector-ALU vs MFMA comparison")
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                     help="target projection weights: bf16, or OCP E4M3 codes with a float32 scale per row")
@@ -328,9 +332,11 @@ def main():
     tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
     dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
     SWEEP_K, SWEEP_REPS = (1, 2, 3, 4, 5, 6, 7, 8, 0), 6  # K = 0 (no draft) last: the draft cache then lags
+    CROSS_P, CROSS_T = 3, 6  # draft-projection comparison: profiled cycles per K, timed cycles
+    CROSS_CYCLES = 2 * (2 + 2 * CROSS_P + CROSS_T + 1)
     max_k = max(K, max(SWEEP_K))
     n_cycles = args.warmup + (2 + args.repeats) * args.steps + args.profile_steps + 2  # timed runs + sync loop
-    max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + 8
+    max_ctx = L + n_cycles * (K + 1) + len(SWEEP_K) * SWEEP_REPS * (max_k + 1) + CROSS_CYCLES * (K + 1) + 8
     Bn = args.batch
     if Bn > 1:
         if Bn * (K + 1) > 16:
@@ -437,6 +443,50 @@ def main():
     if dom["slot"] != "target.forward":
         eng.profile_repeat(dom["slot"], 1)
     eng.profile(False)
+    # The draft's one- and two-row projections on the vector ALUs (the default) against the MFMA
+    # weight-streaming kernels the target uses: per-launch times at M = 2 (the first forward of a
+    # draft_step, the catch-up row and the new one) and M = 1 (the others), and the whole
+    # draft_step at K, HIP events around each launch.
+    crossover = None
+    if not args.no_crossover and Bn == 1 and sched == "stream" and K >= 2:
+        classes = ("qkv", "o_proj", "gate_up", "down", "lm_head")
+        crossover = {"how": f"per-launch µs by HIP events over {CROSS_P} profiled cycles at K = 1 (M = 2) "
+                            f"and K = {K} (one M = 2 forward, then M = 1), draft_step ms by events over "
+                            f"{CROSS_T} graph-replayed cycles"}
+        for kind, on in (("vector_alu", True), ("mfma_stream", False)):
+            eng.use_gemv(on)
+            eng.cycle(1, 1, rnd)
+            eng.cycle(1, K, rnd + 1)
+            rnd += 2
+            eng.profile(True)
+            for _ in range(CROSS_P):
+                eng.cycle(1, 1, rnd)
+                rnd += 1
+            p1 = eng.profile_read()
+            for _ in range(CROSS_P):
+                eng.cycle(1, K, rnd)
+                rnd += 1
+            pk = eng.profile_read()
+            eng.profile(False)
+            row = {}
+            for c in classes:
+                a, b = p1.get("draft." + c), pk.get("draft." + c)
+                if not a or not b:
+                    continue
+                t2 = a["ms"] / a["launches"]
+                n1 = b["launches"] - a["launches"]
+                t1 = (b["ms"] - a["launches"] * t2) / n1 if n1 > 0 else float("nan")
+                row[c] = {"M2_us": t2 * 1e3, "M1_us": t1 * 1e3}
+            ev_c, ms = {}, []
+            eng.cycle(1, K, rnd, events=ev_c)
+            rnd += 1
+            for _ in range(CROSS_T):
+                eng.cycle(1, K, rnd, events=ev_c)
+                rnd += 1
+                ms.append(ev_c["draft"][0].elapsed_time(ev_c["draft"][1]))
+            row["draft_step_ms"] = sorted(ms)[len(ms) // 2]
+            crossover[kind] = row
+        eng.use_gemv(True)
     dprof = prof.get(dom["slot"], {"ms": float("nan"), "launches": 1})
     dom_ms = dprof["ms"] / dprof["launches"]
     # the one-launch forward moves the whole verify's bytes (weights, cache, logits)
@@ -626,6 +676,7 @@ def main():
                                + f"{args.profile_steps} profiled steps after the timed ones"},
         "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
                     for k, v in prof.items()},
+        "draft_projections": crossover,
         "teacher_forced": teacher,
         "adaptive_depth": adaptive,
         "fp8_weights": fp8_run,

@@ -384,6 +384,17 @@ int spec_profile_read(spec_ctx* ctx, double* ms, int64_t* launches);
  * needs a non-default stream.  0: launch kernel by kernel. */
 int spec_use_graphs(spec_ctx* ctx, int32_t enable);
 
+/* Which projections the draft model's one- and two-row forwards take on SPEC_SCHED_STREAM
+ * ("Speculative Decoding on Apple Silicon: 119% Faster...", section "The original result:
+ * Qwen3-8B and a 0.6B draft": the draft runs one token at a time, so its projections move a few
+ * MB for one or two rows).  enable != 0 (the default): the vector-ALU projections (one
+ * workgroup per 16 weight rows, every load issued at once); 0: the MFMA weight-streaming
+ * projections the target uses, rows padded to 16.  Both compute the same contract (each row's
+ * results within float32 summation order of the other's); the switch exists to measure where
+ * one overtakes the other.  Takes effect at the next draft_step; graphs are kept per setting.
+ * Errors: SPEC_E_INVAL for a null context. */
+int spec_use_gemv(spec_ctx* ctx, int32_t enable);
+
 /* Schedule of the forwards of bf16 models over at most 16 rows.
  *   SPEC_SCHED_STEP    one launch per step, one workgroup per 16-row tile of each projection;
  *   SPEC_SCHED_STREAM  (the default) one launch per step, projections streaming their weights

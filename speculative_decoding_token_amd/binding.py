@@ -38,6 +38,7 @@ EXPORTED = [
     "spec_sample", "spec_accept_lists", "spec_philox_uniforms", "spec_ngram_match",
     "spec_profile", "spec_profile_repeat", "spec_profile_read", "spec_use_graphs", "spec_load_history",
     "spec_gate_init", "spec_gate_choose", "spec_gate_update", "spec_set_schedule", "spec_trace_forward",
+    "spec_use_gemv",
     "spec_depth_init", "spec_depth_choose", "spec_depth_update", "spec_gdn_commit_forward",
     "spec_debug_read", "spec_truncate_noalloc", "spec_draft_controls",
 ]
@@ -162,6 +163,7 @@ def lib(path: str = LIB_PATH):
         "spec_profile_read": ([P, P, P], C.c_int),
         "spec_use_graphs": ([P, I32], C.c_int),
         "spec_set_schedule": ([P, I32], C.c_int),
+        "spec_use_gemv": ([P, I32], C.c_int),
         "spec_trace_forward": ([P, P, C.c_int64, C.POINTER(C.c_int32)], C.c_int),
         "spec_load_history": ([P, I32, P, I32], C.c_int),
         "spec_gate_init": ([C.POINTER(spec_gate), I32, C.POINTER(C.c_double), C.c_double, I32], C.c_int),
@@ -445,6 +447,10 @@ def spec_set_schedule(ctx: int, schedule: str) -> None:
 
 def spec_use_graphs(ctx: int, enable: bool) -> None:
     _check(lib().spec_use_graphs(ctx, int(enable)), ctx)
+
+
+def spec_use_gemv(ctx: int, enable: bool) -> None:
+    _check(lib().spec_use_gemv(ctx, int(enable)), ctx)
 
 
 class Depth:

@@ -1075,8 +1075,10 @@ template <typename F>
 int run_graphed(spec_ctx* c, int kind, int batch, int k, const void* const key[8], F enqueue) {
   // cooperative launches stay out of captured graphs
   if (c->prof || !c->graphs || c->stream == nullptr || c->sched == SPEC_SCHED_FORWARD) return enqueue();
+  // graphs are kept per schedule and per projection choice of the draft model
+  const int gkind = kind + 16 * c->sched + 64 * (c->draft.gemv ? 1 : 0);
   for (auto& g : c->gcache) {
-    if (g.kind == kind + 16 * c->sched && g.batch == batch && g.k == k && !memcmp(g.ptrs, key, sizeof g.ptrs)) {
+    if (g.kind == gkind && g.batch == batch && g.k == k && !memcmp(g.ptrs, key, sizeof g.ptrs)) {
       HIPCHK(c, hipGraphLaunch(g.exec, c->stream));
       return SPEC_OK;
     }
@@ -1091,7 +1093,7 @@ int run_graphed(spec_ctx* c, int kind, int batch, int k, const void* const key[8
   }
   if (e != hipSuccess) return fail(c, SPEC_E_HIP, "graph capture: %s", hipGetErrorString(e));
   GraphEntry g;
-  g.kind = kind + 16 * c->sched;
+  g.kind = gkind;
   g.batch = batch;
   g.k = k;
   memcpy(g.ptrs, key, sizeof g.ptrs);
@@ -1506,6 +1508,12 @@ int spec_profile_read(spec_ctx* c, double* ms, int64_t* launches) {
     c->ev_free.push_back(r.b);
   }
   c->recs.clear();
+  return SPEC_OK;
+}
+
+int spec_use_gemv(spec_ctx* c, int32_t enable) {
+  if (need_ctx(c)) return SPEC_E_INVAL;
+  c->draft.gemv = enable != 0 && c->draft.present;
   return SPEC_OK;
 }
 

@@ -308,6 +308,11 @@ class Engine:
     def use_graphs(self, enable: bool):
         B.spec_use_graphs(self.ctx, enable)
 
+    def use_gemv(self, enable: bool):
+        """The draft model's one- and two-row projections on the vector ALUs (True, the
+        default) or on the MFMA weight-streaming kernels (False)."""
+        B.spec_use_gemv(self.ctx, enable)
+
     def stats(self):
         return B.spec_get_stats(self.ctx)
 

@@ -205,9 +205,10 @@ def test_0p6b_full_depth_draft_step(temp):
 def test_0p6b_full_depth_draft_forward_logits(k):
     """The k-th draft forward of a greedy draft_step (the first runs two rows, the tokens at L-1
     and L; the later ones one row, the previous draft) of the 28-layer 0.6B-shape draft: its
-    logits row in the streamed schedule (the vector-ALU projections of one and two rows) and in
-    the per-tile schedule (the MFMA projections), against each other and against the oracle
-    fed the same drafts, beside the oracle's own float32 drift."""
+    logits row in the streamed schedule (the vector-ALU projections of one and two rows), in the
+    streamed schedule with those projections on the MFMA weight-streaming kernels
+    (spec_use_gemv off) and in the per-tile schedule (the MFMA projections), against each other
+    and against the oracle fed the same drafts, beside the oracle's own float32 drift."""
     ts = synth.SHAPES["qwen8b"].with_layers(1)
     ds = synth.SHAPES["qwen0p6b"]
     L = 2048
@@ -217,9 +218,10 @@ def test_0p6b_full_depth_draft_forward_logits(k):
     dk, dv = synth.make_kv_prefix(ds, L - 1, 1, device="cuda")
     prev, last = (int(x) for x in synth.make_tokens(2, ds.vocab, 9))
     got, drafts = {}, {}
-    for sched in ("stream", "step"):
+    for sched in ("stream", "step", "stream_mfma"):
         eng = runtime.Engine(ts, tw, ds, dw, temperature=0.0, seed=5, max_ctx=L + 40, max_k=k)
-        eng.set_schedule(sched)
+        eng.set_schedule("stream" if sched == "stream_mfma" else sched)
+        eng.use_gemv(sched != "stream_mfma")
         eng.load_prefix(0, 0, tk, tv, L)
         eng.load_prefix(1, 0, dk, dv, L - 1)
         eng.set_last(torch.tensor([last], dtype=torch.int32, device="cuda"),
@@ -243,9 +245,12 @@ def test_0p6b_full_depth_draft_forward_logits(k):
     r32 = om.forward_tokens(spec32, W, kv32, toks)[-1]
     e_stream = float(row_rel_err(got["stream"], ref))
     e_step = float(row_rel_err(got["step"], ref))
+    e_mfma = float(row_rel_err(got["stream_mfma"], ref))
     drift = float(row_rel_err(r32, ref))
-    log(f"0.6B 28 layers, draft forward {k}: stream {e_stream:.2e}, step {e_step:.2e} (drafts "
-        f"{'equal' if drafts['stream'] == drafts['step'] else 'differ'}); oracle float32 drift {drift:.2e}")
+    log(f"0.6B 28 layers, draft forward {k}: stream {e_stream:.2e}, step {e_step:.2e}, stream on MFMA "
+        f"{e_mfma:.2e} (drafts {'equal' if drafts['stream'] == drafts['step'] == drafts['stream_mfma'] else 'differ'}); "
+        f"oracle float32 drift {drift:.2e}")
     assert e_stream <= max(RTOL_BF16, 2.0 * drift)
-    if drafts["stream"] == drafts["step"]:
-        assert e_step <= max(RTOL_BF16, 2.0 * drift)
+    for other, e in (("step", e_step), ("stream_mfma", e_mfma)):
+        if drafts["stream"] == drafts[other]:
+            assert e <= max(RTOL_BF16, 2.0 * drift), other
