@@ -18,7 +18,9 @@ recorded rocprofv3 counters, a teacher-forced upper bound (drafts = the target's
 continuation, every draft accepted), the same cycle sampled (T = 1, top_k 20, top_p 0.95) with
 and without the draft-probability control, the adaptive draft length and the cost gate, the
 fp8-weight cycle, the linear-attention state step, the stand-alone accept workload (64
-sequences, K = 8, the 151936-token vocabulary) against its roofline, the draft's one- and
+sequences, K = 8, the 151936-token vocabulary) against its roofline, the n-gram workload
+replayed over a copy-heavy stream after an 8192-token context (the library's lookup and gate,
+steps costed with the 9B-shape verify measured at each draft length), the draft's one- and
 two-row projections on the vector ALUs against the MFMA weight-streaming kernels (per-launch
 times at M = 1 and 2 and the whole draft_step), and the CPU oracle timed on one full greedy
 cycle of the workload after a warm-up cycle.
@@ -61,6 +63,7 @@ def parse():
     ap.add_argument("--schedule", default=None, choices=["step", "stream", "forward"],
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
+    ap.add_argument("--no-ngram", action="store_true", help="skip the n-gram replay on the 9B shape")
     ap.add_argument("--no-crossover", action="store_true",
                     help="skip the draft projections' vector-ALU vs MFMA comparison")
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
@@ -292,6 +295,105 @@ def accept_workload_run(torch, synth, B, batch=64, K=8, sigma=1.0, copies=3, rep
             "acceptance_last_call": acc,
             "timing": f"HIP events around {reps} calls back to back (rotating {copies} input copies); the "
                       f"split into truncation and sample + accept is the median of single calls"}
+
+
+def ngram_replay_run(torch, synth, runtime, B, n_ctx=8192, n_gen=8192, k_max=8, n_min=3, max_match=16,
+                     reps=6, seed=5):
+    """The n-gram workload replayed ("Speculative decoding on Apple Silicon" (OptiQ docs),
+    sections "N-gram lookup: any model" and "Methodology": conversations replayed through the
+    real drafter and gate, each step costed with verify timings measured per draft length).
+    A copy-heavy stream of n_ctx + n_gen tokens (synth.make_copy_stream) plays the target's
+    output after an n_ctx-token context: at each step the library's n-gram lookup
+    (spec_ngram_match, longest-then-latest match of at least n_min tokens over the history so
+    far) proposes up to k drafts, where k comes from the library's acceptance gate
+    (spec_gate_*, fed the measured costs) or is k_max with the gate off; drafts are accepted
+    while they equal the stream's next tokens, and the step emits those plus one.  A step costs
+    the 9B-shape verify at the number of drafts found (HIP events, graph replay, an n_ctx-entry
+    cache) plus one lookup; plain decoding costs the verify at k = 0 per token."""
+    import dataclasses
+    import numpy as np
+    shape = dataclasses.replace(synth.SHAPES["qwen9b_mtp"], mtp=False)
+    stream = synth.make_copy_stream(n_ctx + n_gen, shape.vocab, seed=seed).astype(np.int32)
+    w = synth.make_weights(shape, 0, device="cuda")
+    L = n_ctx - 1
+    kc, vc = synth.make_kv_prefix(shape, L, 0, device="cuda")
+    eng = runtime.Engine(shape, w, temperature=0.0, seed=0, max_ctx=n_ctx + reps * (k_max + 1) * (k_max + 2) + 16,
+                         max_k=k_max, drafter="ngram", ngram=(n_min, max_match))
+    eng.load_prefix(0, 0, kc, vc, L)
+    eng.load_history(0, torch.from_numpy(stream[:L].copy()).cuda())
+    eng.set_last(torch.tensor([int(stream[L])], dtype=torch.int32, device="cuda"))
+    # verify latency per draft length (explicit drafts: the verify alone)
+    ev, verify_ms = {}, []
+    rnd = 0
+    for k in range(k_max + 1):
+        d = torch.from_numpy(stream[L + 1: L + 1 + k].copy()).view(1, k).cuda() if k else None
+        ms = []
+        for i in range(reps):
+            eng.cycle(1, k, rnd, drafts=d, events=ev)
+            rnd += 1
+            if i > 0:
+                ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
+        verify_ms.append(sorted(ms)[len(ms) // 2])
+    eng.close()
+    del w, kc, vc
+    # the lookup at every position of the generated part, k_max drafts each (a shorter k takes
+    # a prefix: the match does not depend on k), contexts as rows of the stream
+    N = n_ctx + n_gen
+    full = torch.from_numpy(stream.copy()).cuda()
+    bt = 256
+    ctx = full.view(1, N).expand(bt, N).contiguous()
+    drafts_all = np.zeros((n_gen, k_max), np.int32)
+    found_all = np.zeros(n_gen, np.int32)
+    dr = torch.empty((bt, k_max), dtype=torch.int32, device="cuda")
+    nf = torch.empty(bt, dtype=torch.int32, device="cuda")
+    mt = torch.empty((bt, 2), dtype=torch.int32, device="cuda")
+    for t0 in range(0, n_gen, bt):
+        n = min(bt, n_gen - t0)
+        lens = torch.arange(n_ctx + t0, n_ctx + t0 + bt, dtype=torch.int32, device="cuda")
+        B.spec_ngram_match(ctx, lens, bt, N, k_max, n_min, max_match, dr, nf, mt)
+        torch.cuda.synchronize()
+        drafts_all[t0:t0 + n] = dr[:n].cpu().numpy()
+        found_all[t0:t0 + n] = nf[:n].cpu().numpy()
+    # one lookup's time over the whole history (one sequence)
+    l1 = torch.tensor([N - 1], dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lk = []
+    for _ in range(reps):
+        e0.record()
+        B.spec_ngram_match(ctx[:1].contiguous(), l1, 1, N, k_max, n_min, max_match, dr, nf, mt)
+        e1.record()
+        torch.cuda.synchronize()
+        lk.append(e0.elapsed_time(e1))
+    lookup_ms = sorted(lk)[len(lk) // 2]
+
+    def replay(gate_on):
+        # the lookup costs a step, not a draft: the gate's per-draft cost is zero
+        gate = B.Gate(k_max, verify_ms, 0.0, gate_on)
+        t, cost, steps, drafted, accepted = 0, 0.0, 0, 0, 0
+        while t < n_gen:
+            k = gate.choose()
+            f = int(min(found_all[t], k))
+            a = 0
+            while a < f and t + a < n_gen and drafts_all[t, a] == stream[n_ctx + t + a]:
+                a += 1
+            gate.update(a, f)
+            cost += verify_ms[f] + (lookup_ms if k > 0 else 0.0)
+            drafted += f
+            accepted += a
+            steps += 1
+            t += a + 1
+        return {"tok_s": t / cost * 1e3, "steps": steps, "tokens_per_step": t / steps,
+                "drafts_per_step": drafted / steps, "acceptance": accepted / drafted if drafted else 0.0}
+
+    plain = 1e3 / verify_ms[0]
+    g, ng = replay(True), replay(False)
+    return {"target": "9B shape (32 layers, d 4096, 32/8 heads, FFN 12288, vocab 151936), bf16",
+            "context": n_ctx, "generated": n_gen, "n_min": n_min, "max_match": max_match, "k_max": k_max,
+            "stream": "synth.make_copy_stream: 32-256-token spans, 40% copies of earlier windows, 60% uniform",
+            "verify_ms_by_k": verify_ms, "lookup_ms": lookup_ms, "plain_tok_s": plain,
+            "gate": dict(g, speedup=g["tok_s"] / plain), "no_gate": dict(ng, speedup=ng["tok_s"] / plain),
+            "how": "the stream plays the target's output; drafts accepted while equal to it; each step costs "
+                   "the measured verify at the drafts found plus one lookup"}
 
 
 def main():
@@ -646,6 +748,7 @@ def main():
     from speculative_decoding_token_amd import binding as SB
     gdn_run = gdn_state_run(torch, synth, SB, K)
     accept_run = accept_workload_run(torch, synth, SB) if not args.no_accept_workload else None
+    ngram_run = ngram_replay_run(torch, synth, runtime, SB) if not args.no_ngram and Bn == 1 and not fp8 else None
 
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -677,6 +780,7 @@ def main():
         "kernels": {k: {"avg_us": v["ms"] / v["launches"] * 1e3, "launches_per_step": v["launches"] / args.profile_steps}
                     for k, v in prof.items()},
         "draft_projections": crossover,
+        "ngram_replay": ngram_run,
         "teacher_forced": teacher,
         "adaptive_depth": adaptive,
         "fp8_weights": fp8_run,
