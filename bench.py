@@ -20,7 +20,10 @@ and without the draft-probability control, the adaptive draft length and the cos
 fp8-weight cycle, the linear-attention state step, the stand-alone accept workload (64
 sequences, K = 8, the 151936-token vocabulary) against its roofline, the n-gram workload
 replayed over a copy-heavy stream after an 8192-token context (the library's lookup and gate,
-steps costed with the 9B-shape verify measured at each draft length), the draft's one- and
+steps costed with the 9B-shape verify measured at each draft length), the 27B-shape target
+with the 0.8B-shape draft (4096-token context, K = 4 cycles, the verify at K = 1, 2, 4, 8, 16)
+and the 9B-shape target with its MTP layer drafting (K = 2 cycles, the verify at K = 1..4),
+the draft's one- and
 two-row projections on the vector ALUs against the MFMA weight-streaming kernels (per-launch
 times at M = 1 and 2 and the whole draft_step), and the CPU oracle timed on one full greedy
 cycle of the workload after a warm-up cycle.
@@ -64,6 +67,8 @@ def parse():
                     help="forward schedule of the bf16 models (default: the library's)")
     ap.add_argument("--no-k-sweep", action="store_true", help="skip the verify latency vs K sweep")
     ap.add_argument("--no-ngram", action="store_true", help="skip the n-gram replay on the 9B shape")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 27B (0.8B draft) and 9B (MTP layer) workloads")
     ap.add_argument("--no-crossover", action="store_true",
                     help="skip the draft projections' vector-ALU vs MFMA comparison")
     ap.add_argument("--no-adaptive", action="store_true", help="skip the adaptive draft length runs")
@@ -295,6 +300,74 @@ def accept_workload_run(torch, synth, B, batch=64, K=8, sigma=1.0, copies=3, rep
             "acceptance_last_call": acc,
             "timing": f"HIP events around {reps} calls back to back (rotating {copies} input copies); the "
                       f"split into truncation and sample + accept is the median of single calls"}
+
+
+def config_run(torch, synth, runtime, name, tshape, dshape, L, ks, k_cycle, cycles=12, reps=5, drafter=None):
+    """One more workload of the pages at its full size: cycles per second at k_cycle (greedy,
+    graph replay, HIP events around each call, the first cycles untimed) and the verify's
+    latency and HBM rate at each k in ks (explicit drafts, or with the MTP drafter, which
+    catches up from every verify, its own drafts; the verify timed alone either way)."""
+    t0 = time.perf_counter()
+    tw = synth.make_weights(tshape, 0, device="cuda")
+    dw = synth.make_weights(dshape, 0, device="cuda") if dshape is not None else None
+    tk, tv = synth.make_kv_prefix(tshape, L, 0, device="cuda")
+    kmax = max(max(ks), k_cycle)
+    max_ctx = L + (cycles + 2 + reps * len(ks)) * (kmax + 1) + 8
+    eng = runtime.Engine(tshape, tw, dshape, dw, temperature=0.0, seed=0, max_ctx=max_ctx, max_k=kmax,
+                         drafter=drafter)
+    eng.load_prefix(0, 0, tk, tv, L)
+    st = synth.make_tokens(2, tshape.vocab, 0, tag="start")
+    hidden = None
+    if dshape is not None:
+        dk, dv = synth.make_kv_prefix(dshape, L - 1, 0, device="cuda")
+        eng.load_prefix(1, 0, dk, dv, L - 1)
+    if drafter == "mtp":
+        # the head's own cache over the same prefix, and a hidden row standing in for the
+        # target's at L - 1
+        mk, mv = synth.make_kv_prefix(tshape, L, 0, device="cuda", tag="mtp-prefix", n_layers=1)
+        eng.load_prefix(2, 0, mk, mv, L)
+        g = torch.Generator(device="cpu").manual_seed(5)
+        hidden = torch.randn((1, tshape.d_model), generator=g, dtype=torch.float32).cuda()
+    eng.set_last(torch.tensor([int(st[1])], dtype=torch.int32, device="cuda"),
+                 torch.tensor([int(st[0])], dtype=torch.int32, device="cuda"), hidden=hidden)
+    ev, rnd = {}, 0
+    out = {"target": f"{tshape.name}: {tshape.n_layers} layers, d {tshape.d_model}, {tshape.n_q_heads}/"
+                     f"{tshape.n_kv_heads} heads, FFN {tshape.d_ffn}, vocab {tshape.vocab}, bf16",
+           "drafter": drafter or (f"{dshape.name}: {dshape.n_layers} layers, d {dshape.d_model}" if dshape else "none"),
+           "context": L}
+    # cycles at k_cycle
+    for _ in range(2):
+        eng.cycle(1, k_cycle, rnd)
+        rnd += 1
+    torch.cuda.synchronize()
+    tt = time.perf_counter()
+    emitted, acc = 0, 0
+    for _ in range(cycles):
+        c = eng.cycle(1, k_cycle, rnd)
+        rnd += 1
+        emitted += len(c.tokens[0])
+        acc += c.n[0]
+    el = time.perf_counter() - tt
+    out["cycle"] = {"k": k_cycle, "tok_s": emitted / el, "ms_per_cycle": el / cycles * 1e3,
+                    "acceptance": acc / (k_cycle * cycles)}
+    vk = {}
+    for k in ks:
+        d = None
+        if k and drafter != "mtp":
+            d = torch.from_numpy(synth.make_tokens(k, tshape.vocab, k, tag="vk").astype("int32")).view(1, k).cuda()
+        ms = []
+        for i in range(reps):
+            eng.cycle(1, k, rnd, drafts=d, events=ev)
+            rnd += 1
+            if i > 0:
+                ms.append(ev["verify"][0].elapsed_time(ev["verify"][1]))
+        m = sorted(ms)[len(ms) // 2]
+        vb = verify_bytes(tshape, k, L)
+        vk[str(k)] = {"verify_ms": m, "GBps": vb / (m * 1e-3) / 1e9, "frac_peak": vb / (m * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    out["verify_by_k"] = vk
+    out["setup_and_run_s"] = time.perf_counter() - t0
+    eng.close()
+    return out
 
 
 def ngram_replay_run(torch, synth, runtime, B, n_ctx=8192, n_gen=8192, k_max=8, n_min=3, max_match=16,
@@ -748,7 +821,17 @@ def main():
     from speculative_decoding_token_amd import binding as SB
     gdn_run = gdn_state_run(torch, synth, SB, K)
     accept_run = accept_workload_run(torch, synth, SB) if not args.no_accept_workload else None
+    # the headline workload's peak, before the other workloads allocate their models
+    peak_gb = torch.cuda.max_memory_allocated() / 1e9
     ngram_run = ngram_replay_run(torch, synth, runtime, SB) if not args.no_ngram and Bn == 1 and not fp8 else None
+    configs = None
+    if not args.no_configs and Bn == 1 and not fp8:
+        configs = {
+            "27b_0p8b": config_run(torch, synth, runtime, "27b", synth.SHAPES["qwen27b"], synth.SHAPES["qwen0p8b"],
+                                   4096, (1, 2, 4, 8, 16), 4),
+            "9b_mtp": config_run(torch, synth, runtime, "9b_mtp", synth.SHAPES["qwen9b_mtp"], None, 2048,
+                                 (1, 2, 3, 4), 2, drafter="mtp"),
+        }
 
     out = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -781,12 +864,13 @@ def main():
                     for k, v in prof.items()},
         "draft_projections": crossover,
         "ngram_replay": ngram_run,
+        "configs": configs,
         "teacher_forced": teacher,
         "adaptive_depth": adaptive,
         "fp8_weights": fp8_run,
         "linear_attention_state": gdn_run,
         "accept_workload": accept_run,
-        "peak_device_memory_GB": torch.cuda.max_memory_allocated() / 1e9,
+        "peak_device_memory_GB": peak_gb,
         "setup_s": setup_s,
     }
     if not args.no_cpu_baseline and Bn == 1 and not fp8:

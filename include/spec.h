@@ -395,7 +395,8 @@ int spec_use_graphs(spec_ctx* ctx, int32_t enable);
  * Errors: SPEC_E_INVAL for a null context. */
 int spec_use_gemv(spec_ctx* ctx, int32_t enable);
 
-/* Schedule of the forwards of bf16 models over at most 16 rows.
+/* Schedule of the forwards of bf16 models over at most 16 rows (the streamed projections also
+ * take 17 to 32 rows, as two launches of at most 16 rows each).
  *   SPEC_SCHED_STEP    one launch per step, one workgroup per 16-row tile of each projection;
  *   SPEC_SCHED_STREAM  (the default) one launch per step, projections streaming their weights
  *                      through an LDS ring with one workgroup per compute unit;

@@ -265,13 +265,17 @@ struct StreamArgs {
   int layer;
   RowMap rm;
   const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
+  // the forward's row of this launch's row 0 (launches of more than 16 rows run as passes of at
+  // most 16): the value rows' cache positions follow it
+  int row0;
   // EPI_QKV, per-launch projections: when > 0, the chunk count of the attention launch that
   // follows (grid nchunk x n_kv x batch), whose cached rows of this layer the workgroups with
   // one unit fewer than the others touch before they end (a pre-read, nothing is written)
   int pf_nchunk;
 };
-// Whether M rows and reduction length K are covered.  bf16 weights: K in whole stages (1024;
-// 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 3072, 4096, 5120}.  fp8 weights
+// Whether M rows and reduction length K are covered (M <= 32: more than 16 rows run as two
+// launches, rows 0..15 and 16..M-1, each streaming the weights).  bf16 weights: K in whole
+// stages (1024; 512 for SwiGLU), normalized inputs only for K in {1024, 2048, 3072, 4096, 5120}.  fp8 weights
 // (wbytes 1): stages of 2048 (1024 for SwiGLU), resident inputs for K in {2048, 4096}, streamed
 // inputs for the residual epilogue, and at most units_per_wg * tiles * 16 <= 1024 row scales
 // per workgroup.

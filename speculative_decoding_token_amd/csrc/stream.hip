@@ -80,7 +80,7 @@ const void* select(int epi, int nst, int wbytes) {
 }  // namespace
 
 bool stream_supported(int M, int K, int epi, bool norm, int wbytes, int units_per_wg) {
-  if (M < 1 || M > 16 || (wbytes != 1 && wbytes != 2)) return false;
+  if (M < 1 || M > 32 || (wbytes != 1 && wbytes != 2)) return false;
   const int nst = nst_of(epi, K, wbytes);
   if (nst < 0) return false;
   if (wbytes == 1 && units_per_wg * (epi == EPI_SWIGLU ? 2 : 1) * 16 > sk::SCALE_MAX) return false;
@@ -118,10 +118,29 @@ hipError_t launch_stream_gemm(int epi, const StreamArgs& a, int grid, hipStream_
     return hipErrorInvalidValue;
   const void* k = select(epi, nst_of(epi, a.K, wb), wb);
   if (!k) return hipErrorInvalidValue;
-  StreamArgs copy = a;
-  copy.wbytes = wb;
-  void* args[] = {&copy};
-  return hipLaunchKernel(k, dim3(g), dim3(sk::SNW * 64), args, stream_lds_bytes(), st);
+  // more than 16 rows: passes of at most 16 (rows 0..15, then the rest), each its own launch
+  // over the whole weight stream, every row computed as in a single pass
+  for (int r0 = 0; r0 < a.M; r0 += 16) {
+    StreamArgs copy = a;
+    copy.wbytes = wb;
+    copy.M = std::min(16, a.M - r0);
+    copy.row0 = a.row0 + r0;
+    if (r0 > 0) {
+      const int64_t xr = (int64_t)r0 * a.K * (a.ss_in ? 4 : 2);
+      copy.x = (const char*)a.x + xr;
+      if (a.ss_in) copy.ss_in = a.ss_in + (int64_t)r0 * a.ss_ld;
+      if (a.out) copy.out = a.out + (int64_t)r0 * a.ld;
+      if (a.ss_out) copy.ss_out = a.ss_out + (int64_t)r0 * a.ss_ld;
+      if (a.y_out) copy.y_out = (float*)a.y_out + (int64_t)r0 * a.ld;
+      if (a.h) copy.h = (bf16_t*)a.h + (int64_t)r0 * a.rows0;
+      if (a.q_stage) copy.q_stage = a.q_stage + (int64_t)r0 * a.rows0;
+      if (a.k_stage) copy.k_stage = a.k_stage + (int64_t)r0 * a.rows1;
+    }
+    void* args[] = {&copy};
+    const hipError_t e = hipLaunchKernel(k, dim3(g), dim3(sk::SNW * 64), args, stream_lds_bytes(), st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace spec

@@ -536,8 +536,9 @@ struct Gemm {
               st<COH>(a.k_stage + (int64_t)mm * a.rows1 + n, v[0]);
             } else {
               const CacheView& cv = a.cache;
-              const int b = mm / a.rm.mseq;
-              const int pos = a.rm.len[b] + a.rm.pos_off + mm % a.rm.mseq;
+              const int row = a.row0 + mm;
+              const int b = row / a.rm.mseq;
+              const int pos = a.rm.len[b] + a.rm.pos_off + row % a.rm.mseq;
               const int kvh = n / cv.hd, dd = n % cv.hd;
               const int64_t idx =
                   ((((int64_t)b * cv.n_layers + a.layer) * cv.n_kv + kvh) * cv.cap + pos) * cv.hd + dd;

@@ -67,8 +67,8 @@ def test_full_shape_two_layer_verify_parity(name, L, K, temp, schedule):
 @pytest.mark.parametrize("K,temp", [(1, 0.0), (2, 1.0), (8, 0.0), (16, 1.0)])
 def test_27b_shape_verify_k_sweep(K, temp):
     """The 27B shape (d 5120, 40/8 heads, FFN 17408, a 4096-entry cache) at the other draft
-    lengths of its workload; K = 16 is 17 rows, past the streamed projections' 16, so that verify
-    runs the per-tile kernels."""
+    lengths of its workload; K = 16 is 17 rows, which the streamed projections take as two passes
+    (rows 0..15, then row 16), each over the whole weight stream."""
     two_layer_verify("qwen27b", 4096, K, temp, "stream")
 
 
