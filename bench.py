@@ -114,11 +114,11 @@ DOMINANT = {
     "stream": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 8> (target gate/up + SwiGLU, weights streamed "
                          "through an LDS ring, one workgroup per CU)",
                "slot": "target.gate_up",
-               "sources": ["stream_core.h", "stream.hip"], "traffic": 202404019, "sha256": "72697b7f71796c5e"},
+               "sources": ["stream_core.h", "stream.hip"], "traffic": 202405029, "sha256": "338e2799e23a26fb"},
     "stream_fp8": {"kernel": "stream_gemm_kernel<EPI_SWIGLU, 4, 1> (target gate/up + SwiGLU over E4M3 weights "
                              "with row scales, streamed through an LDS ring, one workgroup per CU)",
                    "slot": "target.gate_up",
-                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101954426, "sha256": "72697b7f71796c5e"},
+                   "sources": ["stream_core.h", "stream.hip"], "traffic": 101954677, "sha256": "338e2799e23a26fb"},
     "step": {"kernel": "gemm_bf16_kernel<EPI_SWIGLU, 1, NORM, 16> (target gate/up + SwiGLU, one workgroup "
                        "per 16-row tile pair)",
              "slot": "target.gate_up",
