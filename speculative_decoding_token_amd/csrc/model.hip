@@ -1290,6 +1290,11 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
       if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 2>), g1, dim3(256), lds2, st, a);
       else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 2>), g1, dim3(256), lds2, st, a);
       else hipLaunchKernelGGL((attn_chunk_mfma_kernel<32, 2>), g1, dim3(256), lds2, st, a);
+    } else if (hd == 128 && QT == 3) {
+      // (the query loads and their registers scale with the instance's tile count)
+      hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 3>), g1, dim3(256), lds2, st, a);
+    } else if (hd == 128 && QT == 4) {
+      hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 4>), g1, dim3(256), lds2, st, a);
     } else {
       if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 6>), g1, dim3(256), lds2, st, a);
       else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 6>), g1, dim3(256), lds2, st, a);
