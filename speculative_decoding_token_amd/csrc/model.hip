@@ -1286,6 +1286,8 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
     const size_t lds2 = 2 * ((size_t)QT * 16 * (hd + 8) + (size_t)ATTN_CHUNK * (hd + 8) + (size_t)hd * (ATTN_CHUNK + 8));
     if (a.few && hd == 128 && R <= ATTN_FEW_ROWS) {
       hipLaunchKernelGGL(attn_chunk_few_kernel, g1, dim3(256), 0, st, a);
+    } else if (QT == 1 && hd == 128) {
+      hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 1>), g1, dim3(256), lds2, st, a);
     } else if (QT <= 2) {
       if (hd == 128) hipLaunchKernelGGL((attn_chunk_mfma_kernel<128, 2>), g1, dim3(256), lds2, st, a);
       else if (hd == 64) hipLaunchKernelGGL((attn_chunk_mfma_kernel<64, 2>), g1, dim3(256), lds2, st, a);
