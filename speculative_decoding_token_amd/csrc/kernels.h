@@ -143,6 +143,7 @@ struct AttnArgs {
   float scale;
   float* part;         // [M*n_q][nchunk][hd+2]
   int nchunk;
+  int ngrid;           // chunks launched (0: nchunk); covers every position the rows reach
   void* out;           // combine: [M, n_q*hd] model dtype
   const uint32_t* skip;  // draft early stop: when set and non-zero, the launch does nothing
   // bf16, head_dim 128: launches with at most ATTN_FEW_ROWS query rows per kv head run their

@@ -11,6 +11,8 @@
 // Every kernel computes a row's result with the same arithmetic in the same order whatever
 // the number of rows M, so row i of a K+1-row verify is bit-identical to a one-row forward
 // of the same token at the same position.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace spec {
@@ -1279,7 +1281,7 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   const size_t lds = sizeof(float) * ((size_t)R * hd + (size_t)ATTN_CHUNK * (hd + 1) +
                                       (size_t)ATTN_CHUNK * hd + (size_t)R * ATTN_CHUNK + 2 * (size_t)R);
   const int batch = a.rm.M / a.rm.mseq;
-  dim3 g1(a.nchunk, a.cache.n_kv, batch);
+  dim3 g1(a.ngrid > 0 ? std::min(a.ngrid, a.nchunk) : a.nchunk, a.cache.n_kv, batch);
   dim3 g2(a.rm.M * a.n_q);
   if (dtype == SPEC_DTYPE_BF16) {
     const int QT = (R + 15) / 16;

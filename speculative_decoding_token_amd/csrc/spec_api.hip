@@ -124,6 +124,10 @@ struct spec_ctx {
   int cap = 0;
   // host bookkeeping: every sequence's L lies in [len_lo, len_hi]
   int len_lo = 0, len_hi = 0;
+  // attention chunks launched in the current draft_step / verify_step (0 outside them: the
+  // whole capacity): enough for every position the call's rows reach, so that chunks past the
+  // length are not launched; part of the graph key
+  int attn_nch = 0;
   bool started = false;
   Phase phase = IDLE;
   int phase_k = -1, phase_batch = -1;
@@ -484,6 +488,12 @@ bool attn_few(spec_ctx* c, const Model& m) {
          2 * (d.n_q_heads / d.n_kv_heads) <= ATTN_FEW_ROWS;
 }
 
+// Attention chunks to launch for m: those the current draft_step / verify_step can reach (the
+// MTP head keeps its whole capacity: its length follows the target's by its own rule).
+int attn_grid(spec_ctx* c, const Model& m) {
+  return (c->attn_nch > 0 && &m != &c->mtp) ? std::min(c->attn_nch, m.nchunk) : m.nchunk;
+}
+
 // Whether the forwards of m over M rows run on the weight-streaming projections: bf16,
 // at most 16 rows, reduction lengths in whole stages (normalized inputs: d in {1024, 2048,
 // 3072, 4096, 5120}).  The MTP head keeps the per-row-tile kernels: its input projection leaves no
@@ -562,7 +572,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     g.cache = m.cache;
     g.layer = l;
     g.rm = rm;
-    g.pf_nchunk = m.nchunk;  // the attention launch below: grid (nchunk, n_kv, batch)
+    g.pf_nchunk = attn_grid(c, m);  // the attention launch below: grid (chunks, n_kv, batch)
     LAUNCH(c, P + PROF_QKV, proj(EPI_QKV, g));
     AttnArgs at{};
     at.skip = m.skip;
@@ -576,6 +586,7 @@ int run_layers_stream(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     at.scale = 1.0f / sqrtf((float)d.head_dim);
     at.part = m.part;
     at.nchunk = m.nchunk;
+    at.ngrid = attn_grid(c, m);
     at.few = attn_few(c, m);
     at.out = m.attn;
     LAUNCH(c, P + PROF_ATTN, launch_attention(d.dtype, at, c->stream));
@@ -687,6 +698,7 @@ int run_layers(spec_ctx* c, Model& m, int M, RowMap rm, int np) {
     a.scale = 1.0f / sqrtf((float)d.head_dim);
     a.part = m.part;
     a.nchunk = m.nchunk;
+    a.ngrid = attn_grid(c, m);
     a.out = m.attn;
     a.few = attn_few(c, m);
     LAUNCH(c, P + PROF_ATTN, launch_attention(dt, a, st));
@@ -1067,6 +1079,18 @@ int enqueue_verify(spec_ctx* c, const int32_t* draft_tok, int batch, int k, floa
   return SPEC_OK;
 }
 
+// The attention chunks a draft_step / verify_step launches: positions below len_hi + need (the
+// rows it appends), rounded up to 4 chunks (256 positions), so that a growing context takes a
+// new graph every 256 positions; restored to the whole capacity when the call returns.
+struct NchScope {
+  spec_ctx* c;
+  NchScope(spec_ctx* cc, int need) : c(cc) {
+    const int n = (c->len_hi + need + 1) / ATTN_CHUNK + 1;
+    c->attn_nch = (n + 3) / 4 * 4;
+  }
+  ~NchScope() { c->attn_nch = 0; }
+};
+
 // Runs `enqueue` directly, or through a captured graph: the first call with a given
 // (kind, batch, k, buffer addresses) captures the launches on the context stream, later
 // calls replay them.  Every kernel reads lengths and the round from device memory, so a
@@ -1340,6 +1364,7 @@ int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* d
   // the MTP catch-up writes its cache up to mtp_rows - 1 positions past L
   rc = ensure_room(c, batch, std::max(k, kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0) + 1);
   if (rc) return rc;
+  const NchScope nch(c, std::max(k, kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0) + 1);
   const spec_probs qq = *q;
   c->ctl_cycle = c->p_min > 0.0f || c->min_draft > 0;
   if (kind == SPEC_DRAFT_NGRAM) {
@@ -1360,7 +1385,7 @@ int draft_step(spec_ctx* c, int32_t batch, int32_t k, uint64_t round, int32_t* d
     // the threshold is part of the captured launches (the controlled sampling kernel's argument)
     const void* key[8] = {draft_tok, qq.ids, qq.probs, qq.count, (const void*)(intptr_t)qq.cap,
                           (const void*)(intptr_t)(kind == SPEC_DRAFT_MTP ? c->mtp_rows : 0),
-                          (const void*)(uintptr_t)pbits, nullptr};
+                          (const void*)(uintptr_t)pbits, (const void*)(intptr_t)c->attn_nch};
     if (kind == SPEC_DRAFT_MTP)
       rc = run_graphed(c, 2, batch, k, key, [&]() { return enqueue_draft_mtp(c, batch, k, draft_tok, qq); });
     else
@@ -1397,9 +1422,10 @@ int verify_step(spec_ctx* c, const int32_t* draft_tok, int32_t batch, int32_t k,
   }
   rc = ensure_room(c, batch, k + 1);
   if (rc) return rc;
+  const NchScope nch(c, k + 1);
   const spec_probs pp = *p;
   const void* key[8] = {draft_tok, logits_out, pp.ids, pp.probs, pp.count, (const void*)(intptr_t)pp.cap,
-                        nullptr, nullptr};
+                        (const void*)(intptr_t)c->attn_nch, nullptr};
   rc = run_graphed(c, 0, batch, k, key, [&]() { return enqueue_verify(c, draft_tok, batch, k, logits_out, pp); });
   if (rc) return rc;
   c->phase = VERIFIED;
