@@ -355,3 +355,37 @@ def test_pipelined_run_equals_cycle_by_cycle():
         assert all(c.verify_ms is not None and c.verify_ms > 0 for c in cb)
         assert a.cycle(1, 2, 9).tokens == b.cycle(1, 2, 9).tokens
         assert a.lengths(1) == b.lengths(1)
+
+
+def test_graph_replay_across_attention_grid_growth():
+    """The attention launches of a cycle cover only the chunks its rows reach (the host's length
+    bound, in steps of 256 positions), and that count is part of the captured graph's key: a
+    context growing across such a step (cache length 500 -> 540 here, the bound crossing 512)
+    takes new graphs, whose results equal kernel-by-kernel launches bit for bit, cycle after
+    cycle (the 0.6B-shape draft's few-row attention and the 8B-shape target's MFMA attention,
+    one layer each)."""
+    ts = synth.SHAPES["qwen8b"].with_layers(1)
+    ds = synth.SHAPES["qwen0p6b"].with_layers(1)
+    L, K = 500, 4
+    tw = synth.make_weights(ts, 0, device="cuda")
+    dw = synth.make_weights(ds, 1, std=0.05, device="cuda")
+    tk, tv = synth.make_kv_prefix(ts, L, 0, device="cuda")
+    dk, dv = synth.make_kv_prefix(ds, L - 1, 1, device="cuda")
+    prev, last = (int(x) for x in synth.make_tokens(2, ds.vocab, 9))
+    outs = []
+    for graphs in (False, True):
+        eng = runtime.Engine(ts, tw, ds, dw, temperature=0.0, seed=5, max_ctx=L + 100, max_k=K)
+        eng.set_schedule("stream")
+        eng.use_graphs(graphs)
+        eng.load_prefix(0, 0, tk, tv, L)
+        eng.load_prefix(1, 0, dk, dv, L - 1)
+        eng.set_last(torch.tensor([last], dtype=torch.int32, device="cuda"),
+                     torch.tensor([prev], dtype=torch.int32, device="cuda"))
+        cycles = [eng.cycle(1, K, r, keep=True) for r in range(12)]
+        outs.append((cycles, list(eng.lengths(1))))
+        eng.close()
+    (ca, la), (cb, lb) = outs
+    assert la == lb and la[0] >= 512, la
+    for x, y in zip(ca, cb):
+        assert x.tokens == y.tokens and x.drafts == y.drafts
+        assert torch.equal(x.logits, y.logits)
